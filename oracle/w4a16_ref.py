@@ -1,0 +1,285 @@
+"""Plain, slow CPU oracle for the fused W4A16 weight-only matmul.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import this
+module: only the tests, the smoke check and the CPU-baseline leg of the
+benchmark use it.  It shares no code with the HIP library and never reads
+anything the library produced except for the values it is compared against.
+
+What it computes, and where each step comes from (page titles and sections of
+the source pages):
+
+* Group-wise asymmetric INT4 quantisation, one BF16 scale and one INT32 zero
+  point per group of 128 consecutive K-weights -- Axe Corsa model card,
+  "The Two-Stage Pipeline" (asymmetric scheme, groups of 128) and "What the
+  Tensor Types Tell You" (BF16 scales, I32 zero points, packed INT4 codes).
+* The scale/zero/code rule is the affine min/max round-to-nearest quantiser
+  ("Quantization I: int8, int4, the basics", "Concept": a zero point shifts
+  the range, rounding maps nearby reals to one code, clipping maps extremes
+  to the boundary).  Where the pages leave a choice open (fp32 arithmetic,
+  BF16 rounding of the scale toward zero, rounding half away from zero, the
+  unclamped integer zero point, degenerate groups, nibble order) the oracle
+  follows the readings listed in the design notes; each function states its
+  reading.
+* Dequantisation w_hat = (q - z_g) * s_g -- Axe Corsa model card, "The
+  Two-Stage Pipeline", inverse mapping equation.
+* Y = X . W_hat^T accumulated in fp64 (the exact result up to fp64 rounding;
+  the product accumulates in fp32 and stores BF16).
+* AWQ: s_i = importance_i ** alpha, W' = W . diag(s), X' = diag(s)^-1 X folded
+  into the producer -- Axe Corsa model card, "Stage 1: Activation-Aware Weight
+  Scaling".
+
+Every function is deliberately unoptimised: explicit bit manipulation,
+explicit rounding, float64 products.  Vectorisation over whole arrays with
+numpy is used only to apply the same per-element definition everywhere.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+GROUP = 128          # Axe Corsa model card, "The Two-Stage Pipeline": 128 weights per group
+QMAX = 15            # 16 representable unsigned INT4 codes, 0..15
+FLT_MIN = np.float32(2.0 ** -126)
+
+
+# ---------------------------------------------------------------------------
+# BF16 <-> FP32 bit conversions (BF16 = upper 16 bits of an IEEE binary32)
+# ---------------------------------------------------------------------------
+
+def bf16_to_f32(bits) -> np.ndarray:
+    """BF16 bit patterns (uint16) -> float32 values (exact widening)."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def f32_to_bf16_rtz(x) -> np.ndarray:
+    """float32 -> BF16 bits, rounding toward zero: keep the upper 16 bits."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32)
+    return (u >> np.uint32(16)).astype(np.uint16)
+
+
+def f32_to_bf16_rne(x) -> np.ndarray:
+    """float32 -> BF16 bits, round to nearest, ties to even; NaN -> 0x7FC0."""
+    xf = np.asarray(x, dtype=np.float32)
+    u = xf.view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)).astype(np.uint16)
+    return np.where(np.isnan(xf), np.uint16(0x7FC0), r).astype(np.uint16)
+
+
+def round_half_away(v) -> np.ndarray:
+    """Round half away from zero, sign(v) * floor(|v| + 1/2), evaluated in
+    float64 (exact for every float32 input).  Returns float64 integers."""
+    v64 = np.asarray(v, dtype=np.float32).astype(np.float64)
+    return np.sign(v64) * np.floor(np.abs(v64) + 0.5)
+
+
+# ---------------------------------------------------------------------------
+# Quantise (scale, zero point, codes) for one matrix, group by group
+# ---------------------------------------------------------------------------
+
+def group_scale_zero(w_groups: np.ndarray):
+    """Scale and zero point of each group.
+
+    w_groups: float32 [..., 128], the quantiser input of each group.
+    Returns (s_bits uint16 [...], s float32 [...], z int64 [...]).
+
+    Reading of the affine min/max rule (Quantization I, "Concept"; Axe Corsa
+    model card, "The Two-Stage Pipeline": asymmetric, the grid floats to
+    where the weights are, all 16 codes used):
+      D = fl32(max - min); t = fl32(D / 15); s = bf16 of t rounded toward zero.
+      Degenerate group (s zero or subnormal): s = bf16_rtz(max(|min|,|max|)),
+      and 1.0 if that is still zero or subnormal.
+      z = round_half_away(fl32(-min / s)), an unclamped integer (the zero point
+      is an offset on the integer grid, "What the Tensor Types Tell You").
+    """
+    w = np.asarray(w_groups, dtype=np.float32)
+    mn = w.min(axis=-1)
+    mx = w.max(axis=-1)
+    d = (mx - mn).astype(np.float32)
+    t = (d / np.float32(QMAX)).astype(np.float32)
+    s_bits = f32_to_bf16_rtz(t)
+    s = bf16_to_f32(s_bits)
+    degenerate = s < FLT_MIN
+    if np.any(degenerate):
+        m = np.maximum(np.abs(mn), np.abs(mx)).astype(np.float32)
+        alt_bits = f32_to_bf16_rtz(m)
+        alt = bf16_to_f32(alt_bits)
+        alt_bits = np.where(alt < FLT_MIN, np.uint16(0x3F80), alt_bits)  # 1.0
+        s_bits = np.where(degenerate, alt_bits, s_bits).astype(np.uint16)
+        s = bf16_to_f32(s_bits)
+    neg_mn_over_s = (-mn / s).astype(np.float32)
+    z = round_half_away(neg_mn_over_s).astype(np.int64)
+    return s_bits, s, z
+
+
+def group_codes(w_groups: np.ndarray, s: np.ndarray, z: np.ndarray) -> np.ndarray:
+    """Codes q = clamp(round_half_away(fl32(w / s)) + z, 0, 15), rounding
+    against the stored BF16 scale (round-to-nearest on the grid used at
+    dequantisation).  Clipping to the code range follows Quantization I,
+    "Concept".  Returns uint8 [..., 128]."""
+    w = np.asarray(w_groups, dtype=np.float32)
+    ratio = (w / s[..., None]).astype(np.float32)
+    r = round_half_away(ratio).astype(np.int64)
+    q = np.clip(r + z[..., None], 0, QMAX)
+    return q.astype(np.uint8)
+
+
+def quantize(W_bits: np.ndarray, awq_s: np.ndarray | None = None):
+    """Quantise a BF16 weight matrix W [N][K] (uint16 bits) group-wise.
+
+    If awq_s (float32 [K]) is given, the quantiser input is
+    fl32(W[n,k] * awq_s[k]) -- the AWQ rescaled weight W' = W . diag(s)
+    (Axe Corsa model card, "Stage 1: Activation-Aware Weight Scaling").
+
+    Returns (q uint8 [N][K], s_bits uint16 [N][K/128], z int32 [N][K/128]).
+    """
+    W_bits = np.asarray(W_bits, dtype=np.uint16)
+    N, K = W_bits.shape
+    if K % GROUP:
+        raise ValueError("K must be a multiple of 128")
+    w = bf16_to_f32(W_bits)
+    if awq_s is not None:
+        w = (w * np.asarray(awq_s, dtype=np.float32)[None, :]).astype(np.float32)
+    wg = w.reshape(N, K // GROUP, GROUP)
+    s_bits, s, z = group_scale_zero(wg)
+    q = group_codes(wg, s, z).reshape(N, K)
+    if np.any(z > np.iinfo(np.int32).max) or np.any(z < np.iinfo(np.int32).min):
+        raise OverflowError("zero point outside int32 (input outside the documented domain)")
+    return q, s_bits.astype(np.uint16), z.astype(np.int32)
+
+
+# ---------------------------------------------------------------------------
+# Packing: eight 4-bit codes per 32-bit word along K
+# ---------------------------------------------------------------------------
+
+def pack_codes(q: np.ndarray) -> np.ndarray:
+    """q uint8 [N][K] (values 0..15) -> words uint32 [N][K/8].
+
+    Nibble j (bits 4j..4j+3) of word i holds k = 8i + j.  In little-endian
+    byte order each byte then holds two consecutive codes, low nibble first,
+    the byte stream of the compressed-tensors packing (Axe Corsa model card,
+    "What the Tensor Types Tell You": two INT4 values per byte).
+    """
+    q = np.asarray(q, dtype=np.uint32)
+    N, K = q.shape
+    if K % 8:
+        raise ValueError("K must be a multiple of 8")
+    q8 = q.reshape(N, K // 8, 8)
+    words = np.zeros((N, K // 8), dtype=np.uint32)
+    for j in range(8):
+        words |= (q8[:, :, j] & np.uint32(0xF)) << np.uint32(4 * j)
+    return words
+
+
+def unpack_codes(words: np.ndarray) -> np.ndarray:
+    """Inverse of pack_codes: words uint32 [N][K/8] -> q uint8 [N][K]."""
+    w = np.asarray(words, dtype=np.uint32)
+    N, W8 = w.shape
+    q = np.zeros((N, W8, 8), dtype=np.uint8)
+    for j in range(8):
+        q[:, :, j] = ((w >> np.uint32(4 * j)) & np.uint32(0xF)).astype(np.uint8)
+    return q.reshape(N, W8 * 8)
+
+
+def quantize_pack(W_bits: np.ndarray, awq_s: np.ndarray | None = None):
+    """Quantise then pack: returns (codes uint32 [N][K/8], scales uint16
+    [N][K/128] (BF16 bits), zeros int32 [N][K/128])."""
+    q, s_bits, z = quantize(W_bits, awq_s)
+    return pack_codes(q), s_bits, z
+
+
+# ---------------------------------------------------------------------------
+# Dequantise and multiply
+# ---------------------------------------------------------------------------
+
+def dequantize(codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray) -> np.ndarray:
+    """w_hat[n,k] = (q[n,k] - z[n,g]) * s[n,g] in float64, g = k // 128
+    (Axe Corsa model card, "The Two-Stage Pipeline", dequantisation
+    equation).  Exact: the product has at most ~40 significant bits."""
+    q = unpack_codes(codes).astype(np.float64)
+    N, K = q.shape
+    s = bf16_to_f32(scales).astype(np.float64)
+    z = np.asarray(zeros, dtype=np.int64).astype(np.float64)
+    g = np.arange(K) // GROUP
+    return (q - z[:, g]) * s[:, g]
+
+
+def matmul_ref(X_bits: np.ndarray, codes: np.ndarray, scales: np.ndarray,
+               zeros: np.ndarray, rows: np.ndarray | None = None) -> np.ndarray:
+    """Reference output Y[m,n] = sum_k X[m,k] * w_hat[n,k] in float64.
+
+    X_bits: BF16 bits [M][K].  If `rows` is given, only those output columns n
+    are computed (the result has shape [M][len(rows)]).
+    """
+    if rows is not None:
+        codes, scales, zeros = codes[rows], scales[rows], zeros[rows]
+    w_hat = dequantize(codes, scales, zeros)
+    x = bf16_to_f32(X_bits).astype(np.float64)
+    return x @ w_hat.T
+
+
+# ---------------------------------------------------------------------------
+# AWQ (optional fold of the per-input-channel scale into the producer)
+# ---------------------------------------------------------------------------
+
+def awq_importance(Xcal_bits: np.ndarray) -> np.ndarray:
+    """Per-input-channel importance = mean over calibration tokens of |X|.
+    Reading of the stripped importance formula in the Axe Corsa model card,
+    "Stage 1: Activation-Aware Weight Scaling" (per-channel activation
+    magnitudes).  Float64 mean, returned as float64 [K]."""
+    x = bf16_to_f32(Xcal_bits).astype(np.float64)
+    return np.abs(x).mean(axis=0)
+
+
+def awq_scale(importance: np.ndarray, alpha: float) -> np.ndarray:
+    """s_i = importance_i ** alpha (Axe Corsa model card, "Stage 1"), in
+    float64, rounded to float32."""
+    imp = np.asarray(importance, dtype=np.float64)
+    return np.power(imp, np.float64(alpha)).astype(np.float32)
+
+
+def awq_fold(s: np.ndarray, gamma_bits: np.ndarray) -> np.ndarray:
+    """Fold X' = diag(s)^-1 X into the producer's per-channel weight:
+    gamma'[k] = bf16_rne(fl32(gamma[k] / s[k])) (Axe Corsa model card,
+    "Stage 1": the division is absorbed into the preceding LayerNorm)."""
+    g = bf16_to_f32(gamma_bits)
+    return f32_to_bf16_rne((g / np.asarray(s, dtype=np.float32)).astype(np.float32))
+
+
+def apply_channel_scale(X_bits: np.ndarray, gamma_bits: np.ndarray) -> np.ndarray:
+    """The producer's output with a folded per-channel weight:
+    X'[m,k] = bf16_rne(fl32(X[m,k] * gamma[k]))."""
+    x = bf16_to_f32(X_bits)
+    g = bf16_to_f32(gamma_bits)
+    return f32_to_bf16_rne((x * g[None, :]).astype(np.float32))
+
+
+# ---------------------------------------------------------------------------
+# Parity gates on the floating-point output
+# ---------------------------------------------------------------------------
+
+REL_L2_TOL = 2e-3     # relative L2 error of the BF16 output
+ELEM_TOL = 1e-2       # per element: |err| <= ELEM_TOL * (|ref| + 1)
+
+
+def output_errors(y, y_ref):
+    """Returns (relative L2 error, max over elements of |err| / (|ref|+1))."""
+    y = np.asarray(y, dtype=np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    err = y - y_ref
+    denom = np.linalg.norm(y_ref)
+    rel = float(np.linalg.norm(err) / denom) if denom > 0 else float(np.linalg.norm(err))
+    elem = float(np.max(np.abs(err) / (np.abs(y_ref) + 1.0))) if err.size else 0.0
+    return rel, elem
+
+
+def output_ok(y, y_ref) -> bool:
+    rel, elem = output_errors(y, y_ref)
+    return rel <= REL_L2_TOL and elem <= ELEM_TOL
+
+
+def storage_bytes(N: int, K: int) -> int:
+    """Bytes of the packed format: N*K/2 codes + 2 B scale + 4 B zero per
+    group of 128 (Axe Corsa model card, "Storage Cost")."""
+    return N * K // 2 + (N * K // GROUP) * (2 + 4)

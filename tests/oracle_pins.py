@@ -1,0 +1,424 @@
+"""Pins that tie the CPU oracle to facts fixed outside itself.
+
+Each check raises AssertionError on failure.  They are collected by
+test_oracle_pins.py and reused by test_oracle_mutations.py, which plants
+plausible mistakes in the oracle and asserts that some check catches each.
+
+Sources of truth used here (never the oracle's own formulas retyped):
+* closed forms derived by hand for constructed groups (derivations inline),
+* the figures the pages print (tests/golden/storage_cost.json),
+* library routines for special cases: torch's float32->bfloat16 conversion
+  (round to nearest even), Python's decimal ROUND_HALF_UP (half away from
+  zero), fractions.Fraction for exact rational arithmetic,
+* brute force over all 16 codes on tiny inputs,
+* invariants the pages state (all 16 codes used; output unchanged when the
+  weights already lie on the grid).
+"""
+
+from __future__ import annotations
+
+import decimal
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _bf16_bits_of(values) -> np.ndarray:
+    """Exact float -> BF16 bits for values known to be BF16-representable."""
+    f = np.asarray(values, dtype=np.float32)
+    u = f.view(np.uint32)
+    assert np.all((u & 0xFFFF) == 0), "value not exactly representable in BF16"
+    return (u >> 16).astype(np.uint16)
+
+
+def _frac_of_f32(x) -> Fraction:
+    return Fraction(float(np.float32(x)))
+
+
+# ---------------------------------------------------------------------------
+# Conversions and rounding
+# ---------------------------------------------------------------------------
+
+def check_bf16_rne_matches_torch(seed=1):
+    rng = np.random.default_rng(seed)
+    u = rng.integers(0, 2**32, size=200000, dtype=np.uint64).astype(np.uint32)
+    # add exact ties and near-ties around the rounding boundary
+    base = rng.integers(0, 2**16, size=20000, dtype=np.uint64).astype(np.uint32) << 16
+    ties = np.concatenate([base | 0x8000, base | 0x7FFF, base | 0x8001])
+    u = np.concatenate([u, ties]).astype(np.uint32)
+    f = u.view(np.float32)
+    finite = np.isfinite(f)
+    f = f[finite]
+    ours = O.f32_to_bf16_rne(f)
+    ref = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref), "f32->bf16 RNE disagrees with torch"
+    # widening is exact
+    back = O.bf16_to_f32(ref)
+    ref_back = torch.from_numpy(ref.view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+    assert np.array_equal(back.view(np.uint32), ref_back.view(np.uint32))
+
+
+def check_bf16_rtz_hand():
+    # 0x3F80FFFF = 1 + (2^16-1) * 2^-23: truncation keeps 0x3F80, RNE gives 0x3F81
+    x = np.array([0x3F80FFFF, 0xBF80FFFF, 0x3DCCCCCD, 0x3F800000, 0x00000001],
+                 dtype=np.uint32).view(np.float32)
+    assert list(O.f32_to_bf16_rtz(x)) == [0x3F80, 0xBF80, 0x3DCC, 0x3F80, 0x0000]
+    assert list(O.f32_to_bf16_rne(x)) == [0x3F81, 0xBF81, 0x3DCD, 0x3F80, 0x0000]
+
+
+def check_round_half_away(seed=2):
+    hand = {2.5: 3, -2.5: -3, 0.5: 1, -0.5: -1, 1.5: 2, -1.5: -2, 6.5: 7,
+            0.49999997: 0, -0.49999997: 0, 0.0: 0, 7.0: 7, -8.0: -8}
+    for v, r in hand.items():
+        assert O.round_half_away(np.float32(v)) == r, (v, r)
+    rng = np.random.default_rng(seed)
+    vals = np.concatenate([
+        rng.normal(0, 20, size=3000).astype(np.float32),
+        (rng.integers(-40, 40, size=1000) + 0.5).astype(np.float32),
+    ])
+    ours = O.round_half_away(vals)
+    for v, r in zip(vals, ours):
+        d = decimal.Decimal(float(v)).quantize(decimal.Decimal(1), rounding=decimal.ROUND_HALF_UP)
+        assert int(d) == int(r), (float(v), int(d), r)
+
+
+# ---------------------------------------------------------------------------
+# Hand-built groups with closed-form scale, zero point and codes
+# ---------------------------------------------------------------------------
+
+def _quantize_group(values):
+    W = _bf16_bits_of(values).reshape(1, 128)
+    q, s_bits, z = O.quantize(W)
+    return q[0], int(s_bits[0, 0]), int(z[0, 0])
+
+
+def check_hand_groups():
+    j = np.arange(128) % 16
+
+    # G1: w = (j - 8) * 2^-7.  min = -8*2^-7, max = 7*2^-7, D = 15*2^-7,
+    # t = 2^-7 exactly -> s = 2^-7 (bits 0x3C00); z = -min/s = 8; q = j.
+    q, s, z = _quantize_group((j - 8) * 2.0 ** -7)
+    assert (s, z) == (0x3C00, 8)
+    assert np.array_equal(q, j)
+    words = O.pack_codes(q.reshape(1, 128))
+    assert list(words[0, :2]) == [0x76543210, 0xFEDCBA98]
+    assert np.array_equal(words[0], np.tile(np.array([0x76543210, 0xFEDCBA98], np.uint32), 8))
+
+    # G2: all positive, w = 1 + j/16.  D = 15/16, s = 1/16 (0x3D80),
+    # z = -16 (negative zero point), q = j.
+    q, s, z = _quantize_group(1.0 + j / 16.0)
+    assert (s, z) == (0x3D80, -16)
+    assert np.array_equal(q, j)
+
+    # G3: exact ties.  Start from G1 (s = 2^-7, z = 8) and put +-2.5 s and
+    # 0.5 s at some positions: half away from zero gives 3 / -3 / 1, so the
+    # codes are 11 / 5 / 9 (ties-to-even would give 10 / 6 / 8).
+    v = (j - 8) * 2.0 ** -7
+    v[16], v[17], v[18] = 2.5 * 2.0 ** -7, -2.5 * 2.0 ** -7, 0.5 * 2.0 ** -7
+    q, s, z = _quantize_group(v)
+    assert (s, z) == (0x3C00, 8)
+    assert (q[16], q[17], q[18]) == (11, 5, 9)
+
+    # G4: zero-point tie.  min = -6.5 s, max = 8.5 s with s = 2^-7:
+    # D = 15 s -> s exact; -min/s = 6.5 -> z = 7; q(min) = -7 + 7 = 0,
+    # q(max) = 9 + 7 = 16 -> clipped to 15.
+    v = np.full(128, 0.0)
+    v[0], v[1] = -6.5 * 2.0 ** -7, 8.5 * 2.0 ** -7
+    q, s, z = _quantize_group(v)
+    assert (s, z) == (0x3C00, 7)
+    assert (q[0], q[1], q[2]) == (0, 15, 7)
+
+    # G5: BF16 scale rounds toward zero.  min = -0.5, max = 1.0: D = 1.5,
+    # t = fl32(0.1) = 0x3DCCCCCD, s = 0x3DCC (RNE would give 0x3DCD).
+    v = np.zeros(128)
+    v[0], v[1] = -0.5, 1.0
+    q, s, z = _quantize_group(v)
+    assert s == 0x3DCC
+    s_f = np.float32(np.array([0x3DCC0000], np.uint32).view(np.float32)[0])
+    # z = round(0.5 / 0.099609375 = 5.0196) = 5; q(max) = round(10.039) + 5 = 15
+    assert z == 5 and q[0] == 0 and q[1] == 15
+    assert s_f == np.float32(0.099609375)
+
+    # G6: constant groups reconstruct exactly: c = 0.375 -> degenerate,
+    # s = 0.375 (0x3EC0), z = -1, q = 0, w_hat = (0 - (-1)) * 0.375.
+    q, s, z = _quantize_group(np.full(128, 0.375))
+    assert (s, z) == (0x3EC0, -1) and np.all(q == 0)
+    q, s, z = _quantize_group(np.full(128, -0.375))
+    assert (s, z) == (0x3EC0, 1) and np.all(q == 0)
+
+    # G7: all zero -> s = 1.0 (0x3F80), z = 0, q = 0.
+    q, s, z = _quantize_group(np.zeros(128))
+    assert (s, z) == (0x3F80, 0) and np.all(q == 0)
+
+    # G8: subnormal constant 2^-130 -> degenerate, the fallback scale is
+    # itself subnormal, so s = 1.0, z = 0, q = 0 (w_hat = 0).
+    q, s, z = _quantize_group(np.full(128, 2.0 ** -130))
+    assert (s, z) == (0x3F80, 0) and np.all(q == 0)
+
+    # G9: +-2^-125: D/15 is subnormal -> degenerate; s = 2^-125 (0x0100),
+    # z = 1, codes 0 and 2, reconstructing -2^-125 and +2^-125 exactly.
+    v = np.where(np.arange(128) % 2 == 0, -(2.0 ** -125), 2.0 ** -125)
+    q, s, z = _quantize_group(v)
+    assert (s, z) == (0x0100, 1)
+    assert np.all(q[0::2] == 0) and np.all(q[1::2] == 2)
+
+
+def check_dequant_closed_form():
+    # codes j, z = 8, s = 2^-7 -> w_hat = (j - 8) * 2^-7; plus a second group
+    # with z = -16, s = 1/16 -> w_hat = 1 + j/16.  K = 256, two groups.
+    j = np.arange(128) % 16
+    q = np.concatenate([j, j]).reshape(1, 256).astype(np.uint8)
+    codes = O.pack_codes(q)
+    scales = np.array([[0x3C00, 0x3D80]], dtype=np.uint16)
+    zeros = np.array([[8, -16]], dtype=np.int32)
+    w = O.dequantize(codes, scales, zeros)[0]
+    assert np.array_equal(w[:128], (j - 8) * 2.0 ** -7)
+    assert np.array_equal(w[128:], 1.0 + j / 16.0)
+
+
+# ---------------------------------------------------------------------------
+# Packing layout
+# ---------------------------------------------------------------------------
+
+def check_pack_layout(seed=3):
+    rng = np.random.default_rng(seed)
+    q = rng.integers(0, 16, size=(5, 64), dtype=np.uint8)
+    words = O.pack_codes(q)
+    assert words.dtype == np.uint32 and words.shape == (5, 8)
+    # byte stream: byte b holds k = 2b in the low nibble and k = 2b + 1 in the
+    # high nibble (two codes per byte, consecutive along K)
+    byts = words.astype("<u4").view(np.uint8).reshape(5, 32)
+    expect = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+    assert np.array_equal(byts, expect)
+    assert np.array_equal(O.unpack_codes(words), q)
+
+
+# ---------------------------------------------------------------------------
+# Invariants on generated groups (the pages: all 16 INT4 values used)
+# ---------------------------------------------------------------------------
+
+def check_min_max_codes(W_bits):
+    q, s_bits, z = O.quantize(W_bits)
+    N, K = W_bits.shape
+    w = O.bf16_to_f32(W_bits).reshape(N, K // 128, 128)
+    qg = q.reshape(N, K // 128, 128)
+    imin = w.argmin(axis=-1)
+    imax = w.argmax(axis=-1)
+    qmin = np.take_along_axis(qg, imin[..., None], -1)[..., 0]
+    qmax = np.take_along_axis(qg, imax[..., None], -1)[..., 0]
+    assert np.all(qmin == 0), "the group minimum must map to code 0"
+    mn, mx = w.min(-1), w.max(-1)
+    straddles = (mn <= 0) & (mx >= 0) & (mx > mn)
+    assert np.all(qmax[straddles] == 15), "the group maximum must map to code 15"
+    # scale brackets the exact step: s <= D/15 < s * (1 + 2^-7)
+    s = O.bf16_to_f32(s_bits).astype(np.float64)
+    D = (mx.astype(np.float64) - mn.astype(np.float64))
+    nz = D > 0
+    assert np.all(s[nz] <= D[nz] / 15 * (1 + 2.0 ** -23))
+    assert np.all(D[nz] / 15 < s[nz] * (1 + 2.0 ** -7) * (1 + 2.0 ** -22))
+    return straddles.mean()
+
+
+def check_all_codes_on_grid(seed=4, N=64, K=512):
+    """Weights that lie exactly on a grid (q0 - z0) * s0 come back unchanged:
+    pack returns (q0, s0, z0) and every group uses all 16 codes."""
+    rng = np.random.default_rng(seed)
+    G = K // 128
+    q0 = rng.integers(0, 16, size=(N, G, 128))
+    q0[:, :, 0] = 0
+    q0[:, :, 1] = 15
+    for n in range(N):                      # all 16 codes in every group
+        for g in range(G):
+            q0[n, g, 2:18] = rng.permutation(16)
+    z0 = rng.integers(0, 16, size=(N, G))
+    mant = 1.0 + rng.integers(0, 8, size=(N, G)) / 8.0          # <= 4 significant bits
+    s0 = mant * 2.0 ** rng.integers(-12, -2, size=(N, G))
+    w = (q0 - z0[..., None]) * s0[..., None]
+    W_bits = _bf16_bits_of(w.reshape(N, K).astype(np.float32))
+    q, s_bits, z = O.quantize(W_bits)
+    assert np.array_equal(q.reshape(N, G, 128), q0)
+    assert np.array_equal(z, z0)
+    assert np.array_equal(O.bf16_to_f32(s_bits).astype(np.float64), s0)
+    for n in range(N):
+        for g in range(G):
+            assert len(np.unique(q.reshape(N, G, 128)[n, g])) == 16
+    return W_bits, (q, s_bits, z)
+
+
+def check_on_grid_matmul_exact(seed=5):
+    """On-grid weights: the reference output equals the unquantised matmul,
+    exactly (inputs on coarse grids so every fp64 sum is exact)."""
+    W_bits, _ = check_all_codes_on_grid(seed, N=48, K=384)
+    rng = np.random.default_rng(seed + 100)
+    x = (rng.integers(-255, 256, size=(6, 384)) / 8.0).astype(np.float32)
+    X_bits = _bf16_bits_of(x)
+    codes, scales, zeros = O.quantize_pack(W_bits)
+    y = O.matmul_ref(X_bits, codes, scales, zeros)
+    w = O.bf16_to_f32(W_bits).astype(np.float64)
+    exact = x.astype(np.float64) @ w.T
+    assert y.shape == (6, 48)
+    assert np.array_equal(y, exact)
+    rows = np.array([47, 3, 10])
+    assert np.array_equal(O.matmul_ref(X_bits, codes, scales, zeros, rows=rows), exact[:, rows])
+
+
+# ---------------------------------------------------------------------------
+# Brute force on tiny inputs (exact rationals)
+# ---------------------------------------------------------------------------
+
+def check_brute_force(seed=6, M=4, K=128, N=8):
+    rng = np.random.default_rng(seed)
+    w = (rng.normal(0, 0.02, size=(N, K)) + rng.uniform(-0.01, 0.01, size=(N, 1))).astype(np.float32)
+    W_bits = O.f32_to_bf16_rne(w)
+    x = rng.normal(0, 1, size=(M, K)).astype(np.float32)
+    X_bits = O.f32_to_bf16_rne(x)
+    q, s_bits, z = O.quantize(W_bits)
+    wf = O.bf16_to_f32(W_bits)
+    near_ties = 0
+    for n in range(N):
+        for g in range(K // 128):
+            s = _frac_of_f32(O.bf16_to_f32(s_bits[n, g]))
+            zz = int(z[n, g])
+            for k in range(g * 128, (g + 1) * 128):
+                wk = _frac_of_f32(wf[n, k])
+                # argmin over the 16 codes of |w - (c - z) s|, ties away from zero
+                best = min(range(16), key=lambda c: (abs(wk - (c - zz) * s), -abs(c - zz)))
+                if best != q[n, k]:
+                    r = wk / s
+                    frac = r - (r.numerator // r.denominator)
+                    assert abs(frac - Fraction(1, 2)) < abs(r) * Fraction(1, 2 ** 22), \
+                        (n, k, best, q[n, k])
+                    near_ties += 1
+    # output: exact rational sum vs the fp64 reference
+    codes, scales, zeros = O.pack_codes(q), s_bits, z
+    y = O.matmul_ref(X_bits, codes, scales, zeros)
+    xf = O.bf16_to_f32(X_bits)
+    for m in range(M):
+        for n in range(N):
+            acc = Fraction(0)
+            mag = Fraction(0)
+            for k in range(K):
+                g = k // 128
+                s = _frac_of_f32(O.bf16_to_f32(s_bits[n, g]))
+                term = _frac_of_f32(xf[m, k]) * (int(q[n, k]) - int(z[n, g])) * s
+                acc += term
+                mag += abs(term)
+            assert abs(Fraction(float(y[m, n])) - acc) <= mag * Fraction(1, 2 ** 45), (m, n)
+    return near_ties
+
+
+# ---------------------------------------------------------------------------
+# AWQ pieces
+# ---------------------------------------------------------------------------
+
+def check_awq_prescale_power_of_two(seed=7):
+    """Scaling every input channel by 2 doubles each group's scale and leaves
+    codes and zero points unchanged (the quantiser input is W * s)."""
+    rng = np.random.default_rng(seed)
+    W_bits = O.f32_to_bf16_rne(rng.normal(0, 0.02, size=(16, 256)).astype(np.float32))
+    q1, s1, z1 = O.quantize(W_bits)
+    q2, s2, z2 = O.quantize(W_bits, awq_s=np.full(256, 2.0, np.float32))
+    assert np.array_equal(q1, q2) and np.array_equal(z1, z2)
+    assert np.array_equal(O.bf16_to_f32(s2), 2 * O.bf16_to_f32(s1))
+    # a per-channel scale that only touches channel 5 changes only groups 0
+    s = np.ones(256, np.float32)
+    s[5] = 4.0
+    q3, s3, z3 = O.quantize(W_bits, awq_s=s)
+    assert np.array_equal(s3[:, 1], s1[:, 1]) and np.array_equal(q3[:, 128:], q1[:, 128:])
+    w = O.bf16_to_f32(W_bits).astype(np.float64)
+    w[:, 5] *= 4.0
+    wg = w[:, :128]
+    D = wg.max(1) - wg.min(1)
+    s3f = O.bf16_to_f32(s3[:, 0]).astype(np.float64)
+    assert np.all(s3f <= D / 15 * (1 + 2.0 ** -23)) and np.all(D / 15 < s3f * (1 + 2.0 ** -6))
+
+
+def check_awq_fold_hand():
+    g = _bf16_bits_of(np.array([1.0, 1.0, -0.75, 3.0], np.float32))
+    s = np.array([2.0, 3.0, 0.5, 1.0], np.float32)
+    # 1/2 = 0.5 (0x3F00); fl32(1/3) = 0x3EAAAAAB -> RNE 0x3EAB; -1.5 = 0xBFC0; 3 = 0x4040
+    assert list(O.awq_fold(s, g)) == [0x3F00, 0x3EAB, 0xBFC0, 0x4040]
+    # the producer output after folding: X' = X * gamma' (bf16 RNE)
+    X = _bf16_bits_of(np.array([[2.0, 3.0, 1.0, -1.0]], np.float32))
+    assert list(O.apply_channel_scale(X, O.awq_fold(s, g))[0]) == [0x3F80, 0x3F80, 0xBFC0, 0xC040]
+
+
+def check_awq_importance_and_scale(seed=8):
+    rng = np.random.default_rng(seed)
+    x = O.f32_to_bf16_rne(rng.normal(0, 1, size=(7, 5)).astype(np.float32))
+    imp = O.awq_importance(x)
+    xf = O.bf16_to_f32(x)
+    for k in range(5):
+        exact = sum(abs(_frac_of_f32(xf[t, k])) for t in range(7)) / 7
+        assert abs(Fraction(float(imp[k])) - exact) <= exact * Fraction(1, 2 ** 50)
+    # alpha = 1/2 is the square root (correctly rounded in float64, then fp32)
+    v = np.abs(rng.normal(0, 3, size=1000)) + 1e-3
+    assert np.array_equal(O.awq_scale(v, 0.5), np.sqrt(v).astype(np.float32))
+    assert np.array_equal(O.awq_scale(v, 1.0), v.astype(np.float32))
+    assert np.all(O.awq_scale(v, 0.0) == 1.0)
+
+
+def check_awq_equivalence_unquantised(seed=9):
+    """(X/s) (W diag(s))^T = X W^T: the fold leaves the output unchanged
+    before any quantisation; with the BF16 rounding of X' the mismatch is at
+    BF16 resolution."""
+    rng = np.random.default_rng(seed)
+    K, N, M = 256, 32, 4
+    W_bits = O.f32_to_bf16_rne(rng.normal(0, 0.02, size=(N, K)).astype(np.float32))
+    X_bits = O.f32_to_bf16_rne(rng.normal(0, 1, size=(M, K)).astype(np.float32))
+    imp = O.awq_importance(X_bits)
+    s = O.awq_scale(imp, 0.5)
+    w = O.bf16_to_f32(W_bits).astype(np.float64)
+    x = O.bf16_to_f32(X_bits).astype(np.float64)
+    s64 = s.astype(np.float64)
+    y0 = x @ w.T
+    y1 = (x / s64) @ (w * s64).T
+    assert np.max(np.abs(y1 - y0)) <= 1e-12 * np.max(np.abs(y0))
+    one = _bf16_bits_of(np.ones(K, np.float32))
+    xp = O.bf16_to_f32(O.apply_channel_scale(X_bits, O.awq_fold(s, one))).astype(np.float64)
+    w_s = (O.bf16_to_f32(W_bits) * s).astype(np.float32).astype(np.float64)
+    y2 = xp @ w_s.T
+    assert np.linalg.norm(y2 - y0) / np.linalg.norm(y0) < 2.0 ** -7
+
+
+# ---------------------------------------------------------------------------
+# Storage cost (figures printed on the pages)
+# ---------------------------------------------------------------------------
+
+def check_storage_cost():
+    with open(os.path.join(GOLDEN, "storage_cost.json")) as f:
+        gold = json.load(f)
+    N, K = 4096, 4096
+    q = np.zeros((N, K), np.uint8)
+    codes = O.pack_codes(q)
+    s_bits = np.zeros((N, K // 128), np.uint16)
+    z = np.zeros((N, K // 128), np.int32)
+    nbytes = codes.nbytes + s_bits.nbytes + z.nbytes
+    assert nbytes == O.storage_bytes(N, K)
+    bits = 8 * nbytes / (N * K)
+    assert bits == gold["bits_per_weight"]["value"]
+    assert abs(16 / bits - gold["compression_vs_bf16"]["value"]) <= gold["compression_vs_bf16"]["rounding"]
+    g = gold["quantised_layers_27b_gb"]
+    gb = g["params"] * bits / 8 / 1e9
+    assert g["low"] <= gb <= g["high"], gb
+    assert 2 * gold["bf16_27b_gb"]["params"] / 1e9 == gold["bf16_27b_gb"]["value"]
+    assert 0.5 * gold["int4_floor_27b_gb"]["params"] / 1e9 == gold["int4_floor_27b_gb"]["value"]
+    assert 2 * gold["bf16_70b_gb"]["params"] / 1e9 == gold["bf16_70b_gb"]["value"]
+
+
+def check_output_gate():
+    """The tolerance gate itself: BF16 rounding of an exact output passes,
+    a 1% perturbation fails."""
+    rng = np.random.default_rng(10)
+    y = rng.normal(0, 3, size=(8, 512))
+    yb = O.bf16_to_f32(O.f32_to_bf16_rne(y.astype(np.float32))).astype(np.float64)
+    assert O.output_ok(yb, y)
+    assert not O.output_ok(y * 1.01, y)
+    assert not O.output_ok(y + np.where(np.arange(512) == 7, 0.5, 0.0), y)

@@ -1,0 +1,156 @@
+"""Plant plausible mistakes in the CPU oracle and check that a pin catches
+each one.  The mutations live only here, on the CPU, inside monkeypatch."""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.w4a16_ref as R
+import oracle_pins as P
+
+ALL_PINS = [
+    P.check_hand_groups, P.check_dequant_closed_form, P.check_pack_layout,
+    P.check_all_codes_on_grid, P.check_on_grid_matmul_exact,
+    lambda: P.check_brute_force(seed=11, M=3, K=384, N=5),
+    P.check_awq_prescale_power_of_two, P.check_awq_fold_hand,
+    P.check_awq_importance_and_scale, P.check_awq_equivalence_unquantised,
+    P.check_storage_cost,
+]
+
+
+def _patch(monkeypatch, name, fn):
+    monkeypatch.setattr(R, name, fn)
+    monkeypatch.setattr(oracle, name, fn)
+
+
+def _some_pin_fails():
+    failed = 0
+    for pin in ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except (AssertionError, ValueError, OverflowError, ZeroDivisionError, IndexError):
+            failed += 1
+    return failed
+
+
+def _half_even(v):
+    return np.round(np.asarray(v, dtype=np.float32).astype(np.float64))
+
+
+def _scale_rne(x):
+    return R.f32_to_bf16_rne(x)
+
+
+def _pack_reversed(q):
+    q = np.asarray(q, dtype=np.uint32)
+    N, K = q.shape
+    q8 = q.reshape(N, K // 8, 8)
+    w = np.zeros((N, K // 8), np.uint32)
+    for j in range(8):
+        w |= q8[:, :, 7 - j] << np.uint32(4 * j)
+    return w
+
+
+def _dequant_sign(codes, scales, zeros):
+    q = R.unpack_codes(codes).astype(np.float64)
+    K = q.shape[1]
+    s = R.bf16_to_f32(scales).astype(np.float64)
+    z = np.asarray(zeros, np.float64)
+    g = np.arange(K) // 128
+    return (z[:, g] - q) * s[:, g]
+
+
+def _dequant_group_index(codes, scales, zeros):
+    q = R.unpack_codes(codes).astype(np.float64)
+    K = q.shape[1]
+    s = R.bf16_to_f32(scales).astype(np.float64)
+    z = np.asarray(zeros, np.float64)
+    g = np.arange(K) % s.shape[1]
+    return (q - z[:, g]) * s[:, g]
+
+
+def _matmul_transposed(X_bits, codes, scales, zeros, rows=None):
+    if rows is not None:
+        codes, scales, zeros = codes[rows], scales[rows], zeros[rows]
+    w = R.dequantize(codes, scales, zeros)
+    x = R.bf16_to_f32(X_bits).astype(np.float64)
+    return (w @ x.T)
+
+
+def _scale_zero_clamped(wg):
+    s_bits, s, z = ORIG["group_scale_zero"](wg)
+    return s_bits, s, np.clip(z, 0, 15)
+
+
+def _scale_zero_no_degenerate(wg):
+    w = np.asarray(wg, dtype=np.float32)
+    mn, mx = w.min(-1), w.max(-1)
+    t = ((mx - mn) / np.float32(15)).astype(np.float32)
+    s_bits = R.f32_to_bf16_rtz(t)
+    s = R.bf16_to_f32(s_bits)
+    z = R.round_half_away((-mn / s).astype(np.float32)).astype(np.int64)
+    return s_bits, s, z
+
+
+def _scale_zero_div16(wg):
+    w = np.asarray(wg, dtype=np.float32)
+    mn, mx = w.min(-1), w.max(-1)
+    t = ((mx - mn) / np.float32(16)).astype(np.float32)
+    s_bits = R.f32_to_bf16_rtz(t)
+    s = R.bf16_to_f32(s_bits)
+    s_bits = np.where(s < R.FLT_MIN, np.uint16(0x3F80), s_bits).astype(np.uint16)
+    s = R.bf16_to_f32(s_bits)
+    z = R.round_half_away((-mn / s).astype(np.float32)).astype(np.int64)
+    return s_bits, s, z
+
+
+def _codes_against_unrounded(wg, s, z):
+    w = np.asarray(wg, dtype=np.float32)
+    mn, mx = w.min(-1), w.max(-1)
+    t = ((mx - mn) / np.float32(15)).astype(np.float32)
+    t = np.where(t > 0, t, s).astype(np.float32)
+    r = R.round_half_away((w / t[..., None]).astype(np.float32)).astype(np.int64)
+    return np.clip(r + z[..., None], 0, 15).astype(np.uint8)
+
+
+def _quantize_ignores_awq(W_bits, awq_s=None):
+    return ORIG["quantize"](W_bits, None)
+
+
+def _fold_multiplies(s, gamma_bits):
+    g = R.bf16_to_f32(gamma_bits)
+    return R.f32_to_bf16_rne((g * np.asarray(s, np.float32)).astype(np.float32))
+
+
+def _importance_no_abs(Xcal_bits):
+    return R.bf16_to_f32(Xcal_bits).astype(np.float64).mean(axis=0)
+
+
+ORIG = {n: getattr(R, n) for n in ["group_scale_zero", "quantize"]}
+
+MUTATIONS = {
+    "ties_to_even": ("round_half_away", _half_even),
+    "scale_round_nearest": ("f32_to_bf16_rtz", _scale_rne),
+    "nibble_order_reversed": ("pack_codes", _pack_reversed),
+    "dequant_sign_flipped": ("dequantize", _dequant_sign),
+    "dequant_wrong_group": ("dequantize", _dequant_group_index),
+    "matmul_transposed": ("matmul_ref", _matmul_transposed),
+    "zero_point_clamped": ("group_scale_zero", _scale_zero_clamped),
+    "no_degenerate_rule": ("group_scale_zero", _scale_zero_no_degenerate),
+    "divide_by_16": ("group_scale_zero", _scale_zero_div16),
+    "codes_vs_unrounded_scale": ("group_codes", _codes_against_unrounded),
+    "awq_scale_ignored": ("quantize", _quantize_ignores_awq),
+    "fold_multiplies": ("awq_fold", _fold_multiplies),
+    "importance_without_abs": ("awq_importance", _importance_no_abs),
+}
+
+
+def test_unmutated_oracle_passes_all_pins():
+    assert _some_pin_fails() == 0
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(monkeypatch, name):
+    target, fn = MUTATIONS[name]
+    _patch(monkeypatch, target, fn)
+    assert _some_pin_fails() > 0, f"no pin catches mutation {name}"
