@@ -1,0 +1,199 @@
+"""Thin Python binding of the W4A16 HIP library (libw4a16.so).
+
+The functions below carry the names of the C entry points in
+include/w4a16.h and only marshal arguments: they check dtypes, devices and
+shapes of torch tensors, allocate outputs with torch, pass raw device
+pointers and the current HIP stream to the library, and turn a non-zero
+status into an exception.  Every arithmetic step runs in the library's
+kernels; there is no fallback path.  If the library is missing the import
+of this package fails loudly.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libw4a16.so")
+
+GROUP = 128
+GEMV_MAX_M = 32
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build the HIP library first "
+        "(python -m int4_weight_only_gemv_amd.build)")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_SIGS = {
+    "w4a16_abi_version": ([], ctypes.c_int),
+    "w4a16_strerror": ([ctypes.c_int], ctypes.c_char_p),
+    "w4a16_pack": ([_p, _i64, _i64, _i64, _p, _p, _p, _p, _p], ctypes.c_int),
+    "w4a16_gemv": ([_p, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _i64, _p], ctypes.c_int),
+    "w4a16_gemm": ([_p, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _i64, _p], ctypes.c_int),
+    "w4a16_awq_importance": ([_p, _i64, _i64, _i64, _p, _p], ctypes.c_int),
+    "w4a16_awq_scale": ([_p, _i64, ctypes.c_float, _p, _p], ctypes.c_int),
+    "w4a16_awq_fold": ([_p, _i64, _p, _p, _p], ctypes.c_int),
+    "w4a16_scale_channels": ([_p, _i64, _i64, _i64, _p, _p, _i64, _p], ctypes.c_int),
+}
+for _name, (_args, _ret) in _SIGS.items():
+    _f = getattr(lib, _name)
+    _f.argtypes = _args
+    _f.restype = _ret
+
+EXPORTS = tuple(_SIGS)
+
+
+class W4A16Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed with status {status}: {lib.w4a16_strerror(status).decode()}")
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise W4A16Error(fn, status)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _need(t: torch.Tensor, dtype, name: str, ndim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on a GPU")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims")
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name} must be contiguous along its last dim")
+
+
+def abi_version() -> int:
+    return lib.w4a16_abi_version()
+
+
+class PackedLinear:
+    """A packed weight matrix: codes [N][K/8] int32 (uint32 bits),
+    scales [N][K/128] bfloat16, zeros [N][K/128] int32."""
+
+    __slots__ = ("codes", "scales", "zeros", "N", "K")
+
+    def __init__(self, codes, scales, zeros):
+        self.codes, self.scales, self.zeros = codes, scales, zeros
+        self.N = codes.shape[0]
+        self.K = codes.shape[1] * 8
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in (self.codes, self.scales, self.zeros))
+
+
+def empty_packed(N: int, K: int, device) -> PackedLinear:
+    codes = torch.empty(N, K // 8, dtype=torch.int32, device=device)
+    scales = torch.empty(N, K // GROUP, dtype=torch.bfloat16, device=device)
+    zeros = torch.empty(N, K // GROUP, dtype=torch.int32, device=device)
+    return PackedLinear(codes, scales, zeros)
+
+
+def w4a16_pack(W: torch.Tensor, awq_s: torch.Tensor | None = None,
+               out: PackedLinear | None = None) -> PackedLinear:
+    """Quantise + pack a BF16 weight [N][K] (see w4a16_pack in w4a16.h)."""
+    _need(W, torch.bfloat16, "W", 2)
+    N, K = W.shape
+    if awq_s is not None:
+        _need(awq_s, torch.float32, "awq_s", 1)
+        if awq_s.shape[0] != K or not awq_s.is_contiguous():
+            raise ValueError("awq_s must be a contiguous float32 [K]")
+    p = out if out is not None else empty_packed(N, K, W.device)
+    _check("w4a16_pack", lib.w4a16_pack(_ptr(W), N, K, W.stride(0), _ptr(awq_s), _ptr(p.codes),
+                                        _ptr(p.scales), _ptr(p.zeros), _stream(W)))
+    return p
+
+
+def _matmul(fn, name, X: torch.Tensor, p: PackedLinear, out: torch.Tensor | None):
+    _need(X, torch.bfloat16, "X", 2)
+    M, K = X.shape
+    if K != p.K:
+        raise ValueError(f"X has K={K}, weights have K={p.K}")
+    if out is None:
+        out = torch.empty(M, p.N, dtype=torch.bfloat16, device=X.device)
+    else:
+        _need(out, torch.bfloat16, "out", 2)
+        if tuple(out.shape) != (M, p.N):
+            raise ValueError("out has the wrong shape")
+    _check(name, fn(_ptr(X), M, X.stride(0), _ptr(p.codes), _ptr(p.scales), _ptr(p.zeros),
+                    p.N, p.K, _ptr(out), out.stride(0), _stream(X)))
+    return out
+
+
+def w4a16_gemv(X: torch.Tensor, p: PackedLinear, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = X . w_hat^T for 1 <= M <= 32 (decode)."""
+    return _matmul(lib.w4a16_gemv, "w4a16_gemv", X, p, out)
+
+
+def w4a16_gemm(X: torch.Tensor, p: PackedLinear, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = X . w_hat^T on the matrix cores, any M (prefill)."""
+    return _matmul(lib.w4a16_gemm, "w4a16_gemm", X, p, out)
+
+
+def w4a16_linear(X: torch.Tensor, p: PackedLinear, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Pick the decode kernel for M <= 32 and the matrix-core kernel above."""
+    if X.shape[0] <= GEMV_MAX_M:
+        return w4a16_gemv(X, p, out)
+    return w4a16_gemm(X, p, out)
+
+
+def w4a16_awq_importance(Xcal: torch.Tensor) -> torch.Tensor:
+    _need(Xcal, torch.bfloat16, "Xcal", 2)
+    T, K = Xcal.shape
+    out = torch.empty(K, dtype=torch.float32, device=Xcal.device)
+    _check("w4a16_awq_importance",
+           lib.w4a16_awq_importance(_ptr(Xcal), T, K, Xcal.stride(0), _ptr(out), _stream(Xcal)))
+    return out
+
+
+def w4a16_awq_scale(importance: torch.Tensor, alpha: float) -> torch.Tensor:
+    _need(importance, torch.float32, "importance", 1)
+    out = torch.empty_like(importance)
+    _check("w4a16_awq_scale", lib.w4a16_awq_scale(_ptr(importance), importance.shape[0],
+                                                  float(alpha), _ptr(out), _stream(importance)))
+    return out
+
+
+def w4a16_awq_fold(s: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor | None = None):
+    """In place: gamma /= s (and beta), BF16 round to nearest even."""
+    _need(s, torch.float32, "s", 1)
+    _need(gamma, torch.bfloat16, "gamma", 1)
+    if beta is not None:
+        _need(beta, torch.bfloat16, "beta", 1)
+    K = s.shape[0]
+    if gamma.shape[0] != K or (beta is not None and beta.shape[0] != K):
+        raise ValueError("gamma/beta must have K entries")
+    _check("w4a16_awq_fold", lib.w4a16_awq_fold(_ptr(s), K, _ptr(gamma), _ptr(beta), _stream(s)))
+    return gamma, beta
+
+
+def w4a16_scale_channels(X: torch.Tensor, gamma: torch.Tensor,
+                         out: torch.Tensor | None = None) -> torch.Tensor:
+    _need(X, torch.bfloat16, "X", 2)
+    _need(gamma, torch.bfloat16, "gamma", 1)
+    M, K = X.shape
+    if out is None:
+        out = torch.empty(M, K, dtype=torch.bfloat16, device=X.device)
+    _check("w4a16_scale_channels",
+           lib.w4a16_scale_channels(_ptr(X), M, K, X.stride(0), _ptr(gamma), _ptr(out),
+                                    out.stride(0), _stream(X)))
+    return out

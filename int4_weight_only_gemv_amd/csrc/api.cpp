@@ -1,0 +1,118 @@
+// C ABI of the W4A16 library: synchronous argument checks, then one launch
+// on the caller's stream.  See include/w4a16.h for the contract.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "w4a16.h"
+
+namespace w4a16 {
+int launch_pack(const uint16_t*, int64_t, int64_t, int64_t, const float*, uint32_t*, uint16_t*,
+                int32_t*, hipStream_t);
+int launch_gemv(const uint16_t*, int64_t, int64_t, const uint32_t*, const uint16_t*,
+                const int32_t*, int64_t, int64_t, uint16_t*, int64_t, hipStream_t);
+int launch_gemm(const uint16_t*, int64_t, int64_t, const uint32_t*, const uint16_t*,
+                const int32_t*, int64_t, int64_t, uint16_t*, int64_t, hipStream_t);
+int launch_awq_importance(const uint16_t*, int64_t, int64_t, int64_t, float*, hipStream_t);
+int launch_awq_scale(const float*, int64_t, float, float*, hipStream_t);
+int launch_awq_fold(const float*, int64_t, uint16_t*, uint16_t*, hipStream_t);
+int launch_scale_channels(const uint16_t*, int64_t, int64_t, int64_t, const uint16_t*, uint16_t*,
+                          int64_t, hipStream_t);
+}  // namespace w4a16
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;  // N, K, M each below 2^30
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Checks shared by gemv and gemm.
+int check_matmul(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
+                 const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K,
+                 const uint16_t* Y, int64_t ldy) {
+  if (!X || !codes || !scales || !zeros || !Y) return W4A16_ERR_INVALID_ARG;
+  if (M < 1 || N < 1 || K < W4A16_GROUP || K % W4A16_GROUP) return W4A16_ERR_INVALID_ARG;
+  if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return W4A16_ERR_UNSUPPORTED;
+  if (ldx < K || ldy < N) return W4A16_ERR_INVALID_ARG;
+  if (!aligned(X, 16) || ldx % 8 || !aligned(codes, 16) || !aligned(scales, 2) ||
+      !aligned(zeros, 4) || !aligned(Y, 2))
+    return W4A16_ERR_MISALIGNED;
+  return W4A16_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4a16_abi_version(void) { return W4A16_ABI_VERSION; }
+
+const char* w4a16_strerror(int status) {
+  switch (status) {
+    case W4A16_OK: return "ok";
+    case W4A16_ERR_INVALID_ARG: return "invalid argument (null pointer, size or leading dimension)";
+    case W4A16_ERR_MISALIGNED: return "misaligned pointer or leading dimension";
+    case W4A16_ERR_UNSUPPORTED: return "unsupported size or device";
+    case W4A16_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+int w4a16_pack(const uint16_t* W, int64_t N, int64_t K, int64_t ldw, const float* awq_s,
+               uint32_t* codes, uint16_t* scales, int32_t* zeros, void* stream) {
+  if (!W || !codes || !scales || !zeros) return W4A16_ERR_INVALID_ARG;
+  if (N < 1 || K < W4A16_GROUP || K % W4A16_GROUP || ldw < K) return W4A16_ERR_INVALID_ARG;
+  if (N >= kMaxDim || K >= kMaxDim || N * (K / 8) >= ((int64_t)1 << 38)) return W4A16_ERR_UNSUPPORTED;
+  if (!aligned(W, 2) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(zeros, 4) ||
+      (awq_s && !aligned(awq_s, 4)))
+    return W4A16_ERR_MISALIGNED;
+  return w4a16::launch_pack(W, N, K, ldw, awq_s, codes, scales, zeros, (hipStream_t)stream);
+}
+
+int w4a16_gemv(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
+               const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K, uint16_t* Y,
+               int64_t ldy, void* stream) {
+  int st = check_matmul(X, M, ldx, codes, scales, zeros, N, K, Y, ldy);
+  if (st != W4A16_OK) return st;
+  if (M > W4A16_GEMV_MAX_M) return W4A16_ERR_INVALID_ARG;
+  return w4a16::launch_gemv(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, (hipStream_t)stream);
+}
+
+int w4a16_gemm(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
+               const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K, uint16_t* Y,
+               int64_t ldy, void* stream) {
+  int st = check_matmul(X, M, ldx, codes, scales, zeros, N, K, Y, ldy);
+  if (st != W4A16_OK) return st;
+  return w4a16::launch_gemm(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, (hipStream_t)stream);
+}
+
+int w4a16_awq_importance(const uint16_t* Xcal, int64_t T, int64_t K, int64_t ldx,
+                         float* importance, void* stream) {
+  if (!Xcal || !importance || T < 1 || K < 1 || ldx < K) return W4A16_ERR_INVALID_ARG;
+  if (T >= kMaxDim || K >= kMaxDim) return W4A16_ERR_UNSUPPORTED;
+  if (!aligned(Xcal, 2) || !aligned(importance, 4)) return W4A16_ERR_MISALIGNED;
+  return w4a16::launch_awq_importance(Xcal, T, K, ldx, importance, (hipStream_t)stream);
+}
+
+int w4a16_awq_scale(const float* importance, int64_t K, float alpha, float* s, void* stream) {
+  if (!importance || !s || K < 1 || !(alpha >= 0.0f && alpha <= 1.0f)) return W4A16_ERR_INVALID_ARG;
+  if (K >= kMaxDim) return W4A16_ERR_UNSUPPORTED;
+  if (!aligned(importance, 4) || !aligned(s, 4)) return W4A16_ERR_MISALIGNED;
+  return w4a16::launch_awq_scale(importance, K, alpha, s, (hipStream_t)stream);
+}
+
+int w4a16_awq_fold(const float* s, int64_t K, uint16_t* gamma, uint16_t* beta, void* stream) {
+  if (!s || !gamma || K < 1) return W4A16_ERR_INVALID_ARG;
+  if (K >= kMaxDim) return W4A16_ERR_UNSUPPORTED;
+  if (!aligned(s, 4) || !aligned(gamma, 2) || (beta && !aligned(beta, 2))) return W4A16_ERR_MISALIGNED;
+  return w4a16::launch_awq_fold(s, K, gamma, beta, (hipStream_t)stream);
+}
+
+int w4a16_scale_channels(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
+                         const uint16_t* gamma, uint16_t* Xout, int64_t ldo, void* stream) {
+  if (!X || !gamma || !Xout || M < 1 || K < 1 || ldx < K || ldo < K) return W4A16_ERR_INVALID_ARG;
+  if (M >= kMaxDim || K >= kMaxDim || M * K >= ((int64_t)1 << 38)) return W4A16_ERR_UNSUPPORTED;
+  if (!aligned(X, 2) || !aligned(gamma, 2) || !aligned(Xout, 2)) return W4A16_ERR_MISALIGNED;
+  return w4a16::launch_scale_channels(X, M, K, ldx, gamma, Xout, ldo, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// AWQ helpers around the W4A16 path: calibration statistic, smoothing scale,
+// and the fold of diag(s)^-1 into the activations' producer (Axe Corsa model
+// card, "Stage 1: Activation-Aware Weight Scaling").  These run once per
+// model at calibration time; the fold makes the rescaling free at inference.
+
+#include "common.h"
+
+namespace w4a16 {
+namespace {
+
+// importance[k] = (1/T) sum_t |X[t,k]|, float64 sum in token order.
+__global__ __launch_bounds__(256) void importance_kernel(const uint16_t* __restrict__ X, int64_t T,
+                                                         int64_t K, int64_t ldx,
+                                                         float* __restrict__ out) {
+  const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= K) return;
+  double acc = 0.0;
+  for (int64_t t = 0; t < T; ++t) acc += fabs((double)bf16_to_f32(X[t * ldx + k]));
+  out[k] = (float)(acc / (double)T);
+}
+
+// s[k] = importance[k] ** alpha in float64, rounded to float32.
+__global__ __launch_bounds__(256) void scale_kernel(const float* __restrict__ imp, int64_t K,
+                                                    double alpha, float* __restrict__ s) {
+  const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= K) return;
+  s[k] = (float)pow((double)imp[k], alpha);
+}
+
+// gamma[k] = bf16_rne(gamma[k] / s[k]) (and beta likewise).
+__global__ __launch_bounds__(256) void fold_kernel(const float* __restrict__ s, int64_t K,
+                                                   uint16_t* __restrict__ gamma,
+                                                   uint16_t* __restrict__ beta) {
+  const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= K) return;
+  const float sk = s[k];
+  gamma[k] = f32_to_bf16_rne(__fdiv_rn(bf16_to_f32(gamma[k]), sk));
+  if (beta) beta[k] = f32_to_bf16_rne(__fdiv_rn(bf16_to_f32(beta[k]), sk));
+}
+
+// Xout[m,k] = bf16_rne(X[m,k] * gamma[k]).
+__global__ __launch_bounds__(256) void scale_channels_kernel(const uint16_t* __restrict__ X,
+                                                             int64_t M, int64_t K, int64_t ldx,
+                                                             const uint16_t* __restrict__ gamma,
+                                                             uint16_t* Xout, int64_t ldo) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= M * K) return;
+  const int64_t m = i / K, k = i - m * K;
+  Xout[m * ldo + k] = f32_to_bf16_rne(__fmul_rn(bf16_to_f32(X[m * ldx + k]), bf16_to_f32(gamma[k])));
+}
+
+unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
+
+}  // namespace
+
+int launch_awq_importance(const uint16_t* X, int64_t T, int64_t K, int64_t ldx, float* out,
+                          hipStream_t stream) {
+  hipLaunchKernelGGL(importance_kernel, dim3(blocks_for(K)), dim3(256), 0, stream, X, T, K, ldx, out);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+int launch_awq_scale(const float* imp, int64_t K, float alpha, float* s, hipStream_t stream) {
+  hipLaunchKernelGGL(scale_kernel, dim3(blocks_for(K)), dim3(256), 0, stream, imp, K,
+                     (double)alpha, s);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+int launch_awq_fold(const float* s, int64_t K, uint16_t* gamma, uint16_t* beta,
+                    hipStream_t stream) {
+  hipLaunchKernelGGL(fold_kernel, dim3(blocks_for(K)), dim3(256), 0, stream, s, K, gamma, beta);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+int launch_scale_channels(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
+                          const uint16_t* gamma, uint16_t* Xout, int64_t ldo, hipStream_t stream) {
+  hipLaunchKernelGGL(scale_channels_kernel, dim3(blocks_for(M * K)), dim3(256), 0, stream, X, M, K,
+                     ldx, gamma, Xout, ldo);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+}  // namespace w4a16

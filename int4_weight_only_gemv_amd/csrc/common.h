@@ -1,0 +1,68 @@
+// Device helpers shared by the HIP kernels of the W4A16 library (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kGroup = 128;
+constexpr int kWave = 64;
+
+// Two BF16 values 128 + a and 128 + b packed in one dword: BF16 0x4300 is
+// 128.0 and its 7 mantissa bits count in units of 1, so OR-ing a 4-bit code
+// into the mantissa gives 128 + code exactly.
+constexpr uint32_t kBias128Pair = 0x43004300u;
+constexpr uint32_t kNibblePairMask = 0x000F000Fu;
+constexpr uint32_t kOnePair = 0x3F803F80u;  // BF16 (1.0, 1.0)
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// float32 -> BF16 bits, round to nearest even; NaN becomes the quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Eight 4-bit codes of one word -> eight BF16 operands 128 + q, ordered so
+// that dword j holds (code j, code j+4).  The matching activation operand
+// must use the same pairing (see x_pairs_from_natural).
+__device__ __forceinline__ u32x4 codes_to_bias128_pairs(uint32_t w) {
+  u32x4 r;
+  r[0] = (w & kNibblePairMask) | kBias128Pair;
+  r[1] = ((w >> 4) & kNibblePairMask) | kBias128Pair;
+  r[2] = ((w >> 8) & kNibblePairMask) | kBias128Pair;
+  r[3] = ((w >> 12) & kNibblePairMask) | kBias128Pair;
+  return r;
+}
+
+// Eight consecutive BF16 activations x0..x7 loaded as dwords
+// (x0,x1) (x2,x3) (x4,x5) (x6,x7) -> the pairing (x0,x4) (x1,x5) (x2,x6)
+// (x3,x7) used by codes_to_bias128_pairs.
+__device__ __forceinline__ u32x4 x_pairs_from_natural(u32x4 d) {
+  u32x4 r;
+  r[0] = __builtin_amdgcn_perm(d[2], d[0], 0x05040100u);
+  r[1] = __builtin_amdgcn_perm(d[2], d[0], 0x07060302u);
+  r[2] = __builtin_amdgcn_perm(d[3], d[1], 0x05040100u);
+  r[3] = __builtin_amdgcn_perm(d[3], d[1], 0x07060302u);
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// D = A * B + C on a 16x16 output tile with K = 32 (BF16 in, FP32 out).
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+}  // namespace w4a16

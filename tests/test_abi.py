@@ -1,0 +1,130 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header
+declares, and rejects bad arguments before touching the GPU.  No call here
+reaches a kernel launch (every argument set fails validation)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+
+w4 = pytest.importorskip("int4_weight_only_gemv_amd")
+lib = w4.lib
+
+OK, INVALID, MISALIGNED, UNSUPPORTED, HIPERR = 0, 1, 2, 3, 4
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(w4a16_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_expected_entry_points():
+    assert header_functions() == sorted([
+        "w4a16_abi_version", "w4a16_strerror", "w4a16_pack", "w4a16_gemv", "w4a16_gemm",
+        "w4a16_awq_importance", "w4a16_awq_scale", "w4a16_awq_fold", "w4a16_scale_channels"])
+
+
+def test_every_declared_symbol_is_exported():
+    out = subprocess.run(["nm", "-D", "--defined-only", w4.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s+(w4a16_\w+)$", out, re.M))
+    for name in header_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+    assert set(w4.EXPORTS) == set(header_functions())
+
+
+def test_version_and_strerror():
+    assert lib.w4a16_abi_version() == 1
+    for st in range(5):
+        assert lib.w4a16_strerror(st)
+    assert b"unknown" in lib.w4a16_strerror(99)
+
+
+def p(v):
+    return ctypes.c_void_p(v)
+
+
+def gemv(fn=None, X=FAKE, M=1, ldx=4096, codes=FAKE, scales=FAKE, zeros=FAKE, N=4096, K=4096,
+         Y=FAKE, ldy=4096):
+    fn = fn or lib.w4a16_gemv
+    return fn(p(X), M, ldx, p(codes), p(scales), p(zeros), N, K, p(Y), ldy, p(0))
+
+
+@pytest.mark.parametrize("fn", ["w4a16_gemv", "w4a16_gemm"])
+def test_matmul_validation(fn):
+    f = getattr(lib, fn)
+    assert gemv(f, X=0) == INVALID
+    assert gemv(f, codes=0) == INVALID
+    assert gemv(f, scales=0) == INVALID
+    assert gemv(f, zeros=0) == INVALID
+    assert gemv(f, Y=0) == INVALID
+    assert gemv(f, M=0) == INVALID
+    assert gemv(f, N=0) == INVALID
+    assert gemv(f, K=0) == INVALID
+    assert gemv(f, K=4000, ldx=4000) == INVALID          # K % 128
+    assert gemv(f, K=64, ldx=64) == INVALID              # K < 128
+    assert gemv(f, ldx=4095) == INVALID                  # ldx < K
+    assert gemv(f, ldy=100) == INVALID                   # ldy < N
+    assert gemv(f, X=FAKE + 2) == MISALIGNED             # X not 16-byte aligned
+    assert gemv(f, ldx=4100) == MISALIGNED               # ldx % 8
+    assert gemv(f, codes=FAKE + 4) == MISALIGNED
+    assert gemv(f, scales=FAKE + 1) == MISALIGNED
+    assert gemv(f, zeros=FAKE + 2) == MISALIGNED
+    assert gemv(f, Y=FAKE + 1) == MISALIGNED
+    assert gemv(f, N=1 << 30, ldy=1 << 30) == UNSUPPORTED
+
+
+def test_gemv_rejects_large_m():
+    assert gemv(M=33) == INVALID
+    assert gemv(M=1 << 20) == INVALID
+
+
+def test_pack_validation():
+    f = lib.w4a16_pack
+
+    def call(W=FAKE, N=16, K=256, ldw=256, s=0, c=FAKE, sc=FAKE, z=FAKE):
+        return f(p(W), N, K, ldw, p(s), p(c), p(sc), p(z), p(0))
+
+    assert call(W=0) == INVALID
+    assert call(c=0) == INVALID and call(sc=0) == INVALID and call(z=0) == INVALID
+    assert call(N=0) == INVALID
+    assert call(K=200, ldw=200) == INVALID
+    assert call(ldw=255) == INVALID
+    assert call(W=FAKE + 1) == MISALIGNED
+    assert call(c=FAKE + 8) == MISALIGNED
+    assert call(sc=FAKE + 1) == MISALIGNED
+    assert call(z=FAKE + 2) == MISALIGNED
+    assert call(s=FAKE + 2) == MISALIGNED
+    assert call(N=1 << 30) == UNSUPPORTED
+
+
+def test_awq_validation():
+    assert lib.w4a16_awq_importance(p(0), 4, 8, 8, p(FAKE), p(0)) == INVALID
+    assert lib.w4a16_awq_importance(p(FAKE), 0, 8, 8, p(FAKE), p(0)) == INVALID
+    assert lib.w4a16_awq_importance(p(FAKE), 4, 8, 7, p(FAKE), p(0)) == INVALID
+    assert lib.w4a16_awq_importance(p(FAKE + 1), 4, 8, 8, p(FAKE), p(0)) == MISALIGNED
+    assert lib.w4a16_awq_scale(p(FAKE), 8, ctypes.c_float(1.5), p(FAKE), p(0)) == INVALID
+    assert lib.w4a16_awq_scale(p(FAKE), 8, ctypes.c_float(-0.1), p(FAKE), p(0)) == INVALID
+    assert lib.w4a16_awq_scale(p(FAKE), 8, ctypes.c_float(float("nan")), p(FAKE), p(0)) == INVALID
+    assert lib.w4a16_awq_scale(p(FAKE + 2), 8, ctypes.c_float(0.5), p(FAKE), p(0)) == MISALIGNED
+    assert lib.w4a16_awq_fold(p(0), 8, p(FAKE), p(0), p(0)) == INVALID
+    assert lib.w4a16_awq_fold(p(FAKE), 0, p(FAKE), p(0), p(0)) == INVALID
+    assert lib.w4a16_awq_fold(p(FAKE), 8, p(FAKE + 1), p(0), p(0)) == MISALIGNED
+    assert lib.w4a16_scale_channels(p(FAKE), 2, 8, 7, p(FAKE), p(FAKE), 8, p(0)) == INVALID
+    assert lib.w4a16_scale_channels(p(FAKE), 2, 8, 8, p(FAKE), p(FAKE), 7, p(0)) == INVALID
+    assert lib.w4a16_scale_channels(p(FAKE), 2, 8, 8, p(FAKE + 1), p(FAKE), 8, p(0)) == MISALIGNED
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    W = torch.zeros(16, 256, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        w4.w4a16_pack(W)
+    with pytest.raises(TypeError):
+        w4.w4a16_pack(W.float())

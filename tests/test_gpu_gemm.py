@@ -1,0 +1,80 @@
+"""w4a16_gemm (prefill, matrix cores) on the GPU vs the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from synth import gen
+from parity import assert_output_close, reference, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+w4 = pytest.importorskip("int4_weight_only_gemv_amd")
+DEV = "cuda"
+
+
+def check_case(M, N, K, cfg, layer, shift=False, rows=None, mrows=None, label=""):
+    W = gen.weights(N, K, cfg, layer, shift=shift, device=DEV)
+    X = gen.activations(M, K, cfg, layer, device=DEV)
+    p = w4.w4a16_pack(W)
+    y = w4.w4a16_gemm(X, p)
+    torch.cuda.synchronize()
+    if mrows is not None:
+        midx = torch.as_tensor(mrows, device=DEV)
+        X, y = X[midx], y[midx]
+    if rows is None:
+        y_ref, mag = reference(gen.bits(X), gen.bits(W))
+        return assert_output_close(y, y_ref, mag, label=label)
+    ridx = torch.as_tensor(rows, device=DEV)
+    y_ref, mag = reference(gen.bits(X), gen.bits(W[ridx]))
+    return assert_output_close(y[:, ridx], y_ref, mag, label=label)
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (1, 16, 128), (7, 100, 384), (128, 128, 128), (129, 130, 256), (200, 333, 640),
+    (256, 512, 1024), (33, 1000, 512), (512, 64, 2048)])
+def test_small_full(M, N, K):
+    check_case(M, N, K, "gemm", f"{M}x{N}x{K}", shift=True, label=f"{M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M", [512, 2048, 4096])
+def test_llama8b_prefill_sampled(M):
+    for layer in gen.LLAMA8B:
+        rows = sample_rows(layer.N, 48, seed=layer.N + M)
+        mrows = sample_rows(M, 32, seed=M + 7)
+        check_case(M, layer.N, layer.K, "llama8b_prefill", layer.name, rows=rows, mrows=mrows,
+                   label=f"{layer.name} M={M}")
+        torch.cuda.empty_cache()
+
+
+def test_matches_gemv_for_small_m():
+    N, K = 300, 2048
+    W = gen.weights(N, K, "gemm", "vs_gemv", device=DEV)
+    p = w4.w4a16_pack(W)
+    for M in (1, 16, 32):
+        X = gen.activations(M, K, "gemm", "vs_gemv", device=DEV)
+        a = w4.w4a16_gemm(X, p)
+        b = w4.w4a16_gemv(X, p)
+        torch.cuda.synchronize()
+        # same arithmetic up to float32 summation order: within one BF16 ulp
+        fa = a.float(); fb = b.float()
+        assert torch.all((fa - fb).abs() <= 2.0 ** -7 * fb.abs() + 1e-3)
+
+
+def test_canaries_and_determinism():
+    M, N, K = 150, 260, 512
+    W = gen.weights(N, K, "gemm", "canary", device=DEV)
+    p = w4.w4a16_pack(W)
+    X = gen.activations(M, K, "gemm", "canary", device=DEV)
+    canary = torch.full((M + 3, N + 24), -77.0, dtype=torch.bfloat16, device=DEV)
+    out = canary[2:M + 2, 16:N + 16]
+    w4.w4a16_gemm(X, p, out=out)
+    torch.cuda.synchronize()
+    inner = torch.zeros_like(canary, dtype=torch.bool)
+    inner[2:M + 2, 16:N + 16] = True
+    assert torch.all(canary[~inner] == -77.0), "write outside Y"
+    y2 = w4.w4a16_gemm(X, p)
+    torch.cuda.synchronize()
+    assert torch.equal(out, y2)
+    y_ref, mag = reference(gen.bits(X), gen.bits(W))
+    assert_output_close(out, y_ref, mag, label="canary")
