@@ -1,0 +1,276 @@
+"""Benchmark of the fused W4A16 path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--m 1]
+                    [--workload llama8b_decode] [--no-prefill] [--no-cpu-baseline]
+
+A step is one decode pass (M = 1 by default) over the four linears of a
+Llama-3-8B-shaped decoder layer (qkv 6144x4096, o 4096x4096, gate_up
+28672x4096, down 4096x14336), INT4 group-128 weights, BF16 activations.
+Inputs are seeded synthetic tensors already resident in HBM; the packed
+weights are replicated into enough distinct copies (>= 1 GiB) that every step
+streams them from HBM rather than the 256 MB last-level cache.  Each copy's
+four launches are captured in a HIP graph; the timed region replays K graphs
+back to back between two device synchronisations.
+
+value = algorithmic bytes per step / time per step, with algorithmic bytes
+= packed codes + BF16 scales + INT32 zeros + X + Y.
+
+Also reported (same JSON line):
+  roofline      the dominant kernel (the gate_up launch) timed alone with HIP
+                events on its stream, against the 8 TB/s HBM peak;
+  prefill       the same four layers at M = 4096 on the matrix-core kernel,
+                TFLOP/s against the 2.5 PFLOP/s dense BF16 peak;
+  cpu_baseline  the CPU oracle on a bounded sample of the same step.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+ROTATE_BYTES = 1 << 30
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=600)
+    ap.add_argument("--warmup", type=int, default=60)
+    ap.add_argument("--m", type=int, default=1)
+    ap.add_argument("--workload", default="llama8b_decode")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-m", type=int, default=4096)
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_bytes(layer, M):
+    N, K = layer.N, layer.K
+    return N * K // 2 + (N * K // 128) * 6 + 2 * M * K + 2 * M * N
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import int4_weight_only_gemv_amd as w4
+    from synth import gen
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    spec = gen.WORKLOADS[args.workload]
+    layers = spec["layers"]
+    M = args.m
+    linear = w4.w4a16_gemv if M <= w4.GEMV_MAX_M else w4.w4a16_gemm
+
+    # ---- inputs: pack each layer once, replicate packed copies past the LLC
+    log(f"[bench] packing {args.workload} layers on {torch.cuda.get_device_name(0)}")
+    packed, xs, ys = [], [], []
+    for L in layers:
+        W = gen.weights(L.N, L.K, args.workload, L.name, shift=spec["shift"], device=dev)
+        packed.append(w4.w4a16_pack(W))
+        del W
+        xs.append(gen.activations(M, L.K, args.workload, L.name, device=dev))
+        ys.append(torch.empty(M, L.N, dtype=torch.bfloat16, device=dev))
+    set_bytes = sum(p.nbytes() for p in packed)
+    ncopy = max(2, math.ceil(ROTATE_BYTES / set_bytes))
+    copies = [packed] + [[w4.PackedLinear(p.codes.clone(), p.scales.clone(), p.zeros.clone())
+                          for p in packed] for _ in range(ncopy - 1)]
+    torch.cuda.synchronize()
+    step_bytes = sum(decode_bytes(L, M) for L in layers)
+
+    # ---- one HIP graph per copy: the four launches of one step
+    stream = torch.cuda.Stream()
+    graphs = []
+    with torch.cuda.stream(stream):
+        for c in range(ncopy):  # warm the launch path before capture
+            for p, x, y in zip(copies[c], xs, ys):
+                linear(x, p, y)
+        stream.synchronize()
+        for c in range(ncopy):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for p, x, y in zip(copies[c], xs, ys):
+                    linear(x, p, y)
+            graphs.append(g)
+    torch.cuda.synchronize()
+
+    with torch.cuda.stream(stream):
+        for s in range(args.warmup):
+            graphs[s % ncopy].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            graphs[s % ncopy].replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"[bench] decode M={M}: {ms_per_step * 1e3:.2f} us/step, {value:.0f} GB/s over {ncopy} copies")
+
+    # ---- dominant kernel alone: per-layer launch durations with HIP events
+    def time_layer(i, reps=200):
+        L = layers[i]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                for r in range(reps):
+                    linear(xs[i], copies[r % ncopy][i], ys[i])
+            g.replay()
+            stream.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            e1.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        return us, decode_bytes(L, M) / (us * 1e-6) / 1e9
+
+    per_layer = []
+    for i, L in enumerate(layers):
+        us, gbs = time_layer(i)
+        per_layer.append({"layer": L.name, "N": L.N, "K": L.K, "us": round(us, 3),
+                          "GBps": round(gbs, 1), "bytes": decode_bytes(L, M)})
+        log(f"[bench]   {L.name:8s} N={L.N:6d} K={L.K:6d}: {us:8.2f} us {gbs:8.0f} GB/s")
+    dom = max(range(len(layers)), key=lambda i: per_layer[i]["us"])
+    roofline = {
+        "bound": "hbm",
+        "kernel": f"w4a16_gemv ({layers[dom].name}, N={layers[dom].N}, K={layers[dom].K}, M={M})",
+        "achieved": per_layer[dom]["GBps"],
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(per_layer[dom]["GBps"] / HBM_PEAK_GBS, 4),
+        "traffic": None,
+    }
+    del graphs
+    torch.cuda.synchronize()
+
+    # ---- prefill GEMM on the same layers
+    prefill = None
+    if not args.no_prefill:
+        Mp = args.prefill_m
+        pxs = [gen.activations(Mp, L.K, "llama8b_prefill", L.name, device=dev) for L in layers]
+        pys = [torch.empty(Mp, L.N, dtype=torch.bfloat16, device=dev) for L in layers]
+        with torch.cuda.stream(stream):
+            for p, x, y in zip(packed, pxs, pys):
+                w4.w4a16_gemm(x, p, y)
+            stream.synchronize()
+            reps = 5
+            times = []
+            for p, x, y in zip(packed, pxs, pys):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(reps):
+                    w4.w4a16_gemm(x, p, y)
+                e1.record(stream)
+                e1.synchronize()
+                times.append(e0.elapsed_time(e1) * 1e-3 / reps)
+        flops = [2.0 * Mp * L.N * L.K for L in layers]
+        tf = sum(flops) / sum(times) / 1e12
+        dom_p = max(range(len(layers)), key=lambda i: times[i])
+        prefill = {
+            "metric": f"prefill GEMM TFLOP/s (M={Mp})",
+            "value": round(tf, 1), "unit": "TFLOP/s",
+            "ms_per_step": round(sum(times) * 1e3, 4),
+            "layers": [{"layer": L.name, "ms": round(t * 1e3, 4),
+                        "TFLOPs": round(f / t / 1e12, 1)} for L, t, f in zip(layers, times, flops)],
+            "roofline": {"bound": "mfma", "kernel": f"w4a16_gemm ({layers[dom_p].name}, M={Mp})",
+                         "achieved": round(flops[dom_p] / times[dom_p] / 1e12, 1),
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(flops[dom_p] / times[dom_p] / 1e12 / BF16_PEAK_TFLOPS, 4),
+                         "traffic": None},
+        }
+        log(f"[bench] prefill M={Mp}: {tf:.1f} TFLOP/s")
+        del pxs, pys
+
+    # ---- CPU oracle on a bounded sample of the same step
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(layers, args.workload, spec, M, dev)
+
+    out = {
+        "metric": "W4A16 decode GEMV achieved HBM GB/s (M=1) + prefill GEMM TFLOP/s (M=4096)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 activations x int4 weights, fp32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: Llama-3-8B-shaped decode layer set "
+                               f"(qkv 6144x4096, o 4096x4096, gate_up 28672x4096, down 4096x14336), "
+                               f"INT4 group 128",
+                   "M": M, "step_bytes": step_bytes, "rotating_copies": ncopy,
+                   "parallelism": "single GPU"},
+        "per_layer": per_layer,
+        "roofline": roofline,
+        "prefill": prefill,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(layers, workload, spec, M, dev, row_stride=2, min_seconds=10.0):
+    """Time the CPU oracle (unpack, dequantise, fp64 dot) for the same step on
+    every `row_stride`-th output row of each layer, single-threaded."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+    from synth import gen
+
+    prepared = []
+    for L in layers:
+        W = gen.weights(L.N, L.K, workload, L.name, shift=spec["shift"], device=dev)
+        rows = torch.arange(0, L.N, row_stride, device=dev)
+        Wb = gen.bits(W[rows])
+        del W
+        X = gen.bits(gen.activations(M, L.K, workload, L.name, device=dev))
+        codes, scales, zeros = O.quantize_pack(Wb)   # untimed: the oracle's own packing
+        prepared.append((L, X, codes, scales, zeros, len(rows)))
+    nbytes = 0
+    t0 = time.perf_counter()
+    reps = 0
+    with threadpool_limits(limits=1):
+        while True:
+            for L, X, codes, scales, zeros, nr in prepared:
+                O.matmul_ref(X, codes, scales, zeros)
+                nbytes += nr * L.K // 2 + nr * (L.K // 128) * 6 + 2 * M * L.K + 2 * M * nr
+            reps += 1
+            if time.perf_counter() - t0 >= min_seconds or reps >= 5:
+                break
+    dt = time.perf_counter() - t0
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"every {row_stride}th output row of each of the four layers, M={M}, "
+                      f"{reps} pass(es); unpack + dequantise + fp64 dot, one thread"}
+
+
+if __name__ == "__main__":
+    main()

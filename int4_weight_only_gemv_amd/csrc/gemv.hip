@@ -2,32 +2,177 @@
 //
 // Y[m, n] = sum_g s[n,g] * sum_{k in g} X[m,k] * (q[n,k] - z[n,g])
 // (Axe Corsa model card, "The Two-Stage Pipeline": dequantisation fused
-// into the multiply, weights rebuilt in registers).
+// into the multiply, weights rebuilt in registers; "Quantization I",
+// "Concept": only the packed form crosses the memory bus).
 //
-// Per wave and per group of 128 inputs, a 16-row tile of W meets a 16-row
-// (M padded) tile of X on the BF16 matrix cores, v_mfma_f32_16x16x32_bf16:
-//   * the packed codes are the B operand, turned into the exact BF16 values
-//     128 + q by OR-ing each nibble into the mantissa of 128.0 (two ops per
-//     pair of codes, no conversion instructions);
-//   * the same A operand against a B of ones gives sum_{k in g} X[m,k];
-//   * per group, in float32:  acc += s * (P - (128 + z) * Xsum),
-//     the bias and the zero point removed with one fused multiply-add whose
-//     product is exact.  No weight is ever rounded.
+// Both kernels turn a code word into exact BF16 operands 128 + q by OR-ing
+// each nibble into the mantissa of BF16 128.0 (two ops per pair of codes, no
+// conversions) and remove the bias and the zero point once per group in
+// float32 with one fused multiply-add whose product is exact:
+//     acc += s * (P - (128 + z) * Xsum),   P = sum_k x (128 + q).
+// No weight is ever rounded.
 //
-// Work split: a block owns 16 output rows and all of K; its S waves split
-// the K groups evenly and their partial sums are added in a fixed order
-// through LDS, so results are deterministic and no workspace is needed.
-// Each lane streams 16 contiguous bytes (32 codes of one row) per group.
+// gemv_dot (small M): a wave owns a 2048-input slice of K for a run of rows;
+// its 64 lanes read 16 contiguous bytes each, so every load instruction
+// moves 1 KiB of one row -- the fully coalesced pattern that streams HBM
+// fastest.  The lane's 32 activations per batch row stay in registers for
+// all rows, the products run on v_dot2_f32_bf16, and per-row partial sums
+// are folded across lanes with a halving butterfly (ds_bpermute), then
+// across the K slices of the block through LDS in a fixed order.
+//
+// gemv_mfma (larger M): a 16-row tile of W meets a 16-row tile of X
+// (M padded) on v_mfma_f32_16x16x32_bf16; the same A operand against a B of
+// ones gives the per-group activation sums.  The waves of a block split K
+// and add their partial tiles through LDS in a fixed order.
+//
+// Neither kernel uses atomics or workspace: results are deterministic.
 
 #include "common.h"
 
 namespace w4a16 {
 namespace {
 
-constexpr int kMaxWaves = 16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// ---------------------------------------------------------------------------
+// gemv_dot
+// ---------------------------------------------------------------------------
+
+constexpr int kSlice = 2048;      // inputs per wave: 64 lanes x 32
+constexpr int kMaxSlices = 16;    // K <= 32768 on this kernel
+
+constexpr int pow2_at_least(int v) { return v <= 1 ? 1 : 2 * pow2_at_least((v + 1) / 2); }
+constexpr int log2_exact(int v) { return v <= 1 ? 0 : 1 + log2_exact(v / 2); }
+
+// Sum V values (a power of two <= 64) over the 64 lanes.  Afterwards lane l
+// holds in v[0] the total of value (l >> (6 - log2 V)).
+template <int V>
+__device__ __forceinline__ void lane_butterfly(float (&v)[V], int lane) {
+  int mask = 32;
+#pragma unroll
+  for (int cur = V; cur > 1; cur >>= 1) {
+    const bool upper = (lane & mask) != 0;
+#pragma unroll
+    for (int i = 0; i < cur / 2; ++i) {
+      const float lo = v[i], hi = v[i + cur / 2];
+      const float send = upper ? lo : hi;
+      const float keep = upper ? hi : lo;
+      v[i] = keep + __shfl_xor(send, mask);
+    }
+    mask >>= 1;
+  }
+#pragma unroll
+  for (; mask >= 1; mask >>= 1) v[0] += __shfl_xor(v[0], mask);
+}
+
+template <int M, int R, int NB>
+__global__ __launch_bounds__(1024) void gemv_dot_kernel(
+    const uint16_t* __restrict__ X, int64_t ldx, const uint32_t* __restrict__ codes,
+    const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K,
+    uint16_t* __restrict__ Y, int64_t ldy) {
+  constexpr int RB = R * NB;                  // rows per block
+  constexpr int V = pow2_at_least(R * M);     // values per butterfly
+  constexpr int LV = log2_exact(V);
+  static_assert(V <= 64, "too many values per butterfly");
+  __shared__ float red[kMaxSlices][RB * M];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int S = blockDim.x >> 6;
+  const int k0 = wave * kSlice + lane * 32;
+  const bool active = k0 < K;
+  const int kc = active ? k0 : K - 32;        // inactive lanes read valid memory, weigh zero
+  const int G = K / kGroup;
+  const int g = kc >> 7;
+  const int64_t wpr = K / 8;
+
+  // this lane's 32 activations of every batch row, paired like the codes
+  u32x4 xp[M][4];
+  float xs[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const u32x4* xr = reinterpret_cast<const u32x4*>(X + m * ldx + kc);
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u32x4 raw = xr[i];
+      if (!active) raw = u32x4{0u, 0u, 0u, 0u};
+      xp[m][i] = x_pairs_from_natural(raw);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sum = dot2(raw[j], kOnePair, sum);
+    }
+    xs[m] = sum;
+  }
+
+  const int row0 = blockIdx.x * RB;
+  const u32x4* cbase = reinterpret_cast<const u32x4*>(codes) + kc / 32;
+  u32x4 cb[2][R];
+  uint32_t sb[2][R];
+  int zb[2][R];
+  auto load = [&](int buf, int batch) {
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const int row = min(row0 + batch * R + j, N - 1);
+      cb[buf][j] = __builtin_nontemporal_load(cbase + (int64_t)row * (wpr / 4));
+      sb[buf][j] = scales[(int64_t)row * G + g];
+      zb[buf][j] = zeros[(int64_t)row * G + g];
+    }
+  };
+
+  load(0, 0);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int cur = nb & 1;
+    if (nb + 1 < NB) load(cur ^ 1, nb + 1);
+    float part[V];
+#pragma unroll
+    for (int v = R * M; v < V; ++v) part[v] = 0.f;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      float P[M];
+#pragma unroll
+      for (int m = 0; m < M; ++m) P[m] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u32x4 b = codes_to_bias128_pairs(cb[cur][j][i]);
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) P[m] = dot2(b[jj], xp[m][i][jj], P[m]);
+      }
+      const float s = bf16_to_f32(sb[cur][j]);
+      const float zb128 = (float)(128 + zb[cur][j]);
+#pragma unroll
+      for (int m = 0; m < M; ++m) part[j * M + m] = s * fmaf(-zb128, xs[m], P[m]);
+    }
+    lane_butterfly<V>(part, lane);
+    const int vi = lane >> (6 - LV);
+    if ((lane & ((64 >> LV) - 1)) == 0 && vi < R * M) red[wave][nb * R * M + vi] = part[0];
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < RB * M; idx += blockDim.x) {
+    const int j = idx / M, m = idx - j * M;
+    const int row = row0 + j;
+    if (row >= N) continue;
+    float v = red[0][idx];
+    for (int w = 1; w < S; ++w) v += red[w][idx];
+    Y[m * ldy + row] = f32_to_bf16_rne(v);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// gemv_mfma
+// ---------------------------------------------------------------------------
+
+constexpr int kMaxWaves = 8;
 
 template <int MT, int U>
-__global__ __launch_bounds__(1024) void gemv_mfma_kernel(
+__global__ __launch_bounds__(512) void gemv_mfma_kernel(
     const uint16_t* __restrict__ X, int M, int64_t ldx, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K,
     uint16_t* __restrict__ Y, int64_t ldy) {
@@ -49,7 +194,8 @@ __global__ __launch_bounds__(1024) void gemv_mfma_kernel(
   const uint16_t* srow = scales + (int64_t)n_ld * G;
   const int32_t* zrow = zeros + (int64_t)n_ld * G;
 
-  // A-operand rows: m = (lane & 15) + 16 * mt.
+  // A-operand rows m = (lane & 15) + 16 mt; rows past M read row 0 and are
+  // zeroed after the load (no divergent loads)
   const u32x4* xrow[MT];
   bool xvalid[MT];
 #pragma unroll
@@ -64,60 +210,65 @@ __global__ __launch_bounds__(1024) void gemv_mfma_kernel(
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int g0 = gb; g0 < ge; g0 += U) {
-    u32x4 cw[U];
-    u32x4 xr[U][4][MT];
-    float sc[U];
-    float zb[U];
+  if (gb < ge) {
+    u32x4 cw[2][U];
+    u32x4 xr[2][U][4][MT];
+    uint32_t sr[2][U];
+    int zr[2][U];
+    auto load = [&](int buf, int g0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int g = g0 + u;
-      if (g < ge) {
-        cw[u] = __builtin_nontemporal_load(crow + g * 4);
-        sc[u] = bf16_to_f32(srow[g]);
-        zb[u] = (float)(128 + zrow[g]);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            xr[u][i][mt] = xvalid[mt] ? xrow[mt][g * 16 + i] : u32x4{0u, 0u, 0u, 0u};
-        }
-      } else {
-        cw[u] = u32x4{0u, 0u, 0u, 0u};
-        sc[u] = 0.f;
-        zb[u] = 0.f;
+      for (int u = 0; u < U; ++u) {
+        const int gl = min(g0 + u, ge - 1);
+        cw[buf][u] = __builtin_nontemporal_load(crow + gl * 4);
+        sr[buf][u] = srow[gl];
+        zr[buf][u] = zrow[gl];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) xr[u][i][mt] = u32x4{0u, 0u, 0u, 0u};
+          for (int i = 0; i < 4; ++i) xr[buf][u][i][mt] = xrow[mt][gl * 16 + i];
       }
-    }
+    };
+    auto compute = [&](int buf, int g0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      f32x4 pg[MT], xs[MT];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        pg[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        xs[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const u32x4 b = codes_to_bias128_pairs(cw[u][i]);
+      for (int u = 0; u < U; ++u) {
+        f32x4 pg[MT], xs[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          const u32x4 a = x_pairs_from_natural(xr[u][i][mt]);
-          pg[mt] = mfma16x16x32(a, b, pg[mt]);
-          xs[mt] = mfma16x16x32(a, ones, xs[mt]);
+          pg[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          xs[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const u32x4 b = codes_to_bias128_pairs(cw[buf][u][i]);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            u32x4 raw = xr[buf][u][i][mt];
+            if (!xvalid[mt]) raw = u32x4{0u, 0u, 0u, 0u};
+            const u32x4 a = x_pairs_from_natural(raw);
+            pg[mt] = mfma16x16x32(a, b, pg[mt]);
+            xs[mt] = mfma16x16x32(a, ones, xs[mt]);
+          }
+        }
+        const float sc = (g0 + u < ge) ? bf16_to_f32(sr[buf][u]) : 0.f;
+        const float zb = (float)(128 + zr[buf][u]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float d = fmaf(-zb, xs[mt][r], pg[mt][r]);
+            acc[mt][r] = fmaf(sc, d, acc[mt][r]);
+          }
       }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float d = fmaf(-zb[u], xs[mt][r], pg[mt][r]);
-          acc[mt][r] = fmaf(sc[u], d, acc[mt][r]);
-        }
+    };
+    load(0, gb);
+    int g0 = gb;
+    for (; g0 + U < ge; g0 += 2 * U) {
+      load(1, g0 + U);
+      compute(0, g0);
+      if (g0 + 2 * U < ge) load(0, g0 + 2 * U);
+      compute(1, g0 + U);
     }
+    if (g0 < ge) compute(0, g0);
   }
 
   if (S > 1) {
@@ -146,6 +297,40 @@ __global__ __launch_bounds__(1024) void gemv_mfma_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// launch selection
+// ---------------------------------------------------------------------------
+
+constexpr int kDotMaxM = 4;
+
+template <int M>
+void launch_dot(const uint16_t* X, int64_t ldx, const uint32_t* codes, const uint16_t* scales,
+                const int32_t* zeros, int N, int K, uint16_t* Y, int64_t ldy, hipStream_t stream) {
+  const int S = (K + kSlice - 1) / kSlice;
+  const dim3 block(S * kWave);
+  // Rows per block: R rows per batch, NB batches, the next batch's loads in
+  // flight while the current one is reduced.  Take the most batches that
+  // still leave >= 4096 waves (16 per CU) to fill the chip.
+  constexpr int R = 4;
+  const int64_t waves_nb1 = (int64_t)((N + R - 1) / R) * S;
+  if (M >= 4 && waves_nb1 >= 2 * 4096) {  // more batches would spill at M = 4
+    hipLaunchKernelGGL((gemv_dot_kernel<M, R, 2>), dim3((N + 2 * R - 1) / (2 * R)), block, 0, stream,
+                       X, ldx, codes, scales, zeros, N, K, Y, ldy);
+  } else if (waves_nb1 >= 8 * 4096) {
+    hipLaunchKernelGGL((gemv_dot_kernel<M, R, 8>), dim3((N + 8 * R - 1) / (8 * R)), block, 0, stream,
+                       X, ldx, codes, scales, zeros, N, K, Y, ldy);
+  } else if (waves_nb1 >= 4 * 4096) {
+    hipLaunchKernelGGL((gemv_dot_kernel<M, R, 4>), dim3((N + 4 * R - 1) / (4 * R)), block, 0, stream,
+                       X, ldx, codes, scales, zeros, N, K, Y, ldy);
+  } else if (waves_nb1 >= 2 * 4096) {
+    hipLaunchKernelGGL((gemv_dot_kernel<M, R, 2>), dim3((N + 2 * R - 1) / (2 * R)), block, 0, stream,
+                       X, ldx, codes, scales, zeros, N, K, Y, ldy);
+  } else {
+    hipLaunchKernelGGL((gemv_dot_kernel<M, R, 1>), dim3((N + R - 1) / R), block, 0, stream, X,
+                       ldx, codes, scales, zeros, N, K, Y, ldy);
+  }
+}
+
 int pick_waves(int G) {
   int s = G / 4;
   if (s < 1) s = 1;
@@ -158,12 +343,22 @@ int pick_waves(int G) {
 int launch_gemv(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
                 const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K, uint16_t* Y,
                 int64_t ldy, hipStream_t stream) {
+  if (M <= kDotMaxM && K <= (int64_t)kSlice * kMaxSlices) {
+    const int n = (int)N, k = (int)K;
+    switch (M) {
+      case 1: launch_dot<1>(X, ldx, codes, scales, zeros, n, k, Y, ldy, stream); break;
+      case 2: launch_dot<2>(X, ldx, codes, scales, zeros, n, k, Y, ldy, stream); break;
+      case 3: launch_dot<3>(X, ldx, codes, scales, zeros, n, k, Y, ldy, stream); break;
+      default: launch_dot<4>(X, ldx, codes, scales, zeros, n, k, Y, ldy, stream); break;
+    }
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+  }
   const int G = (int)(K / kGroup);
   const int S = pick_waves(G);
   const dim3 grid((unsigned)((N + 15) / 16));
   const dim3 block(S * kWave);
   if (M <= 16)
-    hipLaunchKernelGGL((gemv_mfma_kernel<1, 4>), grid, block, 0, stream, X, (int)M, ldx, codes,
+    hipLaunchKernelGGL((gemv_mfma_kernel<1, 2>), grid, block, 0, stream, X, (int)M, ldx, codes,
                        scales, zeros, (int)N, (int)K, Y, ldy);
   else
     hipLaunchKernelGGL((gemv_mfma_kernel<2, 2>), grid, block, 0, stream, X, (int)M, ldx, codes,
