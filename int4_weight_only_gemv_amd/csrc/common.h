@@ -13,11 +13,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kGroup = 128;
 constexpr int kWave = 64;
 
-// Two BF16 values 128 + a and 128 + b packed in one dword: BF16 0x4300 is
-// 128.0 and its 7 mantissa bits count in units of 1, so OR-ing a 4-bit code
-// into the mantissa gives 128 + code exactly.
-constexpr uint32_t kBias128Pair = 0x43004300u;
-constexpr uint32_t kNibblePairMask = 0x000F000Fu;
+// BF16 0x4300 is 128.0 and its 7 mantissa bits count in units of 1, so a
+// 4-bit code placed in the low mantissa bits gives 128 + code exactly.
 constexpr uint32_t kOnePair = 0x3F803F80u;  // BF16 (1.0, 1.0)
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
@@ -35,12 +32,22 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // Eight 4-bit codes of one word -> eight BF16 operands 128 + q, ordered so
 // that dword j holds (code j, code j+4).  The matching activation operand
 // must use the same pairing (see x_pairs_from_natural).
+//
+// Seven ops per word: one mask for the even codes (one per byte), a shift and
+// a mask for the odd codes, then one byte permute per dword that places two
+// code bytes under the exponent byte 0x43 of BF16 128.0.
+constexpr uint32_t kExpBytes = 0x43434343u;
+constexpr uint32_t kSelLoHalf = 0x04020400u;  // (S1.b0, 0x43, S1.b2, 0x43)
+constexpr uint32_t kSelHiHalf = 0x04030401u;  // (S1.b1, 0x43, S1.b3, 0x43)
+
 __device__ __forceinline__ u32x4 codes_to_bias128_pairs(uint32_t w) {
+  const uint32_t even = w & 0x0F0F0F0Fu;          // bytes: q0 q2 q4 q6
+  const uint32_t odd = (w >> 4) & 0x0F0F0F0Fu;    // bytes: q1 q3 q5 q7
   u32x4 r;
-  r[0] = (w & kNibblePairMask) | kBias128Pair;
-  r[1] = ((w >> 4) & kNibblePairMask) | kBias128Pair;
-  r[2] = ((w >> 8) & kNibblePairMask) | kBias128Pair;
-  r[3] = ((w >> 12) & kNibblePairMask) | kBias128Pair;
+  r[0] = __builtin_amdgcn_perm(kExpBytes, even, kSelLoHalf);  // (q0, q4)
+  r[1] = __builtin_amdgcn_perm(kExpBytes, odd, kSelLoHalf);   // (q1, q5)
+  r[2] = __builtin_amdgcn_perm(kExpBytes, even, kSelHiHalf);  // (q2, q6)
+  r[3] = __builtin_amdgcn_perm(kExpBytes, odd, kSelHiHalf);   // (q3, q7)
   return r;
 }
 
