@@ -1,25 +1,30 @@
 // Prefill-shaped fused W4A16 matmul on the BF16 matrix cores (gfx950).
 //
-// Same arithmetic as the decode kernels (Axe Corsa model card, "The
-// Two-Stage Pipeline": dequantise inside the multiply): per group of 128
-// inputs the codes become exact BF16 operands 128 + q, the matrix cores
-// produce
-//   P[m,n]  = sum_{k in g} X[m,k] (128 + q[n,k])   and
-//   Xs[m]   = sum_{k in g} X[m,k]                  (A against a B of ones),
-// and the group is folded into the float32 accumulator with
-//   acc += s[n,g] * (P - (128 + z[n,g]) * Xs).
-// No weight is rounded to BF16, so the only rounding beyond float32
-// accumulation is the final BF16 store.
+// Y[m,n] = sum_g s[n,g] * sum_{k in g} X[m,k] (q[n,k] - z[n,g])  (Axe Corsa
+// model card, "The Two-Stage Pipeline": dequantise inside the multiply).
 //
-// Tiling: a 512-thread block (8 waves, 4 along M x 2 along N) computes a
-// 256 x 128 tile of Y; each wave owns 64 x 64 (4 x 4 MFMA 16x16x32 tiles).
-// A K step is half a group (64 inputs).  X[256][64] and the codes
-// [128][8 words] of a step go straight from global memory to LDS
-// (global_load_lds_dwordx4, no register staging) into one of three LDS
-// stages, two steps ahead of the matrix cores, with one barrier per step.
-// X rows are stored with their 16-byte chunks XOR-swizzled by row so the
-// A-fragment reads spread over the LDS banks.  Codes are unpacked in natural
-// k order, so X needs no permutation.  Tiles are handed to the 8 XCDs in
+// Operands.  Codes become exact BF16 values 128 + q (each nibble placed in
+// the mantissa of BF16 128.0), so no weight is ever rounded.  Per group the
+// matrix cores add sum_k X (128 + q) into the accumulator; the same A
+// operand against a B of ones gives Xs[m] = sum_{k in g} X[m,k].
+//
+// One accumulator, rescaled per group.  The accumulator T is kept in units
+// of the current group's scale:
+//     end of group g:  T <- (T - (128 + z[n,g]) Xs[m]) * s[n,g] / s[n,g+1]
+// and after the last group the factor is s[n,G-1] itself, so T = Y.  The
+// scale ratios are formed in float32 (about 1e-7 relative each); the
+// packer's scales are positive normal BF16 values.
+//
+// Tiling.  A 512-thread block (8 waves, 2 along M x 4 along N) computes a
+// 256 x 256 tile of Y; each wave owns 128 x 64 (8 x 4 MFMA 16x16x32 tiles).
+// The four waves that share 128 rows each compute the activation sums of two
+// of the eight 16-row tiles and exchange them through LDS.  A K step is a
+// quarter group (32 inputs).  X[256][32] and the codes [256][4 words] of a
+// step go straight from global memory to LDS (global_load_lds_dwordx4) into
+// one of four LDS stages, three steps ahead of the matrix cores, with one
+// barrier per step.  X rows are stored with their 16-byte chunks XOR-swizzled by row
+// so A-fragment reads spread over the LDS banks.  Codes are unpacked in
+// natural k order, so X needs no permutation.  Tiles go to the 8 XCDs in
 // contiguous runs with N fastest, so blocks that share X rows share an L2.
 
 #include "common.h"
@@ -28,24 +33,29 @@ namespace w4a16 {
 namespace {
 
 constexpr int BM = 256;
-constexpr int BN = 128;
-constexpr int KS = 64;                 // inputs per K step (half a group)
+constexpr int BN = 256;
+constexpr int WM = 128, WN = 64;       // wave tile
+constexpr int MT = WM / 16, NT = WN / 16;
+constexpr int KS = 32;                 // inputs per K step (a quarter group)
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
-constexpr int kStages = 3;
-constexpr int X_STAGE = BM * KS * 2;   // bytes of X per stage (32 KiB)
+constexpr int kStages = 4;
+constexpr int X_STAGE = BM * KS * 2;   // bytes of X per stage (16 KiB)
 constexpr int C_STAGE = BN * KS / 2;   // bytes of codes per stage (4 KiB)
-constexpr int X_LOADS = X_STAGE / 1024 / kWaves;  // 1-KiB wave loads of X per wave per step (4)
-constexpr int C_WAVES = C_STAGE / 1024;           // waves that also load one KiB of codes (4)
+constexpr int X_LOADS = X_STAGE / 1024 / kWaves;  // 1-KiB wave copies of X per wave per step
 constexpr int kXcds = 8;
+constexpr int XS_TILES = MT / 4;       // activation-sum tiles computed by each wave
+constexpr int C_WAVES = C_STAGE / 1024;          // waves that also copy 1 KiB of codes
+constexpr int kSteps = kGroup / KS;               // K steps per group
+static_assert(X_LOADS == 2 && C_WAVES == 4, "copy split");
+static_assert(kStages == kSteps, "stage and position in the group are both s mod 4");
 
 typedef __attribute__((address_space(3))) void lds_void;
 
 template <int V>
-struct StageIdx {
+struct Ic {
   static constexpr int value = V;
 };
-static_assert(kStages == 3, "the main loop is unrolled over three stages");
 
 // Eight codes of one word -> BF16 operands 128 + q in natural k order:
 // dword j holds (code 2j, code 2j+1).
@@ -62,11 +72,13 @@ __device__ __forceinline__ u32x4 codes_to_bias128_natural(uint32_t w) {
   return r;
 }
 
-// Wait until at most n vector-memory operations of this wave are in flight.
+// Wait until at most n vector-memory operations of this wave are in flight
+// and all of its LDS operations are done (so LDS writes made before the
+// following barrier are visible to the whole block after it).
 template <int n>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(n < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
 }
 
 __global__ __launch_bounds__(kThreads) void gemm_kernel(
@@ -74,9 +86,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K,
     uint16_t* __restrict__ Y, int64_t ldy, int m_tiles, int n_tiles) {
   // one LDS object per stage, so the compiler can tell the copies into one
-  // stage from the reads of another and never waits for unrelated copies
-  __shared__ __attribute__((aligned(1024))) uint8_t xs0[X_STAGE], xs1[X_STAGE], xs2[X_STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t cs0[C_STAGE], cs1[C_STAGE], cs2[C_STAGE];
+  // stage from the reads of another
+  __shared__ __attribute__((aligned(1024))) uint8_t xs0[X_STAGE], xs1[X_STAGE], xs2[X_STAGE], xs3[X_STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t cs0[C_STAGE], cs1[C_STAGE], cs2[C_STAGE], cs3[C_STAGE];
+  __shared__ __attribute__((aligned(16))) float xsum_lds[BM];
 
   // XCD-aware tile order: consecutive block ids land on different XCDs, so
   // give XCD x the contiguous run of tiles [x T/8, (x+1) T/8), N fastest.
@@ -88,158 +101,174 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+  const int wm = wave & 1, wn = wave >> 1;
   const int r16 = lane & 15, q = lane >> 4;
   const int G = K / kGroup;
-  const int steps = 2 * G;
-  const int64_t words_per_row = K / 8;
+  const int steps = kSteps * G;
 
-  // ---- direct-to-LDS copies.  X: wave load j of wave w fills tile rows
-  // 8 (X_LOADS w + j) .. +7; lane -> row + lane/8, LDS chunk slot lane%8,
-  // which holds global chunk slot ^ (row & 7).
-  const uint16_t* xsrc[X_LOADS];
-  int xoff[X_LOADS];
+  // ---- direct-to-LDS copies, addressed as a block-uniform base plus a
+  // 32-bit per-lane element offset.  X: copy j of wave w fills tile rows
+  // 16 (2w + j) .. +15 (64 B each); lane -> row + lane/4, LDS chunk slot
+  // lane%4, which holds global chunk slot ^ (row & 3) (= (lane >> 2) & 3).
+  // Codes: wave w < 4 fills code rows 64 w .. +63, one 16-byte row per lane.
+  // Rows past M (N) read the last row and are never stored.
+  const uint16_t* xblk = X + (int64_t)m0 * ldx;
+  const int xrow0 = 16 * X_LOADS * wave + (lane >> 2);
+  uint32_t xoffs[X_LOADS];
 #pragma unroll
-  for (int j = 0; j < X_LOADS; ++j) {
-    const int row = 8 * (X_LOADS * wave + j) + (lane >> 3);
-    const int chunk = (lane & 7) ^ (row & 7);
-    xsrc[j] = X + (int64_t)min(m0 + row, M - 1) * ldx + chunk * 8;
-    xoff[j] = 8 * (X_LOADS * wave + j) * (KS * 2);
-  }
-  // codes: wave w < C_WAVES fills code rows 32 w .. +31 (32 B each)
-  const uint32_t* csrc = codes + (int64_t)min(n0 + 32 * wave + (lane >> 1), N - 1) * words_per_row +
-                         (lane & 1) * 4;
-  const int coff = 32 * wave * (KS / 2);
-  auto issue = [&](int s, uint8_t* xdst, uint8_t* cdst) {
+  for (int j = 0; j < X_LOADS; ++j)
+    xoffs[j] = (uint32_t)((min(m0 + xrow0 + 16 * j, M - 1) - m0) * ldx) +
+               ((((lane & 3) ^ ((lane >> 2) & 3))) * 8);
+  const int xoff0 = 16 * X_LOADS * wave * (KS * 2);
+  const uint32_t* cblk = codes + (int64_t)n0 * (K / 8);
+  uint32_t coffs = (uint32_t)((min(n0 + 64 * (wave & (C_WAVES - 1)) + lane, N - 1) - n0) * (K / 8));
+  const int coff = 64 * (wave & (C_WAVES - 1)) * (KS / 2);
+  auto issue = [&](uint8_t* xdst, uint8_t* cdst) {
 #pragma unroll
-    for (int j = 0; j < X_LOADS; ++j)
-      __builtin_amdgcn_global_load_lds(xsrc[j] + s * KS, (lds_void*)&xdst[xoff[j]], 16, 0, 0);
-    if (wave < C_WAVES)
-      __builtin_amdgcn_global_load_lds(csrc + s * (KS / 8), (lds_void*)&cdst[coff], 16, 0, 0);
-  };
-
-  // this lane's output columns (one per 16-wide n tile) for scales / zeros
-  const int ncol0 = n0 + wn * 64 + r16;
-  int64_t meta[4];
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) meta[nt] = (int64_t)min(ncol0 + nt * 16, N - 1) * G;
-  uint32_t sraw[4];
-  int zraw[4];
-  auto fetch_meta = [&](int g) {
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      sraw[nt] = scales[meta[nt] + g];
-      zraw[nt] = zeros[meta[nt] + g];
+    for (int j = 0; j < X_LOADS; ++j) {
+      __builtin_amdgcn_global_load_lds(xblk + xoffs[j], (lds_void*)&xdst[xoff0 + j * 16 * (KS * 2)], 16, 0, 0);
+      xoffs[j] += KS;
+    }
+    if (wave < C_WAVES) {
+      __builtin_amdgcn_global_load_lds(cblk + coffs, (lds_void*)&cdst[coff], 16, 0, 0);
+      coffs += KS / 8;
     }
   };
 
-  // LDS read addresses: A row (wm 64 + mt 16 + r16), logical chunk 2q + kc
-  // (inputs 16q + 8kc .. +7 of the step); B row (wn 64 + nt 16 + r16),
-  // words 2q, 2q + 1.
-  int aoff[4][2];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const int row = wm * 64 + mt * 16 + r16;
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) aoff[mt][kc] = row * (KS * 2) + (((2 * q + kc) ^ (row & 7)) * 16);
-  }
-  int boff[4];
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) boff[nt] = (wn * 64 + nt * 16 + r16) * (KS / 2) + q * 8;
+  // this lane's output columns (one per 16-wide n tile) for scales / zeros:
+  // column ncol + 16 nt, clamped to N - 1
+  const int ncol = n0 + wn * WN + r16;
+  auto meta_index = [&](int nt, int g) { return min(ncol + 16 * nt, N - 1) * G + g; };
+  uint32_t s_cur[NT], s_nxt[NT];
+  int z_cur[NT], z_nxt[NT];
 
-  f32x4 acc[4][4], pg[4][4], xsum[4];
+  // LDS read offsets: A row (wm 128 + mt 16 + r16), logical chunk q (inputs
+  // 8q .. 8q+7 of the step); B row (wn 64 + nt 16 + r16), word q.  Rows r
+  // and r + 16 share the swizzle (r & 3).
+  const int arow = wm * WM + r16;
+  const int aoff = arow * (KS * 2) + ((q ^ (arow & 3)) * 16);
+  const int boff = (wn * WN + r16) * (KS / 2) + q * 4;
+
+  f32x4 acc[MT][NT];
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    xsum[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int a = 0; a < MT; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-      pg[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  }
+    for (int b = 0; b < NT; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 xpart[XS_TILES];  // this wave's share of the group's activation sums
   const u32x4 ones = {kOnePair, kOnePair, kOnePair, kOnePair};
 
-  fetch_meta(0);
-  issue(0, xs0, cs0);
-  if (steps > 1) issue(1, xs1, cs1);
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    s_cur[nt] = scales[meta_index(nt, 0)];
+    z_cur[nt] = zeros[meta_index(nt, 0)];
+    s_nxt[nt] = s_cur[nt];
+    z_nxt[nt] = z_cur[nt];
+  }
+  issue(xs0, cs0);
+  if (steps > 1) issue(xs1, cs1);
+  if (steps > 2) issue(xs2, cs2);
 
-  // one K step on LDS stage ST (= s mod 3); copies for step s + 2 go to
-  // stage (ST + 2) mod 3, which every wave finished reading at step s - 1
+  // fold a finished group into the accumulator: remove bias and zero point,
+  // move to the next group's scale (or, after the last group, apply it)
+  auto group_end = [&](bool last) {
+    float zb[NT], ratio[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      zb[nt] = (float)(128 + z_cur[nt]);
+      const float sc = bf16_to_f32(s_cur[nt]);
+      ratio[nt] = last ? sc : __fdividef(sc, bf16_to_f32(s_nxt[nt]));
+      s_cur[nt] = s_nxt[nt];
+      z_cur[nt] = z_nxt[nt];
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const f32x4 xs = *reinterpret_cast<const f32x4*>(&xsum_lds[wm * WM + mt * 16 + 4 * q]);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[mt][nt][r] = fmaf(-zb[nt], xs[r], acc[mt][nt][r]) * ratio[nt];
+    }
+  };
+
+  // One K step: stage ST = s mod 4 = position of the step in its group.
+  // Copies for step s + 3 go to stage (ST + 3) mod 4, which every wave
+  // finished reading at step s - 1.
   auto step = [&](auto stage, int s) {
     constexpr int ST = decltype(stage)::value;
-    uint8_t* xs = ST == 0 ? xs0 : (ST == 1 ? xs1 : xs2);
-    uint8_t* cs = ST == 0 ? cs0 : (ST == 1 ? cs1 : cs2);
-    uint8_t* xn = ST == 0 ? xs2 : (ST == 1 ? xs0 : xs1);
-    uint8_t* cn = ST == 0 ? cs2 : (ST == 1 ? cs0 : cs1);
-    // step s landed in LDS once only the next step's copies are in flight
-    if (s + 1 < steps) {
+    uint8_t* xs = ST == 0 ? xs0 : (ST == 1 ? xs1 : (ST == 2 ? xs2 : xs3));
+    uint8_t* cs = ST == 0 ? cs0 : (ST == 1 ? cs1 : (ST == 2 ? cs2 : cs3));
+    uint8_t* xn = ST == 0 ? xs3 : (ST == 1 ? xs0 : (ST == 2 ? xs1 : xs2));
+    uint8_t* cn = ST == 0 ? cs3 : (ST == 1 ? cs0 : (ST == 2 ? cs1 : cs2));
+    // step s landed in LDS once at most the next two steps' copies are in flight
+    if (s + 2 < steps) {
+      if (wave < C_WAVES) wait_vmcnt<2 * (X_LOADS + 1)>(); else wait_vmcnt<2 * X_LOADS>();
+    } else if (s + 1 < steps) {
       if (wave < C_WAVES) wait_vmcnt<X_LOADS + 1>(); else wait_vmcnt<X_LOADS>();
     } else {
       wait_vmcnt<0>();
     }
     __builtin_amdgcn_s_barrier();
-    // scale/zero of this step's group, fetched before the next copies so the
-    // in-order vmcnt waits above never wait on the copies just issued
-    if (s > 0 && !(s & 1)) fetch_meta(s / 2);
-    if (s + 2 < steps) issue(s + 2, xn, cn);
-
-    u32x2 bw[4];
+    const int g = s / kSteps;
+    if (ST == 0) {
+      // the previous group's activation sums are in LDS: fold it in
+      if (s > 0) group_end(false);
+      // next group's scale/zero, fetched before the next copies so the
+      // in-order vmcnt waits above never wait on the copies just issued
+      if (g + 1 < G) {
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) bw[nt] = *reinterpret_cast<const u32x2*>(&cs[boff[nt]]);
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      u32x4 af[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) af[mt] = *reinterpret_cast<const u32x4*>(&xs[aoff[mt][kc]]);
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const u32x4 b = codes_to_bias128_natural(bw[nt][kc]);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) pg[mt][nt] = mfma16x16x32(af[mt], b, pg[mt][nt]);
-      }
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) xsum[mt] = mfma16x16x32(af[mt], ones, xsum[mt]);
-    }
-
-    if (s & 1) {  // group complete: fold it into the accumulator
-      float sc[4], zb[4];
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        sc[nt] = bf16_to_f32(sraw[nt]);
-        zb[nt] = (float)(128 + zraw[nt]);
-      }
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float d = fmaf(-zb[nt], xsum[mt][r], pg[mt][nt][r]);
-            acc[mt][nt][r] = fmaf(sc[nt], d, acc[mt][nt][r]);
-          }
-          pg[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int nt = 0; nt < NT; ++nt) {
+          s_nxt[nt] = scales[meta_index(nt, g + 1)];
+          z_nxt[nt] = zeros[meta_index(nt, g + 1)];
         }
-        xsum[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
+    }
+    if (s + 3 < steps) issue(xn, cn);
+
+    u32x4 b[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      b[nt] = codes_to_bias128_natural(*reinterpret_cast<const uint32_t*>(&cs[boff + nt * 16 * (KS / 2)]));
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const u32x4 af = *reinterpret_cast<const u32x4*>(&xs[aoff + mt * 16 * (KS * 2)]);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma16x16x32(af, b[nt], acc[mt][nt]);
+      if (mt / XS_TILES == wn) {
+        const int i = mt % XS_TILES;
+        xpart[i] = mfma16x16x32(af, ones, ST == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : xpart[i]);
+      }
+    }
+    if (ST == kSteps - 1) {
+      // publish this wave's activation sums.  Every column of the ones
+      // product holds the same sums, so all 16 lanes of a row group store
+      // identical values to the same place; keeping the store outside any
+      // lane-dependent branch keeps the matrix-core op that feeds it from
+      // being moved under a partial exec mask.
+#pragma unroll
+      for (int i = 0; i < XS_TILES; ++i)
+        *reinterpret_cast<f32x4*>(&xsum_lds[wm * WM + (wn * XS_TILES + i) * 16 + 4 * q]) = xpart[i];
     }
   };
 
-  for (int s0 = 0; s0 < steps; s0 += kStages) {
-    step(StageIdx<0>{}, s0);
-    if (s0 + 1 < steps) step(StageIdx<1>{}, s0 + 1);
-    if (s0 + 2 < steps) step(StageIdx<2>{}, s0 + 2);
+  for (int s0 = 0; s0 < steps; s0 += kSteps) {
+    step(Ic<0>{}, s0);
+    step(Ic<1>{}, s0 + 1);
+    step(Ic<2>{}, s0 + 2);
+    step(Ic<3>{}, s0 + 3);
   }
+  __syncthreads();   // last group's activation sums
+  group_end(true);
 
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int n = n0 + wn * 64 + nt * 16 + r16;
+    for (int nt = 0; nt < NT; ++nt) {
+      const int n = n0 + wn * WN + nt * 16 + r16;
       if (n >= N) continue;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm * 64 + mt * 16 + 4 * q + r;
+        const int m = m0 + wm * WM + mt * 16 + 4 * q + r;
         if (m < M) Y[(int64_t)m * ldy + n] = f32_to_bf16_rne(acc[mt][nt][r]);
       }
     }
