@@ -165,6 +165,17 @@ def main():
     del graphs
     torch.cuda.synchronize()
 
+    # ---- a plain copy of known size: the reference that scales the HBM
+    # byte counters of a profiling run (64 MiB read + 64 MiB written)
+    cal_src = torch.zeros(16 << 20, dtype=torch.int32, device=dev)
+    cal_dst = torch.empty_like(cal_src)
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            torch.add(cal_src, 1, out=cal_dst)
+        stream.synchronize()
+    del cal_src, cal_dst
+    roofline["traffic"] = measured_traffic(layers[dom], M)
+
     # ---- prefill GEMM on the same layers
     prefill = None
     if not args.no_prefill:
@@ -233,6 +244,35 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def kernel_source_digest() -> str:
+    """sha256 of the decode kernel's sources (the counters recorded under
+    profiles/ only apply to the code they were taken on)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemv.hip", "common.h"):
+        with open(os.path.join(ROOT, "int4_weight_only_gemv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(layer, M):
+    """HBM bytes per launch of the dominant decode launch, from the FETCH_SIZE
+    and WRITE_SIZE counters recorded in profiles/ (each scaled by what the
+    counter read for a copy of known size), or None when they were taken on
+    other kernel sources or another shape."""
+    path = os.path.join(ROOT, "profiles", "gemv_llama8b_decode_m1_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except OSError:
+        return None
+    if rec.get("source_sha256") != kernel_source_digest():
+        return None
+    if (rec.get("N"), rec.get("K"), rec.get("M")) != (layer.N, layer.K, M):
+        return None
+    return rec.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(layers, workload, spec, M, dev, row_stride=2, min_seconds=10.0):
