@@ -91,6 +91,23 @@ __global__ __launch_bounds__(1024) void gemv_dot_kernel(
   const int g = kc >> 7;
   const int64_t wpr = K / 8;
 
+  const int row0 = blockIdx.x * RB;
+  const u32x4* cbase = reinterpret_cast<const u32x4*>(codes) + kc / 32;
+  u32x4 cb[2][R];
+  uint32_t sb[2][R];
+  int zb[2][R];
+  auto load = [&](int buf, int batch) {
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const int row = min(row0 + batch * R + j, N - 1);
+      cb[buf][j] = __builtin_nontemporal_load(cbase + (int64_t)row * (wpr / 4));
+      sb[buf][j] = scales[(int64_t)row * G + g];
+      zb[buf][j] = zeros[(int64_t)row * G + g];
+    }
+  };
+
+  load(0, 0);  // the weight stream first: it is the long-latency path
+
   // this lane's 32 activations of every batch row, paired like the codes
   u32x4 xp[M][4];
   float xs[M];
@@ -109,22 +126,6 @@ __global__ __launch_bounds__(1024) void gemv_dot_kernel(
     xs[m] = sum;
   }
 
-  const int row0 = blockIdx.x * RB;
-  const u32x4* cbase = reinterpret_cast<const u32x4*>(codes) + kc / 32;
-  u32x4 cb[2][R];
-  uint32_t sb[2][R];
-  int zb[2][R];
-  auto load = [&](int buf, int batch) {
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-      const int row = min(row0 + batch * R + j, N - 1);
-      cb[buf][j] = __builtin_nontemporal_load(cbase + (int64_t)row * (wpr / 4));
-      sb[buf][j] = scales[(int64_t)row * G + g];
-      zb[buf][j] = zeros[(int64_t)row * G + g];
-    }
-  };
-
-  load(0, 0);
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int cur = nb & 1;
@@ -309,25 +310,35 @@ void launch_dot(const uint16_t* X, int64_t ldx, const uint32_t* codes, const uin
   const int S = (K + kSlice - 1) / kSlice;
   const dim3 block(S * kWave);
   // Rows per block: R rows per batch, NB batches, the next batch's loads in
-  // flight while the current one is reduced.  Take the most batches that
-  // still leave >= 4096 waves (16 per CU) to fill the chip.
+  // flight while the current one is reduced.  Few batches for small layers
+  // (all loads issued at once), more for long rows (K >= 14336) and for very
+  // tall layers; never fewer blocks than CUs.  Fitted to timings on the
+  // decode shapes of the 8B- and 70B-sized layer sets.
   constexpr int R = 4;
-  const int64_t waves_nb1 = (int64_t)((N + R - 1) / R) * S;
-  if (M >= 4 && waves_nb1 >= 2 * 4096) {  // more batches would spill at M = 4
-    hipLaunchKernelGGL((gemv_dot_kernel<M, R, 2>), dim3((N + 2 * R - 1) / (2 * R)), block, 0, stream,
-                       X, ldx, codes, scales, zeros, N, K, Y, ldy);
-  } else if (waves_nb1 >= 8 * 4096) {
-    hipLaunchKernelGGL((gemv_dot_kernel<M, R, 8>), dim3((N + 8 * R - 1) / (8 * R)), block, 0, stream,
-                       X, ldx, codes, scales, zeros, N, K, Y, ldy);
-  } else if (waves_nb1 >= 4 * 4096) {
-    hipLaunchKernelGGL((gemv_dot_kernel<M, R, 4>), dim3((N + 4 * R - 1) / (4 * R)), block, 0, stream,
-                       X, ldx, codes, scales, zeros, N, K, Y, ldy);
-  } else if (waves_nb1 >= 2 * 4096) {
-    hipLaunchKernelGGL((gemv_dot_kernel<M, R, 2>), dim3((N + 2 * R - 1) / (2 * R)), block, 0, stream,
-                       X, ldx, codes, scales, zeros, N, K, Y, ldy);
-  } else {
-    hipLaunchKernelGGL((gemv_dot_kernel<M, R, 1>), dim3((N + R - 1) / R), block, 0, stream, X,
-                       ldx, codes, scales, zeros, N, K, Y, ldy);
+  const int64_t w1 = (int64_t)((N + R - 1) / R) * S;
+  int nb;
+  if (w1 <= 4096) nb = 1;
+  else if (S >= 7) nb = S >= 14 ? 8 : 4;
+  else nb = w1 <= 16384 ? 2 : 4;
+  while (nb > 1 && N / (R * nb) < 256) nb >>= 1;
+  if (M >= 4 && nb > 2) nb = 2;  // more batches would spill at M = 4
+  const dim3 grid((unsigned)((N + R * nb - 1) / (R * nb)));
+  switch (nb) {
+    case 8:
+      hipLaunchKernelGGL((gemv_dot_kernel<M, R, (M >= 4 ? 2 : 8)>), grid, block, 0, stream, X, ldx,
+                         codes, scales, zeros, N, K, Y, ldy);
+      break;
+    case 4:
+      hipLaunchKernelGGL((gemv_dot_kernel<M, R, (M >= 4 ? 2 : 4)>), grid, block, 0, stream, X, ldx,
+                         codes, scales, zeros, N, K, Y, ldy);
+      break;
+    case 2:
+      hipLaunchKernelGGL((gemv_dot_kernel<M, R, 2>), grid, block, 0, stream, X, ldx, codes, scales,
+                         zeros, N, K, Y, ldy);
+      break;
+    default:
+      hipLaunchKernelGGL((gemv_dot_kernel<M, R, 1>), grid, block, 0, stream, X, ldx, codes, scales,
+                         zeros, N, K, Y, ldy);
   }
 }
 
