@@ -12,8 +12,9 @@
 // of the current group's scale:
 //     end of group g:  T <- (T - (128 + z[n,g]) Xs[m]) * s[n,g] / s[n,g+1]
 // and after the last group the factor is s[n,G-1] itself, so T = Y.  The
-// scale ratios are formed in float32 (about 1e-7 relative each); the
-// packer's scales are positive normal BF16 values.
+// scale ratios come from the hardware reciprocal (1 ulp) and one float32
+// multiply, a few 1e-7 relative each; the packer's scales are positive
+// normal BF16 values.
 //
 // Tiling.  A 512-thread block (8 waves, 2 along M x 4 along N) computes a
 // 256 x 256 tile of Y; each wave owns 128 x 64 (8 x 4 MFMA 16x16x32 tiles).
@@ -22,10 +23,12 @@
 // quarter group (32 inputs).  X[256][32] and the codes [256][4 words] of a
 // step go straight from global memory to LDS (global_load_lds_dwordx4) into
 // one of four LDS stages, three steps ahead of the matrix cores, with one
-// barrier per step.  X rows are stored with their 16-byte chunks XOR-swizzled by row
-// so A-fragment reads spread over the LDS banks.  Codes are unpacked in
-// natural k order, so X needs no permutation.  Tiles go to the 8 XCDs in
-// contiguous runs with N fastest, so blocks that share X rows share an L2.
+// barrier per step.  X rows (64 bytes) are stored with their 16-byte chunks
+// XOR-swizzled by (row >> 1) & 3, so the eight rows that one 128-byte LDS
+// cycle of a 16-byte-per-lane read serves fall on eight distinct bank groups.
+// Codes are unpacked in natural k order, so X needs no permutation.  Tiles go
+// to the 8 XCDs in contiguous runs with N fastest, so blocks that share X rows
+// share an L2.
 
 #include "common.h"
 
@@ -45,7 +48,7 @@ constexpr int C_STAGE = BN * KS / 2;   // bytes of codes per stage (4 KiB)
 constexpr int X_LOADS = X_STAGE / 1024 / kWaves;  // 1-KiB wave copies of X per wave per step
 constexpr int kXcds = 8;
 constexpr int XS_TILES = MT / 4;       // activation-sum tiles computed by each wave
-constexpr int C_WAVES = C_STAGE / 1024;          // waves that also copy 1 KiB of codes
+constexpr int C_WAVES = C_STAGE / 1024;          // 1-KiB code copies per step (each made by two waves)
 constexpr int kSteps = kGroup / KS;               // K steps per group
 static_assert(X_LOADS == 2 && C_WAVES == 4, "copy split");
 static_assert(kStages == kSteps, "stage and position in the group are both s mod 4");
@@ -81,6 +84,19 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
 }
 
+// Wait until the copies of the step at group position ST have landed.  Every
+// step, each wave issues L copies (for the step three ahead, clamped to the
+// last step) and, at position 0, the 2 NT scale/zero loads of the next group
+// (clamped to the last group) before them.  The memory counter retires in
+// issue order, so the wait may leave in flight exactly what was issued after
+// this step's copies: the next two steps' copies and, at positions 1 and 2,
+// the scale/zero loads.  No load is conditional, so the counts are fixed.
+template <int L, int ST>
+__device__ __forceinline__ void wait_step() {
+  constexpr int kMeta = 2 * NT;
+  if (ST == 1 || ST == 2) wait_vmcnt<2 * L + kMeta>(); else wait_vmcnt<2 * L>();
+}
+
 __global__ __launch_bounds__(kThreads) void gemm_kernel(
     const uint16_t* __restrict__ X, int M, int64_t ldx, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K,
@@ -108,46 +124,54 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
   const int steps = kSteps * G;
 
   // ---- direct-to-LDS copies, addressed as a block-uniform base plus a
-  // 32-bit per-lane element offset.  X: copy j of wave w fills tile rows
-  // 16 (2w + j) .. +15 (64 B each); lane -> row + lane/4, LDS chunk slot
-  // lane%4, which holds global chunk slot ^ (row & 3) (= (lane >> 2) & 3).
-  // Codes: wave w < 4 fills code rows 64 w .. +63, one 16-byte row per lane.
-  // Rows past M (N) read the last row and are never stored.
-  const uint16_t* xblk = X + (int64_t)m0 * ldx;
+  // 32-bit per-lane byte offset (the launcher keeps these below 2^32).
+  // X: copy j of wave w fills tile rows 16 (2w + j) .. +15 (64 B each);
+  // lane -> row + lane/4, LDS chunk slot lane%4, which holds global chunk
+  // slot ^ ((row >> 1) & 3) (= (lane >> 3) & 3).  Codes: wave w fills code
+  // rows 64 (w % 4) .. +63, one 16-byte row per lane; waves 4..7 repeat the
+  // copies of waves 0..3 (the same bytes to the same LDS rows), so every wave
+  // issues the same three copies per step and one set of memory-counter
+  // waits holds for all of them.  Rows past M (N) read the last row and are
+  // never stored.
+  const char* xblk = reinterpret_cast<const char*>(X + (int64_t)m0 * ldx);
   const int xrow0 = 16 * X_LOADS * wave + (lane >> 2);
   uint32_t xoffs[X_LOADS];
 #pragma unroll
   for (int j = 0; j < X_LOADS; ++j)
-    xoffs[j] = (uint32_t)((min(m0 + xrow0 + 16 * j, M - 1) - m0) * ldx) +
-               ((((lane & 3) ^ ((lane >> 2) & 3))) * 8);
+    xoffs[j] = (uint32_t)(min(m0 + xrow0 + 16 * j, M - 1) - m0) * (uint32_t)(ldx * 2) +
+               (uint32_t)(((lane & 3) ^ ((lane >> 3) & 3)) * 16);
   const int xoff0 = 16 * X_LOADS * wave * (KS * 2);
-  const uint32_t* cblk = codes + (int64_t)n0 * (K / 8);
-  uint32_t coffs = (uint32_t)((min(n0 + 64 * (wave & (C_WAVES - 1)) + lane, N - 1) - n0) * (K / 8));
+  const char* cblk = reinterpret_cast<const char*>(codes + (int64_t)n0 * (K / 8));
+  const uint32_t coffs =
+      (uint32_t)(min(n0 + 64 * (wave & (C_WAVES - 1)) + lane, N - 1) - n0) * (uint32_t)(K / 2);
   const int coff = 64 * (wave & (C_WAVES - 1)) * (KS / 2);
-  auto issue = [&](uint8_t* xdst, uint8_t* cdst) {
+  // copies of K step t (the caller clamps t to the last step, so the copy
+  // count per step never changes and the memory-counter waits stay fixed)
+  auto issue = [&](uint8_t* xdst, uint8_t* cdst, int t) {
 #pragma unroll
-    for (int j = 0; j < X_LOADS; ++j) {
-      __builtin_amdgcn_global_load_lds(xblk + xoffs[j], (lds_void*)&xdst[xoff0 + j * 16 * (KS * 2)], 16, 0, 0);
-      xoffs[j] += KS;
-    }
-    if (wave < C_WAVES) {
-      __builtin_amdgcn_global_load_lds(cblk + coffs, (lds_void*)&cdst[coff], 16, 0, 0);
-      coffs += KS / 8;
-    }
+    for (int j = 0; j < X_LOADS; ++j)
+      __builtin_amdgcn_global_load_lds(xblk + (xoffs[j] + (uint32_t)(t * KS * 2)),
+                                       (lds_void*)&xdst[xoff0 + j * 16 * (KS * 2)], 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(cblk + (coffs + (uint32_t)(t * (KS / 2))), (lds_void*)&cdst[coff], 16, 0, 0);
   };
 
   // this lane's output columns (one per 16-wide n tile) for scales / zeros:
-  // column ncol + 16 nt, clamped to N - 1
+  // column ncol + 16 nt, clamped to N - 1; element offsets from the block's
+  // first column
   const int ncol = n0 + wn * WN + r16;
-  auto meta_index = [&](int nt, int g) { return min(ncol + 16 * nt, N - 1) * G + g; };
+  const uint16_t* sblk = scales + (int64_t)n0 * G;
+  const int32_t* zblk = zeros + (int64_t)n0 * G;
+  uint32_t moffs[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) moffs[nt] = (uint32_t)(min(ncol + 16 * nt, N - 1) - n0) * (uint32_t)G;
   uint32_t s_cur[NT], s_nxt[NT];
   int z_cur[NT], z_nxt[NT];
 
   // LDS read offsets: A row (wm 128 + mt 16 + r16), logical chunk q (inputs
   // 8q .. 8q+7 of the step); B row (wn 64 + nt 16 + r16), word q.  Rows r
-  // and r + 16 share the swizzle (r & 3).
+  // and r + 16 share the swizzle ((r >> 1) & 3).
   const int arow = wm * WM + r16;
-  const int aoff = arow * (KS * 2) + ((q ^ (arow & 3)) * 16);
+  const int aoff = arow * (KS * 2) + ((q ^ ((arow >> 1) & 3)) * 16);
   const int boff = (wn * WN + r16) * (KS / 2) + q * 4;
 
   f32x4 acc[MT][NT];
@@ -160,14 +184,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    s_cur[nt] = scales[meta_index(nt, 0)];
-    z_cur[nt] = zeros[meta_index(nt, 0)];
+    s_cur[nt] = sblk[moffs[nt]];
+    z_cur[nt] = zblk[moffs[nt]];
     s_nxt[nt] = s_cur[nt];
     z_nxt[nt] = z_cur[nt];
   }
-  issue(xs0, cs0);
-  if (steps > 1) issue(xs1, cs1);
-  if (steps > 2) issue(xs2, cs2);
+  issue(xs0, cs0, 0);   // steps >= 4
+  issue(xs1, cs1, 1);
+  issue(xs2, cs2, 2);
 
   // fold a finished group into the accumulator: remove bias and zero point,
   // move to the next group's scale (or, after the last group, apply it)
@@ -177,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     for (int nt = 0; nt < NT; ++nt) {
       zb[nt] = (float)(128 + z_cur[nt]);
       const float sc = bf16_to_f32(s_cur[nt]);
-      ratio[nt] = last ? sc : __fdividef(sc, bf16_to_f32(s_nxt[nt]));
+      ratio[nt] = last ? sc : sc * __builtin_amdgcn_rcpf(bf16_to_f32(s_nxt[nt]));
       s_cur[nt] = s_nxt[nt];
       z_cur[nt] = z_nxt[nt];
     }
@@ -200,30 +224,22 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     uint8_t* cs = ST == 0 ? cs0 : (ST == 1 ? cs1 : (ST == 2 ? cs2 : cs3));
     uint8_t* xn = ST == 0 ? xs3 : (ST == 1 ? xs0 : (ST == 2 ? xs1 : xs2));
     uint8_t* cn = ST == 0 ? cs3 : (ST == 1 ? cs0 : (ST == 2 ? cs1 : cs2));
-    // step s landed in LDS once at most the next two steps' copies are in flight
-    if (s + 2 < steps) {
-      if (wave < C_WAVES) wait_vmcnt<2 * (X_LOADS + 1)>(); else wait_vmcnt<2 * X_LOADS>();
-    } else if (s + 1 < steps) {
-      if (wave < C_WAVES) wait_vmcnt<X_LOADS + 1>(); else wait_vmcnt<X_LOADS>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    __builtin_amdgcn_s_barrier();
     const int g = s / kSteps;
+    wait_step<X_LOADS + 1, ST>();
+    __builtin_amdgcn_s_barrier();
     if (ST == 0) {
       // the previous group's activation sums are in LDS: fold it in
       if (s > 0) group_end(false);
-      // next group's scale/zero, fetched before the next copies so the
-      // in-order vmcnt waits above never wait on the copies just issued
-      if (g + 1 < G) {
+      // next group's scale/zero (the last group's again after the last),
+      // issued before this step's copies, as wait_step counts them
+      const int gn = min(g + 1, G - 1);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          s_nxt[nt] = scales[meta_index(nt, g + 1)];
-          z_nxt[nt] = zeros[meta_index(nt, g + 1)];
-        }
+      for (int nt = 0; nt < NT; ++nt) {
+        s_nxt[nt] = sblk[moffs[nt] + gn];
+        z_nxt[nt] = zblk[moffs[nt] + gn];
       }
     }
-    if (s + 3 < steps) issue(xn, cn);
+    issue(xn, cn, min(s + 3, steps - 1));
 
     u32x4 b[NT];
 #pragma unroll
@@ -234,10 +250,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
       const u32x4 af = *reinterpret_cast<const u32x4*>(&xs[aoff + mt * 16 * (KS * 2)]);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma16x16x32(af, b[nt], acc[mt][nt]);
-      if (mt / XS_TILES == wn) {
-        const int i = mt % XS_TILES;
-        xpart[i] = mfma16x16x32(af, ones, ST == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : xpart[i]);
-      }
+    }
+    // this wave's share of the activation sums: its own two 16-row tiles,
+    // re-read from LDS so no matrix-core op sits under a per-wave branch
+#pragma unroll
+    for (int i = 0; i < XS_TILES; ++i) {
+      const u32x4 af = *reinterpret_cast<const u32x4*>(&xs[aoff + (wn * XS_TILES + i) * 16 * (KS * 2)]);
+      xpart[i] = mfma16x16x32(af, ones, ST == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : xpart[i]);
     }
     if (ST == kSteps - 1) {
       // publish this wave's activation sums.  Every column of the ones
@@ -257,6 +276,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     step(Ic<2>{}, s0 + 2);
     step(Ic<3>{}, s0 + 3);
   }
+  wait_vmcnt<0>();   // the clamped copies past the last step
   __syncthreads();   // last group's activation sums
   group_end(true);
 
@@ -281,6 +301,8 @@ int launch_gemm(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes
                 int64_t ldy, hipStream_t stream) {
   const int64_t mt = (M + BM - 1) / BM, nt = (N + BN - 1) / BN;
   if (mt * nt >= ((int64_t)1 << 31)) return 3;
+  // per-lane 32-bit byte offsets within a tile's rows of X and of the codes
+  if ((BM - 1) * ldx * 2 + K * 2 >= ((int64_t)1 << 32) || BN * (K / 2) >= ((int64_t)1 << 32)) return 3;
   hipLaunchKernelGGL(gemm_kernel, dim3((unsigned)(mt * nt)), dim3(kThreads), 0, stream, X, (int)M,
                      ldx, codes, scales, zeros, (int)N, (int)K, Y, ldy, (int)mt, (int)nt);
   return hipGetLastError() == hipSuccess ? 0 : 4;
