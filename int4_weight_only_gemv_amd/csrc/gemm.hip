@@ -42,18 +42,25 @@ constexpr int MT = WM / 16, NT = WN / 16;
 constexpr int KS = 32;                 // inputs per K step (a quarter group)
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
-constexpr int kStages = 4;
-constexpr int X_STAGE = BM * KS * 2;   // bytes of X per stage (16 KiB)
-constexpr int C_STAGE = BN * KS / 2;   // bytes of codes per stage (4 KiB)
-constexpr int X_LOADS = X_STAGE / 1024 / kWaves;  // 1-KiB wave copies of X per wave per step
+constexpr int kSteps = kGroup / KS;    // K steps per group
+constexpr int X_STAGE = BM * KS * 2;   // bytes of X per stage (16 KiB), four stages
+constexpr int C_ROW = kGroup / 2;      // bytes of codes per column per group (64)
+constexpr int C_GROUP = BN * C_ROW;    // bytes of codes per group (16 KiB), two buffers
+constexpr int X_LOADS = X_STAGE / 1024 / kWaves;  // 1-KiB X copies per wave per step
+constexpr int C_LOADS = C_GROUP / 1024 / kWaves;  // 1-KiB code copies per wave per group
 constexpr int kXcds = 8;
 constexpr int XS_TILES = MT / 4;       // activation-sum tiles computed by each wave
-constexpr int C_WAVES = C_STAGE / 1024;          // 1-KiB code copies per step (each made by two waves)
-constexpr int kSteps = kGroup / KS;               // K steps per group
-static_assert(X_LOADS == 2 && C_WAVES == 4, "copy split");
-static_assert(kStages == kSteps, "stage and position in the group are both s mod 4");
+static_assert(X_LOADS == 2 && C_LOADS == 2, "copy split");
 
 typedef __attribute__((address_space(3))) void lds_void;
+
+// Block barrier that the compiler may not move memory accesses across
+// (the bare builtin does not order them at the IR level).
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 template <int V>
 struct Ic {
@@ -84,27 +91,29 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
 }
 
-// Wait until the copies of the step at group position ST have landed.  Every
-// step, each wave issues L copies (for the step three ahead, clamped to the
-// last step) and, at position 0, the 2 NT scale/zero loads of the next group
-// (clamped to the last group) before them.  The memory counter retires in
-// issue order, so the wait may leave in flight exactly what was issued after
-// this step's copies: the next two steps' copies and, at positions 1 and 2,
-// the scale/zero loads.  No load is conditional, so the counts are fixed.
-template <int L, int ST>
+// Memory operations each wave issues, in this order: at group position 0,
+// the next group's 2 NT scale/zero loads and C_LOADS code copies; at every
+// step, X_LOADS copies of X for the step four ahead.  Nothing is
+// conditional (indices are clamped to the last group / step), so the
+// in-order memory counter gives fixed waits.  At the step at position ST
+// the wait is for the X copies of the following step; what may stay in
+// flight is everything issued after them: two more steps of X copies and,
+// at positions 1 and 2, the group-start loads.  At position 3 the wait also
+// covers the next group's code copies (issued before the awaited X copies).
+template <int ST>
 __device__ __forceinline__ void wait_step() {
-  constexpr int kMeta = 2 * NT;
-  if (ST == 1 || ST == 2) wait_vmcnt<2 * L + kMeta>(); else wait_vmcnt<2 * L>();
+  constexpr int kGroupStart = 2 * NT + C_LOADS;
+  if (ST == 1 || ST == 2) wait_vmcnt<2 * X_LOADS + kGroupStart>(); else wait_vmcnt<2 * X_LOADS>();
 }
 
 __global__ __launch_bounds__(kThreads) void gemm_kernel(
     const uint16_t* __restrict__ X, int M, int64_t ldx, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K,
     uint16_t* __restrict__ Y, int64_t ldy, int m_tiles, int n_tiles) {
-  // one LDS object per stage, so the compiler can tell the copies into one
-  // stage from the reads of another
+  // one LDS object per buffer, so the compiler can tell the copies into one
+  // buffer from the reads of another
   __shared__ __attribute__((aligned(1024))) uint8_t xs0[X_STAGE], xs1[X_STAGE], xs2[X_STAGE], xs3[X_STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t cs0[C_STAGE], cs1[C_STAGE], cs2[C_STAGE], cs3[C_STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t cg0[C_GROUP], cg1[C_GROUP];
   __shared__ __attribute__((aligned(16))) float xsum_lds[BM];
 
   // XCD-aware tile order: consecutive block ids land on different XCDs, so
@@ -124,35 +133,41 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
   const int steps = kSteps * G;
 
   // ---- direct-to-LDS copies, addressed as a block-uniform base plus a
-  // 32-bit per-lane byte offset (the launcher keeps these below 2^32).
-  // X: copy j of wave w fills tile rows 16 (2w + j) .. +15 (64 B each);
-  // lane -> row + lane/4, LDS chunk slot lane%4, which holds global chunk
-  // slot ^ ((row >> 1) & 3) (= (lane >> 3) & 3).  Codes: wave w fills code
-  // rows 64 (w % 4) .. +63, one 16-byte row per lane; waves 4..7 repeat the
-  // copies of waves 0..3 (the same bytes to the same LDS rows), so every wave
-  // issues the same three copies per step and one set of memory-counter
-  // waits holds for all of them.  Rows past M (N) read the last row and are
-  // never stored.
+  // 32-bit per-lane byte offset (the launcher keeps these below 2^32).  A
+  // copy instruction fills 64 consecutive 16-byte LDS slots, four per row:
+  // lane -> row lane/4, slot lane%4, and slot p of row r holds the row's
+  // 16-byte chunk p ^ ((r >> 1) & 3) (= (lane >> 3) & 3), so that reads of
+  // one chunk from consecutive rows spread over the LDS banks.
+  //   X, per step: rows of 32 inputs (64 B); copy j of wave w fills tile
+  //   rows 16 (2w + j) .. +15.
+  //   Codes, per group: rows of 128 codes (64 B, chunk = step); copy j of
+  //   wave w fills code rows 16 (2w + j) .. +15.
+  // Rows past M (N) read the last row and are never stored.
+  const uint32_t swz = (uint32_t)(((lane & 3) ^ ((lane >> 3) & 3)) * 16);
   const char* xblk = reinterpret_cast<const char*>(X + (int64_t)m0 * ldx);
-  const int xrow0 = 16 * X_LOADS * wave + (lane >> 2);
-  uint32_t xoffs[X_LOADS];
+  const char* cblk = reinterpret_cast<const char*>(codes + (int64_t)n0 * (K / 8));
+  uint32_t xoffs[X_LOADS], coffs[C_LOADS];
 #pragma unroll
   for (int j = 0; j < X_LOADS; ++j)
-    xoffs[j] = (uint32_t)(min(m0 + xrow0 + 16 * j, M - 1) - m0) * (uint32_t)(ldx * 2) +
-               (uint32_t)(((lane & 3) ^ ((lane >> 3) & 3)) * 16);
-  const int xoff0 = 16 * X_LOADS * wave * (KS * 2);
-  const char* cblk = reinterpret_cast<const char*>(codes + (int64_t)n0 * (K / 8));
-  const uint32_t coffs =
-      (uint32_t)(min(n0 + 64 * (wave & (C_WAVES - 1)) + lane, N - 1) - n0) * (uint32_t)(K / 2);
-  const int coff = 64 * (wave & (C_WAVES - 1)) * (KS / 2);
-  // copies of K step t (the caller clamps t to the last step, so the copy
-  // count per step never changes and the memory-counter waits stay fixed)
-  auto issue = [&](uint8_t* xdst, uint8_t* cdst, int t) {
+    xoffs[j] = (uint32_t)(min(m0 + 16 * (X_LOADS * wave + j) + (lane >> 2), M - 1) - m0) * (uint32_t)(ldx * 2) + swz;
+#pragma unroll
+  for (int j = 0; j < C_LOADS; ++j)
+    coffs[j] = (uint32_t)(min(n0 + 16 * (C_LOADS * wave + j) + (lane >> 2), N - 1) - n0) * (uint32_t)(K / 2) + swz;
+  const int xdst0 = 16 * X_LOADS * wave * (KS * 2);
+  const int cdst0 = 16 * C_LOADS * wave * C_ROW;
+  // X copies of K step t (clamped by the caller)
+  auto copy_x = [&](uint8_t* dst, int t) {
 #pragma unroll
     for (int j = 0; j < X_LOADS; ++j)
       __builtin_amdgcn_global_load_lds(xblk + (xoffs[j] + (uint32_t)(t * KS * 2)),
-                                       (lds_void*)&xdst[xoff0 + j * 16 * (KS * 2)], 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(cblk + (coffs + (uint32_t)(t * (KS / 2))), (lds_void*)&cdst[coff], 16, 0, 0);
+                                       (lds_void*)&dst[xdst0 + j * 16 * (KS * 2)], 16, 0, 0);
+  };
+  // code copies of group g (clamped by the caller)
+  auto copy_codes = [&](uint8_t* dst, int g) {
+#pragma unroll
+    for (int j = 0; j < C_LOADS; ++j)
+      __builtin_amdgcn_global_load_lds(cblk + (coffs[j] + (uint32_t)(g * C_ROW)),
+                                       (lds_void*)&dst[cdst0 + j * 16 * C_ROW], 16, 0, 0);
   };
 
   // this lane's output columns (one per 16-wide n tile) for scales / zeros:
@@ -167,12 +182,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
   uint32_t s_cur[NT], s_nxt[NT];
   int z_cur[NT], z_nxt[NT];
 
-  // LDS read offsets: A row (wm 128 + mt 16 + r16), logical chunk q (inputs
-  // 8q .. 8q+7 of the step); B row (wn 64 + nt 16 + r16), word q.  Rows r
-  // and r + 16 share the swizzle ((r >> 1) & 3).
+  // LDS read offsets.  A: row (wm 128 + mt 16 + r16), chunk q (inputs
+  // 8q .. 8q+7 of the step).  B: code row (wn 64 + nt 16 + r16), chunk =
+  // step position, word q.  Rows r and r + 16 share the swizzle.
   const int arow = wm * WM + r16;
   const int aoff = arow * (KS * 2) + ((q ^ ((arow >> 1) & 3)) * 16);
-  const int boff = (wn * WN + r16) * (KS / 2) + q * 4;
+  const int brow = wn * WN + r16;
+  const int bswz = (brow >> 1) & 3;
+  const int boff = brow * C_ROW + q * 4;
 
   f32x4 acc[MT][NT];
 #pragma unroll
@@ -181,17 +198,6 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     for (int b = 0; b < NT; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 xpart[XS_TILES];  // this wave's share of the group's activation sums
   const u32x4 ones = {kOnePair, kOnePair, kOnePair, kOnePair};
-
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    s_cur[nt] = sblk[moffs[nt]];
-    z_cur[nt] = zblk[moffs[nt]];
-    s_nxt[nt] = s_cur[nt];
-    z_nxt[nt] = z_cur[nt];
-  }
-  issue(xs0, cs0, 0);   // steps >= 4
-  issue(xs1, cs1, 1);
-  issue(xs2, cs2, 2);
 
   // fold a finished group into the accumulator: remove bias and zero point,
   // move to the next group's scale (or, after the last group, apply it)
@@ -215,49 +221,101 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     }
   };
 
-  // One K step: stage ST = s mod 4 = position of the step in its group.
-  // Copies for step s + 3 go to stage (ST + 3) mod 4, which every wave
-  // finished reading at step s - 1.
-  auto step = [&](auto stage, int s) {
+  // Operand fragments of one K step, read from LDS one step ahead of use:
+  // A (8 row tiles), the A of this wave's two activation-sum tiles, and the
+  // raw code words of the 4 column tiles (chunk `pos` of the group buffer).
+  u32x4 af[MT], xf[XS_TILES];
+  uint32_t bw[NT];
+  auto read_frags = [&](const uint8_t* xs, const uint8_t* cg, int pos) {
+    const int bo = boff + ((pos ^ bswz) * 16);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) bw[nt] = *reinterpret_cast<const uint32_t*>(&cg[bo + nt * 16 * C_ROW]);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) af[mt] = *reinterpret_cast<const u32x4*>(&xs[aoff + mt * 16 * (KS * 2)]);
+#pragma unroll
+    for (int i = 0; i < XS_TILES; ++i)
+      xf[i] = *reinterpret_cast<const u32x4*>(&xs[aoff + (wn * XS_TILES + i) * 16 * (KS * 2)]);
+  };
+
+  // prologue: group 0's scale/zero and codes, steps 0..3 of X in flight,
+  // step 0's fragments in registers (steps >= 4)
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    s_cur[nt] = sblk[moffs[nt]];
+    z_cur[nt] = zblk[moffs[nt]];
+    s_nxt[nt] = s_cur[nt];
+    z_nxt[nt] = z_cur[nt];
+  }
+  auto prologue = [&](uint8_t* cg_first) {   // group 0's code buffer
+    copy_codes(cg_first, 0);
+    copy_x(xs0, 0);
+    copy_x(xs1, 1);
+    copy_x(xs2, 2);
+    copy_x(xs3, 3);
+    wait_vmcnt<3 * X_LOADS>();
+    block_barrier();
+    read_frags(xs0, cg_first, 0);
+  };
+  // (two static calls rather than one with a selected pointer, so the
+  // compiler still tells the two code buffers apart)
+  if (G & 1) prologue(cg1); else prologue(cg0);
+
+  // One K step s at group position ST = s mod 4 of a group using code
+  // buffer GP, whose X sits in stage ST; its fragments
+  // are already in registers.  After the barrier stage ST is free (its reads
+  // finished before it), so it takes the X of step s + 4; at position 0 the
+  // other code buffer (read last two steps ago) takes the next group's
+  // codes.  Meanwhile the fragments of step s + 1 are read while the matrix
+  // cores work on step s.
+  auto step = [&](auto stage, auto parity, int s) {
     constexpr int ST = decltype(stage)::value;
-    uint8_t* xs = ST == 0 ? xs0 : (ST == 1 ? xs1 : (ST == 2 ? xs2 : xs3));
-    uint8_t* cs = ST == 0 ? cs0 : (ST == 1 ? cs1 : (ST == 2 ? cs2 : cs3));
-    uint8_t* xn = ST == 0 ? xs3 : (ST == 1 ? xs0 : (ST == 2 ? xs1 : xs2));
-    uint8_t* cn = ST == 0 ? cs3 : (ST == 1 ? cs0 : (ST == 2 ? cs1 : cs2));
+    constexpr int GP = decltype(parity)::value;
+    uint8_t* xs_here = ST == 0 ? xs0 : (ST == 1 ? xs1 : (ST == 2 ? xs2 : xs3));
+    uint8_t* xs_next = ST == 0 ? xs1 : (ST == 1 ? xs2 : (ST == 2 ? xs3 : xs0));
+    uint8_t* cg_here = GP == 0 ? cg0 : cg1;
+    uint8_t* cg_other = GP == 0 ? cg1 : cg0;
     const int g = s / kSteps;
-    wait_step<X_LOADS + 1, ST>();
-    __builtin_amdgcn_s_barrier();
+    wait_step<ST>();   // step s + 1 landed, every read of stage ST done
+    block_barrier();
+    // pin this step's fragments here, so the compiler cannot pull their uses
+    // up into the previous step next to the reads that produced them
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) asm volatile("" : "+v"(af[mt]));
+#pragma unroll
+    for (int i = 0; i < XS_TILES; ++i) asm volatile("" : "+v"(xf[i]));
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) asm volatile("" : "+v"(bw[nt]));
     if (ST == 0) {
       // the previous group's activation sums are in LDS: fold it in
       if (s > 0) group_end(false);
-      // next group's scale/zero (the last group's again after the last),
-      // issued before this step's copies, as wait_step counts them
+      // next group's scale/zero and codes (the last group's again after the
+      // last), issued before this step's X copies, as wait_step counts them
       const int gn = min(g + 1, G - 1);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         s_nxt[nt] = sblk[moffs[nt] + gn];
         z_nxt[nt] = zblk[moffs[nt] + gn];
       }
+      copy_codes(cg_other, gn);
     }
-    issue(xn, cn, min(s + 3, steps - 1));
+    copy_x(xs_here, min(s + 4, steps - 1));
 
     u32x4 b[NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      b[nt] = codes_to_bias128_natural(*reinterpret_cast<const uint32_t*>(&cs[boff + nt * 16 * (KS / 2)]));
+    for (int nt = 0; nt < NT; ++nt) b[nt] = codes_to_bias128_natural(bw[nt]);
+    const u32x4 x0 = xf[0], x1 = xf[1];
+    u32x4 a[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const u32x4 af = *reinterpret_cast<const u32x4*>(&xs[aoff + mt * 16 * (KS * 2)]);
+    for (int mt = 0; mt < MT; ++mt) a[mt] = af[mt];
+    // next step's fragments (past the last step: a harmless re-read)
+    if (ST == kSteps - 1) read_frags(xs_next, cg_other, 0); else read_frags(xs_next, cg_here, ST + 1);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma16x16x32(af, b[nt], acc[mt][nt]);
-    }
-    // this wave's share of the activation sums: its own two 16-row tiles,
-    // re-read from LDS so no matrix-core op sits under a per-wave branch
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int i = 0; i < XS_TILES; ++i) {
-      const u32x4 af = *reinterpret_cast<const u32x4*>(&xs[aoff + (wn * XS_TILES + i) * 16 * (KS * 2)]);
-      xpart[i] = mfma16x16x32(af, ones, ST == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : xpart[i]);
-    }
+      for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma16x16x32(a[mt], b[nt], acc[mt][nt]);
+    // this wave's share of the activation sums: its own two 16-row tiles
+    xpart[0] = mfma16x16x32(x0, ones, ST == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : xpart[0]);
+    xpart[1] = mfma16x16x32(x1, ones, ST == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : xpart[1]);
     if (ST == kSteps - 1) {
       // publish this wave's activation sums.  Every column of the ones
       // product holds the same sums, so all 16 lanes of a row group store
@@ -269,12 +327,18 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
         *reinterpret_cast<f32x4*>(&xsum_lds[wm * WM + (wn * XS_TILES + i) * 16 + 4 * q]) = xpart[i];
     }
   };
+  auto group = [&](auto parity, int g) {
+    step(Ic<0>{}, parity, kSteps * g);
+    step(Ic<1>{}, parity, kSteps * g + 1);
+    step(Ic<2>{}, parity, kSteps * g + 2);
+    step(Ic<3>{}, parity, kSteps * g + 3);
+  };
 
-  for (int s0 = 0; s0 < steps; s0 += kSteps) {
-    step(Ic<0>{}, s0);
-    step(Ic<1>{}, s0 + 1);
-    step(Ic<2>{}, s0 + 2);
-    step(Ic<3>{}, s0 + 3);
+  // groups run in pairs (code buffer 0, then 1); an odd count starts with
+  // the second half of a pair
+  for (int g = -(G & 1); g < G; g += 2) {
+    if (g >= 0) group(Ic<0>{}, g);
+    group(Ic<1>{}, g + 1);
   }
   wait_vmcnt<0>();   // the clamped copies past the last step
   __syncthreads();   // last group's activation sums
