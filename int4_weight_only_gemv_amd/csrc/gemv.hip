@@ -49,36 +49,15 @@ constexpr int kMaxSlices = 16;    // K <= 32768 on this kernel
 constexpr int pow2_at_least(int v) { return v <= 1 ? 1 : 2 * pow2_at_least((v + 1) / 2); }
 constexpr int log2_exact(int v) { return v <= 1 ? 0 : 1 + log2_exact(v / 2); }
 
-// Sum V values (a power of two <= 64) over the 64 lanes.  Afterwards lane l
-// holds in v[0] the total of value (l >> (6 - log2 V)).
-template <int V>
-__device__ __forceinline__ void lane_butterfly(float (&v)[V], int lane) {
-  int mask = 32;
-#pragma unroll
-  for (int cur = V; cur > 1; cur >>= 1) {
-    const bool upper = (lane & mask) != 0;
-#pragma unroll
-    for (int i = 0; i < cur / 2; ++i) {
-      const float lo = v[i], hi = v[i + cur / 2];
-      const float send = upper ? lo : hi;
-      const float keep = upper ? hi : lo;
-      v[i] = keep + __shfl_xor(send, mask);
-    }
-    mask >>= 1;
-  }
-#pragma unroll
-  for (; mask >= 1; mask >>= 1) v[0] += __shfl_xor(v[0], mask);
-}
-
 template <int M, int R, int NB>
 __global__ __launch_bounds__(1024) void gemv_dot_kernel(
     const uint16_t* __restrict__ X, int64_t ldx, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K,
     uint16_t* __restrict__ Y, int64_t ldy) {
+  static_assert(R == 4, "a group spans 4 lanes; lane l corrects row l % 4 of its group");
   constexpr int RB = R * NB;                  // rows per block
-  constexpr int V = pow2_at_least(R * M);     // values per butterfly
-  constexpr int LV = log2_exact(V);
-  static_assert(V <= 64, "too many values per butterfly");
+  constexpr int MP = pow2_at_least(M);        // values per lane after the group step
+  constexpr int LM = log2_exact(MP);
   __shared__ float red[kMaxSlices][RB * M];
 
   const int lane = threadIdx.x & 63;
@@ -88,29 +67,31 @@ __global__ __launch_bounds__(1024) void gemv_dot_kernel(
   const bool active = k0 < K;
   const int kc = active ? k0 : K - 32;        // inactive lanes read valid memory, weigh zero
   const int G = K / kGroup;
-  const int g = kc >> 7;
+  const int g = kc >> 7;                      // this lane's group (lanes 4i .. 4i+3 share one)
   const int64_t wpr = K / 8;
 
   const int row0 = blockIdx.x * RB;
   const u32x4* cbase = reinterpret_cast<const u32x4*>(codes) + kc / 32;
   u32x4 cb[2][R];
-  uint32_t sb[2][R];
-  int zb[2][R];
+  uint32_t sb[2];   // scale and zero point of row (lane % 4), group g
+  int zb[2];
   auto load = [&](int buf, int batch) {
 #pragma unroll
     for (int j = 0; j < R; ++j) {
       const int row = min(row0 + batch * R + j, N - 1);
       cb[buf][j] = __builtin_nontemporal_load(cbase + (int64_t)row * (wpr / 4));
-      sb[buf][j] = scales[(int64_t)row * G + g];
-      zb[buf][j] = zeros[(int64_t)row * G + g];
     }
+    const int mrow = min(row0 + batch * R + (lane & 3), N - 1);
+    sb[buf] = scales[(int64_t)mrow * G + g];
+    zb[buf] = zeros[(int64_t)mrow * G + g];
   };
 
   load(0, 0);  // the weight stream first: it is the long-latency path
 
-  // this lane's 32 activations of every batch row, paired like the codes
+  // this lane's 32 activations of every batch row, paired like the codes,
+  // and the activation sums of its group
   u32x4 xp[M][4];
-  float xs[M];
+  float xsg[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     const u32x4* xr = reinterpret_cast<const u32x4*>(X + m * ldx + kc);
@@ -123,37 +104,84 @@ __global__ __launch_bounds__(1024) void gemv_dot_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) sum = dot2(raw[j], kOnePair, sum);
     }
-    xs[m] = sum;
+    sum += __shfl_xor(sum, 1);
+    xsg[m] = sum + __shfl_xor(sum, 2);
   }
 
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int cur = nb & 1;
     if (nb + 1 < NB) load(cur ^ 1, nb + 1);
-    float part[V];
-#pragma unroll
-    for (int v = R * M; v < V; ++v) part[v] = 0.f;
+    // P[j][m]: this lane's 32 products of row j with activation row m
+    float P[R][M];
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-      float P[M];
 #pragma unroll
-      for (int m = 0; m < M; ++m) P[m] = 0.f;
+      for (int m = 0; m < M; ++m) P[j][m] = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const u32x4 b = codes_to_bias128_pairs(cb[cur][j][i]);
 #pragma unroll
         for (int m = 0; m < M; ++m)
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) P[m] = dot2(b[jj], xp[m][i][jj], P[m]);
+          for (int jj = 0; jj < 4; ++jj) P[j][m] = dot2(b[jj], xp[m][i][jj], P[j][m]);
       }
-      const float s = bf16_to_f32(sb[cur][j]);
-      const float zb128 = (float)(128 + zb[cur][j]);
-#pragma unroll
-      for (int m = 0; m < M; ++m) part[j * M + m] = s * fmaf(-zb128, xs[m], P[m]);
     }
-    lane_butterfly<V>(part, lane);
-    const int vi = lane >> (6 - LV);
-    if ((lane & ((64 >> LV) - 1)) == 0 && vi < R * M) red[wave][nb * R * M + vi] = part[0];
+    // Sum over the 4 lanes of the group with a halving butterfly (lane bit 1
+    // picks rows {0,1} or {2,3}, bit 0 one of those), so that lane l ends
+    // with the group sums of row l % 4 ...
+    float h[2][M];
+    {
+      const bool up = (lane & 2) != 0;
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          const float send = up ? P[r][m] : P[r + 2][m];
+          const float keep = up ? P[r + 2][m] : P[r][m];
+          h[r][m] = keep + __shfl_xor(send, 2);
+        }
+    }
+    float part[MP];
+    {
+      const bool up = (lane & 1) != 0;
+      const float s = bf16_to_f32(sb[cur]);
+      const float zb128 = (float)(128 + zb[cur]);
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const float send = up ? h[0][m] : h[1][m];
+        const float keep = up ? h[1][m] : h[0][m];
+        const float q = keep + __shfl_xor(send, 1);
+        // ... and removes the bias and zero point of that (row, group) once
+        part[m] = s * fmaf(-zb128, xsg[m], q);
+      }
+#pragma unroll
+      for (int m = M; m < MP; ++m) part[m] = 0.f;
+    }
+    // then over the 16 groups of the slice (lane bits 2..5): halving on the
+    // activation rows first, plain sums after
+    int mask = 4;
+#pragma unroll
+    for (int cur_n = MP; cur_n > 1; cur_n >>= 1) {
+      const bool up = (lane & mask) != 0;
+#pragma unroll
+      for (int i = 0; i < cur_n / 2; ++i) {
+        const float send = up ? part[i] : part[i + cur_n / 2];
+        const float keep = up ? part[i + cur_n / 2] : part[i];
+        part[i] = keep + __shfl_xor(send, mask);
+      }
+      mask <<= 1;
+    }
+#pragma unroll
+    for (; mask <= 32; mask <<= 1) part[0] += __shfl_xor(part[0], mask);
+    // lane l < 4 MP holds row l % 4 and activation row m from its bits 2..
+    if (lane < 4 * MP) {
+      int m = 0, half = MP / 2;
+#pragma unroll
+      for (int b = 0; b < LM; ++b, half >>= 1)
+        if (lane & (4 << b)) m += half;
+      if (m < M) red[wave][nb * R * M + (lane & 3) * M + m] = part[0];
+    }
   }
   __syncthreads();
   for (int idx = threadIdx.x; idx < RB * M; idx += blockDim.x) {
