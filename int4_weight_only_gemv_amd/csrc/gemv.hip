@@ -345,9 +345,10 @@ void launch_dot(const uint16_t* X, int64_t ldx, const uint32_t* codes, const uin
   constexpr int R = 4;
   const int64_t w1 = (int64_t)((N + R - 1) / R) * S;
   int nb;
-  if (w1 <= 4096) nb = 1;
-  else if (S >= 7) nb = S >= 14 ? 8 : 4;
-  else nb = w1 <= 16384 ? 2 : 4;
+  if (S >= 7) nb = S >= 14 ? 8 : 4;
+  else if (w1 <= 2048) nb = 1;
+  else if (w1 <= 12288) nb = 2;
+  else nb = S <= 2 ? 8 : 4;
   while (nb > 1 && N / (R * nb) < 256) nb >>= 1;
   if (M >= 4 && nb > 2) nb = 2;  // more batches would spill at M = 4
   const dim3 grid((unsigned)((N + R * nb - 1) / (R * nb)));
