@@ -9,8 +9,9 @@ Llama-3-8B-shaped decoder layer (qkv 6144x4096, o 4096x4096, gate_up
 Inputs are seeded synthetic tensors already resident in HBM; the packed
 weights are replicated into enough distinct copies (>= 1 GiB) that every step
 streams them from HBM rather than the 256 MB last-level cache.  Each copy's
-four launches are captured in a HIP graph; the timed region replays K graphs
-back to back between two device synchronisations.
+four launches are captured in a HIP graph, and a rotation through all copies
+in one more; the timed region replays K steps (whole rotations, then single
+steps for any remainder) back to back between two device synchronisations.
 
 value = algorithmic bytes per step / time per step, with algorithmic bytes
 = packed codes + BF16 scales + INT32 zeros + X + Y.
@@ -98,7 +99,9 @@ def main():
     torch.cuda.synchronize()
     step_bytes = sum(decode_bytes(L, M) for L in layers)
 
-    # ---- one HIP graph per copy: the four launches of one step
+    # ---- HIP graphs: one per copy (the four launches of one step) and one
+    # for a whole rotation through the copies (ncopy steps in order), so the
+    # host submits one graph per ncopy steps instead of one per step
     stream = torch.cuda.Stream()
     graphs = []
     with torch.cuda.stream(stream):
@@ -112,15 +115,26 @@ def main():
                 for p, x, y in zip(copies[c], xs, ys):
                     linear(x, p, y)
             graphs.append(g)
+        rotation = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(rotation, stream=stream):
+            for c in range(ncopy):
+                for p, x, y in zip(copies[c], xs, ys):
+                    linear(x, p, y)
     torch.cuda.synchronize()
 
-    with torch.cuda.stream(stream):
-        for s in range(args.warmup):
+    def run_steps(n):
+        """n decode steps, copy (s mod ncopy) at step s, as whole rotations
+        plus single steps for the remainder."""
+        for _ in range(n // ncopy):
+            rotation.replay()
+        for s in range(n - n % ncopy, n):
             graphs[s % ncopy].replay()
+
+    with torch.cuda.stream(stream):
+        run_steps(args.warmup)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for s in range(args.steps):
-            graphs[s % ncopy].replay()
+        run_steps(args.steps)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
