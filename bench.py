@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-m", type=int, default=4096)
+    ap.add_argument("--no-stack", action="store_true",
+                    help="skip the 40-layer decoder-stack stream (about 10.7 GB of packed weights)")
+    ap.add_argument("--stack-tokens", type=int, default=30)
     return ap.parse_args()
 
 
@@ -229,6 +232,12 @@ def main():
         log(f"[bench] prefill M={Mp}: {tf:.1f} TFLOP/s")
         del pxs, pys
 
+    # ---- the full decoder-stack weight stream: 40 layers x 4 linears, AWQ-
+    # folded packing, one token = 160 dependent launches in one graph
+    stack = None
+    if not args.no_stack:
+        stack = stack_decode(args.stack_tokens, dev, stream)
+
     # ---- CPU oracle on a bounded sample of the same step
     cpu = None
     if not args.no_cpu_baseline:
@@ -255,6 +264,7 @@ def main():
         "per_layer": per_layer,
         "roofline": roofline,
         "prefill": prefill,
+        "stack": stack,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -287,6 +297,67 @@ def measured_traffic(layer, M):
     if (rec.get("N"), rec.get("K"), rec.get("M")) != (layer.N, layer.K, M):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def stack_decode(tokens, dev, stream):
+    """Decode of a 40-layer stack (hidden 5120, 40 q / 8 kv heads of 128,
+    SwiGLU 27648): each layer's four linears packed from their own seeded
+    weights after an AWQ pre-scale s = importance^0.5 from a synthetic
+    512-token calibration batch; activations X' = X * (1/s) as the folded
+    producer would emit them.  One token runs the 160 linears in order, at
+    M = 1 (GEMV); the stack (~10.7 GB) is far larger than the last-level
+    cache, so every token streams it from HBM."""
+    import torch
+    import int4_weight_only_gemv_amd as w4
+    from synth import gen
+    spec = gen.WORKLOADS["stack40_decode"]
+    cfg, layers, depth = "stack40_decode", spec["layers"], spec["depth"]
+    t0 = time.perf_counter()
+    seq = []   # (packed, X', Y) per linear, in execution order
+    for d in range(depth):
+        for L in layers:
+            name = f"{L.name}.{d}"
+            W = gen.weights(L.N, L.K, cfg, name, device=dev)
+            xcal = gen.activations(spec["calib_tokens"], L.K, cfg, name, role="Xcal", device=dev)
+            s_awq = w4.w4a16_awq_scale(w4.w4a16_awq_importance(xcal), spec["awq_alpha"])
+            p = w4.w4a16_pack(W, awq_s=s_awq)
+            gamma = torch.ones(L.K, dtype=torch.bfloat16, device=dev)
+            w4.w4a16_awq_fold(s_awq, gamma)
+            x = w4.w4a16_scale_channels(gen.activations(1, L.K, cfg, name, device=dev), gamma)
+            seq.append((p, x, torch.empty(1, L.N, dtype=torch.bfloat16, device=dev)))
+            del W, xcal
+    torch.cuda.synchronize()
+    nbytes = sum(decode_bytes(L, 1) for L in layers) * depth
+    log(f"[bench] stack: {len(seq)} linears, {nbytes / 1e9:.2f} GB per token, "
+        f"built in {time.perf_counter() - t0:.1f} s")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        for p, x, y in seq:
+            w4.w4a16_gemv(x, p, y)
+        stream.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for p, x, y in seq:
+                w4.w4a16_gemv(x, p, y)
+        for _ in range(3):
+            g.replay()
+        stream.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(tokens):
+            g.replay()
+        e1.record(stream)
+        e1.synchronize()
+    ms = e0.elapsed_time(e1) / tokens
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"[bench] stack decode M=1: {ms:.3f} ms/token, {gbs:.0f} GB/s")
+    del seq, g
+    torch.cuda.synchronize()
+    return {"workload": "40-layer decoder stack (hidden 5120, 40/8 heads of 128, SwiGLU 27648), "
+                        "INT4 group 128, AWQ alpha 0.5", "M": 1, "linears_per_token": 4 * depth,
+            "bytes_per_token": nbytes, "ms_per_token": round(ms, 4),
+            "tokens_per_s": round(1e3 / ms, 1), "GBps": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "tokens_timed": tokens}
 
 
 def cpu_baseline(layers, workload, spec, M, dev, row_stride=2, min_seconds=10.0):

@@ -29,6 +29,8 @@
 
 #include "common.h"
 
+#include <cmath>
+
 namespace w4a16 {
 namespace {
 
@@ -332,6 +334,19 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(
 
 constexpr int kDotMaxM = 4;
 
+// compute units of the current device (queried once per device)
+int cu_count() {
+  static int counts[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (counts[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    counts[dev] = n;
+  }
+  return counts[dev];
+}
+
 template <int M>
 void launch_dot(const uint16_t* X, int64_t ldx, const uint32_t* codes, const uint16_t* scales,
                 const int32_t* zeros, int N, int K, uint16_t* Y, int64_t ldy, hipStream_t stream) {
@@ -341,15 +356,29 @@ void launch_dot(const uint16_t* X, int64_t ldx, const uint32_t* codes, const uin
   // flight while the current one is reduced.  Few batches for small layers
   // (all loads issued at once), more for long rows (K >= 14336) and for very
   // tall layers; never fewer blocks than CUs.  Fitted to timings on the
-  // decode shapes of the 8B- and 70B-sized layer sets.
+  // decode shapes of the 8B- and 70B-sized layer sets and the 40-layer
+  // stack.
+  // Blocks are spread evenly over the CUs only if their count is close to
+  // a multiple of the CU count: `balance` is the busy fraction of the
+  // busiest CU's share.
   constexpr int R = 4;
+  const int cus = cu_count();
+  auto balance = [&](int nb) {
+    const double per_cu = (double)((N + R * nb - 1) / (R * nb)) / cus;
+    return per_cu / std::ceil(per_cu);
+  };
   const int64_t w1 = (int64_t)((N + R - 1) / R) * S;
   int nb;
-  if (S >= 7) nb = S >= 14 ? 8 : 4;
-  else if (w1 <= 2048) nb = 1;
-  else if (w1 <= 12288) nb = 2;
-  else nb = S <= 2 ? 8 : 4;
-  while (nb > 1 && N / (R * nb) < 256) nb >>= 1;
+  if (S >= 7) {
+    nb = 8;
+    while (nb > 2 && balance(nb) < 0.8) nb >>= 1;
+  } else {
+    if (w1 <= 2048) nb = 1;
+    else if (w1 <= 12288) nb = 2;
+    else nb = S <= 2 ? 8 : 4;
+    if (nb > 1 && balance(nb) < 0.85 && balance(nb / 2) > balance(nb)) nb >>= 1;
+  }
+  while (nb > 1 && N / (R * nb) < cus) nb >>= 1;
   if (M >= 4 && nb > 2) nb = 2;  // more batches would spill at M = 4
   const dim3 grid((unsigned)((N + R * nb - 1) / (R * nb)));
   switch (nb) {
