@@ -20,10 +20,11 @@
 // are folded across lanes with a halving butterfly (ds_bpermute), then
 // across the K slices of the block through LDS in a fixed order.
 //
-// gemv_mfma (larger M): a 16-row tile of W meets a 16-row tile of X
-// (M padded) on v_mfma_f32_16x16x32_bf16; the same A operand against a B of
-// ones gives the per-group activation sums.  The waves of a block split K
-// and add their partial tiles through LDS in a fixed order.
+// gemv_tile (larger M): 16-row tiles of W meet X (M padded to 16 or 32) on
+// v_mfma_f32_16x16x32_bf16, one group of a tile per 16-byte load per lane;
+// the same A operand against a B of ones gives the per-group activation
+// sums.  The waves of a block split K and add their partial tiles through
+// LDS in a fixed order.
 //
 // Neither kernel uses atomics or workspace: results are deterministic.
 
@@ -197,135 +198,158 @@ __global__ __launch_bounds__(1024) void gemv_dot_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// gemv_mfma
+// gemv_tile (5 <= M <= 32): weights on the matrix cores, codes streamed
 // ---------------------------------------------------------------------------
+//
+// D = A B on v_mfma_f32_16x16x32_bf16 with A = 16 activation rows (M padded)
+// and B = 16 weight rows, so lane (r16, q) of a result tile holds weight row
+// r16 for activation rows 4q .. 4q+3 and needs one scale / zero point.  One
+// 16-byte load per lane brings four code words of one row: a row tile's
+// group (16 rows x 64 B) per instruction; word 4q + t feeds k-step t, so
+// k-step t covers inputs 32q + 8t .. +7 of the group in lane group q, and
+// the activation fragment of lane (m, q) for k-step t is the 16 bytes of X
+// at that position, paired like the codes.  The same A against a B of ones
+// gives the activation sums of the group in the result layout.  A wave runs
+// RT row tiles over its share of the groups, the next group's codes and
+// activations in flight; the waves of a block split K and add their partial
+// tiles through LDS in a fixed order.
 
-constexpr int kMaxWaves = 8;
+constexpr int kTileMaxWaves = 8;
 
-template <int MT, int U>
-__global__ __launch_bounds__(512) void gemv_mfma_kernel(
+template <int MT, int RT>
+__global__ __launch_bounds__(512) void gemv_tile_kernel(
     const uint16_t* __restrict__ X, int M, int64_t ldx, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K,
     uint16_t* __restrict__ Y, int64_t ldy) {
-  __shared__ float red[kMaxWaves][MT * 4][kWave];
+  __shared__ float red[kTileMaxWaves][RT * MT * 4][kWave];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int S = blockDim.x / kWave;
   const int G = K / kGroup;
-  const int col = lane & 15;  // output row of the tile (MFMA column)
-  const int kq = lane >> 4;   // 32-input quarter of the group this lane feeds
+  const int r16 = lane & 15, q = lane >> 4;
+  const int gb = (G * wave) / S, ge = (G * (wave + 1)) / S;
 
-  const int n = blockIdx.x * 16 + col;
-  const int n_ld = n < N ? n : N - 1;
-  const int gb = (G * wave) / S;
-  const int ge = (G * (wave + 1)) / S;
-
-  const u32x4* crow = reinterpret_cast<const u32x4*>(codes + (int64_t)n_ld * (K / 8)) + kq;
-  const uint16_t* srow = scales + (int64_t)n_ld * G;
-  const int32_t* zrow = zeros + (int64_t)n_ld * G;
-
-  // A-operand rows m = (lane & 15) + 16 mt; rows past M read row 0 and are
-  // zeroed after the load (no divergent loads)
+  // weight rows of this lane (one per row tile), clamped for loads
+  const u32x4* crow[RT];
+  const uint16_t* srow[RT];
+  const int32_t* zrow[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int n = min((int)blockIdx.x * 16 * RT + 16 * rt + r16, N - 1);
+    crow[rt] = reinterpret_cast<const u32x4*>(codes + (int64_t)n * (K / 8)) + q;
+    srow[rt] = scales + (int64_t)n * G;
+    zrow[rt] = zeros + (int64_t)n * G;
+  }
+  // activation rows of this lane (A operand rows r16 + 16 mt); rows past M
+  // read row 0 and are zeroed after the load
   const u32x4* xrow[MT];
   bool xvalid[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int m = col + 16 * mt;
+    const int m = r16 + 16 * mt;
     xvalid[mt] = m < M;
-    xrow[mt] = reinterpret_cast<const u32x4*>(X + (int64_t)(xvalid[mt] ? m : 0) * ldx) + kq * 4;
+    xrow[mt] = reinterpret_cast<const u32x4*>(X + (int64_t)(xvalid[mt] ? m : 0) * ldx) + 4 * q;
   }
 
   const u32x4 ones = {kOnePair, kOnePair, kOnePair, kOnePair};
-  f32x4 acc[MT];
+  f32x4 acc[RT][MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[rt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (gb < ge) {
-    u32x4 cw[2][U];
-    u32x4 xr[2][U][4][MT];
-    uint32_t sr[2][U];
-    int zr[2][U];
-    auto load = [&](int buf, int g0) {
+    u32x4 cw[2][RT];          // code words of a group: word 4q + t in element t
+    u32x4 xr[2][4][MT];       // activation fragments of a group, per k-step
+    uint32_t sr[2][RT];
+    int zr[2][RT];
+    auto load = [&](int buf, int g) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int gl = min(g0 + u, ge - 1);
-        cw[buf][u] = __builtin_nontemporal_load(crow + gl * 4);
-        sr[buf][u] = srow[gl];
-        zr[buf][u] = zrow[gl];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) xr[buf][u][i][mt] = xrow[mt][gl * 16 + i];
+      for (int rt = 0; rt < RT; ++rt) {
+        cw[buf][rt] = __builtin_nontemporal_load(crow[rt] + g * 4);
+        sr[buf][rt] = srow[rt][g];
+        zr[buf][rt] = zrow[rt][g];
       }
-    };
-    auto compute = [&](int buf, int g0) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        f32x4 pg[MT], xs[MT];
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) xr[buf][t][mt] = xrow[mt][g * 16 + t];
+    };
+    auto compute = [&](int buf) {
+      f32x4 P[RT][MT], xs[MT];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        u32x4 a[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          pg[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-          xs[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          u32x4 raw = xr[buf][t][mt];
+          if (!xvalid[mt]) raw = u32x4{0u, 0u, 0u, 0u};
+          a[mt] = x_pairs_from_natural(raw);
+          xs[mt] = mfma16x16x32(a[mt], ones, t == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : xs[mt]);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const u32x4 b = codes_to_bias128_pairs(cw[buf][u][i]);
+        for (int rt = 0; rt < RT; ++rt) {
+          const u32x4 b = codes_to_bias128_pairs(cw[buf][rt][t]);
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            u32x4 raw = xr[buf][u][i][mt];
-            if (!xvalid[mt]) raw = u32x4{0u, 0u, 0u, 0u};
-            const u32x4 a = x_pairs_from_natural(raw);
-            pg[mt] = mfma16x16x32(a, b, pg[mt]);
-            xs[mt] = mfma16x16x32(a, ones, xs[mt]);
-          }
+          for (int mt = 0; mt < MT; ++mt)
+            P[rt][mt] = mfma16x16x32(a[mt], b, t == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : P[rt][mt]);
         }
-        const float sc = (g0 + u < ge) ? bf16_to_f32(sr[buf][u]) : 0.f;
-        const float zb = (float)(128 + zr[buf][u]);
+      }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const float sc = bf16_to_f32(sr[buf][rt]);
+        const float zb = (float)(128 + zr[buf][rt]);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float d = fmaf(-zb, xs[mt][r], pg[mt][r]);
-            acc[mt][r] = fmaf(sc, d, acc[mt][r]);
-          }
+          for (int i = 0; i < 4; ++i)
+            acc[rt][mt][i] = fmaf(sc, fmaf(-zb, xs[mt][i], P[rt][mt][i]), acc[rt][mt][i]);
       }
     };
     load(0, gb);
-    int g0 = gb;
-    for (; g0 + U < ge; g0 += 2 * U) {
-      load(1, g0 + U);
-      compute(0, g0);
-      if (g0 + 2 * U < ge) load(0, g0 + 2 * U);
-      compute(1, g0 + U);
+    int g = gb;
+    for (; g + 1 < ge; g += 2) {
+      load(1, g + 1);
+      compute(0);
+      if (g + 2 < ge) load(0, g + 2);
+      compute(1);
     }
-    if (g0 < ge) compute(0, g0);
+    if (g < ge) compute(0);
   }
 
   if (S > 1) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) red[wave][mt * 4 + r][lane] = acc[mt][r];
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave][(rt * MT + mt) * 4 + i][lane] = acc[rt][mt][i];
     __syncthreads();
     if (wave != 0) return;
 #pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = red[0][(rt * MT + mt) * 4 + i][lane];
+          for (int w = 1; w < S; ++w) v += red[w][(rt * MT + mt) * 4 + i][lane];
+          acc[rt][mt][i] = v;
+        }
+  }
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int n = (int)blockIdx.x * 16 * RT + 16 * rt + r16;
+    if (n >= N) continue;
+#pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v = red[0][mt * 4 + r][lane];
-        for (int w = 1; w < S; ++w) v += red[w][mt * 4 + r][lane];
-        acc[mt][r] = v;
+      for (int i = 0; i < 4; ++i) {
+        const int m = 16 * mt + 4 * q + i;
+        if (m < M) Y[(int64_t)m * ldy + n] = f32_to_bf16_rne(acc[rt][mt][i]);
       }
   }
-  if (n >= N) return;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = 16 * mt + 4 * kq + r;
-      if (m < M) Y[(int64_t)m * ldy + n] = f32_to_bf16_rne(acc[mt][r]);
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -400,12 +424,6 @@ void launch_dot(const uint16_t* X, int64_t ldx, const uint32_t* codes, const uin
   }
 }
 
-int pick_waves(int G) {
-  int s = G / 4;
-  if (s < 1) s = 1;
-  if (s > kMaxWaves) s = kMaxWaves;
-  return s;
-}
 
 }  // namespace
 
@@ -422,16 +440,25 @@ int launch_gemv(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes
     }
     return hipGetLastError() == hipSuccess ? 0 : 4;
   }
-  const int G = (int)(K / kGroup);
-  const int S = pick_waves(G);
-  const dim3 grid((unsigned)((N + 15) / 16));
+  // Row tiles per wave: more for tall layers (each activation fragment is
+  // reused by every tile); four waves per block split K.  Fitted to timings
+  // of the 8B- and 70B-shaped layers at M = 8, 16, 32.
+  const int n_ = (int)N, k_ = (int)K, m_ = (int)M;
+  const int G = k_ / kGroup;
+  const int S = max(1, min(4, G / 2));
   const dim3 block(S * kWave);
-  if (M <= 16)
-    hipLaunchKernelGGL((gemv_mfma_kernel<1, 2>), grid, block, 0, stream, X, (int)M, ldx, codes,
-                       scales, zeros, (int)N, (int)K, Y, ldy);
-  else
-    hipLaunchKernelGGL((gemv_mfma_kernel<2, 2>), grid, block, 0, stream, X, (int)M, ldx, codes,
-                       scales, zeros, (int)N, (int)K, Y, ldy);
+  int rt = n_ >= 16384 ? 4 : (n_ >= 6144 ? 2 : 1);
+  if (M > 16 && rt > 2) rt = 2;   // four tiles of 32 activation rows would spill
+  const dim3 grid((unsigned)((n_ + 16 * rt - 1) / (16 * rt)));
+#define W4A16_TILE(MT, RT)                                                                       \
+  hipLaunchKernelGGL((gemv_tile_kernel<MT, RT>), grid, block, 0, stream, X, m_, ldx, codes, scales, \
+                     zeros, n_, k_, Y, ldy)
+  if (M <= 16) {
+    if (rt == 4) W4A16_TILE(1, 4); else if (rt == 2) W4A16_TILE(1, 2); else W4A16_TILE(1, 1);
+  } else {
+    if (rt == 2) W4A16_TILE(2, 2); else W4A16_TILE(2, 1);
+  }
+#undef W4A16_TILE
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 
