@@ -371,56 +371,57 @@ int cu_count() {
   return counts[dev];
 }
 
+template <int M, int NB>
+void launch_dot_nb(const uint16_t* X, int64_t ldx, const uint32_t* codes, const uint16_t* scales,
+                   const int32_t* zeros, int N, int K, uint16_t* Y, int64_t ldy, hipStream_t stream) {
+  constexpr int R = 4;
+  const int S = (K + kSlice - 1) / kSlice;
+  hipLaunchKernelGGL((gemv_dot_kernel<M, R, NB>), dim3((unsigned)((N + R * NB - 1) / (R * NB))),
+                     dim3(S * kWave), 0, stream, X, ldx, codes, scales, zeros, N, K, Y, ldy);
+}
+
 template <int M>
 void launch_dot(const uint16_t* X, int64_t ldx, const uint32_t* codes, const uint16_t* scales,
                 const int32_t* zeros, int N, int K, uint16_t* Y, int64_t ldy, hipStream_t stream) {
-  const int S = (K + kSlice - 1) / kSlice;
-  const dim3 block(S * kWave);
-  // Rows per block: R rows per batch, NB batches, the next batch's loads in
-  // flight while the current one is reduced.  Few batches for small layers
-  // (all loads issued at once), more for long rows (K >= 14336) and for very
-  // tall layers; never fewer blocks than CUs.  Fitted to timings on the
-  // decode shapes of the 8B- and 70B-sized layer sets and the 40-layer
-  // stack.
-  // Blocks are spread evenly over the CUs only if their count is close to
-  // a multiple of the CU count: `balance` is the busy fraction of the
-  // busiest CU's share.
+  // Rows per block: R = 4 rows per batch, NB batches, the next batch's loads
+  // in flight while the current one is reduced.  Per-wave timelines on the
+  // box show that a CU's share of the bandwidth does not grow with the
+  // number of blocks it holds, so a block count that is not a multiple of
+  // the CU count leaves a tail; and that about eight waves per CU with a
+  // few batches each keep the stream full with the least queueing.  So:
+  // aim at 8 waves per CU (NB ~ waves needed / (8 CUs)), then step down to
+  // the nearest NB whose block count fills the CUs evenly.  Fitted to
+  // timings of every decode layer of the 8B- and 70B-shaped sets and the
+  // 40-layer stack.
   constexpr int R = 4;
+  constexpr int kMaxNB = M >= 4 ? 2 : 8;   // more batches would spill at M = 4
+  const int S = (K + kSlice - 1) / kSlice;
   const int cus = cu_count();
   auto balance = [&](int nb) {
     const double per_cu = (double)((N + R * nb - 1) / (R * nb)) / cus;
     return per_cu / std::ceil(per_cu);
   };
-  const int64_t w1 = (int64_t)((N + R - 1) / R) * S;
-  int nb;
-  if (S >= 7) {
-    nb = 8;
-    while (nb > 2 && balance(nb) < 0.8) nb >>= 1;
-  } else {
-    if (w1 <= 2048) nb = 1;
-    else if (w1 <= 12288) nb = 2;
-    else nb = S <= 2 ? 8 : 4;
-    if (nb > 1 && balance(nb) < 0.85 && balance(nb / 2) > balance(nb)) nb >>= 1;
+  const int64_t waves1 = (int64_t)((N + R - 1) / R) * S;   // waves at one batch each
+  int nb0 = (int)std::min<int64_t>(kMaxNB, std::max<int64_t>(1, (waves1 + 8 * cus - 1) / (8 * cus)));
+  int nb = 0;
+  for (int c = nb0; c >= 1 && nb == 0; --c)
+    if (balance(c) >= 0.97) nb = c;
+  if (nb == 0) {   // nothing fills evenly: the best fill, nearest to nb0
+    nb = nb0;
+    for (int c = 1; c <= kMaxNB; ++c)
+      if (balance(c) > balance(nb) + 1e-9 ||
+          (balance(c) > balance(nb) - 1e-9 && std::abs(c - nb0) < std::abs(nb - nb0)))
+        nb = c;
   }
-  while (nb > 1 && N / (R * nb) < cus) nb >>= 1;
-  if (M >= 4 && nb > 2) nb = 2;  // more batches would spill at M = 4
-  const dim3 grid((unsigned)((N + R * nb - 1) / (R * nb)));
   switch (nb) {
-    case 8:
-      hipLaunchKernelGGL((gemv_dot_kernel<M, R, (M >= 4 ? 2 : 8)>), grid, block, 0, stream, X, ldx,
-                         codes, scales, zeros, N, K, Y, ldy);
-      break;
-    case 4:
-      hipLaunchKernelGGL((gemv_dot_kernel<M, R, (M >= 4 ? 2 : 4)>), grid, block, 0, stream, X, ldx,
-                         codes, scales, zeros, N, K, Y, ldy);
-      break;
-    case 2:
-      hipLaunchKernelGGL((gemv_dot_kernel<M, R, 2>), grid, block, 0, stream, X, ldx, codes, scales,
-                         zeros, N, K, Y, ldy);
-      break;
+#define W4A16_DOT(V)                                                                   \
+  case V:                                                                              \
+    launch_dot_nb<M, (V <= kMaxNB ? V : kMaxNB)>(X, ldx, codes, scales, zeros, N, K, Y, ldy, stream); \
+    break;
+    W4A16_DOT(8) W4A16_DOT(7) W4A16_DOT(6) W4A16_DOT(5) W4A16_DOT(4) W4A16_DOT(3) W4A16_DOT(2)
+#undef W4A16_DOT
     default:
-      hipLaunchKernelGGL((gemv_dot_kernel<M, R, 1>), grid, block, 0, stream, X, ldx, codes, scales,
-                         zeros, N, K, Y, ldy);
+      launch_dot_nb<M, 1>(X, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
   }
 }
 
