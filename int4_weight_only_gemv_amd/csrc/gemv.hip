@@ -5,28 +5,34 @@
 // into the multiply, weights rebuilt in registers; "Quantization I",
 // "Concept": only the packed form crosses the memory bus).
 //
-// Both kernels turn a code word into exact BF16 operands 128 + q by OR-ing
+// All kernels turn a code word into exact BF16 operands 128 + q by OR-ing
 // each nibble into the mantissa of BF16 128.0 (two ops per pair of codes, no
 // conversions) and remove the bias and the zero point once per group in
 // float32 with one fused multiply-add whose product is exact:
 //     acc += s * (P - (128 + z) * Xsum),   P = sum_k x (128 + q).
 // No weight is ever rounded.
 //
-// gemv_dot (small M): a wave owns a 2048-input slice of K for a run of rows;
-// its 64 lanes read 16 contiguous bytes each, so every load instruction
-// moves 1 KiB of one row -- the fully coalesced pattern that streams HBM
-// fastest.  The lane's 32 activations per batch row stay in registers for
-// all rows, the products run on v_dot2_f32_bf16, and per-row partial sums
-// are folded across lanes with a halving butterfly (ds_bpermute), then
-// across the K slices of the block through LDS in a fixed order.
+// gemv_dot (M <= 2, and M <= 4 for K > 16384): a wave owns a 2048-input
+// slice of K for a run of rows; its 64 lanes read 16 contiguous bytes each,
+// so every load instruction moves 1 KiB of one row -- the fully coalesced
+// pattern that streams HBM fastest.  The lane's 32 activations per batch row
+// stay in registers for all rows, the products run on v_dot2_f32_bf16, and
+// per-row partial sums are folded across lanes with a halving butterfly
+// (ds_bpermute), then across the K slices of the block through LDS in a
+// fixed order.
 //
-// gemv_tile (larger M): 16-row tiles of W meet X (M padded to 16 or 32) on
-// v_mfma_f32_16x16x32_bf16, one group of a tile per 16-byte load per lane;
-// the same A operand against a B of ones gives the per-group activation
-// sums.  The waves of a block split K and add their partial tiles through
-// LDS in a fixed order.
+// gemv_quad (3 <= M <= 8, K <= 16384): the same streaming pattern (four rows
+// x 256 contiguous bytes per load instruction), but the products run on the
+// matrix cores as sixteen 4x4 blocks per instruction, so more activation
+// rows cost almost no vector ALU time.
 //
-// Neither kernel uses atomics or workspace: results are deterministic.
+// gemv_tile (the rest, up to M = 32): 16-row tiles of W meet X (M padded to
+// 16 or 32) on v_mfma_f32_16x16x32_bf16, one group of a tile per 16-byte
+// load per lane; the same A operand against a B of ones gives the per-group
+// activation sums.  The waves of a block split K and add their partial tiles
+// through LDS in a fixed order.
+//
+// No kernel uses atomics or workspace: results are deterministic.
 
 #include "common.h"
 
@@ -36,6 +42,14 @@ namespace w4a16 {
 namespace {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// up ? a : b as one bit-select on a lane mask (all ones or zero).  Written
+// as bit operations so that the compiler keeps the two values in registers
+// instead of turning a select between array elements into an indexed
+// access (which it lowers to a chain of compares and selects).
+__device__ __forceinline__ float pick(uint32_t up_mask, float a, float b) {
+  return __uint_as_float((__float_as_uint(a) & up_mask) | (__float_as_uint(b) & ~up_mask));
+}
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
@@ -135,25 +149,25 @@ __global__ __launch_bounds__(1024) void gemv_dot_kernel(
     // with the group sums of row l % 4 ...
     float h[2][M];
     {
-      const bool up = (lane & 2) != 0;
+      const uint32_t up = (lane & 2) ? ~0u : 0u;
 #pragma unroll
       for (int r = 0; r < 2; ++r)
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-          const float send = up ? P[r][m] : P[r + 2][m];
-          const float keep = up ? P[r + 2][m] : P[r][m];
+          const float send = pick(up, P[r][m], P[r + 2][m]);
+          const float keep = pick(up, P[r + 2][m], P[r][m]);
           h[r][m] = keep + __shfl_xor(send, 2);
         }
     }
     float part[MP];
     {
-      const bool up = (lane & 1) != 0;
+      const uint32_t up = (lane & 1) ? ~0u : 0u;
       const float s = bf16_to_f32(sb[cur]);
       const float zb128 = (float)(128 + zb[cur]);
 #pragma unroll
       for (int m = 0; m < M; ++m) {
-        const float send = up ? h[0][m] : h[1][m];
-        const float keep = up ? h[1][m] : h[0][m];
+        const float send = pick(up, h[0][m], h[1][m]);
+        const float keep = pick(up, h[1][m], h[0][m]);
         const float q = keep + __shfl_xor(send, 1);
         // ... and removes the bias and zero point of that (row, group) once
         part[m] = s * fmaf(-zb128, xsg[m], q);
@@ -166,11 +180,11 @@ __global__ __launch_bounds__(1024) void gemv_dot_kernel(
     int mask = 4;
 #pragma unroll
     for (int cur_n = MP; cur_n > 1; cur_n >>= 1) {
-      const bool up = (lane & mask) != 0;
+      const uint32_t up = (lane & mask) ? ~0u : 0u;
 #pragma unroll
       for (int i = 0; i < cur_n / 2; ++i) {
-        const float send = up ? part[i] : part[i + cur_n / 2];
-        const float keep = up ? part[i + cur_n / 2] : part[i];
+        const float send = pick(up, part[i], part[i + cur_n / 2]);
+        const float keep = pick(up, part[i + cur_n / 2], part[i]);
         part[i] = keep + __shfl_xor(send, mask);
       }
       mask <<= 1;
@@ -191,6 +205,173 @@ __global__ __launch_bounds__(1024) void gemv_dot_kernel(
     const int j = idx / M, m = idx - j * M;
     const int row = row0 + j;
     if (row >= N) continue;
+    float v = red[0][idx];
+    for (int w = 1; w < S; ++w) v += red[w][idx];
+    Y[m * ldy + row] = f32_to_bf16_rne(v);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// gemv_quad (M <= 8): sixteen 4x4 products per matrix instruction
+// ---------------------------------------------------------------------------
+//
+// v_mfma_f32_4x4x4_16b_bf16 runs 16 independent products of a 4x4 A block
+// and a 4x4 B block (K = 4): lane 4b + i supplies row i of block b's A, lane
+// 4b + j column j of block b's B, and lane 4b + j receives column j of block
+// b's result with row r in register r.  Here the four B columns are four
+// weight rows and the A rows up to four activation rows (two instructions
+// for M <= 8), and block b takes its own 32 inputs of the wave's 512-input
+// slice.  So one 16-byte load per lane brings four weight rows x 256
+// contiguous bytes (eight whole 128-byte lines, as coalesced as one 1 KiB
+// row) and feeds eight instructions, and the products cost no vector ALU
+// time: what remains on the VALU is the unpack (7 ops per word), the
+// per-(row, group) correction and the cross-lane sums, so M = 2..8 runs at
+// nearly the cost of M = 1.  The same A against a B of ones gives the
+// activation sums of each lane's 32 inputs once, up front.  A wave keeps its
+// activations in registers for all of its rows; the waves of a block split
+// K and add their partial rows through LDS in a fixed order.
+
+constexpr int kQuadSlice = 512;   // inputs per wave and slice: 16 blocks x 32
+constexpr int kQuadMaxWaves = 16;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma4x4x4(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1,
+                                           f32x4 c) {
+  const u32x2 a = {a0, a1}, b = {b0, b1};
+  return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+template <int M, int T, int NB>
+__global__ __launch_bounds__(1024) void gemv_quad_kernel(
+    const uint16_t* __restrict__ X, int Mrt, int64_t ldx, const uint32_t* __restrict__ codes,
+    const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K,
+    uint16_t* __restrict__ Y, int64_t ldy) {
+  constexpr int MS = (M + 3) / 4;             // activation row sets of four
+  constexpr int MP = pow2_at_least(M);        // values per lane in the halving butterfly
+  constexpr int LM = log2_exact(MP);
+  static_assert(LM <= 4, "at most 16 values per lane");
+  __shared__ float red[kQuadMaxWaves][NB * 4 * M];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int S = blockDim.x >> 6;
+  const int bq = lane >> 2;                   // block of the 4x4 products: 32 inputs
+  const int j = lane & 3;                     // weight row (B column) / activation row (A row)
+  const int G = K / kGroup;
+  const int64_t vpr = K / 32;                 // 16-byte vectors per code row
+
+  int kc[T], g[T];
+  bool act[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int k = (wave * T + t) * kQuadSlice + 32 * bq;
+    act[t] = k < K;
+    kc[t] = act[t] ? k : K - 32;              // inactive lanes read valid memory, weigh zero
+    g[t] = kc[t] >> 7;
+  }
+  const int row0 = blockIdx.x * NB * 4;
+  const u32x4* cbase = reinterpret_cast<const u32x4*>(codes);
+
+  u32x4 cb[2];
+  uint32_t sb[2];
+  int zb[2];
+  auto load = [&](int buf, int nb, int t) {
+    const int row = min(row0 + nb * 4 + j, N - 1);
+    cb[buf] = __builtin_nontemporal_load(cbase + (int64_t)row * vpr + kc[t] / 32);
+    sb[buf] = scales[(int64_t)row * G + g[t]];
+    zb[buf] = zeros[(int64_t)row * G + g[t]];
+  };
+  load(0, 0, 0);  // the weight stream first
+
+  // lane (bq, i) holds activation rows i, i + 4 of its 32 inputs, paired
+  // like the codes, and every lane the sums of the 32 inputs of its block
+  u32x4 xa[T][MS][4];
+  f32x4 xs[T][MS];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) {
+      const int m = j + 4 * ms;
+      const bool live = act[t] && m < Mrt;
+      const u32x4* xr = reinterpret_cast<const u32x4*>(X + (int64_t)min(m, Mrt - 1) * ldx + kc[t]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u32x4 raw = xr[i];
+        if (!live) raw = u32x4{0u, 0u, 0u, 0u};
+        xa[t][ms][i] = x_pairs_from_natural(raw);
+      }
+      f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          sum = mfma4x4x4(xa[t][ms][i][2 * h], xa[t][ms][i][2 * h + 1], kOnePair, kOnePair, sum);
+      xs[t][ms] = sum;
+    }
+
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    float acc[MP];
+#pragma unroll
+    for (int m = 0; m < MP; ++m) acc[m] = 0.f;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int f = nb * T + t;
+      const int cur = f & 1;
+      if (f + 1 < NB * T) load(cur ^ 1, (f + 1) / T, (f + 1) % T);
+      f32x4 d[MS];
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms) d[ms] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u32x4 q = codes_to_bias128_pairs(cb[cur][i]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int ms = 0; ms < MS; ++ms)
+            d[ms] = mfma4x4x4(xa[t][ms][i][2 * h], xa[t][ms][i][2 * h + 1], q[2 * h], q[2 * h + 1],
+                              d[ms]);
+      }
+      // this lane's block: s * (P - (128 + z) * Xsum) for weight row j, group g[t]
+      const float s = bf16_to_f32(sb[cur]);
+      const float zb128 = (float)(128 + zb[cur]);
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+        acc[m] = fmaf(s, fmaf(-zb128, xs[t][m / 4][m % 4], d[m / 4][m % 4]), acc[m]);
+    }
+    // sum over the 16 blocks (lane bits 2..5): halving on the activation
+    // rows first (bit 5 first), plain sums after
+    int mask = 32;
+#pragma unroll
+    for (int cur_n = MP; cur_n > 1; cur_n >>= 1) {
+      const uint32_t up = (lane & mask) ? ~0u : 0u;
+#pragma unroll
+      for (int i = 0; i < cur_n / 2; ++i) {
+        const float send = pick(up, acc[i], acc[i + cur_n / 2]);
+        const float keep = pick(up, acc[i + cur_n / 2], acc[i]);
+        acc[i] = keep + __shfl_xor(send, mask);
+      }
+      mask >>= 1;
+    }
+#pragma unroll
+    for (; mask >= 4; mask >>= 1) acc[0] += __shfl_xor(acc[0], mask);
+    // lane (bq, j) now holds weight row j and activation row m from the top
+    // LM bits of bq; the lanes with zero low bits store it
+    if ((bq & ((16 >> LM) - 1)) == 0) {
+      int m = 0, half = MP / 2;
+#pragma unroll
+      for (int b = 0; b < LM; ++b, half >>= 1)
+        if (lane & (32 >> b)) m += half;
+      if (m < M) red[wave][nb * 4 * M + j * M + m] = acc[0];
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < NB * 4 * M; idx += blockDim.x) {
+    const int r = idx / M, m = idx - r * M;
+    const int row = row0 + r;
+    if (row >= N || m >= Mrt) continue;
     float v = red[0][idx];
     for (int w = 1; w < S; ++w) v += red[w][idx];
     Y[m * ldy + row] = f32_to_bf16_rne(v);
@@ -426,11 +607,74 @@ void launch_dot(const uint16_t* X, int64_t ldx, const uint32_t* codes, const uin
 }
 
 
+template <int M, int T, int NB>
+void launch_quad_nb(const uint16_t* X, int Mrt, int64_t ldx, const uint32_t* codes,
+                    const uint16_t* scales, const int32_t* zeros, int N, int K, uint16_t* Y,
+                    int64_t ldy, hipStream_t stream) {
+  const int slices = (K + kQuadSlice - 1) / kQuadSlice;
+  const int S = (slices + T - 1) / T;
+  hipLaunchKernelGGL((gemv_quad_kernel<M, T, NB>), dim3((unsigned)((N + 4 * NB - 1) / (4 * NB))),
+                     dim3(S * kWave), 0, stream, X, Mrt, ldx, codes, scales, zeros, N, K, Y, ldy);
+}
+
+template <int M, int T>
+void launch_quad_t(const uint16_t* X, int Mrt, int64_t ldx, const uint32_t* codes,
+                   const uint16_t* scales, const int32_t* zeros, int N, int K, uint16_t* Y,
+                   int64_t ldy, hipStream_t stream) {
+  // Rows per block: 4 x NB.  The largest NB (at most 8) whose block count
+  // fills the CUs evenly; fitted to timings of the decode layers of the 8B-
+  // and 70B-shaped sets and the 40-layer stack at M = 4 and 8.
+  const int cus = cu_count();
+  auto balance = [&](int nb) {
+    const double per_cu = (double)((N + 4 * nb - 1) / (4 * nb)) / cus;
+    return per_cu / std::ceil(per_cu);
+  };
+  int nb = 0;
+  for (int c = 8; c >= 1 && nb == 0; --c)
+    if (balance(c) >= 0.95) nb = c;
+  if (nb == 0) {
+    nb = 1;
+    for (int c = 2; c <= 8; ++c)
+      if (balance(c) > balance(nb) + 1e-9) nb = c;
+  }
+  switch (nb) {
+#define W4A16_QUAD(V)                                                                     \
+  case V:                                                                                 \
+    launch_quad_nb<M, T, V>(X, Mrt, ldx, codes, scales, zeros, N, K, Y, ldy, stream);    \
+    break;
+    W4A16_QUAD(8) W4A16_QUAD(7) W4A16_QUAD(6) W4A16_QUAD(5) W4A16_QUAD(4) W4A16_QUAD(3)
+    W4A16_QUAD(2)
+#undef W4A16_QUAD
+    default:
+      launch_quad_nb<M, T, 1>(X, Mrt, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
+  }
+}
+
+// 3 <= M <= 8, K <= 16384: one wave slice of 512 inputs (T = 1) up to 16
+// waves, two slices per wave beyond that
+template <int M>
+void launch_quad(const uint16_t* X, int Mrt, int64_t ldx, const uint32_t* codes,
+                 const uint16_t* scales, const int32_t* zeros, int N, int K, uint16_t* Y,
+                 int64_t ldy, hipStream_t stream) {
+  const int slices = (K + kQuadSlice - 1) / kQuadSlice;
+  if (slices <= kQuadMaxWaves)
+    launch_quad_t<M, 1>(X, Mrt, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
+  else
+    launch_quad_t<M, 2>(X, Mrt, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
+}
+
 }  // namespace
 
 int launch_gemv(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
                 const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K, uint16_t* Y,
                 int64_t ldy, hipStream_t stream) {
+  if (M >= 3 && M <= 8 && K <= (int64_t)2 * kQuadSlice * kQuadMaxWaves) {
+    if (M <= 4)
+      launch_quad<4>(X, (int)M, ldx, codes, scales, zeros, (int)N, (int)K, Y, ldy, stream);
+    else
+      launch_quad<8>(X, (int)M, ldx, codes, scales, zeros, (int)N, (int)K, Y, ldy, stream);
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+  }
   if (M <= kDotMaxM && K <= (int64_t)kSlice * kMaxSlices) {
     const int n = (int)N, k = (int)K;
     switch (M) {

@@ -66,6 +66,24 @@ def test_llama70b_layers_sampled(M):
         torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_stack40_layers_sampled(M):
+    # one layer of the 40-layer stack (K = 5120, 27648: slices not a power of two)
+    for layer in gen.STACK40_LAYER:
+        rows = sample_rows(layer.N, 96, seed=layer.N + 7 * M)
+        check_case(w4.w4a16_gemv, M, layer.N, layer.K, "stack40_decode", layer.name, rows=rows,
+                   label=f"{layer.name} M={M}")
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("M", [3, 4, 5, 8])
+@pytest.mark.parametrize("N,K", [(37, 640), (256, 8320), (64, 16384), (29, 16512)])
+def test_matrix_core_small_m_shapes(M, N, K):
+    # ragged row counts, partial 512-input slices, two slices per wave, and
+    # just past the two-slice limit
+    check_case(w4.w4a16_gemv, M, N, K, "gemv", f"quad{N}x{K}", shift=True, label=f"M={M} N={N} K={K}")
+
+
 def test_on_grid_weights_match_unquantised_matmul():
     import oracle_pins as P
     W_bits, _ = P.check_all_codes_on_grid(seed=31, N=80, K=512)
