@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--no-stack", action="store_true",
                     help="skip the 40-layer decoder-stack stream (about 10.7 GB of packed weights)")
     ap.add_argument("--stack-tokens", type=int, default=30)
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the decode sweep over the other M values and the 70B-shaped set")
     return ap.parse_args()
 
 
@@ -232,6 +234,12 @@ def main():
         log(f"[bench] prefill M={Mp}: {tf:.1f} TFLOP/s")
         del pxs, pys
 
+    # ---- decode at the other batch sizes of the layer sets (same protocol)
+    sweep = None
+    if not args.no_sweep:
+        sweep = [decode_sweep("llama8b_decode", [4, 8, 16, 32], dev, stream),
+                 decode_sweep("llama70b_decode", [1, 8, 32], dev, stream)]
+
     # ---- the full decoder-stack weight stream: 40 layers x 4 linears, AWQ-
     # folded packing, one token = 160 dependent launches in one graph
     stack = None
@@ -264,6 +272,7 @@ def main():
         "per_layer": per_layer,
         "roofline": roofline,
         "prefill": prefill,
+        "decode_sweep": sweep,
         "stack": stack,
         "cpu_baseline": cpu,
     }
@@ -299,21 +308,73 @@ def measured_traffic(layer, M):
     return rec.get("hbm_bytes_per_launch")
 
 
-def stack_decode(tokens, dev, stream):
+def decode_sweep(workload, Ms, dev, stream, steps=40):
+    """Decode throughput of one layer set at several batch sizes M: the four
+    launches of a step in order, replicated weight copies past the last-level
+    cache, a graph of `steps` steps timed with HIP events on its stream."""
+    import torch
+    import int4_weight_only_gemv_amd as w4
+    from synth import gen
+    spec = gen.WORKLOADS[workload]
+    layers = spec["layers"]
+    packed = []
+    for L in layers:
+        W = gen.weights(L.N, L.K, workload, L.name, shift=spec["shift"], device=dev)
+        packed.append(w4.w4a16_pack(W))
+        del W
+    set_bytes = sum(p.nbytes() for p in packed)
+    ncopy = max(2, math.ceil(ROTATE_BYTES / set_bytes))
+    copies = [packed] + [[w4.PackedLinear(p.codes.clone(), p.scales.clone(), p.zeros.clone())
+                          for p in packed] for _ in range(ncopy - 1)]
+    rows = []
+    for M in Ms:
+        xs = [gen.activations(M, L.K, workload, L.name, device=dev) for L in layers]
+        ys = [torch.empty(M, L.N, dtype=torch.bfloat16, device=dev) for L in layers]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            for p, x, y in zip(packed, xs, ys):
+                w4.w4a16_gemv(x, p, y)
+            stream.synchronize()
+            with torch.cuda.graph(g, stream=stream):
+                for s in range(steps):
+                    for p, x, y in zip(copies[s % ncopy], xs, ys):
+                        w4.w4a16_gemv(x, p, y)
+            g.replay()
+            stream.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            e1.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        nbytes = sum(decode_bytes(L, M) for L in layers)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        rows.append({"M": M, "us_per_step": round(us, 3), "GBps": round(gbs, 1),
+                     "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
+        log(f"[bench] {workload} M={M}: {us:.2f} us/step, {gbs:.0f} GB/s")
+        del g, xs, ys
+    del copies, packed
+    torch.cuda.synchronize()
+    return {"workload": workload, "step_bytes_M1": sum(decode_bytes(L, 1) for L in layers),
+            "rotating_copies": ncopy, "steps_per_graph": steps, "results": rows}
+
+
+def stack_decode(tokens, dev, stream, Ms=(1, 8)):
     """Decode of a 40-layer stack (hidden 5120, 40 q / 8 kv heads of 128,
     SwiGLU 27648): each layer's four linears packed from their own seeded
     weights after an AWQ pre-scale s = importance^0.5 from a synthetic
     512-token calibration batch; activations X' = X * (1/s) as the folded
     producer would emit them.  One token runs the 160 linears in order, at
-    M = 1 (GEMV); the stack (~10.7 GB) is far larger than the last-level
-    cache, so every token streams it from HBM."""
+    each M in Ms (GEMV); the stack (~10.7 GB) is far larger than the
+    last-level cache, so every token streams it from HBM."""
     import torch
     import int4_weight_only_gemv_amd as w4
     from synth import gen
     spec = gen.WORKLOADS["stack40_decode"]
     cfg, layers, depth = "stack40_decode", spec["layers"], spec["depth"]
     t0 = time.perf_counter()
-    seq = []   # (packed, X', Y) per linear, in execution order
+    seq = []   # (packed, gamma', layer, name) per linear, in execution order
     for d in range(depth):
         for L in layers:
             name = f"{L.name}.{d}"
@@ -323,41 +384,47 @@ def stack_decode(tokens, dev, stream):
             p = w4.w4a16_pack(W, awq_s=s_awq)
             gamma = torch.ones(L.K, dtype=torch.bfloat16, device=dev)
             w4.w4a16_awq_fold(s_awq, gamma)
-            x = w4.w4a16_scale_channels(gen.activations(1, L.K, cfg, name, device=dev), gamma)
-            seq.append((p, x, torch.empty(1, L.N, dtype=torch.bfloat16, device=dev)))
+            seq.append((p, gamma, L, name))
             del W, xcal
     torch.cuda.synchronize()
-    nbytes = sum(decode_bytes(L, 1) for L in layers) * depth
-    log(f"[bench] stack: {len(seq)} linears, {nbytes / 1e9:.2f} GB per token, "
+    log(f"[bench] stack: {len(seq)} linears, "
+        f"{sum(decode_bytes(L, 1) for L in layers) * depth / 1e9:.2f} GB per token, "
         f"built in {time.perf_counter() - t0:.1f} s")
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(stream):
-        for p, x, y in seq:
-            w4.w4a16_gemv(x, p, y)
-        stream.synchronize()
-        with torch.cuda.graph(g, stream=stream):
-            for p, x, y in seq:
+    results = []
+    for M in Ms:
+        run = [(p, w4.w4a16_scale_channels(gen.activations(M, L.K, cfg, name, device=dev), gamma),
+                torch.empty(M, L.N, dtype=torch.bfloat16, device=dev)) for p, gamma, L, name in seq]
+        nbytes = sum(decode_bytes(L, M) for L in layers) * depth
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            for p, x, y in run:
                 w4.w4a16_gemv(x, p, y)
-        for _ in range(3):
-            g.replay()
-        stream.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(tokens):
-            g.replay()
-        e1.record(stream)
-        e1.synchronize()
-    ms = e0.elapsed_time(e1) / tokens
-    gbs = nbytes / (ms * 1e-3) / 1e9
-    log(f"[bench] stack decode M=1: {ms:.3f} ms/token, {gbs:.0f} GB/s")
-    del seq, g
+            stream.synchronize()
+            with torch.cuda.graph(g, stream=stream):
+                for p, x, y in run:
+                    w4.w4a16_gemv(x, p, y)
+            for _ in range(3):
+                g.replay()
+            stream.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(tokens):
+                g.replay()
+            e1.record(stream)
+            e1.synchronize()
+        ms = e0.elapsed_time(e1) / tokens
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        log(f"[bench] stack decode M={M}: {ms:.3f} ms/token, {gbs:.0f} GB/s")
+        results.append({"M": M, "bytes_per_token": nbytes, "ms_per_token": round(ms, 4),
+                        "tokens_per_s": round(M * 1e3 / ms, 1), "GBps": round(gbs, 1),
+                        "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
+        del run, g
+    del seq
     torch.cuda.synchronize()
     return {"workload": "40-layer decoder stack (hidden 5120, 40/8 heads of 128, SwiGLU 27648), "
-                        "INT4 group 128, AWQ alpha 0.5", "M": 1, "linears_per_token": 4 * depth,
-            "bytes_per_token": nbytes, "ms_per_token": round(ms, 4),
-            "tokens_per_s": round(1e3 / ms, 1), "GBps": round(gbs, 1),
-            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "tokens_timed": tokens}
+                        "INT4 group 128, AWQ alpha 0.5", "linears_per_token": 4 * depth,
+            "tokens_timed": tokens, "results": results}
 
 
 def cpu_baseline(layers, workload, spec, M, dev, row_stride=2, min_seconds=10.0):

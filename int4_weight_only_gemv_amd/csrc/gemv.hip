@@ -378,6 +378,144 @@ __global__ __launch_bounds__(1024) void gemv_quad_kernel(
   }
 }
 
+// Long rows (more slices than one wave can hold the activations of): each
+// wave runs every S-th slice in turn, loads that slice's activations, and
+// adds into per-row accumulators of all NB batches, so the activations are
+// fetched once per slice and the sums across lanes run once per row at the
+// end.  NB is even so that the double buffer's parity is static.
+template <int M, int NB>
+__global__ __launch_bounds__(1024) void gemv_quad_long_kernel(
+    const uint16_t* __restrict__ X, int Mrt, int64_t ldx, const uint32_t* __restrict__ codes,
+    const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K,
+    uint16_t* __restrict__ Y, int64_t ldy) {
+  static_assert(NB % 2 == 0, "even batch count");
+  constexpr int MS = (M + 3) / 4;
+  constexpr int MP = pow2_at_least(M);
+  constexpr int LM = log2_exact(MP);
+  static_assert(LM <= 4, "at most 16 values per lane");
+  __shared__ float red[kQuadMaxWaves][NB * 4 * M];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int S = blockDim.x >> 6;
+  const int bq = lane >> 2;
+  const int j = lane & 3;
+  const int G = K / kGroup;
+  const int64_t vpr = K / 32;
+  const int slices = (K + kQuadSlice - 1) / kQuadSlice;
+  const int row0 = blockIdx.x * NB * 4;
+  const u32x4* cbase = reinterpret_cast<const u32x4*>(codes);
+
+  float acc[NB][MP];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int m = 0; m < MP; ++m) acc[nb][m] = 0.f;
+
+  if (wave < slices) {
+    auto lane_k = [&](int t, bool& act) {
+      const int k = t * kQuadSlice + 32 * bq;
+      act = k < K;
+      return act ? k : K - 32;
+    };
+    u32x4 cb[2];
+    uint32_t sb[2];
+    int zb[2];
+    auto load = [&](int buf, int nb, int t) {
+      bool act;
+      const int kc = lane_k(t, act);
+      const int row = min(row0 + nb * 4 + j, N - 1);
+      cb[buf] = __builtin_nontemporal_load(cbase + (int64_t)row * vpr + kc / 32);
+      sb[buf] = scales[(int64_t)row * G + (kc >> 7)];
+      zb[buf] = zeros[(int64_t)row * G + (kc >> 7)];
+    };
+    load(0, 0, wave);
+    for (int t = wave; t < slices; t += S) {
+      bool act;
+      const int kc = lane_k(t, act);
+      u32x4 xa[MS][4];
+      f32x4 xs[MS];
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms) {
+        const int m = j + 4 * ms;
+        const bool live = act && m < Mrt;
+        const u32x4* xr = reinterpret_cast<const u32x4*>(X + (int64_t)min(m, Mrt - 1) * ldx + kc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          u32x4 raw = xr[i];
+          if (!live) raw = u32x4{0u, 0u, 0u, 0u};
+          xa[ms][i] = x_pairs_from_natural(raw);
+        }
+        f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            sum = mfma4x4x4(xa[ms][i][2 * h], xa[ms][i][2 * h + 1], kOnePair, kOnePair, sum);
+        xs[ms] = sum;
+      }
+      const int tn = t + S < slices ? t + S : t;   // the last slice re-reads itself
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int cur = nb & 1;
+        if (nb + 1 < NB) load(cur ^ 1, nb + 1, t);
+        else load(cur ^ 1, 0, tn);
+        f32x4 d[MS];
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms) d[ms] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const u32x4 q = codes_to_bias128_pairs(cb[cur][i]);
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int ms = 0; ms < MS; ++ms)
+              d[ms] = mfma4x4x4(xa[ms][i][2 * h], xa[ms][i][2 * h + 1], q[2 * h], q[2 * h + 1],
+                                d[ms]);
+        }
+        const float s = bf16_to_f32(sb[cur]);
+        const float zb128 = (float)(128 + zb[cur]);
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+          acc[nb][m] = fmaf(s, fmaf(-zb128, xs[m / 4][m % 4], d[m / 4][m % 4]), acc[nb][m]);
+      }
+    }
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    int mask = 32;
+#pragma unroll
+    for (int cur_n = MP; cur_n > 1; cur_n >>= 1) {
+      const uint32_t up = (lane & mask) ? ~0u : 0u;
+#pragma unroll
+      for (int i = 0; i < cur_n / 2; ++i) {
+        const float send = pick(up, acc[nb][i], acc[nb][i + cur_n / 2]);
+        const float keep = pick(up, acc[nb][i + cur_n / 2], acc[nb][i]);
+        acc[nb][i] = keep + __shfl_xor(send, mask);
+      }
+      mask >>= 1;
+    }
+#pragma unroll
+    for (; mask >= 4; mask >>= 1) acc[nb][0] += __shfl_xor(acc[nb][0], mask);
+    if ((bq & ((16 >> LM) - 1)) == 0) {
+      int m = 0, half = MP / 2;
+#pragma unroll
+      for (int b = 0; b < LM; ++b, half >>= 1)
+        if (lane & (32 >> b)) m += half;
+      if (m < M) red[wave][nb * 4 * M + j * M + m] = acc[nb][0];
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < NB * 4 * M; idx += blockDim.x) {
+    const int r = idx / M, m = idx - r * M;
+    const int row = row0 + r;
+    if (row >= N || m >= Mrt) continue;
+    float v = red[0][idx];
+    for (int w = 1; w < S; ++w) v += red[w][idx];
+    Y[m * ldy + row] = f32_to_bf16_rne(v);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // gemv_tile (5 <= M <= 32): weights on the matrix cores, codes streamed
 // ---------------------------------------------------------------------------
@@ -650,6 +788,48 @@ void launch_quad_t(const uint16_t* X, int Mrt, int64_t ldx, const uint32_t* code
   }
 }
 
+template <int M, int NB>
+void launch_quad_long_nb(const uint16_t* X, int Mrt, int64_t ldx, const uint32_t* codes,
+                         const uint16_t* scales, const int32_t* zeros, int N, int K, uint16_t* Y,
+                         int64_t ldy, int S, hipStream_t stream) {
+  hipLaunchKernelGGL((gemv_quad_long_kernel<M, NB>), dim3((unsigned)((N + 4 * NB - 1) / (4 * NB))),
+                     dim3(S * kWave), 0, stream, X, Mrt, ldx, codes, scales, zeros, N, K, Y, ldy);
+}
+
+// Long rows: S = 16 waves (one block per CU) or 8 (two), NB = the fewest
+// even batches whose blocks fit on the CUs in one pass; fitted to timings
+// of the down projections of the 70B-shaped set and the 40-layer stack.
+// Returns false when that leaves fewer blocks than half the CUs (a short
+// layer: the caller takes another kernel).
+template <int M>
+bool launch_quad_long(const uint16_t* X, int Mrt, int64_t ldx, const uint32_t* codes,
+                      const uint16_t* scales, const int32_t* zeros, int N, int K, uint16_t* Y,
+                      int64_t ldy, hipStream_t stream, bool need) {
+  constexpr int kMaxNB = M <= 4 ? 8 : 4;   // more rows of accumulators would spill
+  const int cus = cu_count();
+  const int slices = (K + kQuadSlice - 1) / kQuadSlice;
+  int S = 0, nb = 0;
+  for (int s : {16, 8}) {
+    const int st = std::min(s, slices);
+    const int64_t cap = (int64_t)cus * (16 / s);
+    for (int c = 2; c <= kMaxNB && nb == 0; c += 2)
+      if ((N + 4 * c - 1) / (4 * c) <= cap) nb = c;
+    if (nb) { S = st; break; }
+  }
+  if (nb == 0) { S = std::min(8, slices); nb = kMaxNB; }
+  if (!need && (N + 4 * nb - 1) / (4 * nb) < cus / 2) return false;
+  switch (nb) {
+#define W4A16_QL(V)                                                                           \
+  case V:                                                                                     \
+    launch_quad_long_nb<M, (V <= kMaxNB ? V : kMaxNB)>(X, Mrt, ldx, codes, scales, zeros, N, K, \
+                                                       Y, ldy, S, stream);                    \
+    break;
+    W4A16_QL(2) W4A16_QL(4) W4A16_QL(6) W4A16_QL(8)
+  }
+#undef W4A16_QL
+  return true;
+}
+
 // 3 <= M <= 8, K <= 16384: one wave slice of 512 inputs (T = 1) up to 16
 // waves, two slices per wave beyond that
 template <int M>
@@ -674,6 +854,14 @@ int launch_gemv(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes
     else
       launch_quad<8>(X, (int)M, ldx, codes, scales, zeros, (int)N, (int)K, Y, ldy, stream);
     return hipGetLastError() == hipSuccess ? 0 : 4;
+  }
+  if (M >= 3 && M <= 8) {
+    const bool done =
+        M <= 4 ? launch_quad_long<4>(X, (int)M, ldx, codes, scales, zeros, (int)N, (int)K, Y, ldy,
+                                     stream, false)
+               : launch_quad_long<8>(X, (int)M, ldx, codes, scales, zeros, (int)N, (int)K, Y, ldy,
+                                     stream, true);
+    if (done) return hipGetLastError() == hipSuccess ? 0 : 4;
   }
   if (M <= kDotMaxM && K <= (int64_t)kSlice * kMaxSlices) {
     const int n = (int)N, k = (int)K;

@@ -77,10 +77,12 @@ def test_stack40_layers_sampled(M):
 
 
 @pytest.mark.parametrize("M", [3, 4, 5, 8])
-@pytest.mark.parametrize("N,K", [(37, 640), (256, 8320), (64, 16384), (29, 16512)])
+@pytest.mark.parametrize("N,K", [(37, 640), (256, 8320), (64, 16384), (29, 16512), (2048, 20480),
+                                 (40, 33024)])
 def test_matrix_core_small_m_shapes(M, N, K):
-    # ragged row counts, partial 512-input slices, two slices per wave, and
-    # just past the two-slice limit
+    # ragged row counts, partial 512-input slices, two slices per wave, just
+    # past the two-slice limit (long-row kernel, or the dot kernel for few
+    # rows), and rows longer than the dot kernel takes
     check_case(w4.w4a16_gemv, M, N, K, "gemv", f"quad{N}x{K}", shift=True, label=f"M={M} N={N} K={K}")
 
 
