@@ -68,7 +68,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         while procs:
             _wait(procs.pop(0))
         out_tmp = LIB_PATH + ".tmp"
-        cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", out_tmp]
+        cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-Wl,-z,defs", *objs, "-o", out_tmp]
         if verbose:
             print(" ".join(cmd), flush=True)
         _wait(("link", subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

@@ -18,39 +18,51 @@
 //
 // Tiling.  A 512-thread block (8 waves, 2 along M x 4 along N) computes a
 // 256 x 256 tile of Y; each wave owns 128 x 64 (8 x 4 MFMA 16x16x32 tiles).
-// The four waves that share 128 rows each compute the activation sums of two
-// of the eight 16-row tiles and exchange them through LDS.  A K step is a
-// quarter group (32 inputs).  X[256][32] and the codes [256][4 words] of a
-// step go straight from global memory to LDS (global_load_lds_dwordx4) into
-// one of four LDS stages, three steps ahead of the matrix cores, with one
-// barrier per step.  X rows (64 bytes) are stored with their 16-byte chunks
-// XOR-swizzled by (row >> 1) & 3, so the eight rows that one 128-byte LDS
-// cycle of a 16-byte-per-lane read serves fall on eight distinct bank groups.
-// Codes are unpacked in natural k order, so X needs no permutation.  Tiles go
-// to the 8 XCDs in contiguous runs with N fastest, so blocks that share X rows
-// share an L2.
+// (With few such tiles, 256-thread blocks of 128 x 128, waves of 64 x 64.)
+// The waves that share a row half each compute the activation sums of two of
+// its 16-row tiles and exchange them through LDS.  A K step is a quarter
+// group (32 inputs): X[BM][32] of a step goes straight from global memory to
+// LDS (global_load_lds_dwordx4) into one of four stages, issued four steps
+// ahead; the codes of a whole group ([BN][64 bytes]) go the same way into
+// one of two group buffers, a group ahead; one barrier per step.  16-byte
+// chunks of each 64-byte LDS row are XOR-swizzled by (row >> 1) & 3, so the
+// rows that one LDS cycle of a 16-byte-per-lane read serves fall on distinct
+// bank groups.  Codes are unpacked in natural k order, so X needs no
+// permutation.  Tiles go to the 8 XCDs in contiguous runs with N fastest, so
+// blocks that share X rows share an L2.
 
 #include "common.h"
 
 namespace w4a16 {
 namespace {
 
-constexpr int BM = 256;
-constexpr int BN = 256;
-constexpr int WM = 128, WN = 64;       // wave tile
-constexpr int MT = WM / 16, NT = WN / 16;
 constexpr int KS = 32;                 // inputs per K step (a quarter group)
-constexpr int kThreads = 512;
-constexpr int kWaves = kThreads / 64;
 constexpr int kSteps = kGroup / KS;    // K steps per group
-constexpr int X_STAGE = BM * KS * 2;   // bytes of X per stage (16 KiB), four stages
 constexpr int C_ROW = kGroup / 2;      // bytes of codes per column per group (64)
-constexpr int C_GROUP = BN * C_ROW;    // bytes of codes per group (16 KiB), two buffers
-constexpr int X_LOADS = X_STAGE / 1024 / kWaves;  // 1-KiB X copies per wave per step
-constexpr int C_LOADS = C_GROUP / 1024 / kWaves;  // 1-KiB code copies per wave per group
 constexpr int kXcds = 8;
-constexpr int XS_TILES = MT / 4;       // activation-sum tiles computed by each wave
-static_assert(X_LOADS == 2 && C_LOADS == 2, "copy split");
+
+// Block tile BM x BN on (BM / WM) x (BN / WN) waves, each computing a
+// WM x WN wave tile of 16x16 MFMA tiles.  The 256 x 256 tile (8 waves of
+// 128 x 64) is the main one; 128 x 128 (4 waves of 64 x 64) keeps the CUs
+// busy when there are few large tiles.
+template <int BM_, int BN_, int WM_, int WN_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int MT = WM / 16, NT = WN / 16;
+  static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
+  static constexpr int kWaves = WAVES_M * WAVES_N;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int X_STAGE = BM * KS * 2;   // bytes of X per stage, four stages
+  static constexpr int C_GROUP = BN * C_ROW;    // bytes of codes per group, two buffers
+  static constexpr int X_LOADS = X_STAGE / 1024 / kWaves;  // 1-KiB X copies per wave per step
+  static constexpr int C_LOADS = C_GROUP / 1024 / kWaves;  // 1-KiB code copies per wave per group
+  static constexpr int XS_TILES = MT / WAVES_N;  // activation-sum tiles computed by each wave
+  static_assert(WAVES_M == 2, "two waves along M (wm = wave & 1)");
+  static_assert(X_LOADS == 2 && C_LOADS == 2, "copy split");
+  static_assert(XS_TILES == 2, "two activation-sum tiles per wave");
+};
+using TileBig = TileCfg<256, 256, 128, 64>;
+using TileSmall = TileCfg<128, 128, 64, 64>;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -100,16 +112,20 @@ __device__ __forceinline__ void wait_vmcnt() {
 // flight is everything issued after them: two more steps of X copies and,
 // at positions 1 and 2, the group-start loads.  At position 3 the wait also
 // covers the next group's code copies (issued before the awaited X copies).
-template <int ST>
+template <class C, int ST>
 __device__ __forceinline__ void wait_step() {
-  constexpr int kGroupStart = 2 * NT + C_LOADS;
-  if (ST == 1 || ST == 2) wait_vmcnt<2 * X_LOADS + kGroupStart>(); else wait_vmcnt<2 * X_LOADS>();
+  constexpr int kGroupStart = 2 * C::NT + C::C_LOADS;
+  if (ST == 1 || ST == 2) wait_vmcnt<2 * C::X_LOADS + kGroupStart>(); else wait_vmcnt<2 * C::X_LOADS>();
 }
 
-__global__ __launch_bounds__(kThreads) void gemm_kernel(
+template <class C>
+__device__ __forceinline__ void gemm_tile(
     const uint16_t* __restrict__ X, int M, int64_t ldx, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K,
     uint16_t* __restrict__ Y, int64_t ldy, int m_tiles, int n_tiles) {
+  constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, MT = C::MT, NT = C::NT;
+  constexpr int X_STAGE = C::X_STAGE, C_GROUP = C::C_GROUP;
+  constexpr int X_LOADS = C::X_LOADS, C_LOADS = C::C_LOADS, XS_TILES = C::XS_TILES;
   // one LDS object per buffer, so the compiler can tell the copies into one
   // buffer from the reads of another
   __shared__ __attribute__((aligned(1024))) uint8_t xs0[X_STAGE], xs1[X_STAGE], xs2[X_STAGE], xs3[X_STAGE];
@@ -127,7 +143,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave & 1, wn = wave >> 1;   // C::WAVES_M == 2
   const int r16 = lane & 15, q = lane >> 4;
   const int G = K / kGroup;
   const int steps = kSteps * G;
@@ -275,7 +291,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     uint8_t* cg_here = GP == 0 ? cg0 : cg1;
     uint8_t* cg_other = GP == 0 ? cg1 : cg0;
     const int g = s / kSteps;
-    wait_step<ST>();   // step s + 1 landed, every read of stage ST done
+    wait_step<C, ST>();   // step s + 1 landed, every read of stage ST done
     block_barrier();
     // pin this step's fragments here, so the compiler cannot pull their uses
     // up into the previous step next to the reads that produced them
@@ -358,18 +374,54 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     }
 }
 
+// One kernel per tile shape (non-template, so that the host side gets its
+// launch stub).
+__global__ __launch_bounds__(TileBig::kThreads) void gemm_kernel(
+    const uint16_t* __restrict__ X, int M, int64_t ldx, const uint32_t* __restrict__ codes,
+    const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K,
+    uint16_t* __restrict__ Y, int64_t ldy, int m_tiles, int n_tiles) {
+  gemm_tile<TileBig>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, m_tiles, n_tiles);
+}
+
+__global__ __launch_bounds__(TileSmall::kThreads) void gemm_small_kernel(
+    const uint16_t* __restrict__ X, int M, int64_t ldx, const uint32_t* __restrict__ codes,
+    const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K,
+    uint16_t* __restrict__ Y, int64_t ldy, int m_tiles, int n_tiles) {
+  gemm_tile<TileSmall>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, m_tiles, n_tiles);
+}
+
+}  // namespace
+
+namespace {
+template <class C>
+int launch_tiles(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
+                 const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K, uint16_t* Y,
+                 int64_t ldy, hipStream_t stream) {
+  const int64_t mt = (M + C::BM - 1) / C::BM, nt = (N + C::BN - 1) / C::BN;
+  if (mt * nt >= ((int64_t)1 << 31)) return 3;
+  // per-lane 32-bit byte offsets within a tile's rows of X and of the codes
+  if ((C::BM - 1) * ldx * 2 + K * 2 >= ((int64_t)1 << 32) || C::BN * (K / 2) >= ((int64_t)1 << 32))
+    return 3;
+  auto kernel = C::BM == TileBig::BM ? gemm_kernel : gemm_small_kernel;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)(mt * nt)), dim3(C::kThreads), 0, stream, X,
+                     (int)M, ldx, codes, scales, zeros, (int)N, (int)K, Y, ldy, (int)mt, (int)nt);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
 }  // namespace
 
 int launch_gemm(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
                 const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K, uint16_t* Y,
                 int64_t ldy, hipStream_t stream) {
-  const int64_t mt = (M + BM - 1) / BM, nt = (N + BN - 1) / BN;
-  if (mt * nt >= ((int64_t)1 << 31)) return 3;
-  // per-lane 32-bit byte offsets within a tile's rows of X and of the codes
-  if ((BM - 1) * ldx * 2 + K * 2 >= ((int64_t)1 << 32) || BN * (K / 2) >= ((int64_t)1 << 32)) return 3;
-  hipLaunchKernelGGL(gemm_kernel, dim3((unsigned)(mt * nt)), dim3(kThreads), 0, stream, X, (int)M,
-                     ldx, codes, scales, zeros, (int)N, (int)K, Y, ldy, (int)mt, (int)nt);
-  return hipGetLastError() == hipSuccess ? 0 : 4;
+  // 256 x 256 tiles unless they would leave more than half of the CUs idle
+  // (small M and N): then 128 x 128 tiles, a quarter of the work per block,
+  // up to three blocks per CU.  Each small tile runs at about half the rate
+  // of a large one (~450 vs ~860 TFLOP/s on full layers), so the small tiles
+  // win only below half the CUs (measured on the 8B- and 70B-shaped layers,
+  // M = 512 .. 4096).
+  const int64_t big = ((M + TileBig::BM - 1) / TileBig::BM) * ((N + TileBig::BN - 1) / TileBig::BN);
+  if (2 * big >= device_cu_count())
+    return launch_tiles<TileBig>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
+  return launch_tiles<TileSmall>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
 }
 
 }  // namespace w4a16

@@ -677,18 +677,7 @@ __global__ __launch_bounds__(512) void gemv_tile_kernel(
 
 constexpr int kDotMaxM = 4;
 
-// compute units of the current device (queried once per device)
-int cu_count() {
-  static int counts[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (counts[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    counts[dev] = n;
-  }
-  return counts[dev];
-}
+int cu_count() { return device_cu_count(); }
 
 template <int M, int NB>
 void launch_dot_nb(const uint16_t* X, int64_t ldx, const uint32_t* codes, const uint16_t* scales,
