@@ -233,6 +233,35 @@ def main():
         }
         log(f"[bench] prefill M={Mp}: {tf:.1f} TFLOP/s")
         del pxs, pys
+        # the other prefill batch sizes of the layer set, same protocol
+        prefill["other_M"] = []
+        for Mo in (512, 2048):
+            if Mo == Mp:
+                continue
+            oxs = [gen.activations(Mo, L.K, "llama8b_prefill", L.name, device=dev) for L in layers]
+            oys = [torch.empty(Mo, L.N, dtype=torch.bfloat16, device=dev) for L in layers]
+            with torch.cuda.stream(stream):
+                for p, x, y in zip(packed, oxs, oys):
+                    w4.w4a16_gemm(x, p, y)
+                stream.synchronize()
+                otimes = []
+                for p, x, y in zip(packed, oxs, oys):
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    for _ in range(reps):
+                        w4.w4a16_gemm(x, p, y)
+                    e1.record(stream)
+                    e1.synchronize()
+                    otimes.append(e0.elapsed_time(e1) * 1e-3 / reps)
+            oflops = [2.0 * Mo * L.N * L.K for L in layers]
+            otf = sum(oflops) / sum(otimes) / 1e12
+            prefill["other_M"].append({
+                "M": Mo, "TFLOPs": round(otf, 1), "ms_per_step": round(sum(otimes) * 1e3, 4),
+                "layers": [{"layer": L.name, "ms": round(t * 1e3, 4), "TFLOPs": round(f / t / 1e12, 1)}
+                           for L, t, f in zip(layers, otimes, oflops)]})
+            log(f"[bench] prefill M={Mo}: {otf:.1f} TFLOP/s")
+            del oxs, oys
 
     # ---- decode at the other batch sizes of the layer sets (same protocol)
     sweep = None
