@@ -78,3 +78,31 @@ def test_canaries_and_determinism():
     assert torch.equal(out, y2)
     y_ref, mag = reference(gen.bits(X), gen.bits(W))
     assert_output_close(out, y_ref, mag, label="canary")
+
+
+def test_large_tiles_ragged_with_canaries():
+    # enough 256 x 256 tiles for the large-tile kernel (4 x 33 = 132 >= half
+    # the CUs), ragged in M and N, written into a strided view
+    M, N, K = 1000, 8300, 384
+    W = gen.weights(N, K, "gemm", "big_ragged", shift=True, device=DEV)
+    p = w4.w4a16_pack(W)
+    X = gen.activations(M, K, "gemm", "big_ragged", device=DEV)
+    canary = torch.full((M + 3, N + 24), -77.0, dtype=torch.bfloat16, device=DEV)
+    out = canary[1:M + 1, 8:N + 8]
+    w4.w4a16_gemm(X, p, out=out)
+    torch.cuda.synchronize()
+    inner = torch.zeros_like(canary, dtype=torch.bool)
+    inner[1:M + 1, 8:N + 8] = True
+    assert torch.all(canary[~inner] == -77.0), "write outside Y"
+    rows = sample_rows(N, 96, seed=5)
+    mrows = sample_rows(M, 48, seed=6)
+    ridx = torch.as_tensor(rows, device=DEV)
+    midx = torch.as_tensor(mrows, device=DEV)
+    y_ref, mag = reference(gen.bits(X[midx]), gen.bits(W[ridx]))
+    assert_output_close(out[midx][:, ridx], y_ref, mag, label="large tiles, ragged")
+
+
+def test_small_tiles_long_rows():
+    # few large tiles (2 x 8): the 128 x 128 kernel, over 32 groups
+    check_case(300, 2000, 4096, "gemm", "small_long", shift=True, rows=sample_rows(2000, 64, seed=9),
+               label="small tiles, K=4096")
