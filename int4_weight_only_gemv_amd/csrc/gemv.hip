@@ -225,11 +225,12 @@ __global__ __launch_bounds__(1024) void gemv_dot_kernel(
 // contiguous bytes (eight whole 128-byte lines, as coalesced as one 1 KiB
 // row) and feeds eight instructions, and the products cost no vector ALU
 // time: what remains on the VALU is the unpack (7 ops per word), the
-// per-(row, group) correction and the cross-lane sums, so M = 2..8 runs at
-// nearly the cost of M = 1.  The same A against a B of ones gives the
-// activation sums of each lane's 32 inputs once, up front.  A wave keeps its
-// activations in registers for all of its rows; the waves of a block split
-// K and add their partial rows through LDS in a fixed order.
+// per-(row, group) correction and the cross-lane sums, so each further
+// activation row adds little vector ALU work.  The same A against a B of
+// ones gives the activation sums of each lane's 32 inputs once, up front.
+// A wave keeps its activations in registers for all of its rows; the waves
+// of a block split K and add their partial rows through LDS in a fixed
+// order.
 
 constexpr int kQuadSlice = 512;   // inputs per wave and slice: 16 blocks x 32
 constexpr int kQuadMaxWaves = 16;
@@ -517,7 +518,8 @@ __global__ __launch_bounds__(1024) void gemv_quad_long_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// gemv_tile (5 <= M <= 32): weights on the matrix cores, codes streamed
+// gemv_tile (9 <= M <= 32, and the shapes the other kernels leave): weights
+// on the matrix cores, codes streamed
 // ---------------------------------------------------------------------------
 //
 // D = A B on v_mfma_f32_16x16x32_bf16 with A = 16 activation rows (M padded)
