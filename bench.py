@@ -291,7 +291,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 activations x int4 weights, fp32 accumulate",
+        "dtype": "bf16",
+        "dtype_detail": "bf16 activations x int4 weights (exact bf16 operands 128+q), fp32 accumulate, bf16 output",
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: Llama-3-8B-shaped decode layer set "
                                f"(qkv 6144x4096, o 4096x4096, gate_up 28672x4096, down 4096x14336), "
