@@ -18,13 +18,16 @@
 //
 // Tiling.  A 512-thread block (8 waves, 2 along M x 4 along N) computes a
 // 256 x 256 tile of Y; each wave owns 128 x 64 (8 x 4 MFMA 16x16x32 tiles).
-// (With few such tiles, 256-thread blocks of 128 x 128, waves of 64 x 64.)
-// The waves that share a row half each compute the activation sums of two of
-// its 16-row tiles and exchange them through LDS.  A K step is a quarter
+// (With few such tiles, 256-thread blocks of 128 x 128, waves of 64 x 64,
+// three blocks per CU.)  The waves that share a row half each compute the
+// activation sums of two of its 16-row tiles (from A fragments they read
+// anyway) and exchange them through LDS.  A K step is a quarter
 // group (32 inputs): X[BM][32] of a step goes straight from global memory to
 // LDS (global_load_lds_dwordx4) into one of four stages, issued four steps
 // ahead; the codes of a whole group ([BN][64 bytes]) go the same way into
-// one of two group buffers, a group ahead; one barrier per step.  16-byte
+// one of two group buffers, a group ahead; one barrier per step.  The next
+// step's A fragment of a row tile is read right after the row's products,
+// so the LDS reads run under the matrix-core work.  16-byte
 // chunks of each 64-byte LDS row are XOR-swizzled by (row >> 1) & 3, so the
 // rows that one LDS cycle of a 16-byte-per-lane read serves fall on distinct
 // bank groups.  Codes are unpacked in natural k order, so X needs no
@@ -192,6 +195,14 @@ __device__ __forceinline__ void gemm_tile(
   const int ncol = n0 + wn * WN + r16;
   const uint16_t* sblk = scales + (int64_t)n0 * G;
   const int32_t* zblk = zeros + (int64_t)n0 * G;
+  // 32-bit byte offsets from a block-uniform base (the launcher checks the
+  // range), so the loads take a scalar base and no 64-bit lane addresses
+  auto ld_s = [&](uint32_t e) {
+    return (uint32_t)*reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(sblk) + e * 2u);
+  };
+  auto ld_z = [&](uint32_t e) {
+    return *reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(zblk) + e * 4u);
+  };
   uint32_t moffs[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) moffs[nt] = (uint32_t)(min(ncol + 16 * nt, N - 1) - n0) * (uint32_t)G;
@@ -206,6 +217,11 @@ __device__ __forceinline__ void gemm_tile(
   const int brow = wn * WN + r16;
   const int bswz = (brow >> 1) & 3;
   const int boff = brow * C_ROW + q * 4;
+  // Row tiles in a wave-dependent order: register row tile j is row tile
+  // rowt(j), so that the tiles whose activation sums this wave computes
+  // (XS_TILES wn ..) come first and their A fragments are af[0 ..].
+  const int rot = wn * XS_TILES;
+  auto rowt = [&](int j) { return (j + rot) & (MT - 1); };
 
   f32x4 acc[MT][NT];
 #pragma unroll
@@ -229,7 +245,7 @@ __device__ __forceinline__ void gemm_tile(
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const f32x4 xs = *reinterpret_cast<const f32x4*>(&xsum_lds[wm * WM + mt * 16 + 4 * q]);
+      const f32x4 xs = *reinterpret_cast<const f32x4*>(&xsum_lds[wm * WM + rowt(mt) * 16 + 4 * q]);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -238,27 +254,30 @@ __device__ __forceinline__ void gemm_tile(
   };
 
   // Operand fragments of one K step, read from LDS one step ahead of use:
-  // A (8 row tiles), the A of this wave's two activation-sum tiles, and the
-  // raw code words of the 4 column tiles (chunk `pos` of the group buffer).
-  u32x4 af[MT], xf[XS_TILES];
+  // the raw code words of the 4 column tiles (chunk `pos` of the group
+  // buffer) and A of the 8 row tiles.
+  u32x4 af[MT];
   uint32_t bw[NT];
-  auto read_frags = [&](const uint8_t* xs, const uint8_t* cg, int pos) {
+  auto read_b = [&](const uint8_t* cg, int pos) {
     const int bo = boff + ((pos ^ bswz) * 16);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) bw[nt] = *reinterpret_cast<const uint32_t*>(&cg[bo + nt * 16 * C_ROW]);
+  };
+  auto read_a = [&](const uint8_t* xs, int mt) {
+    af[mt] = *reinterpret_cast<const u32x4*>(&xs[aoff + rowt(mt) * 16 * (KS * 2)]);
+  };
+  auto read_frags = [&](const uint8_t* xs, const uint8_t* cg, int pos) {
+    read_b(cg, pos);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) af[mt] = *reinterpret_cast<const u32x4*>(&xs[aoff + mt * 16 * (KS * 2)]);
-#pragma unroll
-    for (int i = 0; i < XS_TILES; ++i)
-      xf[i] = *reinterpret_cast<const u32x4*>(&xs[aoff + (wn * XS_TILES + i) * 16 * (KS * 2)]);
+    for (int mt = 0; mt < MT; ++mt) read_a(xs, mt);
   };
 
   // prologue: group 0's scale/zero and codes, steps 0..3 of X in flight,
   // step 0's fragments in registers (steps >= 4)
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    s_cur[nt] = sblk[moffs[nt]];
-    z_cur[nt] = zblk[moffs[nt]];
+    s_cur[nt] = ld_s(moffs[nt]);
+    z_cur[nt] = ld_z(moffs[nt]);
     s_nxt[nt] = s_cur[nt];
     z_nxt[nt] = z_cur[nt];
   }
@@ -298,8 +317,6 @@ __device__ __forceinline__ void gemm_tile(
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) asm volatile("" : "+v"(af[mt]));
 #pragma unroll
-    for (int i = 0; i < XS_TILES; ++i) asm volatile("" : "+v"(xf[i]));
-#pragma unroll
     for (int nt = 0; nt < NT; ++nt) asm volatile("" : "+v"(bw[nt]));
     if (ST == 0) {
       // the previous group's activation sums are in LDS: fold it in
@@ -309,29 +326,32 @@ __device__ __forceinline__ void gemm_tile(
       const int gn = min(g + 1, G - 1);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        s_nxt[nt] = sblk[moffs[nt] + gn];
-        z_nxt[nt] = zblk[moffs[nt] + gn];
+        s_nxt[nt] = ld_s(moffs[nt] + (uint32_t)gn);
+        z_nxt[nt] = ld_z(moffs[nt] + (uint32_t)gn);
       }
       copy_codes(cg_other, gn);
     }
     copy_x(xs_here, min(s + 4, steps - 1));
 
+    // this wave's share of the activation sums: its own row tiles, the
+    // first XS_TILES register row tiles
+#pragma unroll
+    for (int i = 0; i < XS_TILES; ++i)
+      xpart[i] = mfma16x16x32(af[i], ones, ST == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : xpart[i]);
     u32x4 b[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) b[nt] = codes_to_bias128_natural(bw[nt]);
-    const u32x4 x0 = xf[0], x1 = xf[1];
-    u32x4 a[MT];
+    // the next step's fragments (past the last step: a harmless re-read):
+    // code words into the registers just freed, each A row tile after its
+    // products
+    if (ST == kSteps - 1) read_b(cg_other, 0); else read_b(cg_here, ST + 1);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) a[mt] = af[mt];
-    // next step's fragments (past the last step: a harmless re-read)
-    if (ST == kSteps - 1) read_frags(xs_next, cg_other, 0); else read_frags(xs_next, cg_here, ST + 1);
+    for (int mt = 0; mt < MT; ++mt) {
+      const u32x4 a = af[mt];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma16x16x32(a[mt], b[nt], acc[mt][nt]);
-    // this wave's share of the activation sums: its own two 16-row tiles
-    xpart[0] = mfma16x16x32(x0, ones, ST == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : xpart[0]);
-    xpart[1] = mfma16x16x32(x1, ones, ST == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : xpart[1]);
+      for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma16x16x32(a, b[nt], acc[mt][nt]);
+      read_a(xs_next, mt);
+    }
     if (ST == kSteps - 1) {
       // publish this wave's activation sums.  Every column of the ones
       // product holds the same sums, so all 16 lanes of a row group store
@@ -368,7 +388,7 @@ __device__ __forceinline__ void gemm_tile(
       if (n >= N) continue;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm * WM + mt * 16 + 4 * q + r;
+        const int m = m0 + wm * WM + rowt(mt) * 16 + 4 * q + r;
         if (m < M) Y[(int64_t)m * ldy + n] = f32_to_bf16_rne(acc[mt][nt][r]);
       }
     }
@@ -383,7 +403,10 @@ __global__ __launch_bounds__(TileBig::kThreads) void gemm_kernel(
   gemm_tile<TileBig>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, m_tiles, n_tiles);
 }
 
-__global__ __launch_bounds__(TileSmall::kThreads) void gemm_small_kernel(
+// three blocks per CU: the register budget of three waves per SIMD (without
+// it the compiler keeps the accumulators in AGPRs at one wave per SIMD)
+__global__ __launch_bounds__(TileSmall::kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void gemm_small_kernel(
     const uint16_t* __restrict__ X, int M, int64_t ldx, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K,
     uint16_t* __restrict__ Y, int64_t ldy, int m_tiles, int n_tiles) {
@@ -399,8 +422,10 @@ int launch_tiles(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* code
                  int64_t ldy, hipStream_t stream) {
   const int64_t mt = (M + C::BM - 1) / C::BM, nt = (N + C::BN - 1) / C::BN;
   if (mt * nt >= ((int64_t)1 << 31)) return 3;
-  // per-lane 32-bit byte offsets within a tile's rows of X and of the codes
-  if ((C::BM - 1) * ldx * 2 + K * 2 >= ((int64_t)1 << 32) || C::BN * (K / 2) >= ((int64_t)1 << 32))
+  // per-lane 32-bit byte offsets within a tile's rows of X, of the codes and
+  // of the zero points
+  if ((C::BM - 1) * ldx * 2 + K * 2 >= ((int64_t)1 << 32) || C::BN * (K / 2) >= ((int64_t)1 << 32) ||
+      C::BN * (K / kGroup) * 4 >= ((int64_t)1 << 32))
     return 3;
   auto kernel = C::BM == TileBig::BM ? gemm_kernel : gemm_small_kernel;
   hipLaunchKernelGGL(kernel, dim3((unsigned)(mt * nt)), dim3(C::kThreads), 0, stream, X,
@@ -412,14 +437,14 @@ int launch_tiles(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* code
 int launch_gemm(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
                 const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K, uint16_t* Y,
                 int64_t ldy, hipStream_t stream) {
-  // 256 x 256 tiles unless they would leave more than half of the CUs idle
-  // (small M and N): then 128 x 128 tiles, a quarter of the work per block,
-  // up to three blocks per CU.  Each small tile runs at about half the rate
-  // of a large one (~450 vs ~860 TFLOP/s on full layers), so the small tiles
-  // win only below half the CUs (measured on the 8B- and 70B-shaped layers,
-  // M = 512 .. 4096).
+  // 256 x 256 tiles when there are at least three per four CUs, else
+  // 128 x 128 tiles, a quarter of the work per block, three blocks per CU.
+  // On whole layers the small tiles run at ~560-610 TFLOP/s and the large
+  // ones at ~750-770, so the small tiles win when the large ones would leave
+  // a quarter of the CUs idle (measured on the 8B-shaped layers, M = 512 ..
+  // 4096: at 192 large tiles the two are level).
   const int64_t big = ((M + TileBig::BM - 1) / TileBig::BM) * ((N + TileBig::BN - 1) / TileBig::BN);
-  if (2 * big >= device_cu_count())
+  if (4 * big >= 3 * (int64_t)device_cu_count())
     return launch_tiles<TileBig>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
   return launch_tiles<TileSmall>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
 }
