@@ -81,9 +81,10 @@ def test_canaries_and_determinism():
 
 
 def test_large_tiles_ragged_with_canaries():
-    # enough 256 x 256 tiles for the large-tile kernel (4 x 33 = 132 >= half
-    # the CUs), ragged in M and N, written into a strided view
-    M, N, K = 1000, 8300, 384
+    # enough 256 x 256 tiles for the large-tile kernel (4 x 49 = 196, at least
+    # three per four of the 256 CUs), ragged in M and N, written into a
+    # strided view
+    M, N, K = 1000, 12300, 384
     W = gen.weights(N, K, "gemm", "big_ragged", shift=True, device=DEV)
     p = w4.w4a16_pack(W)
     X = gen.activations(M, K, "gemm", "big_ragged", device=DEV)
@@ -106,3 +107,12 @@ def test_small_tiles_long_rows():
     # few large tiles (2 x 8): the 128 x 128 kernel, over 32 groups
     check_case(300, 2000, 4096, "gemm", "small_long", shift=True, rows=sample_rows(2000, 64, seed=9),
                label="small tiles, K=4096")
+
+
+def test_tile_choice_boundary():
+    # just below and at the large-tile threshold (191 and 192 large tiles of
+    # 256 x 256 on 256 CUs): both kernels, ragged M, against the oracle
+    for M, N in ((200, 256 * 191 - 50), (200, 256 * 192 - 50)):
+        check_case(M, N, 256, "gemm", f"boundary_{N}", shift=True, rows=sample_rows(N, 48, seed=N),
+                   mrows=sample_rows(M, 32, seed=M), label=f"tile boundary {M}x{N}")
+        torch.cuda.empty_cache()
