@@ -27,6 +27,10 @@ the source pages):
 * AWQ: s_i = importance_i ** alpha, W' = W . diag(s), X' = diag(s)^-1 X folded
   into the producer -- Axe Corsa model card, "Stage 1: Activation-Aware Weight
   Scaling".
+* Comparisons outside the fused path: the dense BF16 weights an offline
+  dequantisation would store, and the dense BF16 product -- Zeno AGI,
+  "Weight-only vs mixed precision" (offline-versus-fused table, "7. The
+  Marlin Kernel").
 
 Every function is deliberately unoptimised: explicit bit manipulation,
 explicit rounding, float64 products.  Vectorisation over whole arrays with
@@ -217,6 +221,47 @@ def matmul_ref(X_bits: np.ndarray, codes: np.ndarray, scales: np.ndarray,
     w_hat = dequantize(codes, scales, zeros)
     x = bf16_to_f32(X_bits).astype(np.float64)
     return x @ w_hat.T
+
+
+# ---------------------------------------------------------------------------
+# Dense BF16 comparisons: the offline expansion the pages warn against and
+# the dense product the INT4 path is measured against
+# ---------------------------------------------------------------------------
+
+def dequantize_bf16(codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray) -> np.ndarray:
+    """Dense BF16 weights of an offline dequantisation: w[n,k] =
+    BF16_RNE(fl32(fl32(q - z) * s)), g = k // 128, as BF16 bits [N][K].
+
+    The expansion itself is the "dequantise offline" alternative of Zeno AGI,
+    "Weight-only vs mixed precision" (table of offline versus fused
+    dequantisation) and the middle kernel of its naive three-kernel pipeline
+    ("7. The Marlin Kernel").  Reading: the pages fix no precision for it;
+    here the integer difference becomes float32 (exact below 2**24), one
+    float32 multiply rounds to nearest even, and one more rounding to nearest
+    even gives BF16.  The result is NOT the exact dequantised weight: it is
+    what a dense BF16 model built from the packed weights holds."""
+    q = unpack_codes(codes).astype(np.int64)
+    N, K = q.shape
+    s = bf16_to_f32(scales)
+    z = np.asarray(zeros, dtype=np.int64)
+    g = np.arange(K) // GROUP
+    diff = (q - z[:, g]).astype(np.float32)
+    prod = np.multiply(diff, s[:, g], dtype=np.float32)
+    return f32_to_bf16_rne(prod)
+
+
+def dense_matmul_ref(X_bits: np.ndarray, W_bits: np.ndarray,
+                     rows: np.ndarray | None = None) -> np.ndarray:
+    """Y[m,n] = sum_k X[m,k] * W[n,k] for BF16 X [M][K] and BF16 W [N][K],
+    in float64 (the dense BF16 linear layer, Zeno AGI, "Weight-only vs mixed
+    precision", "1. The Basic Recipe": weights and activations both 16-bit).
+    If `rows` is given only those output columns are computed."""
+    W = np.asarray(W_bits)
+    if rows is not None:
+        W = W[rows]
+    x = bf16_to_f32(X_bits).astype(np.float64)
+    w = bf16_to_f32(W).astype(np.float64)
+    return x @ w.T
 
 
 # ---------------------------------------------------------------------------

@@ -422,3 +422,75 @@ def check_output_gate():
     assert O.output_ok(yb, y)
     assert not O.output_ok(y * 1.01, y)
     assert not O.output_ok(y + np.where(np.arange(512) == 7, 0.5, 0.0), y)
+
+
+# ---------------------------------------------------------------------------
+# Dense BF16 comparisons
+# ---------------------------------------------------------------------------
+
+def check_dequant_bf16_hand():
+    """Offline BF16 expansion on constructed groups.
+    Group 1: s = 2**-3, z = 3: (q - 3)/8 for q = 0..15 is a BF16 value, so
+    the expansion is exact.
+    Group 2: s = 1, z = -250: v = q + 250 runs over 250..265.  BF16 holds
+    every integer below 256 and the even ones in [256, 512) (8 significant
+    bits); an odd v >= 257 is a tie between its neighbours and goes to the
+    one with an even last mantissa bit: 257 -> 256, 259 -> 260, 261 -> 260,
+    263 -> 264, 265 -> 264 (mantissa m = (v - 256)/2)."""
+    words = np.array([[0x76543210, 0xFEDCBA98] * 8, [0x76543210, 0xFEDCBA98] * 8], dtype=np.uint32)
+    scales = np.array([[0x3E00], [0x3F80]], dtype=np.uint16)      # 2**-3, 1.0
+    zeros = np.array([[3], [-250]], dtype=np.int32)
+    got = O.dequantize_bf16(words, scales, zeros)
+    q = np.arange(16)
+    exp1 = _bf16_bits_of((q - 3) / 8.0)
+    v2 = [250, 251, 252, 253, 254, 255, 256, 256, 258, 260, 260, 260, 262, 264, 264, 264]
+    exp2 = _bf16_bits_of(v2)
+    for rep in range(8):
+        assert np.array_equal(got[0, 16 * rep:16 * rep + 16], exp1), got[0, :16]
+        assert np.array_equal(got[1, 16 * rep:16 * rep + 16], exp2), got[1, :16]
+
+
+def check_dequant_bf16_vs_torch(seed=12, N=16, K=512):
+    """Where the float32 product is exact (|q - z| < 2**16 times an 8-bit
+    scale), the expansion is the exact dequantised weight rounded once to
+    BF16: compare with torch's float32 -> bfloat16 conversion (round to
+    nearest even) of the float64 dequantisation."""
+    rng = np.random.default_rng(seed)
+    q = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    codes = O.pack_codes(q)
+    scales = O.f32_to_bf16_rtz(rng.uniform(1e-3, 3.0, size=(N, K // 128)).astype(np.float32))
+    zeros = rng.integers(-400, 400, size=(N, K // 128)).astype(np.int32)
+    exact = O.dequantize(codes, scales, zeros).astype(np.float32)
+    ref = torch.from_numpy(exact).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.dequantize_bf16(codes, scales, zeros), ref)
+
+
+def check_dense_brute_force(seed=13, M=3, N=5, K=40):
+    """Dense product against an exact rational sum of the BF16 inputs."""
+    rng = np.random.default_rng(seed)
+    X_bits = O.f32_to_bf16_rne(rng.normal(0, 1, size=(M, K)).astype(np.float32))
+    W_bits = O.f32_to_bf16_rne(rng.normal(0, 0.05, size=(N, K)).astype(np.float32))
+    y = O.dense_matmul_ref(X_bits, W_bits)
+    assert y.shape == (M, N)
+    xf, wf = O.bf16_to_f32(X_bits), O.bf16_to_f32(W_bits)
+    for m in range(M):
+        for n in range(N):
+            acc = sum(_frac_of_f32(xf[m, k]) * _frac_of_f32(wf[n, k]) for k in range(K))
+            mag = sum(abs(_frac_of_f32(xf[m, k]) * _frac_of_f32(wf[n, k])) for k in range(K))
+            assert abs(Fraction(float(y[m, n])) - acc) <= mag * Fraction(1, 2 ** 45), (m, n)
+    rows = np.array([4, 1])
+    assert np.array_equal(O.dense_matmul_ref(X_bits, W_bits, rows), y[:, rows])
+
+
+def check_dense_matches_fused_on_grid(seed=14, M=4, N=6, K=256):
+    """With power-of-two scales and small |q - z| the BF16 expansion is
+    exact, so the dense product of the expanded weights equals the fused
+    reference term for term."""
+    rng = np.random.default_rng(seed)
+    q = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    codes = O.pack_codes(q)
+    scales = _bf16_bits_of(2.0 ** rng.integers(-8, 2, size=(N, K // 128)))
+    zeros = rng.integers(-20, 20, size=(N, K // 128)).astype(np.int32)
+    X_bits = O.f32_to_bf16_rne(rng.normal(0, 1, size=(M, K)).astype(np.float32))
+    W_bits = O.dequantize_bf16(codes, scales, zeros)
+    assert np.array_equal(O.dense_matmul_ref(X_bits, W_bits), O.matmul_ref(X_bits, codes, scales, zeros))

@@ -14,6 +14,8 @@ ALL_PINS = [
     P.check_awq_prescale_power_of_two, P.check_awq_fold_hand,
     P.check_awq_importance_and_scale, P.check_awq_equivalence_unquantised,
     P.check_storage_cost,
+    P.check_dequant_bf16_hand, P.check_dequant_bf16_vs_torch,
+    P.check_dense_brute_force, P.check_dense_matches_fused_on_grid,
 ]
 
 
@@ -126,6 +128,33 @@ def _importance_no_abs(Xcal_bits):
     return R.bf16_to_f32(Xcal_bits).astype(np.float64).mean(axis=0)
 
 
+def _dequant_bf16_truncated(codes, scales, zeros):
+    q = R.unpack_codes(codes).astype(np.int64)
+    K = q.shape[1]
+    s = R.bf16_to_f32(scales)
+    z = np.asarray(zeros, np.int64)
+    g = np.arange(K) // 128
+    return R.f32_to_bf16_rtz(np.multiply((q - z[:, g]).astype(np.float32), s[:, g], dtype=np.float32))
+
+
+def _dequant_bf16_zero_added(codes, scales, zeros):
+    q = R.unpack_codes(codes).astype(np.int64)
+    K = q.shape[1]
+    s = R.bf16_to_f32(scales)
+    z = np.asarray(zeros, np.int64)
+    g = np.arange(K) // 128
+    return R.f32_to_bf16_rne(np.multiply((q + z[:, g]).astype(np.float32), s[:, g], dtype=np.float32))
+
+
+def _dense_drops_last_k(X_bits, W_bits, rows=None):
+    W = np.asarray(W_bits)
+    if rows is not None:
+        W = W[rows]
+    x = R.bf16_to_f32(X_bits).astype(np.float64)[:, :-1]
+    w = R.bf16_to_f32(W).astype(np.float64)[:, :-1]
+    return x @ w.T
+
+
 ORIG = {n: getattr(R, n) for n in ["group_scale_zero", "quantize"]}
 
 MUTATIONS = {
@@ -142,6 +171,9 @@ MUTATIONS = {
     "awq_scale_ignored": ("quantize", _quantize_ignores_awq),
     "fold_multiplies": ("awq_fold", _fold_multiplies),
     "importance_without_abs": ("awq_importance", _importance_no_abs),
+    "dequant_bf16_truncated": ("dequantize_bf16", _dequant_bf16_truncated),
+    "dequant_bf16_zero_added": ("dequantize_bf16", _dequant_bf16_zero_added),
+    "dense_drops_last_k": ("dense_matmul_ref", _dense_drops_last_k),
 }
 
 

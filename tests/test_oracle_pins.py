@@ -101,3 +101,19 @@ def test_generator_deterministic():
     assert np.array_equal(x, gen.bits(gen.activations(3, 256, 1, "qkv")))
     S = gen.salient_channels(4096, 1, "qkv").numpy()
     assert len(S) == 41 and len(np.unique(S)) == 41
+
+
+def test_dequant_bf16_hand():
+    P.check_dequant_bf16_hand()
+
+
+def test_dequant_bf16_vs_torch():
+    P.check_dequant_bf16_vs_torch()
+
+
+def test_dense_brute_force():
+    P.check_dense_brute_force()
+
+
+def test_dense_matches_fused_on_grid():
+    P.check_dense_matches_fused_on_grid()
