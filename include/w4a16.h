@@ -53,8 +53,9 @@ extern "C" {
 #endif
 
 #define W4A16_GROUP 128
-#define W4A16_ABI_VERSION 1
+#define W4A16_ABI_VERSION 2
 #define W4A16_GEMV_MAX_M 32
+#define W4A16_DENSE_GEMV_MAX_M 8
 
 enum {
   W4A16_OK = 0,
@@ -166,6 +167,47 @@ int w4a16_awq_fold(const float* s, int64_t K, uint16_t* gamma,
 int w4a16_scale_channels(const uint16_t* X, int64_t M, int64_t K,
                          int64_t ldx, const uint16_t* gamma, uint16_t* Xout,
                          int64_t ldo, void* stream);
+
+/*
+ * Dense BF16 comparisons.  Not part of the fused path: they measure the
+ * alternatives it is chosen over (Zeno AGI, "Weight-only vs mixed
+ * precision": the table of offline versus fused dequantisation, the naive
+ * three-kernel pipeline of "7. The Marlin Kernel", and the dense 16-bit
+ * layer of "1. The Basic Recipe") at the same shapes.
+ *
+ * w4a16_dequantize_bf16 -- expand a packed matrix to dense BF16:
+ *   W[n, k] = BF16_rne(fl32(fl32(q[n, k] - z[n, g]) * s[n, g])), g = k / 128,
+ * i.e. the float32 product rounded once to BF16 (the pages fix no precision
+ * for an offline expansion).  Unlike the fused kernels this rounds every
+ * weight.  codes, scales, zeros as for w4a16_gemv; W BF16 [N][ldw] output,
+ * 16-byte aligned, ldw % 8 == 0, ldw >= K.  Requires N >= 1, K >= 128,
+ * K % 128 == 0, and |q - z| < 2^31.  Bit-exact.
+ */
+int w4a16_dequantize_bf16(const uint32_t* codes, const uint16_t* scales,
+                          const int32_t* zeros, int64_t N, int64_t K,
+                          uint16_t* W, int64_t ldw, void* stream);
+
+/*
+ * w4a16_dense_gemv -- dense BF16 decode-shaped Y = X * W^T,
+ * 1 <= M <= W4A16_DENSE_GEMV_MAX_M (8).
+ *   X  BF16 [M][ldx];  W  BF16 [N][ldw], row n the K input weights of
+ *   output n;  Y  BF16 [M][ldy].
+ * Exact BF16 products accumulated in float32, rounded once to BF16 (nearest
+ * even).  Requires N >= 1, K >= 128, K % 128 == 0, ldx >= K, ldw >= K,
+ * ldy >= N; X and W 16-byte aligned, ldx % 8 == 0, ldw % 8 == 0.
+ */
+int w4a16_dense_gemv(const uint16_t* X, int64_t M, int64_t ldx,
+                     const uint16_t* W, int64_t ldw, int64_t N, int64_t K,
+                     uint16_t* Y, int64_t ldy, void* stream);
+
+/*
+ * w4a16_dense_gemm -- dense BF16 prefill-shaped Y = X * W^T on the matrix
+ * cores, any M >= 1.  Same arguments, accuracy and rules as
+ * w4a16_dense_gemv without the limit on M.
+ */
+int w4a16_dense_gemm(const uint16_t* X, int64_t M, int64_t ldx,
+                     const uint16_t* W, int64_t ldw, int64_t N, int64_t K,
+                     uint16_t* Y, int64_t ldy, void* stream);
 
 #ifdef __cplusplus
 }

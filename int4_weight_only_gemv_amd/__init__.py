@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libw4a16.so")
 
 GROUP = 128
 GEMV_MAX_M = 32
+DENSE_GEMV_MAX_M = 8
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -41,6 +42,9 @@ _SIGS = {
     "w4a16_awq_scale": ([_p, _i64, ctypes.c_float, _p, _p], ctypes.c_int),
     "w4a16_awq_fold": ([_p, _i64, _p, _p, _p], ctypes.c_int),
     "w4a16_scale_channels": ([_p, _i64, _i64, _i64, _p, _p, _i64, _p], ctypes.c_int),
+    "w4a16_dequantize_bf16": ([_p, _p, _p, _i64, _i64, _p, _i64, _p], ctypes.c_int),
+    "w4a16_dense_gemv": ([_p, _i64, _i64, _p, _i64, _i64, _i64, _p, _i64, _p], ctypes.c_int),
+    "w4a16_dense_gemm": ([_p, _i64, _i64, _p, _i64, _i64, _i64, _p, _i64, _p], ctypes.c_int),
 }
 for _name, (_args, _ret) in _SIGS.items():
     _f = getattr(lib, _name)
@@ -197,3 +201,49 @@ def w4a16_scale_channels(X: torch.Tensor, gamma: torch.Tensor,
            lib.w4a16_scale_channels(_ptr(X), M, K, X.stride(0), _ptr(gamma), _ptr(out),
                                     out.stride(0), _stream(X)))
     return out
+
+
+# ---------------------------------------------------------------------------
+# Dense BF16 comparisons (not the fused path; see w4a16.h)
+# ---------------------------------------------------------------------------
+
+def w4a16_dequantize_bf16(p: PackedLinear, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Dense BF16 weights [N][K] of an offline expansion of `p`."""
+    if out is None:
+        out = torch.empty(p.N, p.K, dtype=torch.bfloat16, device=p.codes.device)
+    else:
+        _need(out, torch.bfloat16, "out", 2)
+        if tuple(out.shape) != (p.N, p.K):
+            raise ValueError("out has the wrong shape")
+    _check("w4a16_dequantize_bf16",
+           lib.w4a16_dequantize_bf16(_ptr(p.codes), _ptr(p.scales), _ptr(p.zeros), p.N, p.K,
+                                     _ptr(out), out.stride(0), _stream(out)))
+    return out
+
+
+def _dense(fn, name, X: torch.Tensor, W: torch.Tensor, out: torch.Tensor | None):
+    _need(X, torch.bfloat16, "X", 2)
+    _need(W, torch.bfloat16, "W", 2)
+    M, K = X.shape
+    N = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError(f"X has K={K}, W has K={W.shape[1]}")
+    if out is None:
+        out = torch.empty(M, N, dtype=torch.bfloat16, device=X.device)
+    else:
+        _need(out, torch.bfloat16, "out", 2)
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out has the wrong shape")
+    _check(name, fn(_ptr(X), M, X.stride(0), _ptr(W), W.stride(0), N, K, _ptr(out), out.stride(0),
+                    _stream(X)))
+    return out
+
+
+def w4a16_dense_gemv(X: torch.Tensor, W: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Dense BF16 Y = X . W^T for 1 <= M <= 8 (decode comparison)."""
+    return _dense(lib.w4a16_dense_gemv, "w4a16_dense_gemv", X, W, out)
+
+
+def w4a16_dense_gemm(X: torch.Tensor, W: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Dense BF16 Y = X . W^T on the matrix cores, any M (prefill comparison)."""
+    return _dense(lib.w4a16_dense_gemm, "w4a16_dense_gemm", X, W, out)

@@ -38,6 +38,7 @@ SOURCES = {
     "gemv.hip": [],
     "gemm.hip": [],
     "awq.hip": EXACT,
+    "dense.hip": EXACT,
 }
 
 

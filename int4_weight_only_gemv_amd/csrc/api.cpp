@@ -18,6 +18,12 @@ int launch_awq_scale(const float*, int64_t, float, float*, hipStream_t);
 int launch_awq_fold(const float*, int64_t, uint16_t*, uint16_t*, hipStream_t);
 int launch_scale_channels(const uint16_t*, int64_t, int64_t, int64_t, const uint16_t*, uint16_t*,
                           int64_t, hipStream_t);
+int launch_dequant_bf16(const uint32_t*, const uint16_t*, const int32_t*, int64_t, int64_t,
+                        uint16_t*, int64_t, hipStream_t);
+int launch_dense_gemv(const uint16_t*, int64_t, int64_t, const uint16_t*, int64_t, int64_t, int64_t,
+                      uint16_t*, int64_t, hipStream_t);
+int launch_dense_gemm(const uint16_t*, int64_t, int64_t, const uint16_t*, int64_t, int64_t, int64_t,
+                      uint16_t*, int64_t, hipStream_t);
 }  // namespace w4a16
 
 namespace {
@@ -36,6 +42,18 @@ int check_matmul(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* code
   if (ldx < K || ldy < N) return W4A16_ERR_INVALID_ARG;
   if (!aligned(X, 16) || ldx % 8 || !aligned(codes, 16) || !aligned(scales, 2) ||
       !aligned(zeros, 4) || !aligned(Y, 2))
+    return W4A16_ERR_MISALIGNED;
+  return W4A16_OK;
+}
+
+// Checks shared by the dense comparisons.
+int check_dense(const uint16_t* X, int64_t M, int64_t ldx, const uint16_t* W, int64_t ldw,
+                int64_t N, int64_t K, const uint16_t* Y, int64_t ldy) {
+  if (!X || !W || !Y) return W4A16_ERR_INVALID_ARG;
+  if (M < 1 || N < 1 || K < W4A16_GROUP || K % W4A16_GROUP) return W4A16_ERR_INVALID_ARG;
+  if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return W4A16_ERR_UNSUPPORTED;
+  if (ldx < K || ldw < K || ldy < N) return W4A16_ERR_INVALID_ARG;
+  if (!aligned(X, 16) || ldx % 8 || !aligned(W, 16) || ldw % 8 || !aligned(Y, 2))
     return W4A16_ERR_MISALIGNED;
   return W4A16_OK;
 }
@@ -113,6 +131,31 @@ int w4a16_scale_channels(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
   if (M >= kMaxDim || K >= kMaxDim || M * K >= ((int64_t)1 << 38)) return W4A16_ERR_UNSUPPORTED;
   if (!aligned(X, 2) || !aligned(gamma, 2) || !aligned(Xout, 2)) return W4A16_ERR_MISALIGNED;
   return w4a16::launch_scale_channels(X, M, K, ldx, gamma, Xout, ldo, (hipStream_t)stream);
+}
+
+int w4a16_dequantize_bf16(const uint32_t* codes, const uint16_t* scales, const int32_t* zeros,
+                          int64_t N, int64_t K, uint16_t* W, int64_t ldw, void* stream) {
+  if (!codes || !scales || !zeros || !W) return W4A16_ERR_INVALID_ARG;
+  if (N < 1 || K < W4A16_GROUP || K % W4A16_GROUP || ldw < K) return W4A16_ERR_INVALID_ARG;
+  if (N >= kMaxDim || K >= kMaxDim || N * (K / 8) >= ((int64_t)1 << 38)) return W4A16_ERR_UNSUPPORTED;
+  if (!aligned(codes, 16) || !aligned(scales, 2) || !aligned(zeros, 4) || !aligned(W, 16) || ldw % 8)
+    return W4A16_ERR_MISALIGNED;
+  return w4a16::launch_dequant_bf16(codes, scales, zeros, N, K, W, ldw, (hipStream_t)stream);
+}
+
+int w4a16_dense_gemv(const uint16_t* X, int64_t M, int64_t ldx, const uint16_t* W, int64_t ldw,
+                     int64_t N, int64_t K, uint16_t* Y, int64_t ldy, void* stream) {
+  int st = check_dense(X, M, ldx, W, ldw, N, K, Y, ldy);
+  if (st != W4A16_OK) return st;
+  if (M > W4A16_DENSE_GEMV_MAX_M) return W4A16_ERR_INVALID_ARG;
+  return w4a16::launch_dense_gemv(X, M, ldx, W, ldw, N, K, Y, ldy, (hipStream_t)stream);
+}
+
+int w4a16_dense_gemm(const uint16_t* X, int64_t M, int64_t ldx, const uint16_t* W, int64_t ldw,
+                     int64_t N, int64_t K, uint16_t* Y, int64_t ldy, void* stream) {
+  int st = check_dense(X, M, ldx, W, ldw, N, K, Y, ldy);
+  if (st != W4A16_OK) return st;
+  return w4a16::launch_dense_gemm(X, M, ldx, W, ldw, N, K, Y, ldy, (hipStream_t)stream);
 }
 
 }  // extern "C"

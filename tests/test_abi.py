@@ -26,7 +26,8 @@ def header_functions():
 def test_header_declares_expected_entry_points():
     assert header_functions() == sorted([
         "w4a16_abi_version", "w4a16_strerror", "w4a16_pack", "w4a16_gemv", "w4a16_gemm",
-        "w4a16_awq_importance", "w4a16_awq_scale", "w4a16_awq_fold", "w4a16_scale_channels"])
+        "w4a16_awq_importance", "w4a16_awq_scale", "w4a16_awq_fold", "w4a16_scale_channels",
+        "w4a16_dequantize_bf16", "w4a16_dense_gemv", "w4a16_dense_gemm"])
 
 
 def test_every_declared_symbol_is_exported():
@@ -40,7 +41,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strerror():
-    assert lib.w4a16_abi_version() == 1
+    assert lib.w4a16_abi_version() == 2
     for st in range(5):
         assert lib.w4a16_strerror(st)
     assert b"unknown" in lib.w4a16_strerror(99)
@@ -128,3 +129,48 @@ def test_binding_rejects_cpu_tensors():
         w4.w4a16_pack(W)
     with pytest.raises(TypeError):
         w4.w4a16_pack(W.float())
+
+
+def dense(fn, X=FAKE, M=1, ldx=4096, W=FAKE, ldw=4096, N=4096, K=4096, Y=FAKE, ldy=4096):
+    return fn(p(X), M, ldx, p(W), ldw, N, K, p(Y), ldy, p(0))
+
+
+@pytest.mark.parametrize("fn", ["w4a16_dense_gemv", "w4a16_dense_gemm"])
+def test_dense_validation(fn):
+    f = getattr(lib, fn)
+    assert dense(f, X=0) == INVALID
+    assert dense(f, W=0) == INVALID
+    assert dense(f, Y=0) == INVALID
+    assert dense(f, M=0) == INVALID
+    assert dense(f, N=0) == INVALID
+    assert dense(f, K=4000, ldx=4000, ldw=4000) == INVALID   # K % 128
+    assert dense(f, ldw=4000) == INVALID                     # ldw < K
+    assert dense(f, ldx=4095) == INVALID
+    assert dense(f, ldy=100) == INVALID
+    assert dense(f, X=FAKE + 2) == MISALIGNED
+    assert dense(f, W=FAKE + 8) == MISALIGNED
+    assert dense(f, ldw=4100) == MISALIGNED
+    assert dense(f, Y=FAKE + 1) == MISALIGNED
+    assert dense(f, N=1 << 30, ldy=1 << 30) == UNSUPPORTED
+
+
+def test_dense_gemv_m_limit():
+    assert dense(lib.w4a16_dense_gemv, M=9) == INVALID
+
+
+def test_dequantize_validation():
+    f = lib.w4a16_dequantize_bf16
+
+    def call(codes=FAKE, scales=FAKE, zeros=FAKE, N=16, K=256, W=FAKE, ldw=256):
+        return f(p(codes), p(scales), p(zeros), N, K, p(W), ldw, p(0))
+    assert call(codes=0) == INVALID
+    assert call(W=0) == INVALID
+    assert call(N=0) == INVALID
+    assert call(K=200, ldw=200) == INVALID
+    assert call(ldw=128) == INVALID
+    assert call(codes=FAKE + 4) == MISALIGNED
+    assert call(scales=FAKE + 1) == MISALIGNED
+    assert call(zeros=FAKE + 2) == MISALIGNED
+    assert call(W=FAKE + 2) == MISALIGNED
+    assert call(ldw=260) == MISALIGNED
+    assert call(N=1 << 30) == UNSUPPORTED
