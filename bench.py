@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--no-stack", action="store_true",
                     help="skip the 40-layer decoder-stack stream (about 10.7 GB of packed weights)")
     ap.add_argument("--stack-tokens", type=int, default=30)
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip the dense BF16 and naive-pipeline comparisons")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the decode sweep over the other M values and the 70B-shaped set")
     return ap.parse_args()
@@ -275,6 +277,13 @@ def main():
     if not args.no_stack:
         stack = stack_decode(args.stack_tokens, dev, stream)
 
+    # ---- the alternatives the fused path is chosen over (dense BF16 layers,
+    # the naive expand-then-multiply pipeline)
+    compare = None
+    if not args.no_compare and args.workload == "llama8b_decode" and M == 1:
+        compare = comparisons(args.workload, ms_per_step, prefill, dev, stream,
+                              prefill_m=args.prefill_m)
+
     # ---- CPU oracle on a bounded sample of the same step
     cpu = None
     if not args.no_cpu_baseline:
@@ -304,6 +313,7 @@ def main():
         "prefill": prefill,
         "decode_sweep": sweep,
         "stack": stack,
+        "comparisons": compare,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -388,6 +398,136 @@ def decode_sweep(workload, Ms, dev, stream, steps=40):
     torch.cuda.synchronize()
     return {"workload": workload, "step_bytes_M1": sum(decode_bytes(L, 1) for L in layers),
             "rotating_copies": ncopy, "steps_per_graph": steps, "results": rows}
+
+
+def _graph_us(stream, body, reps):
+    """Average microseconds of `body` over `reps` replays captured in one
+    graph (after one untimed replay), timed with HIP events on `stream`."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        body(0)
+        stream.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for r in range(reps):
+                body(r)
+        g.replay()
+        stream.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        e1.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def comparisons(workload, fused_ms_per_step, fused_prefill, dev, stream, steps=40, prefill_m=4096):
+    """The alternatives the fused path is chosen over, on the same layer set
+    and step protocol (weights past the last-level cache, graphs of whole
+    steps):
+      dense BF16 decode (M=1): the dense layer the INT4 weights replace, and
+        the decode cost of an offline BF16 expansion of them;
+      naive three-kernel decode: expand each layer's packed weights to a BF16
+        buffer, then the dense product (an HBM round trip per layer);
+      dense BF16 prefill (M=prefill_m) on this library's matrix-core kernel,
+        and torch's BF16 linear (hipBLASLt) for context."""
+    import torch
+    import int4_weight_only_gemv_amd as w4
+    from synth import gen
+    spec = gen.WORKLOADS[workload]
+    layers = spec["layers"]
+    out = {}
+    # dense BF16 weights: the generator's weights, the model before quantising
+    dense = [gen.weights(L.N, L.K, workload, L.name, shift=spec["shift"], device=dev) for L in layers]
+    dense_bytes = sum(w.numel() * 2 for w in dense)
+    ncopy = max(2, math.ceil(ROTATE_BYTES / dense_bytes))
+    dcopies = [dense] + [[w.clone() for w in dense] for _ in range(ncopy - 1)]
+    xs = [gen.activations(1, L.K, workload, L.name, device=dev) for L in layers]
+    ys = [torch.empty(1, L.N, dtype=torch.bfloat16, device=dev) for L in layers]
+
+    def dense_step(s):
+        for w, x, y in zip(dcopies[s % ncopy], xs, ys):
+            w4.w4a16_dense_gemv(x, w, y)
+    us_dense = _graph_us(stream, dense_step, steps)
+    step_dense_bytes = dense_bytes + sum(2 * (L.K + L.N) for L in layers)
+    del dcopies
+    torch.cuda.synchronize()
+
+    packed = [w4.w4a16_pack(w) for w in dense]
+    pset = sum(p.nbytes() for p in packed)
+    pcopy = max(2, math.ceil(ROTATE_BYTES / pset))
+    pcopies = [packed] + [[w4.PackedLinear(p.codes.clone(), p.scales.clone(), p.zeros.clone())
+                           for p in packed] for _ in range(pcopy - 1)]
+    scratch = [torch.empty(L.N, L.K, dtype=torch.bfloat16, device=dev) for L in layers]
+
+    def naive_step(s):
+        for p, buf, x, y in zip(pcopies[s % pcopy], scratch, xs, ys):
+            w4.w4a16_dequantize_bf16(p, out=buf)
+            w4.w4a16_dense_gemv(x, buf, y)
+    us_naive = _graph_us(stream, naive_step, steps)
+
+    def expand_only(s):
+        for p, buf in zip(pcopies[s % pcopy], scratch):
+            w4.w4a16_dequantize_bf16(p, out=buf)
+    us_expand = _graph_us(stream, expand_only, steps)
+    fused_us = fused_ms_per_step * 1e3
+    out["decode_M1"] = {
+        "fused_w4a16_us_per_step": round(fused_us, 3),
+        "dense_bf16_us_per_step": round(us_dense, 3),
+        "dense_bf16_GBps": round(step_dense_bytes / (us_dense * 1e-6) / 1e9, 1),
+        "speedup_fused_vs_dense": round(us_dense / fused_us, 3),
+        "offline_expansion_decode_us_per_step": round(us_dense, 3),
+        "naive_three_kernel_us_per_step": round(us_naive, 3),
+        "naive_expand_kernels_us_per_step": round(us_expand, 3),
+        "speedup_fused_vs_naive": round(us_naive / fused_us, 3),
+        "dense_rotating_copies": ncopy,
+    }
+    log(f"[bench] compare decode M=1: fused {fused_us:.1f} us, dense bf16 {us_dense:.1f} us "
+        f"({us_dense / fused_us:.2f}x), naive 3-kernel {us_naive:.1f} us ({us_naive / fused_us:.2f}x)")
+    del pcopies, scratch, xs, ys
+    torch.cuda.synchronize()
+
+    # prefill: dense BF16 on this library's matrix-core kernel and torch's
+    if fused_prefill is not None:
+        Mp = prefill_m
+        pxs = [gen.activations(Mp, L.K, "llama8b_prefill", L.name, device=dev) for L in layers]
+        pys = [torch.empty(Mp, L.N, dtype=torch.bfloat16, device=dev) for L in layers]
+        t_dense, t_torch = [], []
+        for w, x, y in zip(dense, pxs, pys):
+            t_dense.append(_graph_us(stream, lambda r, w=w, x=x, y=y: w4.w4a16_dense_gemm(x, w, y), 5))
+            # torch's BF16 product, eager, on a contiguous K x N copy (no
+            # transposed operand views, no graph capture of library calls)
+            wt = w.t().contiguous()
+            with torch.cuda.stream(stream):
+                torch.mm(x, wt, out=y)
+                stream.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(5):
+                    torch.mm(x, wt, out=y)
+                e1.record(stream)
+                e1.synchronize()
+            t_torch.append(e0.elapsed_time(e1) * 1e3 / 5)
+            del wt
+        flops = sum(2.0 * Mp * L.N * L.K for L in layers)
+        tf_dense = flops / (sum(t_dense) * 1e-6) / 1e12
+        tf_torch = flops / (sum(t_torch) * 1e-6) / 1e12
+        out[f"prefill_M{Mp}"] = {
+            "fused_w4a16_TFLOPs": fused_prefill["value"],
+            "dense_bf16_TFLOPs": round(tf_dense, 1),
+            "ratio_fused_vs_dense": round(fused_prefill["value"] / tf_dense, 3),
+            "torch_bf16_linear_TFLOPs": round(tf_torch, 1),
+            "layers": [{"layer": L.name, "dense_ms": round(a * 1e-3, 4), "torch_ms": round(b * 1e-3, 4)}
+                       for L, a, b in zip(layers, t_dense, t_torch)],
+        }
+        log(f"[bench] compare prefill M={Mp}: fused {fused_prefill['value']:.1f}, dense bf16 "
+            f"{tf_dense:.1f}, torch bf16 {tf_torch:.1f} TFLOP/s")
+        del pxs, pys
+    del dense, packed
+    torch.cuda.synchronize()
+    return out
 
 
 def stack_decode(tokens, dev, stream, Ms=(1, 8)):
