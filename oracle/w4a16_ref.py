@@ -154,6 +154,64 @@ def quantize(W_bits: np.ndarray, awq_s: np.ndarray | None = None):
 
 
 # ---------------------------------------------------------------------------
+# Symmetric variant: zero point fixed at the middle of the code range
+# ---------------------------------------------------------------------------
+
+SYM_ZERO = 8         # signed codes -7..7 stored as 1..15
+
+
+def group_scale_symmetric(w_groups: np.ndarray):
+    """Scale of each group for symmetric INT4.
+
+    The pages name symmetric uniform quantisation and argue that it wastes
+    range ("Quantization I: int8, int4, the basics", "Concept"; Axe Corsa
+    model card, "The Two-Stage Pipeline"), but their formula is stripped.
+    Reading: the grid is centred on zero and reaches the largest magnitude,
+      A = max |w|; t = fl32(A / 7); s = bf16 of t rounded toward zero,
+    with the asymmetric rule's fallback for a zero or subnormal s (s =
+    bf16_rtz(A), then 1.0).  Codes are round_half_away(w / s) in -7..7,
+    stored with zero point 8, so the dequantisation (q - z) s and every
+    kernel are those of the asymmetric format.
+    Returns (s_bits uint16 [...], s float32 [...])."""
+    w = np.asarray(w_groups, dtype=np.float32)
+    a = np.abs(w).max(axis=-1).astype(np.float32)
+    t = (a / np.float32(7)).astype(np.float32)
+    s_bits = f32_to_bf16_rtz(t)
+    s = bf16_to_f32(s_bits)
+    degenerate = s < FLT_MIN
+    if np.any(degenerate):
+        alt_bits = f32_to_bf16_rtz(a)
+        alt = bf16_to_f32(alt_bits)
+        alt_bits = np.where(alt < FLT_MIN, np.uint16(0x3F80), alt_bits)  # 1.0
+        s_bits = np.where(degenerate, alt_bits, s_bits).astype(np.uint16)
+        s = bf16_to_f32(s_bits)
+    return s_bits, s
+
+
+def quantize_symmetric(W_bits: np.ndarray, awq_s: np.ndarray | None = None):
+    """Symmetric group-wise INT4 of a BF16 matrix W [N][K]: returns (q uint8
+    [N][K] in 1..15, s_bits uint16 [N][K/128], z int32 [N][K/128] all 8).
+    awq_s as for quantize()."""
+    W_bits = np.asarray(W_bits, dtype=np.uint16)
+    N, K = W_bits.shape
+    if K % GROUP:
+        raise ValueError("K must be a multiple of 128")
+    w = bf16_to_f32(W_bits)
+    if awq_s is not None:
+        w = (w * np.asarray(awq_s, dtype=np.float32)[None, :]).astype(np.float32)
+    wg = w.reshape(N, K // GROUP, GROUP)
+    s_bits, s = group_scale_symmetric(wg)
+    z = np.full(s_bits.shape, SYM_ZERO, dtype=np.int64)
+    q = group_codes(wg, s, z).reshape(N, K)
+    return q, s_bits.astype(np.uint16), z.astype(np.int32)
+
+
+def quantize_pack_symmetric(W_bits: np.ndarray, awq_s: np.ndarray | None = None):
+    q, s_bits, z = quantize_symmetric(W_bits, awq_s)
+    return pack_codes(q), s_bits, z
+
+
+# ---------------------------------------------------------------------------
 # Packing: eight 4-bit codes per 32-bit word along K
 # ---------------------------------------------------------------------------
 
@@ -174,6 +232,22 @@ def pack_codes(q: np.ndarray) -> np.ndarray:
     for j in range(8):
         words |= (q8[:, :, j] & np.uint32(0xF)) << np.uint32(4 * j)
     return words
+
+
+def pack_codes_i64(q: np.ndarray) -> np.ndarray:
+    """q uint8 [N][K] -> int64 [N][K/16], the compressed-tensors container
+    (Axe Corsa model card, "What the Tensor Types Tell You": packed INT4
+    codes held in I64 tensors, two values per byte): nibble j of word i is
+    k = 16i + j, little endian."""
+    q = np.asarray(q, dtype=np.uint64)
+    N, K = q.shape
+    if K % 16:
+        raise ValueError("K must be a multiple of 16")
+    q16 = q.reshape(N, K // 16, 16)
+    words = np.zeros((N, K // 16), dtype=np.uint64)
+    for j in range(16):
+        words |= (q16[:, :, j] & np.uint64(0xF)) << np.uint64(4 * j)
+    return words.view(np.int64)
 
 
 def unpack_codes(words: np.ndarray) -> np.ndarray:

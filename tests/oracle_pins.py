@@ -494,3 +494,85 @@ def check_dense_matches_fused_on_grid(seed=14, M=4, N=6, K=256):
     X_bits = O.f32_to_bf16_rne(rng.normal(0, 1, size=(M, K)).astype(np.float32))
     W_bits = O.dequantize_bf16(codes, scales, zeros)
     assert np.array_equal(O.dense_matmul_ref(X_bits, W_bits), O.matmul_ref(X_bits, codes, scales, zeros))
+
+
+# ---------------------------------------------------------------------------
+# Format variants: symmetric INT4 and the I64 code container
+# ---------------------------------------------------------------------------
+
+def check_symmetric_hand():
+    """Constructed groups.
+    G1: k * 2^-4 for k = -7..7 (and zeros): A = 7 * 2^-4, t = 2^-4 exactly,
+    s = 2^-4 (bits 0x3D80), code = k + 8.
+    G2: the same values times -3: A = 21 * 2^-4, t = 3 * 2^-4 = 0.1875 is a
+    BF16 value (bits 0x3E40), codes = -k + 8.
+    G3: all zero: t = 0 -> fallback bf16_rtz(0) = 0 -> s = 1.0 (0x3F80),
+    every code 8.
+    G4: one value 2^-126 (the smallest normal), the rest 0: t = 2^-126/7 is
+    subnormal -> fallback s = 2^-126 (0x0080); the value becomes code 9
+    (ratio 1), the zeros code 8."""
+    k = np.concatenate([np.arange(-7, 8), np.zeros(113)]).astype(np.float64)
+    groups = np.stack([k * 2.0 ** -4, -3 * k * 2.0 ** -4, np.zeros(128),
+                       np.where(np.arange(128) == 5, 2.0 ** -126, 0.0)])
+    W_bits = _bf16_bits_of(groups.reshape(1, 4 * 128))
+    q, s_bits, z = O.quantize_symmetric(W_bits)
+    assert list(s_bits[0]) == [0x3D80, 0x3E40, 0x3F80, 0x0080], [hex(v) for v in s_bits[0]]
+    assert np.all(z == 8)
+    q = q.reshape(4, 128).astype(np.int64)
+    assert np.array_equal(q[0], (k + 8).astype(np.int64))
+    assert np.array_equal(q[1], (-k + 8).astype(np.int64))
+    assert np.all(q[2] == 8)
+    assert q[3, 5] == 9 and np.all(np.delete(q[3], 5) == 8)
+
+
+def check_symmetric_invariants(seed=15, N=48, K=1024):
+    """Generated groups (with per-group shifts, so many groups are skewed):
+    zero point 8; codes 1..15 (the code -8 is never needed); the largest
+    magnitude maps to code 1 or 15; every weight is within half a scale step
+    of its dequantised value (no clipping: |w|/s < 7.5)."""
+    rng = np.random.default_rng(seed)
+    w = (rng.normal(0, 0.02, size=(N, K)) + np.repeat(rng.uniform(-0.03, 0.03, size=(N, K // 128)), 128, 1))
+    W_bits = O.f32_to_bf16_rne(w.astype(np.float32))
+    q, s_bits, z = O.quantize_symmetric(W_bits)
+    assert np.all(z == 8)
+    assert q.min() >= 1 and q.max() <= 15
+    wf = O.bf16_to_f32(W_bits).astype(np.float64).reshape(N, K // 128, 128)
+    s = O.bf16_to_f32(s_bits).astype(np.float64)
+    qg = q.reshape(N, K // 128, 128).astype(np.float64)
+    err = np.abs(wf - (qg - 8) * s[..., None])
+    assert np.all(err <= s[..., None] * (0.5 + 2.0 ** -20)), err.max()
+    top = np.abs(wf).argmax(axis=-1)
+    qtop = np.take_along_axis(qg, top[..., None], -1)[..., 0]
+    assert np.all((qtop == 1) | (qtop == 15))
+    # the scale reaches the largest magnitude: A/7 * (1 - 2^-7) < s <= A/7
+    A = np.abs(wf).max(axis=-1)
+    assert np.all(s <= A / 7) and np.all(s > A / 7 * (1 - 2.0 ** -7))
+
+
+def check_symmetric_brute_force(seed=16, N=3, K=128):
+    """Each code is the nearest of the 16 grid points (c - 8) s to w, ties
+    away from zero, with exact rational arithmetic."""
+    rng = np.random.default_rng(seed)
+    W_bits = O.f32_to_bf16_rne(rng.normal(0, 0.05, size=(N, K)).astype(np.float32))
+    q, s_bits, z = O.quantize_symmetric(W_bits)
+    wf = O.bf16_to_f32(W_bits)
+    for n in range(N):
+        sc = _frac_of_f32(O.bf16_to_f32(s_bits[n, 0]))
+        for k in range(K):
+            wk = _frac_of_f32(wf[n, k])
+            best = min(range(16), key=lambda c: (abs(wk - (c - 8) * sc), -abs(c - 8)))
+            assert best == q[n, k], (n, k, best, q[n, k])
+
+
+def check_i64_container(seed=17):
+    """The I64 container holds sixteen codes per word, two per byte, low
+    nibble first, consecutive along K: its byte stream is that of the
+    two-codes-per-byte description, and so equals the 32-bit packing's."""
+    rng = np.random.default_rng(seed)
+    q = rng.integers(0, 16, size=(4, 256), dtype=np.uint8)
+    w64 = O.pack_codes_i64(q)
+    assert w64.dtype == np.int64 and w64.shape == (4, 16)
+    byts = w64.astype("<i8").view(np.uint8).reshape(4, 128)
+    expect = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+    assert np.array_equal(byts, expect)
+    assert np.array_equal(w64.astype("<i8").view("<u4").reshape(4, 32), O.pack_codes(q).astype("<u4"))

@@ -16,6 +16,8 @@ ALL_PINS = [
     P.check_storage_cost,
     P.check_dequant_bf16_hand, P.check_dequant_bf16_vs_torch,
     P.check_dense_brute_force, P.check_dense_matches_fused_on_grid,
+    P.check_symmetric_hand, P.check_symmetric_invariants, P.check_symmetric_brute_force,
+    P.check_i64_container,
 ]
 
 
@@ -155,6 +157,32 @@ def _dense_drops_last_k(X_bits, W_bits, rows=None):
     return x @ w.T
 
 
+def _sym_scale_div8(wg):
+    w = np.asarray(wg, dtype=np.float32)
+    a = np.abs(w).max(axis=-1).astype(np.float32)
+    s_bits = R.f32_to_bf16_rtz((a / np.float32(8)).astype(np.float32))
+    s_bits = np.where(R.bf16_to_f32(s_bits) < R.FLT_MIN, np.uint16(0x3F80), s_bits).astype(np.uint16)
+    return s_bits, R.bf16_to_f32(s_bits)
+
+
+def _sym_scale_max_only(wg):
+    w = np.asarray(wg, dtype=np.float32)
+    a = w.max(axis=-1).astype(np.float32)
+    s_bits = R.f32_to_bf16_rtz((a / np.float32(7)).astype(np.float32))
+    s_bits = np.where(R.bf16_to_f32(s_bits) < R.FLT_MIN, np.uint16(0x3F80), s_bits).astype(np.uint16)
+    return s_bits, R.bf16_to_f32(s_bits)
+
+
+def _i64_high_nibble_first(q):
+    q = np.asarray(q, dtype=np.uint64)
+    N, K = q.shape
+    q16 = q.reshape(N, K // 16, 16)
+    words = np.zeros((N, K // 16), dtype=np.uint64)
+    for j in range(16):
+        words |= (q16[:, :, j ^ 1] & np.uint64(0xF)) << np.uint64(4 * j)
+    return words.view(np.int64)
+
+
 ORIG = {n: getattr(R, n) for n in ["group_scale_zero", "quantize"]}
 
 MUTATIONS = {
@@ -174,6 +202,9 @@ MUTATIONS = {
     "dequant_bf16_truncated": ("dequantize_bf16", _dequant_bf16_truncated),
     "dequant_bf16_zero_added": ("dequantize_bf16", _dequant_bf16_zero_added),
     "dense_drops_last_k": ("dense_matmul_ref", _dense_drops_last_k),
+    "symmetric_divide_by_8": ("group_scale_symmetric", _sym_scale_div8),
+    "symmetric_scale_from_max_not_magnitude": ("group_scale_symmetric", _sym_scale_max_only),
+    "i64_high_nibble_first": ("pack_codes_i64", _i64_high_nibble_first),
 }
 
 

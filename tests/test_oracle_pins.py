@@ -117,3 +117,19 @@ def test_dense_brute_force():
 
 def test_dense_matches_fused_on_grid():
     P.check_dense_matches_fused_on_grid()
+
+
+def test_symmetric_hand():
+    P.check_symmetric_hand()
+
+
+def test_symmetric_invariants():
+    P.check_symmetric_invariants()
+
+
+def test_symmetric_brute_force():
+    P.check_symmetric_brute_force()
+
+
+def test_i64_container():
+    P.check_i64_container()
