@@ -37,7 +37,10 @@
  *                             each byte holds two consecutive codes, low
  *                             nibble first -- the two-codes-per-byte stream of
  *                             the compressed-tensors format ("What the Tensor
- *                             Types Tell You").  16-byte aligned.
+ *                             Types Tell You").  16-byte aligned.  The
+ *                             same bytes viewed as int64 [N][K/16] are that
+ *                             format's I64 container, so such a container
+ *                             is consumed in place (no copy, no repacking).
  *   scales uint16_t [N][K/128] BF16 scale bits.
  *   zeros  int32_t  [N][K/128] zero points, not clamped to 0..15.
  * That is 4 + 16/128 + 32/128 = 4.375 bits per weight (Axe Corsa model card,
@@ -53,7 +56,7 @@ extern "C" {
 #endif
 
 #define W4A16_GROUP 128
-#define W4A16_ABI_VERSION 2
+#define W4A16_ABI_VERSION 3
 #define W4A16_GEMV_MAX_M 32
 #define W4A16_DENSE_GEMV_MAX_M 8
 
@@ -99,6 +102,23 @@ const char* w4a16_strerror(int status);
 int w4a16_pack(const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
                const float* awq_s, uint32_t* codes, uint16_t* scales,
                int32_t* zeros, void* stream);
+
+/*
+ * w4a16_pack_symmetric -- the symmetric INT4 variant ("Quantization I",
+ * "Concept", and the Axe Corsa model card, "The Two-Stage Pipeline", name it
+ * and argue it wastes range; the formula on the pages is lost, this is the
+ * reading used).  Same arguments, rules and output layout as w4a16_pack;
+ * per group of 128 values w (float32, as above):
+ *   A = max |w|;  s = BF16 of A / 7 rounded toward zero;
+ *   if s is zero or subnormal: s = BF16 toward zero of A, and 1.0 if that
+ *       is still zero or subnormal;
+ *   z = 8;  q = clamp(round_half_away_from_zero(w / s) + 8, 0, 15).
+ * Codes are 1..15 (signed -7..7 around the zero point 8), so every matmul
+ * entry point consumes the result unchanged.  Bit-exact.
+ */
+int w4a16_pack_symmetric(const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
+                         const float* awq_s, uint32_t* codes, uint16_t* scales,
+                         int32_t* zeros, void* stream);
 
 /*
  * w4a16_gemv -- decode-shaped fused dequantise-multiply, 1 <= M <= 32.

@@ -42,6 +42,7 @@ _SIGS = {
     "w4a16_awq_scale": ([_p, _i64, ctypes.c_float, _p, _p], ctypes.c_int),
     "w4a16_awq_fold": ([_p, _i64, _p, _p, _p], ctypes.c_int),
     "w4a16_scale_channels": ([_p, _i64, _i64, _i64, _p, _p, _i64, _p], ctypes.c_int),
+    "w4a16_pack_symmetric": ([_p, _i64, _i64, _i64, _p, _p, _p, _p, _p], ctypes.c_int),
     "w4a16_dequantize_bf16": ([_p, _p, _p, _i64, _i64, _p, _i64, _p], ctypes.c_int),
     "w4a16_dense_gemv": ([_p, _i64, _i64, _p, _i64, _i64, _i64, _p, _i64, _p], ctypes.c_int),
     "w4a16_dense_gemm": ([_p, _i64, _i64, _p, _i64, _i64, _i64, _p, _i64, _p], ctypes.c_int),
@@ -112,9 +113,7 @@ def empty_packed(N: int, K: int, device) -> PackedLinear:
     return PackedLinear(codes, scales, zeros)
 
 
-def w4a16_pack(W: torch.Tensor, awq_s: torch.Tensor | None = None,
-               out: PackedLinear | None = None) -> PackedLinear:
-    """Quantise + pack a BF16 weight [N][K] (see w4a16_pack in w4a16.h)."""
+def _pack(fn, name, W, awq_s, out):
     _need(W, torch.bfloat16, "W", 2)
     N, K = W.shape
     if awq_s is not None:
@@ -122,9 +121,36 @@ def w4a16_pack(W: torch.Tensor, awq_s: torch.Tensor | None = None,
         if awq_s.shape[0] != K or not awq_s.is_contiguous():
             raise ValueError("awq_s must be a contiguous float32 [K]")
     p = out if out is not None else empty_packed(N, K, W.device)
-    _check("w4a16_pack", lib.w4a16_pack(_ptr(W), N, K, W.stride(0), _ptr(awq_s), _ptr(p.codes),
-                                        _ptr(p.scales), _ptr(p.zeros), _stream(W)))
+    _check(name, fn(_ptr(W), N, K, W.stride(0), _ptr(awq_s), _ptr(p.codes), _ptr(p.scales),
+                    _ptr(p.zeros), _stream(W)))
     return p
+
+
+def w4a16_pack(W: torch.Tensor, awq_s: torch.Tensor | None = None,
+               out: PackedLinear | None = None) -> PackedLinear:
+    """Quantise + pack a BF16 weight [N][K] (see w4a16_pack in w4a16.h)."""
+    return _pack(lib.w4a16_pack, "w4a16_pack", W, awq_s, out)
+
+
+def w4a16_pack_symmetric(W: torch.Tensor, awq_s: torch.Tensor | None = None,
+                         out: PackedLinear | None = None) -> PackedLinear:
+    """Symmetric INT4 variant (zero point 8; see w4a16_pack_symmetric)."""
+    return _pack(lib.w4a16_pack_symmetric, "w4a16_pack_symmetric", W, awq_s, out)
+
+
+def packed_from_i64(codes_i64: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor) -> PackedLinear:
+    """A packed matrix whose codes sit in an I64 container [N][K/16] (sixteen
+    codes per word, two per byte, low nibble first): the same bytes as the
+    32-bit layout, taken as a view (no copy)."""
+    _need(codes_i64, torch.int64, "codes_i64", 2)
+    if not codes_i64.is_contiguous():
+        raise ValueError("codes_i64 must be contiguous")
+    return PackedLinear(codes_i64.view(torch.int32), scales, zeros)
+
+
+def codes_as_i64(p: PackedLinear) -> torch.Tensor:
+    """The codes of `p` viewed as the I64 container [N][K/16] (no copy)."""
+    return p.codes.view(torch.int64)
 
 
 def _matmul(fn, name, X: torch.Tensor, p: PackedLinear, out: torch.Tensor | None):

@@ -8,7 +8,7 @@
 
 namespace w4a16 {
 int launch_pack(const uint16_t*, int64_t, int64_t, int64_t, const float*, uint32_t*, uint16_t*,
-                int32_t*, hipStream_t);
+                int32_t*, bool, hipStream_t);
 int launch_gemv(const uint16_t*, int64_t, int64_t, const uint32_t*, const uint16_t*,
                 const int32_t*, int64_t, int64_t, uint16_t*, int64_t, hipStream_t);
 int launch_gemm(const uint16_t*, int64_t, int64_t, const uint32_t*, const uint16_t*,
@@ -75,15 +75,28 @@ const char* w4a16_strerror(int status) {
   }
 }
 
-int w4a16_pack(const uint16_t* W, int64_t N, int64_t K, int64_t ldw, const float* awq_s,
-               uint32_t* codes, uint16_t* scales, int32_t* zeros, void* stream) {
+namespace {
+int pack_checked(const uint16_t* W, int64_t N, int64_t K, int64_t ldw, const float* awq_s,
+                 uint32_t* codes, uint16_t* scales, int32_t* zeros, bool symmetric, void* stream) {
   if (!W || !codes || !scales || !zeros) return W4A16_ERR_INVALID_ARG;
   if (N < 1 || K < W4A16_GROUP || K % W4A16_GROUP || ldw < K) return W4A16_ERR_INVALID_ARG;
   if (N >= kMaxDim || K >= kMaxDim || N * (K / 8) >= ((int64_t)1 << 38)) return W4A16_ERR_UNSUPPORTED;
   if (!aligned(W, 2) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(zeros, 4) ||
       (awq_s && !aligned(awq_s, 4)))
     return W4A16_ERR_MISALIGNED;
-  return w4a16::launch_pack(W, N, K, ldw, awq_s, codes, scales, zeros, (hipStream_t)stream);
+  return w4a16::launch_pack(W, N, K, ldw, awq_s, codes, scales, zeros, symmetric,
+                            (hipStream_t)stream);
+}
+}  // namespace
+
+int w4a16_pack(const uint16_t* W, int64_t N, int64_t K, int64_t ldw, const float* awq_s,
+               uint32_t* codes, uint16_t* scales, int32_t* zeros, void* stream) {
+  return pack_checked(W, N, K, ldw, awq_s, codes, scales, zeros, false, stream);
+}
+
+int w4a16_pack_symmetric(const uint16_t* W, int64_t N, int64_t K, int64_t ldw, const float* awq_s,
+                         uint32_t* codes, uint16_t* scales, int32_t* zeros, void* stream) {
+  return pack_checked(W, N, K, ldw, awq_s, codes, scales, zeros, true, stream);
 }
 
 int w4a16_gemv(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,

@@ -1,4 +1,5 @@
-// Group-wise asymmetric INT4 quantise + pack (offline step of the W4A16 path).
+// Group-wise asymmetric (and, as a variant, symmetric) INT4 quantise + pack
+// (offline step of the W4A16 path).
 //
 // Scheme: Axe Corsa model card, "The Two-Stage Pipeline" (asymmetric, one
 // BF16 scale and one INT32 zero point per group of 128 consecutive weights)
@@ -34,7 +35,7 @@ __device__ __forceinline__ float bf16_rtz(float f) {
   return __uint_as_float(__float_as_uint(f) & 0xFFFF0000u);
 }
 
-template <bool kVecLoad, bool kAwq>
+template <bool kVecLoad, bool kAwq, bool kSym>
 __global__ __launch_bounds__(256) void pack_kernel(
     const uint16_t* __restrict__ W, int64_t ldw, const float* __restrict__ awq_s,
     int64_t words_per_row, int64_t total_words, uint32_t* __restrict__ codes,
@@ -74,13 +75,27 @@ __global__ __launch_bounds__(256) void pack_kernel(
   mn = seg16_min(mn);
   mx = seg16_max(mx);
 
-  const float d = __fsub_rn(mx, mn);
-  float s = bf16_rtz(__fdiv_rn(d, 15.0f));
-  if (!(s >= kFltMin)) {  // degenerate group: zero or subnormal step
-    s = bf16_rtz(fmaxf(fabsf(mn), fabsf(mx)));
-    if (!(s >= kFltMin)) s = 1.0f;
+  float s;
+  int z;
+  if (kSym) {
+    // symmetric: the grid centred on zero reaches the largest magnitude,
+    // codes -7..7 stored with zero point 8
+    const float a = fmaxf(fabsf(mn), fabsf(mx));
+    s = bf16_rtz(__fdiv_rn(a, 7.0f));
+    if (!(s >= kFltMin)) {
+      s = bf16_rtz(a);
+      if (!(s >= kFltMin)) s = 1.0f;
+    }
+    z = 8;
+  } else {
+    const float d = __fsub_rn(mx, mn);
+    s = bf16_rtz(__fdiv_rn(d, 15.0f));
+    if (!(s >= kFltMin)) {  // degenerate group: zero or subnormal step
+      s = bf16_rtz(fmaxf(fabsf(mn), fabsf(mx)));
+      if (!(s >= kFltMin)) s = 1.0f;
+    }
+    z = (int)roundf(__fdiv_rn(-mn, s));
   }
-  const int z = (int)roundf(__fdiv_rn(-mn, s));
 
   uint32_t word = 0;
 #pragma unroll
@@ -101,28 +116,41 @@ __global__ __launch_bounds__(256) void pack_kernel(
 
 }  // namespace
 
-int launch_pack(const uint16_t* W, int64_t N, int64_t K, int64_t ldw, const float* awq_s,
-                uint32_t* codes, uint16_t* scales, int32_t* zeros, hipStream_t stream) {
-  const int64_t words_per_row = K / 8;
-  const int64_t total = N * words_per_row;
+namespace {
+template <bool kSym>
+void launch_pack_t(const uint16_t* W, int64_t ldw, const float* awq_s, int64_t words_per_row,
+                   int64_t total, uint32_t* codes, uint16_t* scales, int32_t* zeros, bool vec,
+                   hipStream_t stream) {
   const int threads = 256;
-  const int64_t blocks = (total + threads - 1) / threads;
-  const bool vec = ((reinterpret_cast<uintptr_t>(W) & 15u) == 0) && (ldw % 8 == 0);
+  const dim3 grid((unsigned)((total + threads - 1) / threads));
   if (vec) {
     if (awq_s)
-      hipLaunchKernelGGL((pack_kernel<true, true>), dim3((unsigned)blocks), dim3(threads), 0, stream,
-                         W, ldw, awq_s, words_per_row, total, codes, scales, zeros);
+      hipLaunchKernelGGL((pack_kernel<true, true, kSym>), grid, dim3(threads), 0, stream, W, ldw,
+                         awq_s, words_per_row, total, codes, scales, zeros);
     else
-      hipLaunchKernelGGL((pack_kernel<true, false>), dim3((unsigned)blocks), dim3(threads), 0, stream,
-                         W, ldw, awq_s, words_per_row, total, codes, scales, zeros);
+      hipLaunchKernelGGL((pack_kernel<true, false, kSym>), grid, dim3(threads), 0, stream, W, ldw,
+                         awq_s, words_per_row, total, codes, scales, zeros);
   } else {
     if (awq_s)
-      hipLaunchKernelGGL((pack_kernel<false, true>), dim3((unsigned)blocks), dim3(threads), 0, stream,
-                         W, ldw, awq_s, words_per_row, total, codes, scales, zeros);
+      hipLaunchKernelGGL((pack_kernel<false, true, kSym>), grid, dim3(threads), 0, stream, W, ldw,
+                         awq_s, words_per_row, total, codes, scales, zeros);
     else
-      hipLaunchKernelGGL((pack_kernel<false, false>), dim3((unsigned)blocks), dim3(threads), 0, stream,
-                         W, ldw, awq_s, words_per_row, total, codes, scales, zeros);
+      hipLaunchKernelGGL((pack_kernel<false, false, kSym>), grid, dim3(threads), 0, stream, W, ldw,
+                         awq_s, words_per_row, total, codes, scales, zeros);
   }
+}
+}  // namespace
+
+int launch_pack(const uint16_t* W, int64_t N, int64_t K, int64_t ldw, const float* awq_s,
+                uint32_t* codes, uint16_t* scales, int32_t* zeros, bool symmetric,
+                hipStream_t stream) {
+  const int64_t words_per_row = K / 8;
+  const int64_t total = N * words_per_row;
+  const bool vec = ((reinterpret_cast<uintptr_t>(W) & 15u) == 0) && (ldw % 8 == 0);
+  if (symmetric)
+    launch_pack_t<true>(W, ldw, awq_s, words_per_row, total, codes, scales, zeros, vec, stream);
+  else
+    launch_pack_t<false>(W, ldw, awq_s, words_per_row, total, codes, scales, zeros, vec, stream);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 

@@ -27,7 +27,7 @@ def test_header_declares_expected_entry_points():
     assert header_functions() == sorted([
         "w4a16_abi_version", "w4a16_strerror", "w4a16_pack", "w4a16_gemv", "w4a16_gemm",
         "w4a16_awq_importance", "w4a16_awq_scale", "w4a16_awq_fold", "w4a16_scale_channels",
-        "w4a16_dequantize_bf16", "w4a16_dense_gemv", "w4a16_dense_gemm"])
+        "w4a16_dequantize_bf16", "w4a16_dense_gemv", "w4a16_dense_gemm", "w4a16_pack_symmetric"])
 
 
 def test_every_declared_symbol_is_exported():
@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strerror():
-    assert lib.w4a16_abi_version() == 2
+    assert lib.w4a16_abi_version() == 3
     for st in range(5):
         assert lib.w4a16_strerror(st)
     assert b"unknown" in lib.w4a16_strerror(99)
@@ -86,8 +86,9 @@ def test_gemv_rejects_large_m():
     assert gemv(M=1 << 20) == INVALID
 
 
-def test_pack_validation():
-    f = lib.w4a16_pack
+@pytest.mark.parametrize("fn", ["w4a16_pack", "w4a16_pack_symmetric"])
+def test_pack_validation(fn):
+    f = getattr(lib, fn)
 
     def call(W=FAKE, N=16, K=256, ldw=256, s=0, c=FAKE, sc=FAKE, z=FAKE):
         return f(p(W), N, K, ldw, p(s), p(c), p(sc), p(z), p(0))
