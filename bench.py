@@ -525,6 +525,26 @@ def comparisons(workload, fused_ms_per_step, fused_prefill, dev, stream, steps=4
         log(f"[bench] compare prefill M={Mp}: fused {fused_prefill['value']:.1f}, dense bf16 "
             f"{tf_dense:.1f}, torch bf16 {tf_torch:.1f} TFLOP/s")
         del pxs, pys
+    # output error of the quantised layer against the dense BF16 layer,
+    # asymmetric (the format) and symmetric (the variant the pages argue
+    # wastes range), on plain weights and on weights with per-group offsets
+    errs = []
+    Mq = 64
+    for shift in (False, True):
+        for L in layers:
+            W = gen.weights(L.N, L.K, workload, L.name, shift=shift, device=dev)
+            X = gen.activations(Mq, L.K, workload, L.name, device=dev)
+            yd = w4.w4a16_dense_gemm(X, W).float()
+            row = {"layer": L.name, "group_offsets": shift}
+            for name, pk in (("asymmetric", w4.w4a16_pack), ("symmetric", w4.w4a16_pack_symmetric)):
+                yq = w4.w4a16_gemm(X, pk(W)).float()
+                row[f"{name}_rel_l2"] = round(float((yq - yd).norm() / yd.norm()), 5)
+            errs.append(row)
+            del W, X, yd, yq
+    out["quantisation_error_vs_dense"] = {"M": Mq, "layers": errs}
+    log("[bench] compare error vs dense: " + ", ".join(
+        f"{r['layer']}{'+off' if r['group_offsets'] else ''} asym {r['asymmetric_rel_l2']:.4f} "
+        f"sym {r['symmetric_rel_l2']:.4f}" for r in errs))
     del dense, packed
     torch.cuda.synchronize()
     return out
