@@ -374,6 +374,35 @@ def apply_channel_scale(X_bits: np.ndarray, gamma_bits: np.ndarray) -> np.ndarra
     return f32_to_bf16_rne((x * g[None, :]).astype(np.float32))
 
 
+def awq_search(W_bits: np.ndarray, Xcal_bits: np.ndarray, alphas, X_bits: np.ndarray | None = None):
+    """AWQ's one-dimensional search over the exponent of s = importance^alpha
+    (Axe Corsa model card, "Stage 1: Activation-Aware Weight Scaling";
+    cyankiwi docs, "The Baseline: AWQ": a light grid search rather than
+    training).  For each alpha: s from the calibration batch, the weights
+    quantised as W' = W diag(s), the activations fed through the folded
+    producer weight gamma' = bf16(1 / s) (producer weight 1), and the
+    relative L2 error of the layer output against the dense BF16 product
+    X W^T measured on X (default: the calibration batch).
+    Reading: the pages name neither the grid nor the objective's norm; the
+    objective is the layer-output error the AWQ pages describe, in L2.
+    Returns (errors float64 [len(alphas)], index of the smallest)."""
+    W_bits = np.asarray(W_bits, dtype=np.uint16)
+    X_bits = Xcal_bits if X_bits is None else X_bits
+    K = W_bits.shape[1]
+    imp = awq_importance(Xcal_bits)
+    y_dense = dense_matmul_ref(X_bits, W_bits)
+    ones = np.full(K, 0x3F80, dtype=np.uint16)
+    errs = []
+    for a in alphas:
+        s = awq_scale(imp, a)
+        codes, scales, zeros = quantize_pack(W_bits, s)
+        Xs = apply_channel_scale(X_bits, awq_fold(s, ones))
+        y = matmul_ref(Xs, codes, scales, zeros)
+        errs.append(np.linalg.norm(y - y_dense) / np.linalg.norm(y_dense))
+    errs = np.asarray(errs, dtype=np.float64)
+    return errs, int(np.argmin(errs))
+
+
 # ---------------------------------------------------------------------------
 # Parity gates on the floating-point output
 # ---------------------------------------------------------------------------

@@ -576,3 +576,44 @@ def check_i64_container(seed=17):
     expect = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
     assert np.array_equal(byts, expect)
     assert np.array_equal(w64.astype("<i8").view("<u4").reshape(4, 32), O.pack_codes(q).astype("<u4"))
+
+
+# ---------------------------------------------------------------------------
+# AWQ exponent search
+# ---------------------------------------------------------------------------
+
+def _salient_case(seed, N=64, K=512, T=64, w_salient=1.0):
+    rng = np.random.default_rng(seed)
+    w = rng.normal(0, 0.02, size=(N, K))
+    sal = rng.choice(K, 5, replace=False)
+    w[:, sal] *= w_salient
+    x = rng.normal(0, 1, size=(T, K))
+    x[:, sal] *= 20.0
+    return O.f32_to_bf16_rne(w.astype(np.float32)), O.f32_to_bf16_rne(x.astype(np.float32))
+
+
+def check_awq_search_alpha_zero_is_plain(seed=19):
+    """alpha = 0 gives s = 1 exactly, so its error is that of the plain
+    quantiser with the activations untouched."""
+    Wb, Xb = _salient_case(seed)
+    errs, _ = O.awq_search(Wb, Xb, [0.0, 0.5])
+    codes, scales, zeros = O.quantize_pack(Wb)
+    y = O.matmul_ref(Xb, codes, scales, zeros)
+    yd = O.bf16_to_f32(Xb).astype(np.float64) @ O.bf16_to_f32(Wb).astype(np.float64).T
+    assert errs[0] == np.linalg.norm(y - yd) / np.linalg.norm(yd)
+
+
+def check_awq_search_protects_salient(seed=18):
+    """The property AWQ rests on (Axe Corsa model card, "Stage 1"; cyankiwi
+    docs, "The Baseline: AWQ": a few input channels with large activations
+    carry the error): with five channels of 20x activations and ordinary
+    weights, scaling those channels up cuts the output error by more than a
+    fifth, and too large an exponent makes it worse again (the other
+    channels lose resolution), so the best exponent is inside (0, 1)."""
+    Wb, Xb = _salient_case(seed)
+    alphas = np.linspace(0, 1, 11)
+    errs, best = O.awq_search(Wb, Xb, alphas)
+    assert errs[best] == errs.min()
+    assert errs[best] < 0.8 * errs[0], errs
+    assert 0 < best < len(alphas) - 1, errs
+    assert errs[-1] > errs[best] * 1.5, errs

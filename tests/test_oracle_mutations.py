@@ -18,6 +18,7 @@ ALL_PINS = [
     P.check_dense_brute_force, P.check_dense_matches_fused_on_grid,
     P.check_symmetric_hand, P.check_symmetric_invariants, P.check_symmetric_brute_force,
     P.check_i64_container,
+    P.check_awq_search_alpha_zero_is_plain, P.check_awq_search_protects_salient,
 ]
 
 
@@ -183,6 +184,21 @@ def _i64_high_nibble_first(q):
     return words.view(np.int64)
 
 
+def _search_multiplies_x(W_bits, Xcal_bits, alphas, X_bits=None):
+    X_bits = Xcal_bits if X_bits is None else X_bits
+    imp = R.awq_importance(Xcal_bits)
+    yd = R.dense_matmul_ref(X_bits, W_bits)
+    errs = []
+    for a in alphas:
+        s = R.awq_scale(imp, a)
+        codes, scales, zeros = R.quantize_pack(W_bits, s)
+        g = R.f32_to_bf16_rne(np.asarray(s, np.float32))
+        y = R.matmul_ref(R.apply_channel_scale(X_bits, g), codes, scales, zeros)
+        errs.append(np.linalg.norm(y - yd) / np.linalg.norm(yd))
+    errs = np.asarray(errs)
+    return errs, int(np.argmin(errs))
+
+
 ORIG = {n: getattr(R, n) for n in ["group_scale_zero", "quantize"]}
 
 MUTATIONS = {
@@ -205,6 +221,7 @@ MUTATIONS = {
     "symmetric_divide_by_8": ("group_scale_symmetric", _sym_scale_div8),
     "symmetric_scale_from_max_not_magnitude": ("group_scale_symmetric", _sym_scale_max_only),
     "i64_high_nibble_first": ("pack_codes_i64", _i64_high_nibble_first),
+    "awq_search_multiplies_x": ("awq_search", _search_multiplies_x),
 }
 
 

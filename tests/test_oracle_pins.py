@@ -133,3 +133,11 @@ def test_symmetric_brute_force():
 
 def test_i64_container():
     P.check_i64_container()
+
+
+def test_awq_search_alpha_zero_is_plain():
+    P.check_awq_search_alpha_zero_is_plain()
+
+
+def test_awq_search_protects_salient():
+    P.check_awq_search_protects_salient()
