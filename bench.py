@@ -542,6 +542,31 @@ def comparisons(workload, fused_ms_per_step, fused_prefill, dev, stream, steps=4
             errs.append(row)
             del W, X, yd, yq
     out["quantisation_error_vs_dense"] = {"M": Mq, "layers": errs}
+
+    # AWQ exponent search on the library's kernels: calibration tokens from
+    # one batch, the error measured on another; the recipe's weights (their
+    # salient input channels already x8) and, as a contrast, the same layers
+    # with those weight columns at ordinary size
+    alphas = [round(0.1 * i, 1) for i in range(11)]
+    search = []
+    for contrast in (False, True):
+        for L in layers:
+            W = gen.weights(L.N, L.K, workload, L.name, device=dev)
+            if contrast:
+                S = gen.salient_channels(L.K, workload, L.name).to(dev)
+                W[:, S] = (W[:, S].float() / 8.0).to(torch.bfloat16)
+            Xc = gen.activations(512, L.K, workload, L.name, role="Xcal", device=dev)
+            Xe = gen.activations(256, L.K, workload, L.name, role="Xeval", device=dev)
+            best, e = w4.w4a16_awq_search(W, Xc, alphas, Xe)
+            search.append({"layer": L.name, "salient_weights_x8": not contrast, "best_alpha": alphas[best],
+                           "error_alpha0": round(e[0], 5), "error_best": round(e[best], 5),
+                           "errors": [round(v, 5) for v in e]})
+            del W, Xc, Xe
+    out["awq_search"] = {"alphas": alphas, "calibration_tokens": 512, "eval_tokens": 256,
+                         "layers": search}
+    log("[bench] AWQ search: " + ", ".join(
+        f"{r['layer']}{'' if r['salient_weights_x8'] else '(w1)'} a={r['best_alpha']} "
+        f"{r['error_alpha0']:.4f}->{r['error_best']:.4f}" for r in search))
     log("[bench] compare error vs dense: " + ", ".join(
         f"{r['layer']}{'+off' if r['group_offsets'] else ''} asym {r['asymmetric_rel_l2']:.4f} "
         f"sym {r['symmetric_rel_l2']:.4f}" for r in errs))

@@ -229,6 +229,33 @@ def w4a16_scale_channels(X: torch.Tensor, gamma: torch.Tensor,
     return out
 
 
+def w4a16_awq_search(W: torch.Tensor, Xcal: torch.Tensor, alphas, X: torch.Tensor | None = None):
+    """AWQ's grid search over the exponent alpha of s = importance^alpha,
+    run on this library's kernels: importance from Xcal, then per alpha the
+    scale, the packed W diag(s), the activations X diag(s)^-1 through the
+    folded producer weight bf16(1/s), the fused product, and its relative
+    L2 error against the dense BF16 product of X and W (X defaults to Xcal).
+    Only the final norms are torch reductions.  Returns (index of the best
+    alpha, list of errors)."""
+    _need(W, torch.bfloat16, "W", 2)
+    X = Xcal if X is None else X
+    K = W.shape[1]
+    imp = w4a16_awq_importance(Xcal)
+    y_dense = w4a16_dense_gemm(X, W).float()
+    dnorm = torch.linalg.vector_norm(y_dense)
+    errs = []
+    for a in alphas:
+        s = w4a16_awq_scale(imp, float(a))
+        p = w4a16_pack(W, awq_s=s)
+        gamma = torch.ones(K, dtype=torch.bfloat16, device=W.device)
+        w4a16_awq_fold(s, gamma)
+        Xs = w4a16_scale_channels(X, gamma)
+        y = w4a16_gemm(Xs, p).float()
+        errs.append(float(torch.linalg.vector_norm(y - y_dense) / dnorm))
+    best = min(range(len(errs)), key=lambda i: errs[i])
+    return best, errs
+
+
 # ---------------------------------------------------------------------------
 # Dense BF16 comparisons (not the fused path; see w4a16.h)
 # ---------------------------------------------------------------------------

@@ -80,3 +80,37 @@ def test_awq_folded_stack_layer(M):
         assert_output_close(y[:, ridx], y_ref, mag, label=f"{layer.name} M={M}", strict=same_s)
         del W, p
         torch.cuda.empty_cache()
+
+
+def _salient_case(seed, N=64, K=512, T=64):
+    rng = np.random.default_rng(seed)
+    w = rng.normal(0, 0.02, size=(N, K))
+    sal = rng.choice(K, 5, replace=False)
+    x = rng.normal(0, 1, size=(T, K))
+    x[:, sal] *= 20.0
+    return O.f32_to_bf16_rne(w.astype(np.float32)), O.f32_to_bf16_rne(x.astype(np.float32))
+
+
+@pytest.mark.parametrize("case", ["salient", "generated"])
+def test_awq_search_matches_oracle(case):
+    """The search on the library's kernels against the oracle's: every error
+    within 3% (the GPU outputs are BF16-rounded, the oracle's are fp64), and
+    the chosen exponent is one whose oracle error is within 2% of the
+    oracle's best."""
+    alphas = np.linspace(0, 1, 11)
+    if case == "salient":
+        Wb, Xb = _salient_case(18)
+        Xeb = None
+    else:
+        N, K = 256, 1024
+        Wb = gen.bits(gen.weights(N, K, "awq", "search", device=DEV))
+        Xb = gen.bits(gen.activations(128, K, "awq", "search", role="Xcal", device=DEV))
+        Xeb = gen.bits(gen.activations(96, K, "awq", "search", device=DEV))
+    W = gen.from_bits(Wb, DEV)
+    Xc = gen.from_bits(Xb, DEV)
+    Xe = None if Xeb is None else gen.from_bits(Xeb, DEV)
+    best, errs = w4.w4a16_awq_search(W, Xc, alphas, Xe)
+    torch.cuda.synchronize()
+    ref, ref_best = O.awq_search(Wb, Xb, alphas, Xeb)
+    assert np.allclose(errs, ref, rtol=3e-2), (errs, ref)
+    assert ref[best] <= ref[ref_best] * 1.02, (best, ref_best, ref)
