@@ -19,7 +19,7 @@
 // Tiling.  A 512-thread block (8 waves, 2 along M x 4 along N) computes a
 // 256 x 256 tile of Y; each wave owns 128 x 64 (8 x 4 MFMA 16x16x32 tiles).
 // (With few such tiles, 256-thread blocks of 128 x 128, waves of 64 x 64,
-// three blocks per CU.)  The waves that share a row half each compute the
+// three blocks per CU, or 128-thread blocks of 64 x 128.)  The waves that share a row half each compute the
 // activation sums of two of its 16-row tiles (from A fragments they read
 // anyway) and exchange them through LDS.  A K step is a quarter
 // group (32 inputs): X[BM][32] of a step goes straight from global memory to
@@ -60,12 +60,13 @@ struct TileCfg {
   static constexpr int X_LOADS = X_STAGE / 1024 / kWaves;  // 1-KiB X copies per wave per step
   static constexpr int C_LOADS = C_GROUP / 1024 / kWaves;  // 1-KiB code copies per wave per group
   static constexpr int XS_TILES = MT / WAVES_N;  // activation-sum tiles computed by each wave
-  static_assert(WAVES_M == 2, "two waves along M (wm = wave & 1)");
-  static_assert(X_LOADS == 2 && C_LOADS == 2, "copy split");
+  static_assert(WAVES_M == 1 || WAVES_M == 2, "wm = wave % WAVES_M");
+  static_assert(X_LOADS == 2 && (C_LOADS == 2 || C_LOADS == 4), "copy split");
   static_assert(XS_TILES == 2, "two activation-sum tiles per wave");
 };
 using TileBig = TileCfg<256, 256, 128, 64>;
 using TileSmall = TileCfg<128, 128, 64, 64>;
+using TileTiny = TileCfg<64, 128, 64, 64>;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -146,7 +147,7 @@ __device__ __forceinline__ void gemm_tile(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
-  const int wm = wave & 1, wn = wave >> 1;   // C::WAVES_M == 2
+  const int wm = wave % C::WAVES_M, wn = wave / C::WAVES_M;
   const int r16 = lane & 15, q = lane >> 4;
   const int G = K / kGroup;
   const int steps = kSteps * G;
@@ -413,6 +414,17 @@ void gemm_small_kernel(
   gemm_tile<TileSmall>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, m_tiles, n_tiles);
 }
 
+// 64 x 128 tiles on two waves of 64 x 64, for layers whose 128 x 128 tiles
+// would still leave CUs idle (two waves per SIMD: at three the compiler
+// moves values into AGPRs)
+__global__ __launch_bounds__(TileTiny::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_tiny_kernel(
+    const uint16_t* __restrict__ X, int M, int64_t ldx, const uint32_t* __restrict__ codes,
+    const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K,
+    uint16_t* __restrict__ Y, int64_t ldy, int m_tiles, int n_tiles) {
+  gemm_tile<TileTiny>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, m_tiles, n_tiles);
+}
+
 }  // namespace
 
 namespace {
@@ -427,7 +439,8 @@ int launch_tiles(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* code
   if ((C::BM - 1) * ldx * 2 + K * 2 >= ((int64_t)1 << 32) || C::BN * (K / 2) >= ((int64_t)1 << 32) ||
       C::BN * (K / kGroup) * 4 >= ((int64_t)1 << 32))
     return 3;
-  auto kernel = C::BM == TileBig::BM ? gemm_kernel : gemm_small_kernel;
+  auto kernel = C::BM == TileBig::BM ? gemm_kernel
+                : (C::BM == TileSmall::BM ? gemm_small_kernel : gemm_tiny_kernel);
   hipLaunchKernelGGL(kernel, dim3((unsigned)(mt * nt)), dim3(C::kThreads), 0, stream, X,
                      (int)M, ldx, codes, scales, zeros, (int)N, (int)K, Y, ldy, (int)mt, (int)nt);
   return hipGetLastError() == hipSuccess ? 0 : 4;
@@ -437,15 +450,21 @@ int launch_tiles(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* code
 int launch_gemm(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
                 const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K, uint16_t* Y,
                 int64_t ldy, hipStream_t stream) {
-  // 256 x 256 tiles when there are at least three per four CUs, else
-  // 128 x 128 tiles, a quarter of the work per block, three blocks per CU.
-  // On whole layers the small tiles run at ~560-610 TFLOP/s and the large
-  // ones at ~750-770, so the small tiles win when the large ones would leave
-  // a quarter of the CUs idle (measured on the 8B-shaped layers, M = 512 ..
-  // 4096: at 192 large tiles the two are level).
-  const int64_t big = ((M + TileBig::BM - 1) / TileBig::BM) * ((N + TileBig::BN - 1) / TileBig::BN);
-  if (4 * big >= 3 * (int64_t)device_cu_count())
+  // 256 x 256 tiles when there are at least three per four CUs.  On whole
+  // layers the 128 x 128 tiles run at ~560-610 TFLOP/s and the large ones at
+  // ~750-770, so smaller tiles win only when the large ones would leave a
+  // quarter of the CUs idle (at 192 large tiles the two are level).  Between
+  // 128 x 128 and 64 x 128 tiles the one whose block count fills the rounds
+  // of CUs better wins, ties to the larger tile (measured on the 8B-shaped
+  // layers, M = 512 .. 4096).
+  const int64_t cus = device_cu_count();
+  auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  auto fill = [&](int64_t t) { return (double)t / (double)(((t + cus - 1) / cus) * cus); };
+  const int64_t big = tiles(TileBig::BM, TileBig::BN);
+  if (4 * big >= 3 * cus)
     return launch_tiles<TileBig>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
+  if (fill(tiles(TileTiny::BM, TileTiny::BN)) > fill(tiles(TileSmall::BM, TileSmall::BN)) + 1e-9)
+    return launch_tiles<TileTiny>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
   return launch_tiles<TileSmall>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
 }
 

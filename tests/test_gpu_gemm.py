@@ -103,10 +103,18 @@ def test_large_tiles_ragged_with_canaries():
     assert_output_close(out[midx][:, ridx], y_ref, mag, label="large tiles, ragged")
 
 
-def test_small_tiles_long_rows():
-    # few large tiles (2 x 8): the 128 x 128 kernel, over 32 groups
+def test_tiny_tiles_long_rows():
+    # few large tiles (2 x 8), and 64 x 128 tiles fill the CUs better than
+    # 128 x 128 (80 against 48 blocks): the 64 x 128 kernel, ragged M, 32 groups
     check_case(300, 2000, 4096, "gemm", "small_long", shift=True, rows=sample_rows(2000, 64, seed=9),
-               label="small tiles, K=4096")
+               label="64x128 tiles, K=4096")
+
+
+def test_small_tiles_ragged():
+    # 48 large tiles; 128 x 128 (4 x 48 = 192 blocks) and 64 x 128 (384) fill
+    # the same share of the CU rounds, so the 128 x 128 kernel; ragged M and N
+    check_case(500, 6100, 512, "gemm", "small_ragged", shift=True, rows=sample_rows(6100, 64, seed=10),
+               mrows=sample_rows(500, 48, seed=11), label="128x128 tiles, ragged")
 
 
 def test_tile_choice_boundary():
