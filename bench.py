@@ -675,7 +675,7 @@ def cpu_baseline(layers, workload, spec, M, dev, row_stride=2, min_seconds=10.0)
     dt = time.perf_counter() - t0
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "seconds": round(dt, 2),
-            "sample": f"every {row_stride}th output row of each of the four layers, M={M}, "
+            "sample": f"one output row in {row_stride} of each of the four layers, M={M}, "
                       f"{reps} pass(es); unpack + dequantise + fp64 dot, one thread"}
 
 
