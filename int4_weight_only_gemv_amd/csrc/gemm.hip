@@ -31,7 +31,9 @@
 // chunks of each 64-byte LDS row are XOR-swizzled by (row >> 1) & 3, so the
 // rows that one LDS cycle of a 16-byte-per-lane read serves fall on distinct
 // bank groups.  Codes are unpacked in natural k order, so X needs no
-// permutation.  Tiles go to the 8 XCDs in contiguous runs with N fastest, so
+// permutation.  Each lane loads the scale and zero point of one column of
+// its wave per group; lane permutes spread the factors to the accumulator
+// layout.  Tiles go to the 8 XCDs in contiguous runs with N fastest, so
 // blocks that share X rows share an L2.
 
 #include "common.h"
@@ -108,7 +110,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // Memory operations each wave issues, in this order: at group position 0,
-// the next group's 2 NT scale/zero loads and C_LOADS code copies; at every
+// the next group's scale and zero-point loads and C_LOADS code copies; at every
 // step, X_LOADS copies of X for the step four ahead.  Nothing is
 // conditional (indices are clamped to the last group / step), so the
 // in-order memory counter gives fixed waits.  At the step at position ST
@@ -118,7 +120,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 // covers the next group's code copies (issued before the awaited X copies).
 template <class C, int ST>
 __device__ __forceinline__ void wait_step() {
-  constexpr int kGroupStart = 2 * C::NT + C::C_LOADS;
+  constexpr int kGroupStart = 2 + C::C_LOADS;
   if (ST == 1 || ST == 2) wait_vmcnt<2 * C::X_LOADS + kGroupStart>(); else wait_vmcnt<2 * C::X_LOADS>();
 }
 
@@ -190,25 +192,24 @@ __device__ __forceinline__ void gemm_tile(
                                        (lds_void*)&dst[cdst0 + j * 16 * C_ROW], 16, 0, 0);
   };
 
-  // this lane's output columns (one per 16-wide n tile) for scales / zeros:
-  // column ncol + 16 nt, clamped to N - 1; element offsets from the block's
-  // first column
-  const int ncol = n0 + wn * WN + r16;
+  // Scales and zero points: lane l of a wave fetches those of the wave's
+  // column l (its WN = 64 columns, one per lane; clamped to N - 1), one
+  // load of each per group, as 32-bit byte offsets from a block-uniform
+  // base (the launcher checks the range) so the loads take a scalar base.
+  // The per-column factors are then moved to the lanes of the accumulator
+  // layout (column r16 + 16 nt) by lane permutes.
+  static_assert(WN == 64, "one metadata column per lane");
   const uint16_t* sblk = scales + (int64_t)n0 * G;
   const int32_t* zblk = zeros + (int64_t)n0 * G;
-  // 32-bit byte offsets from a block-uniform base (the launcher checks the
-  // range), so the loads take a scalar base and no 64-bit lane addresses
   auto ld_s = [&](uint32_t e) {
     return (uint32_t)*reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(sblk) + e * 2u);
   };
   auto ld_z = [&](uint32_t e) {
     return *reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(zblk) + e * 4u);
   };
-  uint32_t moffs[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) moffs[nt] = (uint32_t)(min(ncol + 16 * nt, N - 1) - n0) * (uint32_t)G;
-  uint32_t s_cur[NT], s_nxt[NT];
-  int z_cur[NT], z_nxt[NT];
+  const uint32_t moff = (uint32_t)(min(n0 + wn * WN + lane, N - 1) - n0) * (uint32_t)G;
+  uint32_t s_cur, s_nxt;
+  int z_cur, z_nxt;
 
   // LDS read offsets.  A: row (wm 128 + mt 16 + r16), chunk q (inputs
   // 8q .. 8q+7 of the step).  B: code row (wn 64 + nt 16 + r16), chunk =
@@ -235,14 +236,19 @@ __device__ __forceinline__ void gemm_tile(
   // fold a finished group into the accumulator: remove bias and zero point,
   // move to the next group's scale (or, after the last group, apply it)
   auto group_end = [&](bool last) {
+    // this lane's column: bias + zero point and the scale factor
+    const float zl = (float)(128 + z_cur);
+    const float sc = bf16_to_f32(s_cur);
+    const float rl = last ? sc : sc * __builtin_amdgcn_rcpf(bf16_to_f32(s_nxt));
+    s_cur = s_nxt;
+    z_cur = z_nxt;
+    // n tile nt's column r16 + 16 nt sits in that lane
     float zb[NT], ratio[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      zb[nt] = (float)(128 + z_cur[nt]);
-      const float sc = bf16_to_f32(s_cur[nt]);
-      ratio[nt] = last ? sc : sc * __builtin_amdgcn_rcpf(bf16_to_f32(s_nxt[nt]));
-      s_cur[nt] = s_nxt[nt];
-      z_cur[nt] = z_nxt[nt];
+      const int src = (r16 + 16 * nt) * 4;
+      zb[nt] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(zl)));
+      ratio[nt] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(rl)));
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -275,13 +281,10 @@ __device__ __forceinline__ void gemm_tile(
 
   // prologue: group 0's scale/zero and codes, steps 0..3 of X in flight,
   // step 0's fragments in registers (steps >= 4)
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    s_cur[nt] = ld_s(moffs[nt]);
-    z_cur[nt] = ld_z(moffs[nt]);
-    s_nxt[nt] = s_cur[nt];
-    z_nxt[nt] = z_cur[nt];
-  }
+  s_cur = ld_s(moff);
+  z_cur = ld_z(moff);
+  s_nxt = s_cur;
+  z_nxt = z_cur;
   auto prologue = [&](uint8_t* cg_first) {   // group 0's code buffer
     copy_codes(cg_first, 0);
     copy_x(xs0, 0);
@@ -325,11 +328,8 @@ __device__ __forceinline__ void gemm_tile(
       // next group's scale/zero and codes (the last group's again after the
       // last), issued before this step's X copies, as wait_step counts them
       const int gn = min(g + 1, G - 1);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        s_nxt[nt] = ld_s(moffs[nt] + (uint32_t)gn);
-        z_nxt[nt] = ld_z(moffs[nt] + (uint32_t)gn);
-      }
+      s_nxt = ld_s(moff + (uint32_t)gn);
+      z_nxt = ld_z(moff + (uint32_t)gn);
       copy_codes(cg_other, gn);
     }
     copy_x(xs_here, min(s + 4, steps - 1));
