@@ -133,8 +133,10 @@ __device__ __forceinline__ void gemm_tile(
   constexpr int X_STAGE = C::X_STAGE, C_GROUP = C::C_GROUP;
   constexpr int X_LOADS = C::X_LOADS, C_LOADS = C::C_LOADS, XS_TILES = C::XS_TILES;
   // one LDS object per buffer, so the compiler can tell the copies into one
-  // buffer from the reads of another
-  __shared__ __attribute__((aligned(1024))) uint8_t xs0[X_STAGE], xs1[X_STAGE], xs2[X_STAGE], xs3[X_STAGE];
+  // buffer from the reads of another.  The X stages' larger alignment places
+  // them first, below 64 KiB, where their addresses fit the immediate offset
+  // of the LDS reads.
+  __shared__ __attribute__((aligned(4096))) uint8_t xs0[X_STAGE], xs1[X_STAGE], xs2[X_STAGE], xs3[X_STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t cg0[C_GROUP], cg1[C_GROUP];
   __shared__ __attribute__((aligned(16))) float xsum_lds[BM];
 
@@ -270,8 +272,17 @@ __device__ __forceinline__ void gemm_tile(
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) bw[nt] = *reinterpret_cast<const uint32_t*>(&cg[bo + nt * 16 * C_ROW]);
   };
+  // per-lane A read offsets of the row tiles, kept in registers (opaque to
+  // the compiler) so that each read is one instruction: the stage buffer's
+  // address goes into its immediate offset
+  uint32_t aoffs[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    aoffs[mt] = (uint32_t)(aoff + rowt(mt) * 16 * (KS * 2));
+    asm volatile("" : "+v"(aoffs[mt]));
+  }
   auto read_a = [&](const uint8_t* xs, int mt) {
-    af[mt] = *reinterpret_cast<const u32x4*>(&xs[aoff + rowt(mt) * 16 * (KS * 2)]);
+    af[mt] = *reinterpret_cast<const u32x4*>(&xs[aoffs[mt]]);
   };
   auto read_frags = [&](const uint8_t* xs, const uint8_t* cg, int pos) {
     read_b(cg, pos);
