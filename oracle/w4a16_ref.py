@@ -42,6 +42,18 @@ from __future__ import annotations
 import numpy as np
 
 GROUP = 128          # Axe Corsa model card, "The Two-Stage Pipeline": 128 weights per group
+# Smaller groups the pages name as common settings ("Quantization I",
+# "Concept"; Zeno AGI, "Weight-only vs mixed precision", its summary of
+# settings): the same rules per group of 32 or 64.
+GROUPS = (32, 64, 128)
+
+
+def _group_of(K: int, n_groups: int) -> int:
+    """Group size of a packed matrix from its shapes (K inputs, n_groups
+    scales per row)."""
+    if n_groups < 1 or K % n_groups or K // n_groups not in GROUPS:
+        raise ValueError(f"K={K} with {n_groups} groups per row is not a group of {GROUPS}")
+    return K // n_groups
 QMAX = 15            # 16 representable unsigned INT4 codes, 0..15
 FLT_MIN = np.float32(2.0 ** -126)
 
@@ -129,23 +141,26 @@ def group_codes(w_groups: np.ndarray, s: np.ndarray, z: np.ndarray) -> np.ndarra
     return q.astype(np.uint8)
 
 
-def quantize(W_bits: np.ndarray, awq_s: np.ndarray | None = None):
-    """Quantise a BF16 weight matrix W [N][K] (uint16 bits) group-wise.
+def quantize(W_bits: np.ndarray, awq_s: np.ndarray | None = None, group: int = GROUP):
+    """Quantise a BF16 weight matrix W [N][K] (uint16 bits) group-wise, in
+    groups of `group` consecutive inputs (32, 64 or 128).
 
     If awq_s (float32 [K]) is given, the quantiser input is
     fl32(W[n,k] * awq_s[k]) -- the AWQ rescaled weight W' = W . diag(s)
     (Axe Corsa model card, "Stage 1: Activation-Aware Weight Scaling").
 
-    Returns (q uint8 [N][K], s_bits uint16 [N][K/128], z int32 [N][K/128]).
+    Returns (q uint8 [N][K], s_bits uint16 [N][K/group], z int32 [N][K/group]).
     """
     W_bits = np.asarray(W_bits, dtype=np.uint16)
     N, K = W_bits.shape
+    if group not in GROUPS:
+        raise ValueError(f"group must be one of {GROUPS}")
     if K % GROUP:
         raise ValueError("K must be a multiple of 128")
     w = bf16_to_f32(W_bits)
     if awq_s is not None:
         w = (w * np.asarray(awq_s, dtype=np.float32)[None, :]).astype(np.float32)
-    wg = w.reshape(N, K // GROUP, GROUP)
+    wg = w.reshape(N, K // group, group)
     s_bits, s, z = group_scale_zero(wg)
     q = group_codes(wg, s, z).reshape(N, K)
     if np.any(z > np.iinfo(np.int32).max) or np.any(z < np.iinfo(np.int32).min):
@@ -260,10 +275,10 @@ def unpack_codes(words: np.ndarray) -> np.ndarray:
     return q.reshape(N, W8 * 8)
 
 
-def quantize_pack(W_bits: np.ndarray, awq_s: np.ndarray | None = None):
+def quantize_pack(W_bits: np.ndarray, awq_s: np.ndarray | None = None, group: int = GROUP):
     """Quantise then pack: returns (codes uint32 [N][K/8], scales uint16
-    [N][K/128] (BF16 bits), zeros int32 [N][K/128])."""
-    q, s_bits, z = quantize(W_bits, awq_s)
+    [N][K/group] (BF16 bits), zeros int32 [N][K/group])."""
+    q, s_bits, z = quantize(W_bits, awq_s, group)
     return pack_codes(q), s_bits, z
 
 
@@ -272,14 +287,15 @@ def quantize_pack(W_bits: np.ndarray, awq_s: np.ndarray | None = None):
 # ---------------------------------------------------------------------------
 
 def dequantize(codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray) -> np.ndarray:
-    """w_hat[n,k] = (q[n,k] - z[n,g]) * s[n,g] in float64, g = k // 128
+    """w_hat[n,k] = (q[n,k] - z[n,g]) * s[n,g] in float64, g = k // group
     (Axe Corsa model card, "The Two-Stage Pipeline", dequantisation
-    equation).  Exact: the product has at most ~40 significant bits."""
+    equation), the group size read from the shapes.  Exact: the product has
+    at most ~40 significant bits."""
     q = unpack_codes(codes).astype(np.float64)
     N, K = q.shape
     s = bf16_to_f32(scales).astype(np.float64)
     z = np.asarray(zeros, dtype=np.int64).astype(np.float64)
-    g = np.arange(K) // GROUP
+    g = np.arange(K) // _group_of(K, s.shape[1])
     return (q - z[:, g]) * s[:, g]
 
 
@@ -318,7 +334,7 @@ def dequantize_bf16(codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray) ->
     N, K = q.shape
     s = bf16_to_f32(scales)
     z = np.asarray(zeros, dtype=np.int64)
-    g = np.arange(K) // GROUP
+    g = np.arange(K) // _group_of(K, s.shape[1])
     diff = (q - z[:, g]).astype(np.float32)
     prod = np.multiply(diff, s[:, g], dtype=np.float32)
     return f32_to_bf16_rne(prod)

@@ -183,6 +183,35 @@ def check_dequant_closed_form():
     assert np.array_equal(w[128:], 1.0 + j / 16.0)
 
 
+def check_grouped_hand():
+    """Groups of 32 and 64 (the smaller group sizes "Quantization I",
+    "Concept", names), worked by hand on one row of 128 weights: quarter i
+    holds (j - 8) * 2^-(7+i), j = k mod 16.
+    * group 32: every group is its own grid, s = 2^-(7+i) (BF16 bits 0x3C00,
+      0x3B80, 0x3B00, 0x3A80), z = 8, q = j;
+    * group 64: group 0 spans quarters 0 and 1, so s = 2^-7, z = 8; quarter
+      1's values are half a step apart and round half away from zero:
+      q = 8 + round_half_away((j - 8) / 2); group 1 likewise with s = 2^-9;
+    * group 128: one grid for the row, s = 2^-7, z = 8."""
+    k = np.arange(128)
+    j = k % 16
+    w = (j - 8) * 2.0 ** -(7 + k // 32)
+    Wb = _bf16_bits_of(w).reshape(1, 128)
+    half = np.array([8 + int(np.sign(v) * np.floor(abs(v) + 0.5)) for v in (j[:32] - 8) / 2.0])
+    q, s, z = O.quantize(Wb, group=32)
+    assert list(s[0]) == [0x3C00, 0x3B80, 0x3B00, 0x3A80] and list(z[0]) == [8] * 4
+    assert np.array_equal(q[0], j)
+    q, s, z = O.quantize(Wb, group=64)
+    assert list(s[0]) == [0x3C00, 0x3B00] and list(z[0]) == [8, 8]
+    assert np.array_equal(q[0], np.concatenate([j[:32], half, j[:32], half]))
+    assert list(half[:4]) == [4, 4, 5, 5] and list(half[-4:]) == [10, 11, 11, 12]
+    q, s, z = O.quantize(Wb, group=128)
+    assert list(s[0]) == [0x3C00] and list(z[0]) == [8]
+    # dequantisation reads the group size from the shapes: group 32 here
+    codes, scales, zeros = O.quantize_pack(Wb, group=32)
+    assert np.array_equal(O.dequantize(codes, scales, zeros)[0], w)
+
+
 # ---------------------------------------------------------------------------
 # Packing layout
 # ---------------------------------------------------------------------------
@@ -204,11 +233,11 @@ def check_pack_layout(seed=3):
 # Invariants on generated groups (the pages: all 16 INT4 values used)
 # ---------------------------------------------------------------------------
 
-def check_min_max_codes(W_bits):
-    q, s_bits, z = O.quantize(W_bits)
+def check_min_max_codes(W_bits, group=128):
+    q, s_bits, z = O.quantize(W_bits, group=group)
     N, K = W_bits.shape
-    w = O.bf16_to_f32(W_bits).reshape(N, K // 128, 128)
-    qg = q.reshape(N, K // 128, 128)
+    w = O.bf16_to_f32(W_bits).reshape(N, K // group, group)
+    qg = q.reshape(N, K // group, group)
     imin = w.argmin(axis=-1)
     imax = w.argmax(axis=-1)
     qmin = np.take_along_axis(qg, imin[..., None], -1)[..., 0]
@@ -226,12 +255,12 @@ def check_min_max_codes(W_bits):
     return straddles.mean()
 
 
-def check_all_codes_on_grid(seed=4, N=64, K=512):
+def check_all_codes_on_grid(seed=4, N=64, K=512, group=128):
     """Weights that lie exactly on a grid (q0 - z0) * s0 come back unchanged:
     pack returns (q0, s0, z0) and every group uses all 16 codes."""
     rng = np.random.default_rng(seed)
-    G = K // 128
-    q0 = rng.integers(0, 16, size=(N, G, 128))
+    G = K // group
+    q0 = rng.integers(0, 16, size=(N, G, group))
     q0[:, :, 0] = 0
     q0[:, :, 1] = 15
     for n in range(N):                      # all 16 codes in every group
@@ -242,13 +271,13 @@ def check_all_codes_on_grid(seed=4, N=64, K=512):
     s0 = mant * 2.0 ** rng.integers(-12, -2, size=(N, G))
     w = (q0 - z0[..., None]) * s0[..., None]
     W_bits = _bf16_bits_of(w.reshape(N, K).astype(np.float32))
-    q, s_bits, z = O.quantize(W_bits)
-    assert np.array_equal(q.reshape(N, G, 128), q0)
+    q, s_bits, z = O.quantize(W_bits, group=group)
+    assert np.array_equal(q.reshape(N, G, group), q0)
     assert np.array_equal(z, z0)
     assert np.array_equal(O.bf16_to_f32(s_bits).astype(np.float64), s0)
     for n in range(N):
         for g in range(G):
-            assert len(np.unique(q.reshape(N, G, 128)[n, g])) == 16
+            assert len(np.unique(q.reshape(N, G, group)[n, g])) == 16
     return W_bits, (q, s_bits, z)
 
 
@@ -273,20 +302,20 @@ def check_on_grid_matmul_exact(seed=5):
 # Brute force on tiny inputs (exact rationals)
 # ---------------------------------------------------------------------------
 
-def check_brute_force(seed=6, M=4, K=128, N=8):
+def check_brute_force(seed=6, M=4, K=128, N=8, group=128):
     rng = np.random.default_rng(seed)
     w = (rng.normal(0, 0.02, size=(N, K)) + rng.uniform(-0.01, 0.01, size=(N, 1))).astype(np.float32)
     W_bits = O.f32_to_bf16_rne(w)
     x = rng.normal(0, 1, size=(M, K)).astype(np.float32)
     X_bits = O.f32_to_bf16_rne(x)
-    q, s_bits, z = O.quantize(W_bits)
+    q, s_bits, z = O.quantize(W_bits, group=group)
     wf = O.bf16_to_f32(W_bits)
     near_ties = 0
     for n in range(N):
-        for g in range(K // 128):
+        for g in range(K // group):
             s = _frac_of_f32(O.bf16_to_f32(s_bits[n, g]))
             zz = int(z[n, g])
-            for k in range(g * 128, (g + 1) * 128):
+            for k in range(g * group, (g + 1) * group):
                 wk = _frac_of_f32(wf[n, k])
                 # argmin over the 16 codes of |w - (c - z) s|, ties away from zero
                 best = min(range(16), key=lambda c: (abs(wk - (c - zz) * s), -abs(c - zz)))
@@ -305,7 +334,7 @@ def check_brute_force(seed=6, M=4, K=128, N=8):
             acc = Fraction(0)
             mag = Fraction(0)
             for k in range(K):
-                g = k // 128
+                g = k // group
                 s = _frac_of_f32(O.bf16_to_f32(s_bits[n, g]))
                 term = _frac_of_f32(xf[m, k]) * (int(q[n, k]) - int(z[n, g])) * s
                 acc += term

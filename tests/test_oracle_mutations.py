@@ -19,6 +19,9 @@ ALL_PINS = [
     P.check_symmetric_hand, P.check_symmetric_invariants, P.check_symmetric_brute_force,
     P.check_i64_container,
     P.check_awq_search_alpha_zero_is_plain, P.check_awq_search_protects_salient,
+    P.check_grouped_hand,
+    lambda: P.check_all_codes_on_grid(seed=21, N=8, K=256, group=32),
+    lambda: P.check_brute_force(seed=22, M=2, K=128, N=3, group=32),
 ]
 
 
@@ -118,8 +121,22 @@ def _codes_against_unrounded(wg, s, z):
     return np.clip(r + z[..., None], 0, 15).astype(np.uint8)
 
 
-def _quantize_ignores_awq(W_bits, awq_s=None):
-    return ORIG["quantize"](W_bits, None)
+def _quantize_ignores_awq(W_bits, awq_s=None, group=128):
+    return ORIG["quantize"](W_bits, None, group)
+
+
+def _quantize_ignores_group(W_bits, awq_s=None, group=128):
+    return ORIG["quantize"](W_bits, awq_s)
+
+
+def _dequant_group_128(codes, scales, zeros):
+    # the group index taken as k // 128 whatever the shapes say
+    q = R.unpack_codes(codes).astype(np.float64)
+    K = q.shape[1]
+    s = R.bf16_to_f32(scales).astype(np.float64)
+    z = np.asarray(zeros, np.float64)
+    g = np.arange(K) // 128
+    return (q - z[:, g]) * s[:, g]
 
 
 def _fold_multiplies(s, gamma_bits):
@@ -222,6 +239,8 @@ MUTATIONS = {
     "symmetric_scale_from_max_not_magnitude": ("group_scale_symmetric", _sym_scale_max_only),
     "i64_high_nibble_first": ("pack_codes_i64", _i64_high_nibble_first),
     "awq_search_multiplies_x": ("awq_search", _search_multiplies_x),
+    "quantize_ignores_group": ("quantize", _quantize_ignores_group),
+    "dequant_group_always_128": ("dequantize", _dequant_group_128),
 }
 
 

@@ -48,6 +48,26 @@ def test_brute_force_three_groups():
     assert P.check_brute_force(seed=11, M=3, K=384, N=5) == 0
 
 
+def test_grouped_hand():
+    P.check_grouped_hand()
+
+
+@pytest.mark.parametrize("group", [32, 64])
+def test_grouped_all_codes_on_grid(group):
+    P.check_all_codes_on_grid(seed=30 + group, N=16, K=512, group=group)
+
+
+@pytest.mark.parametrize("group", [32, 64])
+def test_grouped_brute_force(group):
+    assert P.check_brute_force(seed=40 + group, M=3, K=256, N=4, group=group) == 0
+
+
+@pytest.mark.parametrize("group", [32, 64])
+def test_grouped_min_max_codes_generated(group):
+    W = gen.weights(64, 1024, "pins", f"g{group}", shift=True)
+    assert P.check_min_max_codes(gen.bits(W), group=group) > 0.99
+
+
 def test_awq_prescale():
     P.check_awq_prescale_power_of_two()
 
