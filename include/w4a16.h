@@ -44,7 +44,9 @@
  *   scales uint16_t [N][K/128] BF16 scale bits.
  *   zeros  int32_t  [N][K/128] zero points, not clamped to 0..15.
  * That is 4 + 16/128 + 32/128 = 4.375 bits per weight (Axe Corsa model card,
- * "Storage Cost").
+ * "Storage Cost").  The *_grouped entry points take groups of 32 or 64
+ * inputs as well (scales and zeros then [N][K/group]; K stays a multiple of
+ * 128).
  */
 #ifndef W4A16_H
 #define W4A16_H
@@ -56,7 +58,7 @@ extern "C" {
 #endif
 
 #define W4A16_GROUP 128
-#define W4A16_ABI_VERSION 3
+#define W4A16_ABI_VERSION 4
 #define W4A16_GEMV_MAX_M 32
 #define W4A16_DENSE_GEMV_MAX_M 8
 
@@ -148,6 +150,30 @@ int w4a16_gemm(const uint16_t* X, int64_t M, int64_t ldx,
                const uint32_t* codes, const uint16_t* scales,
                const int32_t* zeros, int64_t N, int64_t K,
                uint16_t* Y, int64_t ldy, void* stream);
+
+/*
+ * w4a16_pack_grouped, w4a16_gemv_grouped, w4a16_gemm_grouped -- the same
+ * three operations with a group of `group` consecutive inputs per scale and
+ * zero point, group = 32, 64 or 128 (the group sizes "Quantization I",
+ * "Concept", and Zeno AGI, "Weight-only vs mixed precision" (its summary of
+ * common settings) name; 128 gives exactly w4a16_pack / w4a16_gemv /
+ * w4a16_gemm).  scales and zeros are [N][K/group]; K must still be a
+ * multiple of 128.  The quantiser rules of w4a16_pack apply per group; the
+ * matmuls keep the accuracy rules of w4a16_gemv / w4a16_gemm.  For group 32
+ * and 64 the matmuls also require scales and zeros 16-byte aligned.
+ * Any other group value: W4A16_ERR_INVALID_ARG.
+ */
+int w4a16_pack_grouped(const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
+                       const float* awq_s, int64_t group, uint32_t* codes,
+                       uint16_t* scales, int32_t* zeros, void* stream);
+int w4a16_gemv_grouped(const uint16_t* X, int64_t M, int64_t ldx,
+                       const uint32_t* codes, const uint16_t* scales,
+                       const int32_t* zeros, int64_t N, int64_t K, int64_t group,
+                       uint16_t* Y, int64_t ldy, void* stream);
+int w4a16_gemm_grouped(const uint16_t* X, int64_t M, int64_t ldx,
+                       const uint32_t* codes, const uint16_t* scales,
+                       const int32_t* zeros, int64_t N, int64_t K, int64_t group,
+                       uint16_t* Y, int64_t ldy, void* stream);
 
 /*
  * w4a16_awq_importance -- per-input-channel activation magnitude from a

@@ -46,6 +46,9 @@ _SIGS = {
     "w4a16_dequantize_bf16": ([_p, _p, _p, _i64, _i64, _p, _i64, _p], ctypes.c_int),
     "w4a16_dense_gemv": ([_p, _i64, _i64, _p, _i64, _i64, _i64, _p, _i64, _p], ctypes.c_int),
     "w4a16_dense_gemm": ([_p, _i64, _i64, _p, _i64, _i64, _i64, _p, _i64, _p], ctypes.c_int),
+    "w4a16_pack_grouped": ([_p, _i64, _i64, _i64, _p, _i64, _p, _p, _p, _p], ctypes.c_int),
+    "w4a16_gemv_grouped": ([_p, _i64, _i64, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _p], ctypes.c_int),
+    "w4a16_gemm_grouped": ([_p, _i64, _i64, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _p], ctypes.c_int),
 }
 for _name, (_args, _ret) in _SIGS.items():
     _f = getattr(lib, _name)
@@ -93,43 +96,54 @@ def abi_version() -> int:
 
 class PackedLinear:
     """A packed weight matrix: codes [N][K/8] int32 (uint32 bits),
-    scales [N][K/128] bfloat16, zeros [N][K/128] int32."""
+    scales [N][K/group] bfloat16, zeros [N][K/group] int32; the group size
+    (32, 64 or 128) follows from the shapes."""
 
-    __slots__ = ("codes", "scales", "zeros", "N", "K")
+    __slots__ = ("codes", "scales", "zeros", "N", "K", "group")
 
     def __init__(self, codes, scales, zeros):
         self.codes, self.scales, self.zeros = codes, scales, zeros
         self.N = codes.shape[0]
         self.K = codes.shape[1] * 8
+        self.group = self.K // scales.shape[1] if scales.shape[1] else GROUP
 
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size() for t in (self.codes, self.scales, self.zeros))
 
 
-def empty_packed(N: int, K: int, device) -> PackedLinear:
+def empty_packed(N: int, K: int, device, group: int = GROUP) -> PackedLinear:
     codes = torch.empty(N, K // 8, dtype=torch.int32, device=device)
-    scales = torch.empty(N, K // GROUP, dtype=torch.bfloat16, device=device)
-    zeros = torch.empty(N, K // GROUP, dtype=torch.int32, device=device)
+    scales = torch.empty(N, K // group, dtype=torch.bfloat16, device=device)
+    zeros = torch.empty(N, K // group, dtype=torch.int32, device=device)
     return PackedLinear(codes, scales, zeros)
 
 
-def _pack(fn, name, W, awq_s, out):
+def _pack(fn, name, W, awq_s, out, group=None):
     _need(W, torch.bfloat16, "W", 2)
     N, K = W.shape
     if awq_s is not None:
         _need(awq_s, torch.float32, "awq_s", 1)
         if awq_s.shape[0] != K or not awq_s.is_contiguous():
             raise ValueError("awq_s must be a contiguous float32 [K]")
-    p = out if out is not None else empty_packed(N, K, W.device)
-    _check(name, fn(_ptr(W), N, K, W.stride(0), _ptr(awq_s), _ptr(p.codes), _ptr(p.scales),
-                    _ptr(p.zeros), _stream(W)))
+    p = out if out is not None else empty_packed(N, K, W.device, group or GROUP)
+    if group is None:
+        _check(name, fn(_ptr(W), N, K, W.stride(0), _ptr(awq_s), _ptr(p.codes), _ptr(p.scales),
+                        _ptr(p.zeros), _stream(W)))
+    else:
+        if p.group != group:
+            raise ValueError("out has the wrong group size")
+        _check(name, fn(_ptr(W), N, K, W.stride(0), _ptr(awq_s), group, _ptr(p.codes),
+                        _ptr(p.scales), _ptr(p.zeros), _stream(W)))
     return p
 
 
 def w4a16_pack(W: torch.Tensor, awq_s: torch.Tensor | None = None,
-               out: PackedLinear | None = None) -> PackedLinear:
-    """Quantise + pack a BF16 weight [N][K] (see w4a16_pack in w4a16.h)."""
-    return _pack(lib.w4a16_pack, "w4a16_pack", W, awq_s, out)
+               out: PackedLinear | None = None, group: int = GROUP) -> PackedLinear:
+    """Quantise + pack a BF16 weight [N][K] (see w4a16_pack in w4a16.h);
+    group 32 or 64 goes through w4a16_pack_grouped."""
+    if group == GROUP:
+        return _pack(lib.w4a16_pack, "w4a16_pack", W, awq_s, out)
+    return _pack(lib.w4a16_pack_grouped, "w4a16_pack_grouped", W, awq_s, out, group)
 
 
 def w4a16_pack_symmetric(W: torch.Tensor, awq_s: torch.Tensor | None = None,
@@ -164,18 +178,26 @@ def _matmul(fn, name, X: torch.Tensor, p: PackedLinear, out: torch.Tensor | None
         _need(out, torch.bfloat16, "out", 2)
         if tuple(out.shape) != (M, p.N):
             raise ValueError("out has the wrong shape")
-    _check(name, fn(_ptr(X), M, X.stride(0), _ptr(p.codes), _ptr(p.scales), _ptr(p.zeros),
-                    p.N, p.K, _ptr(out), out.stride(0), _stream(X)))
+    if p.group == GROUP:
+        st = fn(_ptr(X), M, X.stride(0), _ptr(p.codes), _ptr(p.scales), _ptr(p.zeros),
+                p.N, p.K, _ptr(out), out.stride(0), _stream(X))
+    else:
+        fn, name = getattr(lib, name + "_grouped"), name + "_grouped"
+        st = fn(_ptr(X), M, X.stride(0), _ptr(p.codes), _ptr(p.scales), _ptr(p.zeros),
+                p.N, p.K, p.group, _ptr(out), out.stride(0), _stream(X))
+    _check(name, st)
     return out
 
 
 def w4a16_gemv(X: torch.Tensor, p: PackedLinear, out: torch.Tensor | None = None) -> torch.Tensor:
-    """Y = X . w_hat^T for 1 <= M <= 32 (decode)."""
+    """Y = X . w_hat^T for 1 <= M <= 32 (decode); groups other than 128 go
+    through w4a16_gemv_grouped."""
     return _matmul(lib.w4a16_gemv, "w4a16_gemv", X, p, out)
 
 
 def w4a16_gemm(X: torch.Tensor, p: PackedLinear, out: torch.Tensor | None = None) -> torch.Tensor:
-    """Y = X . w_hat^T on the matrix cores, any M (prefill)."""
+    """Y = X . w_hat^T on the matrix cores, any M (prefill); groups other than
+    128 go through w4a16_gemm_grouped."""
     return _matmul(lib.w4a16_gemm, "w4a16_gemm", X, p, out)
 
 

@@ -7,12 +7,12 @@
 #include "w4a16.h"
 
 namespace w4a16 {
-int launch_pack(const uint16_t*, int64_t, int64_t, int64_t, const float*, uint32_t*, uint16_t*,
-                int32_t*, bool, hipStream_t);
+int launch_pack(const uint16_t*, int64_t, int64_t, int64_t, const float*, int, uint32_t*,
+                uint16_t*, int32_t*, bool, hipStream_t);
 int launch_gemv(const uint16_t*, int64_t, int64_t, const uint32_t*, const uint16_t*,
-                const int32_t*, int64_t, int64_t, uint16_t*, int64_t, hipStream_t);
+                const int32_t*, int64_t, int64_t, int, uint16_t*, int64_t, hipStream_t);
 int launch_gemm(const uint16_t*, int64_t, int64_t, const uint32_t*, const uint16_t*,
-                const int32_t*, int64_t, int64_t, uint16_t*, int64_t, hipStream_t);
+                const int32_t*, int64_t, int64_t, int, uint16_t*, int64_t, hipStream_t);
 int launch_awq_importance(const uint16_t*, int64_t, int64_t, int64_t, float*, hipStream_t);
 int launch_awq_scale(const float*, int64_t, float, float*, hipStream_t);
 int launch_awq_fold(const float*, int64_t, uint16_t*, uint16_t*, hipStream_t);
@@ -32,17 +32,21 @@ constexpr int64_t kMaxDim = (int64_t)1 << 30;  // N, K, M each below 2^30
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-// Checks shared by gemv and gemm.
+bool group_ok(int64_t group) { return group == 32 || group == 64 || group == 128; }
+
+// Checks shared by gemv and gemm (any group size; smaller groups need
+// 16-byte aligned scales and zero points).
 int check_matmul(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
                  const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K,
-                 const uint16_t* Y, int64_t ldy) {
-  if (!X || !codes || !scales || !zeros || !Y) return W4A16_ERR_INVALID_ARG;
+                 const uint16_t* Y, int64_t ldy, int64_t group = W4A16_GROUP) {
+  if (!X || !codes || !scales || !zeros || !Y || !group_ok(group)) return W4A16_ERR_INVALID_ARG;
   if (M < 1 || N < 1 || K < W4A16_GROUP || K % W4A16_GROUP) return W4A16_ERR_INVALID_ARG;
   if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return W4A16_ERR_UNSUPPORTED;
   if (ldx < K || ldy < N) return W4A16_ERR_INVALID_ARG;
   if (!aligned(X, 16) || ldx % 8 || !aligned(codes, 16) || !aligned(scales, 2) ||
       !aligned(zeros, 4) || !aligned(Y, 2))
     return W4A16_ERR_MISALIGNED;
+  if (group != W4A16_GROUP && (!aligned(scales, 16) || !aligned(zeros, 16))) return W4A16_ERR_MISALIGNED;
   return W4A16_OK;
 }
 
@@ -77,26 +81,33 @@ const char* w4a16_strerror(int status) {
 
 namespace {
 int pack_checked(const uint16_t* W, int64_t N, int64_t K, int64_t ldw, const float* awq_s,
-                 uint32_t* codes, uint16_t* scales, int32_t* zeros, bool symmetric, void* stream) {
-  if (!W || !codes || !scales || !zeros) return W4A16_ERR_INVALID_ARG;
+                 int64_t group, uint32_t* codes, uint16_t* scales, int32_t* zeros, bool symmetric,
+                 void* stream) {
+  if (!W || !codes || !scales || !zeros || !group_ok(group)) return W4A16_ERR_INVALID_ARG;
   if (N < 1 || K < W4A16_GROUP || K % W4A16_GROUP || ldw < K) return W4A16_ERR_INVALID_ARG;
   if (N >= kMaxDim || K >= kMaxDim || N * (K / 8) >= ((int64_t)1 << 38)) return W4A16_ERR_UNSUPPORTED;
   if (!aligned(W, 2) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(zeros, 4) ||
       (awq_s && !aligned(awq_s, 4)))
     return W4A16_ERR_MISALIGNED;
-  return w4a16::launch_pack(W, N, K, ldw, awq_s, codes, scales, zeros, symmetric,
+  return w4a16::launch_pack(W, N, K, ldw, awq_s, (int)group, codes, scales, zeros, symmetric,
                             (hipStream_t)stream);
 }
 }  // namespace
 
 int w4a16_pack(const uint16_t* W, int64_t N, int64_t K, int64_t ldw, const float* awq_s,
                uint32_t* codes, uint16_t* scales, int32_t* zeros, void* stream) {
-  return pack_checked(W, N, K, ldw, awq_s, codes, scales, zeros, false, stream);
+  return pack_checked(W, N, K, ldw, awq_s, W4A16_GROUP, codes, scales, zeros, false, stream);
+}
+
+int w4a16_pack_grouped(const uint16_t* W, int64_t N, int64_t K, int64_t ldw, const float* awq_s,
+                       int64_t group, uint32_t* codes, uint16_t* scales, int32_t* zeros,
+                       void* stream) {
+  return pack_checked(W, N, K, ldw, awq_s, group, codes, scales, zeros, false, stream);
 }
 
 int w4a16_pack_symmetric(const uint16_t* W, int64_t N, int64_t K, int64_t ldw, const float* awq_s,
                          uint32_t* codes, uint16_t* scales, int32_t* zeros, void* stream) {
-  return pack_checked(W, N, K, ldw, awq_s, codes, scales, zeros, true, stream);
+  return pack_checked(W, N, K, ldw, awq_s, W4A16_GROUP, codes, scales, zeros, true, stream);
 }
 
 int w4a16_gemv(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
@@ -105,7 +116,18 @@ int w4a16_gemv(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
   int st = check_matmul(X, M, ldx, codes, scales, zeros, N, K, Y, ldy);
   if (st != W4A16_OK) return st;
   if (M > W4A16_GEMV_MAX_M) return W4A16_ERR_INVALID_ARG;
-  return w4a16::launch_gemv(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, (hipStream_t)stream);
+  return w4a16::launch_gemv(X, M, ldx, codes, scales, zeros, N, K, W4A16_GROUP, Y, ldy,
+                            (hipStream_t)stream);
+}
+
+int w4a16_gemv_grouped(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
+                       const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K,
+                       int64_t group, uint16_t* Y, int64_t ldy, void* stream) {
+  int st = check_matmul(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, group);
+  if (st != W4A16_OK) return st;
+  if (M > W4A16_GEMV_MAX_M) return W4A16_ERR_INVALID_ARG;
+  return w4a16::launch_gemv(X, M, ldx, codes, scales, zeros, N, K, (int)group, Y, ldy,
+                            (hipStream_t)stream);
 }
 
 int w4a16_gemm(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
@@ -113,7 +135,17 @@ int w4a16_gemm(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
                int64_t ldy, void* stream) {
   int st = check_matmul(X, M, ldx, codes, scales, zeros, N, K, Y, ldy);
   if (st != W4A16_OK) return st;
-  return w4a16::launch_gemm(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, (hipStream_t)stream);
+  return w4a16::launch_gemm(X, M, ldx, codes, scales, zeros, N, K, W4A16_GROUP, Y, ldy,
+                            (hipStream_t)stream);
+}
+
+int w4a16_gemm_grouped(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
+                       const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K,
+                       int64_t group, uint16_t* Y, int64_t ldy, void* stream) {
+  int st = check_matmul(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, group);
+  if (st != W4A16_OK) return st;
+  return w4a16::launch_gemm(X, M, ldx, codes, scales, zeros, N, K, (int)group, Y, ldy,
+                            (hipStream_t)stream);
 }
 
 int w4a16_awq_importance(const uint16_t* Xcal, int64_t T, int64_t K, int64_t ldx,

@@ -124,11 +124,16 @@ __device__ __forceinline__ void wait_step() {
   if (ST == 1 || ST == 2) wait_vmcnt<2 * C::X_LOADS + kGroupStart>(); else wait_vmcnt<2 * C::X_LOADS>();
 }
 
-template <class C>
+// GS: K steps per quantisation group (1, 2 or 4: groups of 32, 64 or 128
+// inputs).  Codes always move in blocks of 128 inputs (four steps); a block
+// holds kSteps / GS groups.
+template <class C, int GS>
 __device__ __forceinline__ void gemm_tile(
     const uint16_t* __restrict__ X, int M, int64_t ldx, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K,
     uint16_t* __restrict__ Y, int64_t ldy, int m_tiles, int n_tiles) {
+  static_assert(GS == 1 || GS == 2 || GS == 4, "groups of 32, 64 or 128 inputs");
+  constexpr int GPB = kSteps / GS;   // groups per 128-input block
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, MT = C::MT, NT = C::NT;
   constexpr int X_STAGE = C::X_STAGE, C_GROUP = C::C_GROUP;
   constexpr int X_LOADS = C::X_LOADS, C_LOADS = C::C_LOADS, XS_TILES = C::XS_TILES;
@@ -138,7 +143,10 @@ __device__ __forceinline__ void gemm_tile(
   // of the LDS reads.
   __shared__ __attribute__((aligned(4096))) uint8_t xs0[X_STAGE], xs1[X_STAGE], xs2[X_STAGE], xs3[X_STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t cg0[C_GROUP], cg1[C_GROUP];
-  __shared__ __attribute__((aligned(16))) float xsum_lds[BM];
+  // activation sums of a group, double-buffered by group parity (a group's
+  // sums are read after the barrier that follows their store, and the next
+  // store into the same buffer comes two groups later)
+  __shared__ __attribute__((aligned(16))) float xsum_lds[2][BM];
 
   // XCD-aware tile order: consecutive block ids land on different XCDs, so
   // give XCD x the contiguous run of tiles [x T/8, (x+1) T/8), N fastest.
@@ -153,7 +161,8 @@ __device__ __forceinline__ void gemm_tile(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int wm = wave % C::WAVES_M, wn = wave / C::WAVES_M;
   const int r16 = lane & 15, q = lane >> 4;
-  const int G = K / kGroup;
+  const int G = K / kGroup;           // 128-input blocks
+  const int GR = G * GPB;             // quantisation groups per row
   const int steps = kSteps * G;
 
   // ---- direct-to-LDS copies, addressed as a block-uniform base plus a
@@ -196,22 +205,42 @@ __device__ __forceinline__ void gemm_tile(
 
   // Scales and zero points: lane l of a wave fetches those of the wave's
   // column l (its WN = 64 columns, one per lane; clamped to N - 1), one
-  // load of each per group, as 32-bit byte offsets from a block-uniform
-  // base (the launcher checks the range) so the loads take a scalar base.
-  // The per-column factors are then moved to the lanes of the accumulator
+  // load of each per 128-input block (the block's GPB groups are adjacent
+  // in memory), as 32-bit byte offsets from a block-uniform base (the
+  // launcher checks the range) so the loads take a scalar base.  The
+  // per-column factors are then moved to the lanes of the accumulator
   // layout (column r16 + 16 nt) by lane permutes.
   static_assert(WN == 64, "one metadata column per lane");
-  const uint16_t* sblk = scales + (int64_t)n0 * G;
-  const int32_t* zblk = zeros + (int64_t)n0 * G;
-  auto ld_s = [&](uint32_t e) {
-    return (uint32_t)*reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(sblk) + e * 2u);
+  const uint16_t* sblk = scales + (int64_t)n0 * GR;
+  const int32_t* zblk = zeros + (int64_t)n0 * GR;
+  const uint32_t moff = (uint32_t)(min(n0 + wn * WN + lane, N - 1) - n0) * (uint32_t)GR;
+  // block b's scales of this lane's column, two per dword, and zero points
+  uint32_t s_cur[(GPB + 1) / 2], s_nxt[(GPB + 1) / 2];
+  int z_cur[GPB], z_nxt[GPB];
+  auto ld_meta = [&](int b) {
+    const uint32_t e = moff + (uint32_t)(b * GPB);
+    const char* sp = reinterpret_cast<const char*>(sblk) + e * 2u;
+    const char* zp = reinterpret_cast<const char*>(zblk) + e * 4u;
+    if constexpr (GPB == 1) {
+      s_nxt[0] = *reinterpret_cast<const uint16_t*>(sp);
+      z_nxt[0] = *reinterpret_cast<const int32_t*>(zp);
+    } else if constexpr (GPB == 2) {
+      s_nxt[0] = *reinterpret_cast<const uint32_t*>(sp);
+      const int2 z = *reinterpret_cast<const int2*>(zp);
+      z_nxt[0] = z.x;
+      z_nxt[1] = z.y;
+    } else {
+      const uint2 sv = *reinterpret_cast<const uint2*>(sp);
+      s_nxt[0] = sv.x;
+      s_nxt[1] = sv.y;
+      const int4 z = *reinterpret_cast<const int4*>(zp);
+      z_nxt[0] = z.x;
+      z_nxt[1] = z.y;
+      z_nxt[2] = z.z;
+      z_nxt[3] = z.w;
+    }
   };
-  auto ld_z = [&](uint32_t e) {
-    return *reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(zblk) + e * 4u);
-  };
-  const uint32_t moff = (uint32_t)(min(n0 + wn * WN + lane, N - 1) - n0) * (uint32_t)G;
-  uint32_t s_cur, s_nxt;
-  int z_cur, z_nxt;
+  auto scale_of = [](const uint32_t* sv, int i) { return (i & 1) ? (sv[i >> 1] >> 16) : (sv[i >> 1] & 0xFFFFu); };
 
   // LDS read offsets.  A: row (wm 128 + mt 16 + r16), chunk q (inputs
   // 8q .. 8q+7 of the step).  B: code row (wn 64 + nt 16 + r16), chunk =
@@ -237,13 +266,11 @@ __device__ __forceinline__ void gemm_tile(
 
   // fold a finished group into the accumulator: remove bias and zero point,
   // move to the next group's scale (or, after the last group, apply it)
-  auto group_end = [&](bool last) {
+  auto group_end = [&](uint32_t s_fin, int z_fin, uint32_t s_next, bool last, const float* xbuf) {
     // this lane's column: bias + zero point and the scale factor
-    const float zl = (float)(128 + z_cur);
-    const float sc = bf16_to_f32(s_cur);
-    const float rl = last ? sc : sc * __builtin_amdgcn_rcpf(bf16_to_f32(s_nxt));
-    s_cur = s_nxt;
-    z_cur = z_nxt;
+    const float zl = (float)(128 + z_fin);
+    const float sc = bf16_to_f32(s_fin);
+    const float rl = last ? sc : sc * __builtin_amdgcn_rcpf(bf16_to_f32(s_next));
     // n tile nt's column r16 + 16 nt sits in that lane
     float zb[NT], ratio[NT];
 #pragma unroll
@@ -254,7 +281,7 @@ __device__ __forceinline__ void gemm_tile(
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const f32x4 xs = *reinterpret_cast<const f32x4*>(&xsum_lds[wm * WM + rowt(mt) * 16 + 4 * q]);
+      const f32x4 xs = *reinterpret_cast<const f32x4*>(&xbuf[wm * WM + rowt(mt) * 16 + 4 * q]);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -292,10 +319,7 @@ __device__ __forceinline__ void gemm_tile(
 
   // prologue: group 0's scale/zero and codes, steps 0..3 of X in flight,
   // step 0's fragments in registers (steps >= 4)
-  s_cur = ld_s(moff);
-  z_cur = ld_z(moff);
-  s_nxt = s_cur;
-  z_nxt = z_cur;
+  ld_meta(0);   // block 0's, moved to the current set at step 0
   auto prologue = [&](uint8_t* cg_first) {   // group 0's code buffer
     copy_codes(cg_first, 0);
     copy_x(xs0, 0);
@@ -334,14 +358,24 @@ __device__ __forceinline__ void gemm_tile(
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) asm volatile("" : "+v"(bw[nt]));
     if (ST == 0) {
-      // the previous group's activation sums are in LDS: fold it in
-      if (s > 0) group_end(false);
-      // next group's scale/zero and codes (the last group's again after the
-      // last), issued before this step's X copies, as wait_step counts them
+      // the previous block's last group: its activation sums are in LDS
+      if (s > 0)
+        group_end(scale_of(s_cur, GPB - 1), z_cur[GPB - 1], scale_of(s_nxt, 0), false,
+                  xsum_lds[GS == kSteps ? GP ^ 1 : 1]);
+#pragma unroll
+      for (int i = 0; i < (GPB + 1) / 2; ++i) s_cur[i] = s_nxt[i];
+#pragma unroll
+      for (int i = 0; i < GPB; ++i) z_cur[i] = z_nxt[i];
+      // next block's scales/zeros and codes (the last block's again after
+      // the last), issued before this step's X copies, as wait_step counts
+      // them
       const int gn = min(g + 1, G - 1);
-      s_nxt = ld_s(moff + (uint32_t)gn);
-      z_nxt = ld_z(moff + (uint32_t)gn);
+      ld_meta(gn);
       copy_codes(cg_other, gn);
+    } else if (ST % GS == 0) {
+      // a group inside the block ends
+      constexpr int i = ST / GS;
+      group_end(scale_of(s_cur, i - 1), z_cur[i - 1], scale_of(s_cur, i), false, xsum_lds[(i - 1) & 1]);
     }
     copy_x(xs_here, min(s + 4, steps - 1));
 
@@ -349,7 +383,7 @@ __device__ __forceinline__ void gemm_tile(
     // first XS_TILES register row tiles
 #pragma unroll
     for (int i = 0; i < XS_TILES; ++i)
-      xpart[i] = mfma16x16x32(af[i], ones, ST == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : xpart[i]);
+      xpart[i] = mfma16x16x32(af[i], ones, ST % GS == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : xpart[i]);
     u32x4 b[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) b[nt] = codes_to_bias128_natural(bw[nt]);
@@ -364,15 +398,15 @@ __device__ __forceinline__ void gemm_tile(
       for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma16x16x32(a, b[nt], acc[mt][nt]);
       read_a(xs_next, mt);
     }
-    if (ST == kSteps - 1) {
-      // publish this wave's activation sums.  Every column of the ones
+    if (ST % GS == GS - 1) {
+      // publish this wave's activation sums of the group.  Every column of the ones
       // product holds the same sums, so all 16 lanes of a row group store
       // identical values to the same place; keeping the store outside any
       // lane-dependent branch keeps the matrix-core op that feeds it from
       // being moved under a partial exec mask.
 #pragma unroll
       for (int i = 0; i < XS_TILES; ++i)
-        *reinterpret_cast<f32x4*>(&xsum_lds[wm * WM + (wn * XS_TILES + i) * 16 + 4 * q]) = xpart[i];
+        *reinterpret_cast<f32x4*>(&xsum_lds[GS == kSteps ? GP : (ST / GS) & 1][wm * WM + (wn * XS_TILES + i) * 16 + 4 * q]) = xpart[i];
     }
   };
   auto group = [&](auto parity, int g) {
@@ -389,8 +423,8 @@ __device__ __forceinline__ void gemm_tile(
     group(Ic<1>{}, g + 1);
   }
   wait_vmcnt<0>();   // the clamped copies past the last step
-  __syncthreads();   // last group's activation sums
-  group_end(true);
+  __syncthreads();   // last group's activation sums (odd parity: see above)
+  group_end(scale_of(s_cur, GPB - 1), z_cur[GPB - 1], 0u, true, xsum_lds[1]);
 
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -406,40 +440,42 @@ __device__ __forceinline__ void gemm_tile(
     }
 }
 
-// One kernel per tile shape (non-template, so that the host side gets its
-// launch stub).
+// One kernel per tile shape, templated on the steps per group.
+template <int GS>
 __global__ __launch_bounds__(TileBig::kThreads) void gemm_kernel(
     const uint16_t* __restrict__ X, int M, int64_t ldx, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K,
     uint16_t* __restrict__ Y, int64_t ldy, int m_tiles, int n_tiles) {
-  gemm_tile<TileBig>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, m_tiles, n_tiles);
+  gemm_tile<TileBig, GS>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, m_tiles, n_tiles);
 }
 
 // three blocks per CU: the register budget of three waves per SIMD (without
 // it the compiler keeps the accumulators in AGPRs at one wave per SIMD)
+template <int GS>
 __global__ __launch_bounds__(TileSmall::kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void gemm_small_kernel(
     const uint16_t* __restrict__ X, int M, int64_t ldx, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K,
     uint16_t* __restrict__ Y, int64_t ldy, int m_tiles, int n_tiles) {
-  gemm_tile<TileSmall>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, m_tiles, n_tiles);
+  gemm_tile<TileSmall, GS>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, m_tiles, n_tiles);
 }
 
 // 64 x 128 tiles on two waves of 64 x 64, for layers whose 128 x 128 tiles
 // would still leave CUs idle (two waves per SIMD: at three the compiler
 // moves values into AGPRs)
+template <int GS>
 __global__ __launch_bounds__(TileTiny::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_tiny_kernel(
     const uint16_t* __restrict__ X, int M, int64_t ldx, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K,
     uint16_t* __restrict__ Y, int64_t ldy, int m_tiles, int n_tiles) {
-  gemm_tile<TileTiny>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, m_tiles, n_tiles);
+  gemm_tile<TileTiny, GS>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, m_tiles, n_tiles);
 }
 
 }  // namespace
 
 namespace {
-template <class C>
+template <class C, int GS>
 int launch_tiles(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
                  const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K, uint16_t* Y,
                  int64_t ldy, hipStream_t stream) {
@@ -448,35 +484,56 @@ int launch_tiles(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* code
   // per-lane 32-bit byte offsets within a tile's rows of X, of the codes and
   // of the zero points
   if ((C::BM - 1) * ldx * 2 + K * 2 >= ((int64_t)1 << 32) || C::BN * (K / 2) >= ((int64_t)1 << 32) ||
-      C::BN * (K / kGroup) * 4 >= ((int64_t)1 << 32))
+      C::BN * (K / (KS * GS)) * 4 >= ((int64_t)1 << 32))
     return 3;
-  auto kernel = C::BM == TileBig::BM ? gemm_kernel
-                : (C::BM == TileSmall::BM ? gemm_small_kernel : gemm_tiny_kernel);
-  hipLaunchKernelGGL(kernel, dim3((unsigned)(mt * nt)), dim3(C::kThreads), 0, stream, X,
-                     (int)M, ldx, codes, scales, zeros, (int)N, (int)K, Y, ldy, (int)mt, (int)nt);
+  const dim3 grid((unsigned)(mt * nt)), block(C::kThreads);
+  if constexpr (C::BM == TileBig::BM)
+    hipLaunchKernelGGL(gemm_kernel<GS>, grid, block, 0, stream, X, (int)M, ldx, codes, scales,
+                       zeros, (int)N, (int)K, Y, ldy, (int)mt, (int)nt);
+  else if constexpr (C::BM == TileSmall::BM)
+    hipLaunchKernelGGL(gemm_small_kernel<GS>, grid, block, 0, stream, X, (int)M, ldx, codes, scales,
+                       zeros, (int)N, (int)K, Y, ldy, (int)mt, (int)nt);
+  else
+    hipLaunchKernelGGL(gemm_tiny_kernel<GS>, grid, block, 0, stream, X, (int)M, ldx, codes, scales,
+                       zeros, (int)N, (int)K, Y, ldy, (int)mt, (int)nt);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 }  // namespace
 
-int launch_gemm(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
-                const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K, uint16_t* Y,
-                int64_t ldy, hipStream_t stream) {
-  // 256 x 256 tiles when there are at least three per four CUs.  On whole
-  // layers the 128 x 128 tiles run at ~560-610 TFLOP/s and the large ones at
-  // ~750-770, so smaller tiles win only when the large ones would leave a
-  // quarter of the CUs idle (at 192 large tiles the two are level).  Between
-  // 128 x 128 and 64 x 128 tiles the one whose block count fills the rounds
-  // of CUs better wins, ties to the larger tile (measured on the 8B-shaped
-  // layers, M = 512 .. 4096).
+namespace {
+// Groups of 128: 256 x 256 tiles when there are at least three per four
+// CUs.  On whole layers the 128 x 128 tiles run at ~560-610 TFLOP/s and the
+// large ones at ~750-770, so smaller tiles win only when the large ones would
+// leave a quarter of the CUs idle (at 192 large tiles the two are level).
+// Between 128 x 128 and 64 x 128 tiles the one whose block count fills the
+// rounds of CUs better wins, ties to the larger tile (measured on the
+// 8B-shaped layers, M = 512 .. 4096).
+int launch_gemm_g128(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
+                     const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K, uint16_t* Y,
+                     int64_t ldy, hipStream_t stream) {
   const int64_t cus = device_cu_count();
   auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   auto fill = [&](int64_t t) { return (double)t / (double)(((t + cus - 1) / cus) * cus); };
   const int64_t big = tiles(TileBig::BM, TileBig::BN);
   if (4 * big >= 3 * cus)
-    return launch_tiles<TileBig>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
+    return launch_tiles<TileBig, kSteps>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
   if (fill(tiles(TileTiny::BM, TileTiny::BN)) > fill(tiles(TileSmall::BM, TileSmall::BN)) + 1e-9)
-    return launch_tiles<TileTiny>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
-  return launch_tiles<TileSmall>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
+    return launch_tiles<TileTiny, kSteps>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
+  return launch_tiles<TileSmall, kSteps>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
+}
+}  // namespace
+
+// group: 32, 64 or 128 inputs per quantisation group (checked by the caller)
+int launch_gemm(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
+                const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K, int group,
+                uint16_t* Y, int64_t ldy, hipStream_t stream) {
+  // Groups of 32 or 64: a rescale every one or two steps; the larger tiles
+  // would spill their accumulators, so 64 x 128 tiles only.
+  if (group == 32)
+    return launch_tiles<TileTiny, 1>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
+  if (group == 64)
+    return launch_tiles<TileTiny, 2>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
+  return launch_gemm_g128(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
 }
 
 }  // namespace w4a16

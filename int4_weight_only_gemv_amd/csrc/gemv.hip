@@ -66,10 +66,15 @@ constexpr int kMaxSlices = 16;    // K <= 32768 on this kernel
 constexpr int pow2_at_least(int v) { return v <= 1 ? 1 : 2 * pow2_at_least((v + 1) / 2); }
 constexpr int log2_exact(int v) { return v <= 1 ? 0 : 1 + log2_exact(v / 2); }
 
-template <int M, int R, int NB>
+// PL: groups smaller than 128 inputs (lg = log2 of the group size, 5 or 6):
+// each lane folds scale and zero point into its own 32 products for all R
+// rows (the fold is linear, so a group split over lanes sums correctly)
+// before the cross-lane sums.  Otherwise lg = 7 and the four lanes of a
+// group are summed first and fold once.
+template <int M, int R, int NB, bool PL>
 __global__ __launch_bounds__(1024) void gemv_dot_kernel(
     const uint16_t* __restrict__ X, int64_t ldx, const uint32_t* __restrict__ codes,
-    const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K,
+    const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K, int lg,
     uint16_t* __restrict__ Y, int64_t ldy) {
   static_assert(R == 4, "a group spans 4 lanes; lane l corrects row l % 4 of its group");
   constexpr int RB = R * NB;                  // rows per block
@@ -83,24 +88,35 @@ __global__ __launch_bounds__(1024) void gemv_dot_kernel(
   const int k0 = wave * kSlice + lane * 32;
   const bool active = k0 < K;
   const int kc = active ? k0 : K - 32;        // inactive lanes read valid memory, weigh zero
-  const int G = K / kGroup;
-  const int g = kc >> 7;                      // this lane's group (lanes 4i .. 4i+3 share one)
+  const int G = K >> lg;
+  const int g = kc >> lg;                     // this lane's group (lanes 4i .. 4i+3 share one at 128)
   const int64_t wpr = K / 8;
 
   const int row0 = blockIdx.x * RB;
   const u32x4* cbase = reinterpret_cast<const u32x4*>(codes) + kc / 32;
   u32x4 cb[2][R];
-  uint32_t sb[2];   // scale and zero point of row (lane % 4), group g
-  int zb[2];
+  // scale and zero point of row (lane % 4), group g; with PL those of all
+  // R rows
+  uint32_t sb[2][PL ? R : 1];
+  int zb[2][PL ? R : 1];
   auto load = [&](int buf, int batch) {
 #pragma unroll
     for (int j = 0; j < R; ++j) {
       const int row = min(row0 + batch * R + j, N - 1);
       cb[buf][j] = __builtin_nontemporal_load(cbase + (int64_t)row * (wpr / 4));
     }
-    const int mrow = min(row0 + batch * R + (lane & 3), N - 1);
-    sb[buf] = scales[(int64_t)mrow * G + g];
-    zb[buf] = zeros[(int64_t)mrow * G + g];
+    if constexpr (PL) {
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        const int row = min(row0 + batch * R + j, N - 1);
+        sb[buf][j] = scales[(int64_t)row * G + g];
+        zb[buf][j] = zeros[(int64_t)row * G + g];
+      }
+    } else {
+      const int mrow = min(row0 + batch * R + (lane & 3), N - 1);
+      sb[buf][0] = scales[(int64_t)mrow * G + g];
+      zb[buf][0] = zeros[(int64_t)mrow * G + g];
+    }
   };
 
   load(0, 0);  // the weight stream first: it is the long-latency path
@@ -108,7 +124,7 @@ __global__ __launch_bounds__(1024) void gemv_dot_kernel(
   // this lane's 32 activations of every batch row, paired like the codes,
   // and the activation sums of its group
   u32x4 xp[M][4];
-  float xsg[M];
+  float xsg[M];   // activation sums of the lane's group (with PL: of its own 32 inputs)
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     const u32x4* xr = reinterpret_cast<const u32x4*>(X + m * ldx + kc);
@@ -121,8 +137,12 @@ __global__ __launch_bounds__(1024) void gemv_dot_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) sum = dot2(raw[j], kOnePair, sum);
     }
-    sum += __shfl_xor(sum, 1);
-    xsg[m] = sum + __shfl_xor(sum, 2);
+    if constexpr (PL) {
+      xsg[m] = sum;
+    } else {
+      sum += __shfl_xor(sum, 1);
+      xsg[m] = sum + __shfl_xor(sum, 2);
+    }
   }
 
 #pragma unroll
@@ -143,6 +163,12 @@ __global__ __launch_bounds__(1024) void gemv_dot_kernel(
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) P[j][m] = dot2(b[jj], xp[m][i][jj], P[j][m]);
       }
+      if constexpr (PL) {
+        const float s = bf16_to_f32(sb[cur][j]);
+        const float zb128 = (float)(128 + zb[cur][j]);
+#pragma unroll
+        for (int m = 0; m < M; ++m) P[j][m] = s * fmaf(-zb128, xsg[m], P[j][m]);
+      }
     }
     // Sum over the 4 lanes of the group with a halving butterfly (lane bit 1
     // picks rows {0,1} or {2,3}, bit 0 one of those), so that lane l ends
@@ -162,15 +188,16 @@ __global__ __launch_bounds__(1024) void gemv_dot_kernel(
     float part[MP];
     {
       const uint32_t up = (lane & 1) ? ~0u : 0u;
-      const float s = bf16_to_f32(sb[cur]);
-      const float zb128 = (float)(128 + zb[cur]);
+      const float s = bf16_to_f32(sb[cur][0]);
+      const float zb128 = (float)(128 + zb[cur][0]);
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         const float send = pick(up, h[0][m], h[1][m]);
         const float keep = pick(up, h[1][m], h[0][m]);
         const float q = keep + __shfl_xor(send, 1);
         // ... and removes the bias and zero point of that (row, group) once
-        part[m] = s * fmaf(-zb128, xsg[m], q);
+        // (already done per lane with PL)
+        part[m] = PL ? q : s * fmaf(-zb128, xsg[m], q);
       }
 #pragma unroll
       for (int m = M; m < MP; ++m) part[m] = 0.f;
@@ -247,7 +274,7 @@ __device__ __forceinline__ f32x4 mfma4x4x4(uint32_t a0, uint32_t a1, uint32_t b0
 template <int M, int T, int NB>
 __global__ __launch_bounds__(1024) void gemv_quad_kernel(
     const uint16_t* __restrict__ X, int Mrt, int64_t ldx, const uint32_t* __restrict__ codes,
-    const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K,
+    const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K, int lg,
     uint16_t* __restrict__ Y, int64_t ldy) {
   constexpr int MS = (M + 3) / 4;             // activation row sets of four
   constexpr int MP = pow2_at_least(M);        // values per lane in the halving butterfly
@@ -260,7 +287,7 @@ __global__ __launch_bounds__(1024) void gemv_quad_kernel(
   const int S = blockDim.x >> 6;
   const int bq = lane >> 2;                   // block of the 4x4 products: 32 inputs
   const int j = lane & 3;                     // weight row (B column) / activation row (A row)
-  const int G = K / kGroup;
+  const int G = K >> lg;                      // groups of 2^lg inputs (32, 64 or 128)
   const int64_t vpr = K / 32;                 // 16-byte vectors per code row
 
   int kc[T], g[T];
@@ -270,7 +297,7 @@ __global__ __launch_bounds__(1024) void gemv_quad_kernel(
     const int k = (wave * T + t) * kQuadSlice + 32 * bq;
     act[t] = k < K;
     kc[t] = act[t] ? k : K - 32;              // inactive lanes read valid memory, weigh zero
-    g[t] = kc[t] >> 7;
+    g[t] = kc[t] >> lg;                       // a block of 32 inputs lies in one group
   }
   const int row0 = blockIdx.x * NB * 4;
   const u32x4* cbase = reinterpret_cast<const u32x4*>(codes);
@@ -387,7 +414,7 @@ __global__ __launch_bounds__(1024) void gemv_quad_kernel(
 template <int M, int NB>
 __global__ __launch_bounds__(1024) void gemv_quad_long_kernel(
     const uint16_t* __restrict__ X, int Mrt, int64_t ldx, const uint32_t* __restrict__ codes,
-    const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K,
+    const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K, int lg,
     uint16_t* __restrict__ Y, int64_t ldy) {
   static_assert(NB % 2 == 0, "even batch count");
   constexpr int MS = (M + 3) / 4;
@@ -401,7 +428,7 @@ __global__ __launch_bounds__(1024) void gemv_quad_long_kernel(
   const int S = blockDim.x >> 6;
   const int bq = lane >> 2;
   const int j = lane & 3;
-  const int G = K / kGroup;
+  const int G = K >> lg;
   const int64_t vpr = K / 32;
   const int slices = (K + kQuadSlice - 1) / kQuadSlice;
   const int row0 = blockIdx.x * NB * 4;
@@ -427,8 +454,8 @@ __global__ __launch_bounds__(1024) void gemv_quad_long_kernel(
       const int kc = lane_k(t, act);
       const int row = min(row0 + nb * 4 + j, N - 1);
       cb[buf] = __builtin_nontemporal_load(cbase + (int64_t)row * vpr + kc / 32);
-      sb[buf] = scales[(int64_t)row * G + (kc >> 7)];
-      zb[buf] = zeros[(int64_t)row * G + (kc >> 7)];
+      sb[buf] = scales[(int64_t)row * G + (kc >> lg)];
+      zb[buf] = zeros[(int64_t)row * G + (kc >> lg)];
     };
     load(0, 0, wave);
     for (int t = wave; t < slices; t += S) {
@@ -681,18 +708,20 @@ constexpr int kDotMaxM = 4;
 
 int cu_count() { return device_cu_count(); }
 
-template <int M, int NB>
+template <int M, int NB, bool PL>
 void launch_dot_nb(const uint16_t* X, int64_t ldx, const uint32_t* codes, const uint16_t* scales,
-                   const int32_t* zeros, int N, int K, uint16_t* Y, int64_t ldy, hipStream_t stream) {
+                   const int32_t* zeros, int N, int K, int lg, uint16_t* Y, int64_t ldy,
+                   hipStream_t stream) {
   constexpr int R = 4;
   const int S = (K + kSlice - 1) / kSlice;
-  hipLaunchKernelGGL((gemv_dot_kernel<M, R, NB>), dim3((unsigned)((N + R * NB - 1) / (R * NB))),
-                     dim3(S * kWave), 0, stream, X, ldx, codes, scales, zeros, N, K, Y, ldy);
+  hipLaunchKernelGGL((gemv_dot_kernel<M, R, NB, PL>), dim3((unsigned)((N + R * NB - 1) / (R * NB))),
+                     dim3(S * kWave), 0, stream, X, ldx, codes, scales, zeros, N, K, lg, Y, ldy);
 }
 
-template <int M>
+template <int M, bool PL>
 void launch_dot(const uint16_t* X, int64_t ldx, const uint32_t* codes, const uint16_t* scales,
-                const int32_t* zeros, int N, int K, uint16_t* Y, int64_t ldy, hipStream_t stream) {
+                const int32_t* zeros, int N, int K, int lg, uint16_t* Y, int64_t ldy,
+                hipStream_t stream) {
   // Rows per block: R = 4 rows per batch, NB batches, the next batch's loads
   // in flight while the current one is reduced.  Per-wave timelines on the
   // box show that a CU's share of the bandwidth does not grow with the
@@ -726,29 +755,29 @@ void launch_dot(const uint16_t* X, int64_t ldx, const uint32_t* codes, const uin
   switch (nb) {
 #define W4A16_DOT(V)                                                                   \
   case V:                                                                              \
-    launch_dot_nb<M, (V <= kMaxNB ? V : kMaxNB)>(X, ldx, codes, scales, zeros, N, K, Y, ldy, stream); \
+    launch_dot_nb<M, (V <= kMaxNB ? V : kMaxNB), PL>(X, ldx, codes, scales, zeros, N, K, lg, Y, ldy, stream); \
     break;
     W4A16_DOT(8) W4A16_DOT(7) W4A16_DOT(6) W4A16_DOT(5) W4A16_DOT(4) W4A16_DOT(3) W4A16_DOT(2)
 #undef W4A16_DOT
     default:
-      launch_dot_nb<M, 1>(X, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
+      launch_dot_nb<M, 1, PL>(X, ldx, codes, scales, zeros, N, K, lg, Y, ldy, stream);
   }
 }
 
 
 template <int M, int T, int NB>
 void launch_quad_nb(const uint16_t* X, int Mrt, int64_t ldx, const uint32_t* codes,
-                    const uint16_t* scales, const int32_t* zeros, int N, int K, uint16_t* Y,
+                    const uint16_t* scales, const int32_t* zeros, int N, int K, int lg, uint16_t* Y,
                     int64_t ldy, hipStream_t stream) {
   const int slices = (K + kQuadSlice - 1) / kQuadSlice;
   const int S = (slices + T - 1) / T;
   hipLaunchKernelGGL((gemv_quad_kernel<M, T, NB>), dim3((unsigned)((N + 4 * NB - 1) / (4 * NB))),
-                     dim3(S * kWave), 0, stream, X, Mrt, ldx, codes, scales, zeros, N, K, Y, ldy);
+                     dim3(S * kWave), 0, stream, X, Mrt, ldx, codes, scales, zeros, N, K, lg, Y, ldy);
 }
 
 template <int M, int T>
 void launch_quad_t(const uint16_t* X, int Mrt, int64_t ldx, const uint32_t* codes,
-                   const uint16_t* scales, const int32_t* zeros, int N, int K, uint16_t* Y,
+                   const uint16_t* scales, const int32_t* zeros, int N, int K, int lg, uint16_t* Y,
                    int64_t ldy, hipStream_t stream) {
   // Rows per block: 4 x NB.  The largest NB (at most 8) whose block count
   // fills the CUs evenly; fitted to timings of the decode layers of the 8B-
@@ -769,22 +798,22 @@ void launch_quad_t(const uint16_t* X, int Mrt, int64_t ldx, const uint32_t* code
   switch (nb) {
 #define W4A16_QUAD(V)                                                                     \
   case V:                                                                                 \
-    launch_quad_nb<M, T, V>(X, Mrt, ldx, codes, scales, zeros, N, K, Y, ldy, stream);    \
+    launch_quad_nb<M, T, V>(X, Mrt, ldx, codes, scales, zeros, N, K, lg, Y, ldy, stream); \
     break;
     W4A16_QUAD(8) W4A16_QUAD(7) W4A16_QUAD(6) W4A16_QUAD(5) W4A16_QUAD(4) W4A16_QUAD(3)
     W4A16_QUAD(2)
 #undef W4A16_QUAD
     default:
-      launch_quad_nb<M, T, 1>(X, Mrt, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
+      launch_quad_nb<M, T, 1>(X, Mrt, ldx, codes, scales, zeros, N, K, lg, Y, ldy, stream);
   }
 }
 
 template <int M, int NB>
 void launch_quad_long_nb(const uint16_t* X, int Mrt, int64_t ldx, const uint32_t* codes,
-                         const uint16_t* scales, const int32_t* zeros, int N, int K, uint16_t* Y,
-                         int64_t ldy, int S, hipStream_t stream) {
+                         const uint16_t* scales, const int32_t* zeros, int N, int K, int lg,
+                         uint16_t* Y, int64_t ldy, int S, hipStream_t stream) {
   hipLaunchKernelGGL((gemv_quad_long_kernel<M, NB>), dim3((unsigned)((N + 4 * NB - 1) / (4 * NB))),
-                     dim3(S * kWave), 0, stream, X, Mrt, ldx, codes, scales, zeros, N, K, Y, ldy);
+                     dim3(S * kWave), 0, stream, X, Mrt, ldx, codes, scales, zeros, N, K, lg, Y, ldy);
 }
 
 // Long rows: S = 16 waves (one block per CU) or 8 (two), NB = the fewest
@@ -794,7 +823,7 @@ void launch_quad_long_nb(const uint16_t* X, int Mrt, int64_t ldx, const uint32_t
 // layer: the caller takes another kernel).
 template <int M>
 bool launch_quad_long(const uint16_t* X, int Mrt, int64_t ldx, const uint32_t* codes,
-                      const uint16_t* scales, const int32_t* zeros, int N, int K, uint16_t* Y,
+                      const uint16_t* scales, const int32_t* zeros, int N, int K, int lg, uint16_t* Y,
                       int64_t ldy, hipStream_t stream, bool need) {
   constexpr int kMaxNB = M <= 4 ? 8 : 4;   // more rows of accumulators would spill
   const int cus = cu_count();
@@ -813,7 +842,7 @@ bool launch_quad_long(const uint16_t* X, int Mrt, int64_t ldx, const uint32_t* c
 #define W4A16_QL(V)                                                                           \
   case V:                                                                                     \
     launch_quad_long_nb<M, (V <= kMaxNB ? V : kMaxNB)>(X, Mrt, ldx, codes, scales, zeros, N, K, \
-                                                       Y, ldy, S, stream);                    \
+                                                       lg, Y, ldy, S, stream);                \
     break;
     W4A16_QL(2) W4A16_QL(4) W4A16_QL(6) W4A16_QL(8)
   }
@@ -825,42 +854,74 @@ bool launch_quad_long(const uint16_t* X, int Mrt, int64_t ldx, const uint32_t* c
 // waves, two slices per wave beyond that
 template <int M>
 void launch_quad(const uint16_t* X, int Mrt, int64_t ldx, const uint32_t* codes,
-                 const uint16_t* scales, const int32_t* zeros, int N, int K, uint16_t* Y,
+                 const uint16_t* scales, const int32_t* zeros, int N, int K, int lg, uint16_t* Y,
                  int64_t ldy, hipStream_t stream) {
   const int slices = (K + kQuadSlice - 1) / kQuadSlice;
   if (slices <= kQuadMaxWaves)
-    launch_quad_t<M, 1>(X, Mrt, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
+    launch_quad_t<M, 1>(X, Mrt, ldx, codes, scales, zeros, N, K, lg, Y, ldy, stream);
   else
-    launch_quad_t<M, 2>(X, Mrt, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
+    launch_quad_t<M, 2>(X, Mrt, ldx, codes, scales, zeros, N, K, lg, Y, ldy, stream);
 }
 
 }  // namespace
 
+int launch_gemm(const uint16_t*, int64_t, int64_t, const uint32_t*, const uint16_t*, const int32_t*,
+                int64_t, int64_t, int, uint16_t*, int64_t, hipStream_t);
+
+namespace {
+// Groups of 32 or 64 inputs (lg = 5, 6): the per-lane fold of gemv_dot for
+// M <= 2, the 32-input blocks of the quad kernels (one group per block at
+// any size) up to M = 8, and the prefill kernel above.
+int launch_gemv_small_groups(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
+                             const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K,
+                             int lg, uint16_t* Y, int64_t ldy, hipStream_t stream) {
+  const int n = (int)N, k = (int)K, m = (int)M;
+  if (M <= 2 && K <= (int64_t)kSlice * kMaxSlices) {
+    if (M == 1) launch_dot<1, true>(X, ldx, codes, scales, zeros, n, k, lg, Y, ldy, stream);
+    else launch_dot<2, true>(X, ldx, codes, scales, zeros, n, k, lg, Y, ldy, stream);
+  } else if (M <= 8 && K <= (int64_t)2 * kQuadSlice * kQuadMaxWaves) {
+    if (M <= 4) launch_quad<4>(X, m, ldx, codes, scales, zeros, n, k, lg, Y, ldy, stream);
+    else launch_quad<8>(X, m, ldx, codes, scales, zeros, n, k, lg, Y, ldy, stream);
+  } else if (M <= 8) {
+    if (M <= 4) launch_quad_long<4>(X, m, ldx, codes, scales, zeros, n, k, lg, Y, ldy, stream, true);
+    else launch_quad_long<8>(X, m, ldx, codes, scales, zeros, n, k, lg, Y, ldy, stream, true);
+  } else {
+    return launch_gemm(X, M, ldx, codes, scales, zeros, N, K, 1 << lg, Y, ldy, stream);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+}  // namespace
+
+// group: 32, 64 or 128 inputs per quantisation group (checked by the caller)
 int launch_gemv(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
-                const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K, uint16_t* Y,
-                int64_t ldy, hipStream_t stream) {
+                const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K, int group,
+                uint16_t* Y, int64_t ldy, hipStream_t stream) {
+  if (group != kGroup)
+    return launch_gemv_small_groups(X, M, ldx, codes, scales, zeros, N, K, group == 32 ? 5 : 6, Y,
+                                    ldy, stream);
+  constexpr int lg = 7;
   if (M >= 3 && M <= 8 && K <= (int64_t)2 * kQuadSlice * kQuadMaxWaves) {
     if (M <= 4)
-      launch_quad<4>(X, (int)M, ldx, codes, scales, zeros, (int)N, (int)K, Y, ldy, stream);
+      launch_quad<4>(X, (int)M, ldx, codes, scales, zeros, (int)N, (int)K, lg, Y, ldy, stream);
     else
-      launch_quad<8>(X, (int)M, ldx, codes, scales, zeros, (int)N, (int)K, Y, ldy, stream);
+      launch_quad<8>(X, (int)M, ldx, codes, scales, zeros, (int)N, (int)K, lg, Y, ldy, stream);
     return hipGetLastError() == hipSuccess ? 0 : 4;
   }
   if (M >= 3 && M <= 8) {
     const bool done =
-        M <= 4 ? launch_quad_long<4>(X, (int)M, ldx, codes, scales, zeros, (int)N, (int)K, Y, ldy,
-                                     stream, false)
-               : launch_quad_long<8>(X, (int)M, ldx, codes, scales, zeros, (int)N, (int)K, Y, ldy,
-                                     stream, true);
+        M <= 4 ? launch_quad_long<4>(X, (int)M, ldx, codes, scales, zeros, (int)N, (int)K, lg, Y,
+                                     ldy, stream, false)
+               : launch_quad_long<8>(X, (int)M, ldx, codes, scales, zeros, (int)N, (int)K, lg, Y,
+                                     ldy, stream, true);
     if (done) return hipGetLastError() == hipSuccess ? 0 : 4;
   }
   if (M <= kDotMaxM && K <= (int64_t)kSlice * kMaxSlices) {
     const int n = (int)N, k = (int)K;
     switch (M) {
-      case 1: launch_dot<1>(X, ldx, codes, scales, zeros, n, k, Y, ldy, stream); break;
-      case 2: launch_dot<2>(X, ldx, codes, scales, zeros, n, k, Y, ldy, stream); break;
-      case 3: launch_dot<3>(X, ldx, codes, scales, zeros, n, k, Y, ldy, stream); break;
-      default: launch_dot<4>(X, ldx, codes, scales, zeros, n, k, Y, ldy, stream); break;
+      case 1: launch_dot<1, false>(X, ldx, codes, scales, zeros, n, k, lg, Y, ldy, stream); break;
+      case 2: launch_dot<2, false>(X, ldx, codes, scales, zeros, n, k, lg, Y, ldy, stream); break;
+      case 3: launch_dot<3, false>(X, ldx, codes, scales, zeros, n, k, lg, Y, ldy, stream); break;
+      default: launch_dot<4, false>(X, ldx, codes, scales, zeros, n, k, lg, Y, ldy, stream); break;
     }
     return hipGetLastError() == hipSuccess ? 0 : 4;
   }

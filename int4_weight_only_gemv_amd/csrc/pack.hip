@@ -10,8 +10,9 @@
 // correctly rounded division so that every step is a single IEEE operation.
 //
 // Mapping: one lane per output word (8 consecutive k of one row); the 16
-// lanes of an aligned 16-lane segment cover one group of 128, so the group
-// min/max is a 4-step butterfly inside the segment.
+// lanes of an aligned 16-lane segment cover one group of 128 (8 or 4 lanes a
+// group of 64 or 32), so the group min/max is a butterfly inside the
+// segment.
 
 #include "common.h"
 
@@ -20,14 +21,13 @@ namespace {
 
 constexpr float kFltMin = 1.17549435e-38f;  // 2^-126
 
-__device__ __forceinline__ float seg16_min(float v) {
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) v = fminf(v, __shfl_xor(v, off, 16));
+// min / max over an aligned segment of `seg` lanes (4, 8 or 16)
+__device__ __forceinline__ float seg_min(float v, int seg) {
+  for (int off = seg >> 1; off >= 1; off >>= 1) v = fminf(v, __shfl_xor(v, off, 16));
   return v;
 }
-__device__ __forceinline__ float seg16_max(float v) {
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 16));
+__device__ __forceinline__ float seg_max(float v, int seg) {
+  for (int off = seg >> 1; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 16));
   return v;
 }
 
@@ -38,11 +38,11 @@ __device__ __forceinline__ float bf16_rtz(float f) {
 template <bool kVecLoad, bool kAwq, bool kSym>
 __global__ __launch_bounds__(256) void pack_kernel(
     const uint16_t* __restrict__ W, int64_t ldw, const float* __restrict__ awq_s,
-    int64_t words_per_row, int64_t total_words, uint32_t* __restrict__ codes,
+    int64_t words_per_row, int64_t total_words, int seg, uint32_t* __restrict__ codes,
     uint16_t* __restrict__ scales, int32_t* __restrict__ zeros) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  // Every lane of a live 16-lane segment takes part in the shuffles; segments
-  // are whole because words_per_row is a multiple of 16.
+  // Every lane of a live segment takes part in the shuffles; segments are
+  // whole because words_per_row is a multiple of 16.
   const bool live = t < total_words;
   const int64_t tw = live ? t : total_words - 1;
   const int64_t n = tw / words_per_row;
@@ -72,8 +72,8 @@ __global__ __launch_bounds__(256) void pack_kernel(
   float mn = w[0], mx = w[0];
 #pragma unroll
   for (int j = 1; j < 8; ++j) { mn = fminf(mn, w[j]); mx = fmaxf(mx, w[j]); }
-  mn = seg16_min(mn);
-  mx = seg16_max(mx);
+  mn = seg_min(mn, seg);
+  mx = seg_max(mx, seg);
 
   float s;
   int z;
@@ -106,8 +106,8 @@ __global__ __launch_bounds__(256) void pack_kernel(
   }
   if (live) {
     codes[t] = word;
-    if ((wi & 15) == 0) {
-      const int64_t gi = n * (words_per_row / 16) + wi / 16;
+    if ((wi & (seg - 1)) == 0) {
+      const int64_t gi = n * (words_per_row / seg) + wi / seg;
       scales[gi] = (uint16_t)(__float_as_uint(s) >> 16);
       zeros[gi] = z;
     }
@@ -119,38 +119,40 @@ __global__ __launch_bounds__(256) void pack_kernel(
 namespace {
 template <bool kSym>
 void launch_pack_t(const uint16_t* W, int64_t ldw, const float* awq_s, int64_t words_per_row,
-                   int64_t total, uint32_t* codes, uint16_t* scales, int32_t* zeros, bool vec,
-                   hipStream_t stream) {
+                   int64_t total, int seg, uint32_t* codes, uint16_t* scales, int32_t* zeros,
+                   bool vec, hipStream_t stream) {
   const int threads = 256;
   const dim3 grid((unsigned)((total + threads - 1) / threads));
   if (vec) {
     if (awq_s)
       hipLaunchKernelGGL((pack_kernel<true, true, kSym>), grid, dim3(threads), 0, stream, W, ldw,
-                         awq_s, words_per_row, total, codes, scales, zeros);
+                         awq_s, words_per_row, total, seg, codes, scales, zeros);
     else
       hipLaunchKernelGGL((pack_kernel<true, false, kSym>), grid, dim3(threads), 0, stream, W, ldw,
-                         awq_s, words_per_row, total, codes, scales, zeros);
+                         awq_s, words_per_row, total, seg, codes, scales, zeros);
   } else {
     if (awq_s)
       hipLaunchKernelGGL((pack_kernel<false, true, kSym>), grid, dim3(threads), 0, stream, W, ldw,
-                         awq_s, words_per_row, total, codes, scales, zeros);
+                         awq_s, words_per_row, total, seg, codes, scales, zeros);
     else
       hipLaunchKernelGGL((pack_kernel<false, false, kSym>), grid, dim3(threads), 0, stream, W, ldw,
-                         awq_s, words_per_row, total, codes, scales, zeros);
+                         awq_s, words_per_row, total, seg, codes, scales, zeros);
   }
 }
 }  // namespace
 
+// group: 32, 64 or 128 inputs per quantisation group (checked by the caller)
 int launch_pack(const uint16_t* W, int64_t N, int64_t K, int64_t ldw, const float* awq_s,
-                uint32_t* codes, uint16_t* scales, int32_t* zeros, bool symmetric,
+                int group, uint32_t* codes, uint16_t* scales, int32_t* zeros, bool symmetric,
                 hipStream_t stream) {
   const int64_t words_per_row = K / 8;
   const int64_t total = N * words_per_row;
+  const int seg = group / 8;
   const bool vec = ((reinterpret_cast<uintptr_t>(W) & 15u) == 0) && (ldw % 8 == 0);
   if (symmetric)
-    launch_pack_t<true>(W, ldw, awq_s, words_per_row, total, codes, scales, zeros, vec, stream);
+    launch_pack_t<true>(W, ldw, awq_s, words_per_row, total, seg, codes, scales, zeros, vec, stream);
   else
-    launch_pack_t<false>(W, ldw, awq_s, words_per_row, total, codes, scales, zeros, vec, stream);
+    launch_pack_t<false>(W, ldw, awq_s, words_per_row, total, seg, codes, scales, zeros, vec, stream);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 

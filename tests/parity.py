@@ -24,12 +24,12 @@ def i32(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().contiguous().numpy().astype(np.int32)
 
 
-def assert_pack_equal(p, W_bits, rows=None, awq_s=None):
+def assert_pack_equal(p, W_bits, rows=None, awq_s=None, group=128):
     """Packed output of the library equals the oracle's bit for bit (on the
     given rows, or all rows)."""
     if rows is None:
         rows = np.arange(W_bits.shape[0])
-    codes, scales, zeros = O.quantize_pack(W_bits[rows], awq_s)
+    codes, scales, zeros = O.quantize_pack(W_bits[rows], awq_s, group)
     g_codes = u32(p.codes)[rows]
     g_scales = gen.bits(p.scales)[rows]
     g_zeros = i32(p.zeros)[rows]
@@ -41,11 +41,11 @@ def assert_pack_equal(p, W_bits, rows=None, awq_s=None):
                                  f"gpu {a[r, c]:#x} oracle {b[r, c]:#x}")
 
 
-def reference(X_bits, W_bits, rows=None, awq_s=None):
+def reference(X_bits, W_bits, rows=None, awq_s=None, group=128):
     """Oracle output Y_ref [M][len(rows)] and sum_k |x w_hat| for the bound."""
     if rows is None:
         rows = np.arange(W_bits.shape[0])
-    codes, scales, zeros = O.quantize_pack(W_bits[rows], awq_s)
+    codes, scales, zeros = O.quantize_pack(W_bits[rows], awq_s, group)
     y_ref = O.matmul_ref(X_bits, codes, scales, zeros)
     w_hat = O.dequantize(codes, scales, zeros)
     x = O.bf16_to_f32(X_bits).astype(np.float64)

@@ -27,7 +27,8 @@ def test_header_declares_expected_entry_points():
     assert header_functions() == sorted([
         "w4a16_abi_version", "w4a16_strerror", "w4a16_pack", "w4a16_gemv", "w4a16_gemm",
         "w4a16_awq_importance", "w4a16_awq_scale", "w4a16_awq_fold", "w4a16_scale_channels",
-        "w4a16_dequantize_bf16", "w4a16_dense_gemv", "w4a16_dense_gemm", "w4a16_pack_symmetric"])
+        "w4a16_dequantize_bf16", "w4a16_dense_gemv", "w4a16_dense_gemm", "w4a16_pack_symmetric",
+        "w4a16_pack_grouped", "w4a16_gemv_grouped", "w4a16_gemm_grouped"])
 
 
 def test_every_declared_symbol_is_exported():
@@ -41,7 +42,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strerror():
-    assert lib.w4a16_abi_version() == 3
+    assert lib.w4a16_abi_version() == 4
     for st in range(5):
         assert lib.w4a16_strerror(st)
     assert b"unknown" in lib.w4a16_strerror(99)
@@ -174,4 +175,33 @@ def test_dequantize_validation():
     assert call(zeros=FAKE + 2) == MISALIGNED
     assert call(W=FAKE + 2) == MISALIGNED
     assert call(ldw=260) == MISALIGNED
+    assert call(N=1 << 30) == UNSUPPORTED
+
+
+@pytest.mark.parametrize("fn", ["w4a16_gemv_grouped", "w4a16_gemm_grouped"])
+def test_grouped_matmul_validation(fn):
+    f = getattr(lib, fn)
+
+    def call(group=64, X=FAKE, M=1, ldx=4096, codes=FAKE, scales=FAKE, zeros=FAKE, N=4096, K=4096,
+             Y=FAKE, ldy=4096):
+        return f(p(X), M, ldx, p(codes), p(scales), p(zeros), N, K, group, p(Y), ldy, p(0))
+    for g in (0, 16, 96, 256, -64):
+        assert call(group=g) == INVALID
+    assert call(K=4000, ldx=4000) == INVALID              # K % 128 for every group
+    assert call(X=0) == INVALID
+    assert call(scales=FAKE + 8) == MISALIGNED            # 16-byte rule below 128
+    assert call(zeros=FAKE + 4) == MISALIGNED
+    assert call(group=128, scales=FAKE + 8, zeros=FAKE + 4, M=0) == INVALID
+    assert call(N=1 << 30, ldy=1 << 30) == UNSUPPORTED
+
+
+def test_grouped_pack_validation():
+    f = lib.w4a16_pack_grouped
+
+    def call(group=32, W=FAKE, N=16, K=256, ldw=256, c=FAKE, sc=FAKE, z=FAKE):
+        return f(p(W), N, K, ldw, p(0), group, p(c), p(sc), p(z), p(0))
+    for g in (0, 8, 48, 256):
+        assert call(group=g) == INVALID
+    assert call(K=96, ldw=96) == INVALID
+    assert call(c=FAKE + 8) == MISALIGNED
     assert call(N=1 << 30) == UNSUPPORTED
