@@ -543,6 +543,53 @@ def comparisons(workload, fused_ms_per_step, fused_prefill, dev, stream, steps=4
             del W, X, yd, yq
     out["quantisation_error_vs_dense"] = {"M": Mq, "layers": errs}
 
+    # quantisation groups of 32 / 64 / 128 inputs: decode step (M=1, same
+    # protocol as the headline), prefill at prefill_m, and the output error
+    # against the dense BF16 layer
+    groups = []
+    for group in (32, 64, 128):
+        gpk = [w4.w4a16_pack(w, group=group) for w in dense]
+        gset = sum(p.nbytes() for p in gpk)
+        gcopy = max(2, math.ceil(ROTATE_BYTES / gset))
+        gcopies = [gpk] + [[w4.PackedLinear(p.codes.clone(), p.scales.clone(), p.zeros.clone())
+                            for p in gpk] for _ in range(gcopy - 1)]
+        gxs = [gen.activations(1, L.K, workload, L.name, device=dev) for L in layers]
+        gys = [torch.empty(1, L.N, dtype=torch.bfloat16, device=dev) for L in layers]
+
+        def group_step(s, gcopies=gcopies, gxs=gxs, gys=gys):
+            for p, x, y in zip(gcopies[s % len(gcopies)], gxs, gys):
+                w4.w4a16_gemv(x, p, y)
+        us = _graph_us(stream, group_step, steps)
+        step_bytes = gset + sum(2 * (L.K + L.N) for L in layers)
+        row = {"group": group, "bits_per_weight": round(8.0 * gset / sum(L.N * L.K for L in layers), 3),
+               "decode_M1_us_per_step": round(us, 3),
+               "decode_M1_GBps": round(step_bytes / (us * 1e-6) / 1e9, 1)}
+        del gcopies, gxs, gys
+        torch.cuda.synchronize()
+        if fused_prefill is not None:
+            t = []
+            for L, p in zip(layers, gpk):
+                x = gen.activations(prefill_m, L.K, "llama8b_prefill", L.name, device=dev)
+                y = torch.empty(prefill_m, L.N, dtype=torch.bfloat16, device=dev)
+                t.append(_graph_us(stream, lambda r, x=x, p=p, y=y: w4.w4a16_gemm(x, p, y), 5))
+                del x, y
+            flops = sum(2.0 * prefill_m * L.N * L.K for L in layers)
+            row[f"prefill_M{prefill_m}_TFLOPs"] = round(flops / (sum(t) * 1e-6) / 1e12, 1)
+        rel = []
+        for L, W, p in zip(layers, dense, gpk):
+            X = gen.activations(64, L.K, workload, L.name, device=dev)
+            yd = w4.w4a16_dense_gemm(X, W).float()
+            yq = w4.w4a16_gemm(X, p).float()
+            rel.append(float((yq - yd).norm() / yd.norm()))
+        row["rel_l2_vs_dense"] = [round(v, 5) for v in rel]
+        groups.append(row)
+        log(f"[bench] group {group}: decode {row['decode_M1_us_per_step']:.1f} us/step "
+            f"({row['decode_M1_GBps']:.0f} GB/s), prefill {row.get(f'prefill_M{prefill_m}_TFLOPs')} "
+            f"TFLOP/s, rel l2 {max(rel):.4f}")
+        del gpk
+        torch.cuda.synchronize()
+    out["group_sizes"] = groups
+
     # AWQ exponent search on the library's kernels: calibration tokens from
     # one batch, the error measured on another; the recipe's weights (their
     # salient input channels already x8) and, as a contrast, the same layers
