@@ -55,6 +55,7 @@ def _group_of(K: int, n_groups: int) -> int:
         raise ValueError(f"K={K} with {n_groups} groups per row is not a group of {GROUPS}")
     return K // n_groups
 QMAX = 15            # 16 representable unsigned INT4 codes, 0..15
+QMAX8 = 255          # W8A16 variant: 256 unsigned INT8 codes, 0..255
 FLT_MIN = np.float32(2.0 ** -126)
 
 
@@ -94,7 +95,7 @@ def round_half_away(v) -> np.ndarray:
 # Quantise (scale, zero point, codes) for one matrix, group by group
 # ---------------------------------------------------------------------------
 
-def group_scale_zero(w_groups: np.ndarray):
+def group_scale_zero(w_groups: np.ndarray, qmax: int = QMAX):
     """Scale and zero point of each group.
 
     w_groups: float32 [..., 128], the quantiser input of each group.
@@ -113,7 +114,7 @@ def group_scale_zero(w_groups: np.ndarray):
     mn = w.min(axis=-1)
     mx = w.max(axis=-1)
     d = (mx - mn).astype(np.float32)
-    t = (d / np.float32(QMAX)).astype(np.float32)
+    t = (d / np.float32(qmax)).astype(np.float32)
     s_bits = f32_to_bf16_rtz(t)
     s = bf16_to_f32(s_bits)
     degenerate = s < FLT_MIN
@@ -129,7 +130,7 @@ def group_scale_zero(w_groups: np.ndarray):
     return s_bits, s, z
 
 
-def group_codes(w_groups: np.ndarray, s: np.ndarray, z: np.ndarray) -> np.ndarray:
+def group_codes(w_groups: np.ndarray, s: np.ndarray, z: np.ndarray, qmax: int = QMAX) -> np.ndarray:
     """Codes q = clamp(round_half_away(fl32(w / s)) + z, 0, 15), rounding
     against the stored BF16 scale (round-to-nearest on the grid used at
     dequantisation).  Clipping to the code range follows Quantization I,
@@ -137,7 +138,7 @@ def group_codes(w_groups: np.ndarray, s: np.ndarray, z: np.ndarray) -> np.ndarra
     w = np.asarray(w_groups, dtype=np.float32)
     ratio = (w / s[..., None]).astype(np.float32)
     r = round_half_away(ratio).astype(np.int64)
-    q = np.clip(r + z[..., None], 0, QMAX)
+    q = np.clip(r + z[..., None], 0, qmax)
     return q.astype(np.uint8)
 
 
@@ -166,6 +167,72 @@ def quantize(W_bits: np.ndarray, awq_s: np.ndarray | None = None, group: int = G
     if np.any(z > np.iinfo(np.int32).max) or np.any(z < np.iinfo(np.int32).min):
         raise OverflowError("zero point outside int32 (input outside the documented domain)")
     return q, s_bits.astype(np.uint16), z.astype(np.int32)
+
+
+# ---------------------------------------------------------------------------
+# W8A16 variant: the same asymmetric rules with 8-bit codes
+# ---------------------------------------------------------------------------
+
+def quantize_int8(W_bits: np.ndarray, awq_s: np.ndarray | None = None):
+    """W8A16 (Zeno AGI, "Weight-only vs mixed precision", its precision
+    matrix): the asymmetric min/max rules of `quantize` with 256 levels,
+    D / 255 for the step and codes clamped to 0..255; groups of 128.
+    Returns (q uint8 [N][K], s_bits uint16 [N][K/128], z int32 [N][K/128])."""
+    W_bits = np.asarray(W_bits, dtype=np.uint16)
+    N, K = W_bits.shape
+    if K % GROUP:
+        raise ValueError("K must be a multiple of 128")
+    w = bf16_to_f32(W_bits)
+    if awq_s is not None:
+        w = (w * np.asarray(awq_s, dtype=np.float32)[None, :]).astype(np.float32)
+    wg = w.reshape(N, K // GROUP, GROUP)
+    s_bits, s, z = group_scale_zero(wg, QMAX8)
+    q = group_codes(wg, s, z, QMAX8).reshape(N, K)
+    return q, s_bits.astype(np.uint16), z.astype(np.int32)
+
+
+def pack_codes_int8(q: np.ndarray) -> np.ndarray:
+    """q uint8 [N][K] (0..255) -> words uint32 [N][K/4]: byte j of word i
+    holds k = 4i + j, so the little-endian byte stream is q row by row."""
+    q = np.asarray(q, dtype=np.uint32)
+    N, K = q.shape
+    q4 = q.reshape(N, K // 4, 4)
+    words = np.zeros((N, K // 4), dtype=np.uint32)
+    for j in range(4):
+        words |= (q4[:, :, j] & np.uint32(0xFF)) << np.uint32(8 * j)
+    return words
+
+
+def unpack_codes_int8(words: np.ndarray) -> np.ndarray:
+    w = np.asarray(words, dtype=np.uint32)
+    N, W4 = w.shape
+    q = np.zeros((N, W4, 4), dtype=np.uint8)
+    for j in range(4):
+        q[:, :, j] = ((w >> np.uint32(8 * j)) & np.uint32(0xFF)).astype(np.uint8)
+    return q.reshape(N, W4 * 4)
+
+
+def quantize_pack_int8(W_bits: np.ndarray, awq_s: np.ndarray | None = None):
+    q, s_bits, z = quantize_int8(W_bits, awq_s)
+    return pack_codes_int8(q), s_bits, z
+
+
+def dequantize_int8(codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray) -> np.ndarray:
+    """w_hat = (q - z) * s in float64 for 8-bit codes, g = k // 128."""
+    q = unpack_codes_int8(codes).astype(np.float64)
+    N, K = q.shape
+    s = bf16_to_f32(scales).astype(np.float64)
+    z = np.asarray(zeros, dtype=np.int64).astype(np.float64)
+    g = np.arange(K) // GROUP
+    return (q - z[:, g]) * s[:, g]
+
+
+def matmul_ref_int8(X_bits: np.ndarray, codes: np.ndarray, scales: np.ndarray,
+                    zeros: np.ndarray, rows: np.ndarray | None = None) -> np.ndarray:
+    """Y[m,n] = sum_k X[m,k] * w_hat[n,k] in float64, 8-bit codes."""
+    if rows is not None:
+        codes, scales, zeros = codes[rows], scales[rows], zeros[rows]
+    return bf16_to_f32(X_bits).astype(np.float64) @ dequantize_int8(codes, scales, zeros).T
 
 
 # ---------------------------------------------------------------------------

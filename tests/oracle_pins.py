@@ -212,6 +212,59 @@ def check_grouped_hand():
     assert np.array_equal(O.dequantize(codes, scales, zeros)[0], w)
 
 
+def check_int8_on_grid_and_layout(seed=50, N=24, K=384):
+    """W8A16: weights exactly on a grid (c - z0) * s0 with codes 0 and 255 in
+    every group come back unchanged (s0 a power of two, so D / 255 = s0
+    exactly); the bytes of the packed words are the codes in order; the
+    dequantised weights equal the inputs and the output equals the
+    unquantised matmul exactly (coarse inputs, exact fp64 sums)."""
+    rng = np.random.default_rng(seed)
+    G = K // 128
+    c = rng.integers(0, 256, size=(N, G, 128))
+    c[:, :, 5] = 0
+    c[:, :, 77] = 255
+    z0 = rng.integers(0, 256, size=(N, G))
+    s0 = 2.0 ** rng.integers(-14, -8, size=(N, G))
+    w = (c - z0[..., None]) * s0[..., None]
+    W_bits = _bf16_bits_of(w.reshape(N, K).astype(np.float32))
+    q, s_bits, z = O.quantize_int8(W_bits)
+    assert np.array_equal(q.reshape(N, G, 128), c) and np.array_equal(z, z0)
+    assert np.array_equal(O.bf16_to_f32(s_bits).astype(np.float64), s0)
+    words = O.pack_codes_int8(q)
+    assert words.shape == (N, K // 4)
+    assert np.array_equal(words.astype("<u4").view(np.uint8).reshape(N, K), q)
+    assert np.array_equal(O.unpack_codes_int8(words), q)
+    assert np.array_equal(O.dequantize_int8(words, s_bits, z), w.reshape(N, K))
+    x = (rng.integers(-63, 64, size=(3, K)) / 4.0).astype(np.float32)
+    y = O.matmul_ref_int8(_bf16_bits_of(x), words, s_bits, z)
+    assert np.array_equal(y, x.astype(np.float64) @ w.reshape(N, K).T)
+
+
+def check_int8_brute_force(seed=51, N=3, K=128):
+    """W8A16 codes are the nearest of the 256 grid points (ties away from
+    zero), against the stored BF16 scale, on generated weights."""
+    rng = np.random.default_rng(seed)
+    w = (rng.normal(0, 0.02, size=(N, K)) + rng.uniform(-0.01, 0.01, size=(N, 1))).astype(np.float32)
+    W_bits = O.f32_to_bf16_rne(w)
+    q, s_bits, z = O.quantize_int8(W_bits)
+    wf = O.bf16_to_f32(W_bits)
+    mn, mx = wf.min(axis=1), wf.max(axis=1)
+    for n in range(N):
+        s = _frac_of_f32(O.bf16_to_f32(s_bits[n, 0]))
+        # the step: s <= D / 255 < s (1 + 2^-7)
+        D = _frac_of_f32(mx[n]) - _frac_of_f32(mn[n])
+        assert s <= D / 255 < s * (1 + Fraction(1, 128))
+        zz = int(z[n, 0])
+        for k in range(K):
+            wk = _frac_of_f32(wf[n, k])
+            best = min(range(256), key=lambda cc: (abs(wk - (cc - zz) * s), -abs(cc - zz)))
+            if best != q[n, k]:
+                r = wk / s
+                frac = r - (r.numerator // r.denominator)
+                assert abs(frac - Fraction(1, 2)) < abs(r) * Fraction(1, 2 ** 22), (n, k, best, q[n, k])
+        assert q[n].min() == 0 and q[n].max() >= 254
+
+
 # ---------------------------------------------------------------------------
 # Packing layout
 # ---------------------------------------------------------------------------

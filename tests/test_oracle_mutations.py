@@ -22,6 +22,7 @@ ALL_PINS = [
     P.check_grouped_hand,
     lambda: P.check_all_codes_on_grid(seed=21, N=8, K=256, group=32),
     lambda: P.check_brute_force(seed=22, M=2, K=128, N=3, group=32),
+    P.check_int8_on_grid_and_layout, P.check_int8_brute_force,
 ]
 
 
@@ -85,12 +86,12 @@ def _matmul_transposed(X_bits, codes, scales, zeros, rows=None):
     return (w @ x.T)
 
 
-def _scale_zero_clamped(wg):
-    s_bits, s, z = ORIG["group_scale_zero"](wg)
-    return s_bits, s, np.clip(z, 0, 15)
+def _scale_zero_clamped(wg, qmax=15):
+    s_bits, s, z = ORIG["group_scale_zero"](wg, qmax)
+    return s_bits, s, np.clip(z, 0, qmax)
 
 
-def _scale_zero_no_degenerate(wg):
+def _scale_zero_no_degenerate(wg, qmax=15):
     w = np.asarray(wg, dtype=np.float32)
     mn, mx = w.min(-1), w.max(-1)
     t = ((mx - mn) / np.float32(15)).astype(np.float32)
@@ -100,7 +101,7 @@ def _scale_zero_no_degenerate(wg):
     return s_bits, s, z
 
 
-def _scale_zero_div16(wg):
+def _scale_zero_div16(wg, qmax=15):
     w = np.asarray(wg, dtype=np.float32)
     mn, mx = w.min(-1), w.max(-1)
     t = ((mx - mn) / np.float32(16)).astype(np.float32)
@@ -112,7 +113,7 @@ def _scale_zero_div16(wg):
     return s_bits, s, z
 
 
-def _codes_against_unrounded(wg, s, z):
+def _codes_against_unrounded(wg, s, z, qmax=15):
     w = np.asarray(wg, dtype=np.float32)
     mn, mx = w.min(-1), w.max(-1)
     t = ((mx - mn) / np.float32(15)).astype(np.float32)
@@ -127,6 +128,23 @@ def _quantize_ignores_awq(W_bits, awq_s=None, group=128):
 
 def _quantize_ignores_group(W_bits, awq_s=None, group=128):
     return ORIG["quantize"](W_bits, awq_s)
+
+
+def _quantize_int8_div256(W_bits, awq_s=None):
+    N, K = W_bits.shape
+    wg = R.bf16_to_f32(W_bits).reshape(N, K // 128, 128)
+    s_bits, s, z = R.group_scale_zero(wg, 256)
+    return R.group_codes(wg, s, z, 255).reshape(N, K), s_bits, z.astype(np.int32)
+
+
+def _pack_int8_reversed(q):
+    q = np.asarray(q, dtype=np.uint32)
+    N, K = q.shape
+    q4 = q.reshape(N, K // 4, 4)
+    words = np.zeros((N, K // 4), dtype=np.uint32)
+    for j in range(4):
+        words |= q4[:, :, 3 - j] << np.uint32(8 * j)
+    return words
 
 
 def _dequant_group_128(codes, scales, zeros):
@@ -241,6 +259,8 @@ MUTATIONS = {
     "awq_search_multiplies_x": ("awq_search", _search_multiplies_x),
     "quantize_ignores_group": ("quantize", _quantize_ignores_group),
     "dequant_group_always_128": ("dequantize", _dequant_group_128),
+    "int8_divide_by_256": ("quantize_int8", _quantize_int8_div256),
+    "int8_bytes_reversed": ("pack_codes_int8", _pack_int8_reversed),
 }
 
 

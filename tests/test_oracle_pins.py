@@ -68,6 +68,14 @@ def test_grouped_min_max_codes_generated(group):
     assert P.check_min_max_codes(gen.bits(W), group=group) > 0.99
 
 
+def test_int8_on_grid_and_layout():
+    P.check_int8_on_grid_and_layout()
+
+
+def test_int8_brute_force():
+    P.check_int8_brute_force()
+
+
 def test_awq_prescale():
     P.check_awq_prescale_power_of_two()
 
