@@ -58,9 +58,11 @@ extern "C" {
 #endif
 
 #define W4A16_GROUP 128
-#define W4A16_ABI_VERSION 4
+#define W4A16_ABI_VERSION 5
 #define W4A16_GEMV_MAX_M 32
 #define W4A16_DENSE_GEMV_MAX_M 8
+#define W4A16_INT8_GEMV_MAX_M 4
+#define W4A16_INT8_GEMV_MAX_K 32768
 
 enum {
   W4A16_OK = 0,
@@ -174,6 +176,27 @@ int w4a16_gemm_grouped(const uint16_t* X, int64_t M, int64_t ldx,
                        const uint32_t* codes, const uint16_t* scales,
                        const int32_t* zeros, int64_t N, int64_t K, int64_t group,
                        uint16_t* Y, int64_t ldy, void* stream);
+
+/*
+ * w4a16_pack_int8, w4a16_gemv_int8 -- the W8A16 variant (Zeno AGI, "Weight-
+ * only vs mixed precision", its precision matrix: 8-bit weights, 16-bit
+ * activations).  Codes are 8-bit, four per word: codes uint32_t [N][K/4],
+ * byte j of word i of row n is q[n, 4i + j] (the byte stream is q row by
+ * row); scales and zeros as above (groups of 128).  The quantiser is
+ * w4a16_pack's with 255 steps: t = D / 255 and q = clamp(..., 0, 255).
+ * w4a16_gemv_int8 is the decode product for 1 <= M <= W4A16_INT8_GEMV_MAX_M
+ * and K <= W4A16_INT8_GEMV_MAX_K (larger K: W4A16_ERR_UNSUPPORTED), with the
+ * accuracy and alignment rules of w4a16_gemv; each code's two nibbles feed
+ * the matrix product as exact BF16 operands, so no weight is rounded.
+ * There is no prefill entry point for 8-bit codes.
+ */
+int w4a16_pack_int8(const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
+                    const float* awq_s, uint32_t* codes, uint16_t* scales,
+                    int32_t* zeros, void* stream);
+int w4a16_gemv_int8(const uint16_t* X, int64_t M, int64_t ldx,
+                    const uint32_t* codes, const uint16_t* scales,
+                    const int32_t* zeros, int64_t N, int64_t K,
+                    uint16_t* Y, int64_t ldy, void* stream);
 
 /*
  * w4a16_awq_importance -- per-input-channel activation magnitude from a

@@ -47,6 +47,8 @@ _SIGS = {
     "w4a16_dense_gemv": ([_p, _i64, _i64, _p, _i64, _i64, _i64, _p, _i64, _p], ctypes.c_int),
     "w4a16_dense_gemm": ([_p, _i64, _i64, _p, _i64, _i64, _i64, _p, _i64, _p], ctypes.c_int),
     "w4a16_pack_grouped": ([_p, _i64, _i64, _i64, _p, _i64, _p, _p, _p, _p], ctypes.c_int),
+    "w4a16_pack_int8": ([_p, _i64, _i64, _i64, _p, _p, _p, _p, _p], ctypes.c_int),
+    "w4a16_gemv_int8": ([_p, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _i64, _p], ctypes.c_int),
     "w4a16_gemv_grouped": ([_p, _i64, _i64, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _p], ctypes.c_int),
     "w4a16_gemm_grouped": ([_p, _i64, _i64, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _p], ctypes.c_int),
 }
@@ -152,6 +154,42 @@ def w4a16_pack_symmetric(W: torch.Tensor, awq_s: torch.Tensor | None = None,
     return _pack(lib.w4a16_pack_symmetric, "w4a16_pack_symmetric", W, awq_s, out)
 
 
+class PackedLinearInt8:
+    """W8A16 packed matrix: codes [N][K/4] int32 (four 8-bit codes per word),
+    scales [N][K/128] bfloat16, zeros [N][K/128] int32."""
+
+    __slots__ = ("codes", "scales", "zeros", "N", "K")
+
+    def __init__(self, codes, scales, zeros):
+        self.codes, self.scales, self.zeros = codes, scales, zeros
+        self.N = codes.shape[0]
+        self.K = codes.shape[1] * 4
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in (self.codes, self.scales, self.zeros))
+
+
+def w4a16_pack_int8(W: torch.Tensor, awq_s: torch.Tensor | None = None) -> PackedLinearInt8:
+    """W8A16 quantise + pack (see w4a16_pack_int8 in w4a16.h)."""
+    _need(W, torch.bfloat16, "W", 2)
+    N, K = W.shape
+    if awq_s is not None:
+        _need(awq_s, torch.float32, "awq_s", 1)
+        if awq_s.shape[0] != K or not awq_s.is_contiguous():
+            raise ValueError("awq_s must be a contiguous float32 [K]")
+    p = PackedLinearInt8(torch.empty(N, K // 4, dtype=torch.int32, device=W.device),
+                         torch.empty(N, K // GROUP, dtype=torch.bfloat16, device=W.device),
+                         torch.empty(N, K // GROUP, dtype=torch.int32, device=W.device))
+    _check("w4a16_pack_int8", lib.w4a16_pack_int8(_ptr(W), N, K, W.stride(0), _ptr(awq_s), _ptr(p.codes),
+                                                  _ptr(p.scales), _ptr(p.zeros), _stream(W)))
+    return p
+
+
+def w4a16_gemv_int8(X: torch.Tensor, p: PackedLinearInt8, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = X . w_hat^T for 8-bit codes, 1 <= M <= 4 (decode)."""
+    return _matmul(lib.w4a16_gemv_int8, "w4a16_gemv_int8", X, p, out)
+
+
 def packed_from_i64(codes_i64: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor) -> PackedLinear:
     """A packed matrix whose codes sit in an I64 container [N][K/16] (sixteen
     codes per word, two per byte, low nibble first): the same bytes as the
@@ -178,7 +216,7 @@ def _matmul(fn, name, X: torch.Tensor, p: PackedLinear, out: torch.Tensor | None
         _need(out, torch.bfloat16, "out", 2)
         if tuple(out.shape) != (M, p.N):
             raise ValueError("out has the wrong shape")
-    if p.group == GROUP:
+    if getattr(p, "group", GROUP) == GROUP:
         st = fn(_ptr(X), M, X.stride(0), _ptr(p.codes), _ptr(p.scales), _ptr(p.zeros),
                 p.N, p.K, _ptr(out), out.stride(0), _stream(X))
     else:

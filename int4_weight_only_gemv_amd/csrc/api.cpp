@@ -8,7 +8,9 @@
 
 namespace w4a16 {
 int launch_pack(const uint16_t*, int64_t, int64_t, int64_t, const float*, int, uint32_t*,
-                uint16_t*, int32_t*, bool, hipStream_t);
+                uint16_t*, int32_t*, bool, bool, hipStream_t);
+int launch_gemv_int8(const uint16_t*, int64_t, int64_t, const uint32_t*, const uint16_t*,
+                     const int32_t*, int64_t, int64_t, uint16_t*, int64_t, hipStream_t);
 int launch_gemv(const uint16_t*, int64_t, int64_t, const uint32_t*, const uint16_t*,
                 const int32_t*, int64_t, int64_t, int, uint16_t*, int64_t, hipStream_t);
 int launch_gemm(const uint16_t*, int64_t, int64_t, const uint32_t*, const uint16_t*,
@@ -82,7 +84,7 @@ const char* w4a16_strerror(int status) {
 namespace {
 int pack_checked(const uint16_t* W, int64_t N, int64_t K, int64_t ldw, const float* awq_s,
                  int64_t group, uint32_t* codes, uint16_t* scales, int32_t* zeros, bool symmetric,
-                 void* stream) {
+                 void* stream, bool int8 = false) {
   if (!W || !codes || !scales || !zeros || !group_ok(group)) return W4A16_ERR_INVALID_ARG;
   if (N < 1 || K < W4A16_GROUP || K % W4A16_GROUP || ldw < K) return W4A16_ERR_INVALID_ARG;
   if (N >= kMaxDim || K >= kMaxDim || N * (K / 8) >= ((int64_t)1 << 38)) return W4A16_ERR_UNSUPPORTED;
@@ -90,13 +92,28 @@ int pack_checked(const uint16_t* W, int64_t N, int64_t K, int64_t ldw, const flo
       (awq_s && !aligned(awq_s, 4)))
     return W4A16_ERR_MISALIGNED;
   return w4a16::launch_pack(W, N, K, ldw, awq_s, (int)group, codes, scales, zeros, symmetric,
-                            (hipStream_t)stream);
+                            int8, (hipStream_t)stream);
 }
 }  // namespace
 
 int w4a16_pack(const uint16_t* W, int64_t N, int64_t K, int64_t ldw, const float* awq_s,
                uint32_t* codes, uint16_t* scales, int32_t* zeros, void* stream) {
   return pack_checked(W, N, K, ldw, awq_s, W4A16_GROUP, codes, scales, zeros, false, stream);
+}
+
+int w4a16_pack_int8(const uint16_t* W, int64_t N, int64_t K, int64_t ldw, const float* awq_s,
+                    uint32_t* codes, uint16_t* scales, int32_t* zeros, void* stream) {
+  return pack_checked(W, N, K, ldw, awq_s, W4A16_GROUP, codes, scales, zeros, false, stream, true);
+}
+
+int w4a16_gemv_int8(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
+                    const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K, uint16_t* Y,
+                    int64_t ldy, void* stream) {
+  int st = check_matmul(X, M, ldx, codes, scales, zeros, N, K, Y, ldy);
+  if (st != W4A16_OK) return st;
+  if (M > W4A16_INT8_GEMV_MAX_M) return W4A16_ERR_INVALID_ARG;
+  if (K > W4A16_INT8_GEMV_MAX_K) return W4A16_ERR_UNSUPPORTED;
+  return w4a16::launch_gemv_int8(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, (hipStream_t)stream);
 }
 
 int w4a16_pack_grouped(const uint16_t* W, int64_t N, int64_t K, int64_t ldw, const float* awq_s,

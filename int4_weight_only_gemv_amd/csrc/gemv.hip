@@ -71,7 +71,10 @@ constexpr int log2_exact(int v) { return v <= 1 ? 0 : 1 + log2_exact(v / 2); }
 // rows (the fold is linear, so a group split over lanes sums correctly)
 // before the cross-lane sums.  Otherwise lg = 7 and the four lanes of a
 // group are summed first and fold once.
-template <int M, int R, int NB, bool PL>
+// W8: the W8A16 variant, 8-bit codes (byte j of word i is k = 4i + j); each
+// byte's two nibbles h, l become BF16 128 + h and 128 + l like INT4 codes,
+// with two product chains per row, P = 16 P_h + P_l = sum x q + 17 * 128 * Xsum.
+template <int M, int R, int NB, bool PL, bool W8>
 __global__ __launch_bounds__(1024) void gemv_dot_kernel(
     const uint16_t* __restrict__ X, int64_t ldx, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K, int lg,
@@ -93,8 +96,10 @@ __global__ __launch_bounds__(1024) void gemv_dot_kernel(
   const int64_t wpr = K / 8;
 
   const int row0 = blockIdx.x * RB;
-  const u32x4* cbase = reinterpret_cast<const u32x4*>(codes) + kc / 32;
-  u32x4 cb[2][R];
+  constexpr int CW = W8 ? 2 : 1;              // 16-byte code vectors per lane and row
+  const int64_t vrow = W8 ? K / 16 : wpr / 4; // 16-byte vectors per code row
+  const u32x4* cbase = reinterpret_cast<const u32x4*>(codes) + kc / (32 / CW);
+  u32x4 cb[2][R][CW];
   // scale and zero point of row (lane % 4), group g; with PL those of all
   // R rows
   uint32_t sb[2][PL ? R : 1];
@@ -103,7 +108,8 @@ __global__ __launch_bounds__(1024) void gemv_dot_kernel(
 #pragma unroll
     for (int j = 0; j < R; ++j) {
       const int row = min(row0 + batch * R + j, N - 1);
-      cb[buf][j] = __builtin_nontemporal_load(cbase + (int64_t)row * (wpr / 4));
+#pragma unroll
+      for (int v = 0; v < CW; ++v) cb[buf][j][v] = __builtin_nontemporal_load(cbase + (int64_t)row * vrow + v);
     }
     if constexpr (PL) {
 #pragma unroll
@@ -133,7 +139,7 @@ __global__ __launch_bounds__(1024) void gemv_dot_kernel(
     for (int i = 0; i < 4; ++i) {
       u32x4 raw = xr[i];
       if (!active) raw = u32x4{0u, 0u, 0u, 0u};
-      xp[m][i] = x_pairs_from_natural(raw);
+      xp[m][i] = W8 ? raw : x_pairs_from_natural(raw);
 #pragma unroll
       for (int j = 0; j < 4; ++j) sum = dot2(raw[j], kOnePair, sum);
     }
@@ -155,13 +161,41 @@ __global__ __launch_bounds__(1024) void gemv_dot_kernel(
     for (int j = 0; j < R; ++j) {
 #pragma unroll
       for (int m = 0; m < M; ++m) P[j][m] = 0.f;
+      if constexpr (W8) {
+        float Ph[M];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const u32x4 b = codes_to_bias128_pairs(cb[cur][j][i]);
+        for (int m = 0; m < M; ++m) Ph[m] = 0.f;
 #pragma unroll
-        for (int m = 0; m < M; ++m)
+        for (int v = 0; v < CW; ++v)
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) P[j][m] = dot2(b[jj], xp[m][i][jj], P[j][m]);
+          for (int i = 0; i < 4; ++i) {
+            // word i of vector v: inputs 16 v + 4 i .. +3, activation dwords d, d + 1
+            const uint32_t w = cb[cur][j][v][i];
+            const uint32_t lb = w & 0x0F0F0F0Fu, hb = (w >> 4) & 0x0F0F0F0Fu;
+            const uint32_t l01 = __builtin_amdgcn_perm(kExpBytes, lb, 0x04010400u);
+            const uint32_t l23 = __builtin_amdgcn_perm(kExpBytes, lb, 0x04030402u);
+            const uint32_t h01 = __builtin_amdgcn_perm(kExpBytes, hb, 0x04010400u);
+            const uint32_t h23 = __builtin_amdgcn_perm(kExpBytes, hb, 0x04030402u);
+            const int d = 8 * v + 2 * i;
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+              P[j][m] = dot2(l01, xp[m][d >> 2][d & 3], P[j][m]);
+              P[j][m] = dot2(l23, xp[m][d >> 2][(d & 3) + 1], P[j][m]);
+              Ph[m] = dot2(h01, xp[m][d >> 2][d & 3], Ph[m]);
+              Ph[m] = dot2(h23, xp[m][d >> 2][(d & 3) + 1], Ph[m]);
+            }
+          }
+#pragma unroll
+        for (int m = 0; m < M; ++m) P[j][m] = fmaf(16.f, Ph[m], P[j][m]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const u32x4 b = codes_to_bias128_pairs(cb[cur][j][0][i]);
+#pragma unroll
+          for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) P[j][m] = dot2(b[jj], xp[m][i][jj], P[j][m]);
+        }
       }
       if constexpr (PL) {
         const float s = bf16_to_f32(sb[cur][j]);
@@ -189,7 +223,7 @@ __global__ __launch_bounds__(1024) void gemv_dot_kernel(
     {
       const uint32_t up = (lane & 1) ? ~0u : 0u;
       const float s = bf16_to_f32(sb[cur][0]);
-      const float zb128 = (float)(128 + zb[cur][0]);
+      const float zb128 = (float)((W8 ? 17 * 128 : 128) + zb[cur][0]);
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         const float send = pick(up, h[0][m], h[1][m]);
@@ -708,17 +742,17 @@ constexpr int kDotMaxM = 4;
 
 int cu_count() { return device_cu_count(); }
 
-template <int M, int NB, bool PL>
+template <int M, int NB, bool PL, bool W8>
 void launch_dot_nb(const uint16_t* X, int64_t ldx, const uint32_t* codes, const uint16_t* scales,
                    const int32_t* zeros, int N, int K, int lg, uint16_t* Y, int64_t ldy,
                    hipStream_t stream) {
   constexpr int R = 4;
   const int S = (K + kSlice - 1) / kSlice;
-  hipLaunchKernelGGL((gemv_dot_kernel<M, R, NB, PL>), dim3((unsigned)((N + R * NB - 1) / (R * NB))),
+  hipLaunchKernelGGL((gemv_dot_kernel<M, R, NB, PL, W8>), dim3((unsigned)((N + R * NB - 1) / (R * NB))),
                      dim3(S * kWave), 0, stream, X, ldx, codes, scales, zeros, N, K, lg, Y, ldy);
 }
 
-template <int M, bool PL>
+template <int M, bool PL, bool W8 = false>
 void launch_dot(const uint16_t* X, int64_t ldx, const uint32_t* codes, const uint16_t* scales,
                 const int32_t* zeros, int N, int K, int lg, uint16_t* Y, int64_t ldy,
                 hipStream_t stream) {
@@ -733,7 +767,8 @@ void launch_dot(const uint16_t* X, int64_t ldx, const uint32_t* codes, const uin
   // timings of every decode layer of the 8B- and 70B-shaped sets and the
   // 40-layer stack.
   constexpr int R = 4;
-  constexpr int kMaxNB = M >= 4 ? 2 : 8;   // more batches would spill at M = 4
+  // more batches would spill at M = 4 (with 8-bit codes, from M = 3)
+  constexpr int kMaxNB = (W8 && M >= 3) ? 1 : (M >= 4 ? 2 : 8);
   const int S = (K + kSlice - 1) / kSlice;
   const int cus = cu_count();
   auto balance = [&](int nb) {
@@ -755,12 +790,12 @@ void launch_dot(const uint16_t* X, int64_t ldx, const uint32_t* codes, const uin
   switch (nb) {
 #define W4A16_DOT(V)                                                                   \
   case V:                                                                              \
-    launch_dot_nb<M, (V <= kMaxNB ? V : kMaxNB), PL>(X, ldx, codes, scales, zeros, N, K, lg, Y, ldy, stream); \
+    launch_dot_nb<M, (V <= kMaxNB ? V : kMaxNB), PL, W8>(X, ldx, codes, scales, zeros, N, K, lg, Y, ldy, stream); \
     break;
     W4A16_DOT(8) W4A16_DOT(7) W4A16_DOT(6) W4A16_DOT(5) W4A16_DOT(4) W4A16_DOT(3) W4A16_DOT(2)
 #undef W4A16_DOT
     default:
-      launch_dot_nb<M, 1, PL>(X, ldx, codes, scales, zeros, N, K, lg, Y, ldy, stream);
+      launch_dot_nb<M, 1, PL, W8>(X, ldx, codes, scales, zeros, N, K, lg, Y, ldy, stream);
   }
 }
 
@@ -891,6 +926,20 @@ int launch_gemv_small_groups(const uint16_t* X, int64_t M, int64_t ldx, const ui
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 }  // namespace
+
+// W8A16 variant, 1 <= M <= 4, K <= 32768 (checked by the caller)
+int launch_gemv_int8(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
+                     const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K,
+                     uint16_t* Y, int64_t ldy, hipStream_t stream) {
+  const int n = (int)N, k = (int)K;
+  switch (M) {
+    case 1: launch_dot<1, false, true>(X, ldx, codes, scales, zeros, n, k, 7, Y, ldy, stream); break;
+    case 2: launch_dot<2, false, true>(X, ldx, codes, scales, zeros, n, k, 7, Y, ldy, stream); break;
+    case 3: launch_dot<3, false, true>(X, ldx, codes, scales, zeros, n, k, 7, Y, ldy, stream); break;
+    default: launch_dot<4, false, true>(X, ldx, codes, scales, zeros, n, k, 7, Y, ldy, stream); break;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
 
 // group: 32, 64 or 128 inputs per quantisation group (checked by the caller)
 int launch_gemv(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,

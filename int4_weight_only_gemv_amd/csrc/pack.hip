@@ -35,7 +35,9 @@ __device__ __forceinline__ float bf16_rtz(float f) {
   return __uint_as_float(__float_as_uint(f) & 0xFFFF0000u);
 }
 
-template <bool kVecLoad, bool kAwq, bool kSym>
+// kW8: the W8A16 variant, 8-bit codes 0..255 (step D / 255), two code words
+// per lane (byte j of word i holds k = 4i + j)
+template <bool kVecLoad, bool kAwq, bool kSym, bool kW8>
 __global__ __launch_bounds__(256) void pack_kernel(
     const uint16_t* __restrict__ W, int64_t ldw, const float* __restrict__ awq_s,
     int64_t words_per_row, int64_t total_words, int seg, uint32_t* __restrict__ codes,
@@ -89,7 +91,7 @@ __global__ __launch_bounds__(256) void pack_kernel(
     z = 8;
   } else {
     const float d = __fsub_rn(mx, mn);
-    s = bf16_rtz(__fdiv_rn(d, 15.0f));
+    s = bf16_rtz(__fdiv_rn(d, kW8 ? 255.0f : 15.0f));
     if (!(s >= kFltMin)) {  // degenerate group: zero or subnormal step
       s = bf16_rtz(fmaxf(fabsf(mn), fabsf(mx)));
       if (!(s >= kFltMin)) s = 1.0f;
@@ -97,15 +99,26 @@ __global__ __launch_bounds__(256) void pack_kernel(
     z = (int)roundf(__fdiv_rn(-mn, s));
   }
 
-  uint32_t word = 0;
+  constexpr int kQmax = kW8 ? 255 : 15;
+  uint32_t word = 0, word2 = 0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     int q = (int)roundf(__fdiv_rn(w[j], s)) + z;
-    q = q < 0 ? 0 : (q > 15 ? 15 : q);
-    word |= (uint32_t)q << (4 * j);
+    q = q < 0 ? 0 : (q > kQmax ? kQmax : q);
+    if (kW8) {
+      if (j < 4) word |= (uint32_t)q << (8 * j);
+      else word2 |= (uint32_t)q << (8 * (j - 4));
+    } else {
+      word |= (uint32_t)q << (4 * j);
+    }
   }
   if (live) {
-    codes[t] = word;
+    if (kW8) {
+      codes[2 * t] = word;
+      codes[2 * t + 1] = word2;
+    } else {
+      codes[t] = word;
+    }
     if ((wi & (seg - 1)) == 0) {
       const int64_t gi = n * (words_per_row / seg) + wi / seg;
       scales[gi] = (uint16_t)(__float_as_uint(s) >> 16);
@@ -117,7 +130,7 @@ __global__ __launch_bounds__(256) void pack_kernel(
 }  // namespace
 
 namespace {
-template <bool kSym>
+template <bool kSym, bool kW8>
 void launch_pack_t(const uint16_t* W, int64_t ldw, const float* awq_s, int64_t words_per_row,
                    int64_t total, int seg, uint32_t* codes, uint16_t* scales, int32_t* zeros,
                    bool vec, hipStream_t stream) {
@@ -125,17 +138,17 @@ void launch_pack_t(const uint16_t* W, int64_t ldw, const float* awq_s, int64_t w
   const dim3 grid((unsigned)((total + threads - 1) / threads));
   if (vec) {
     if (awq_s)
-      hipLaunchKernelGGL((pack_kernel<true, true, kSym>), grid, dim3(threads), 0, stream, W, ldw,
+      hipLaunchKernelGGL((pack_kernel<true, true, kSym, kW8>), grid, dim3(threads), 0, stream, W, ldw,
                          awq_s, words_per_row, total, seg, codes, scales, zeros);
     else
-      hipLaunchKernelGGL((pack_kernel<true, false, kSym>), grid, dim3(threads), 0, stream, W, ldw,
+      hipLaunchKernelGGL((pack_kernel<true, false, kSym, kW8>), grid, dim3(threads), 0, stream, W, ldw,
                          awq_s, words_per_row, total, seg, codes, scales, zeros);
   } else {
     if (awq_s)
-      hipLaunchKernelGGL((pack_kernel<false, true, kSym>), grid, dim3(threads), 0, stream, W, ldw,
+      hipLaunchKernelGGL((pack_kernel<false, true, kSym, kW8>), grid, dim3(threads), 0, stream, W, ldw,
                          awq_s, words_per_row, total, seg, codes, scales, zeros);
     else
-      hipLaunchKernelGGL((pack_kernel<false, false, kSym>), grid, dim3(threads), 0, stream, W, ldw,
+      hipLaunchKernelGGL((pack_kernel<false, false, kSym, kW8>), grid, dim3(threads), 0, stream, W, ldw,
                          awq_s, words_per_row, total, seg, codes, scales, zeros);
   }
 }
@@ -144,15 +157,17 @@ void launch_pack_t(const uint16_t* W, int64_t ldw, const float* awq_s, int64_t w
 // group: 32, 64 or 128 inputs per quantisation group (checked by the caller)
 int launch_pack(const uint16_t* W, int64_t N, int64_t K, int64_t ldw, const float* awq_s,
                 int group, uint32_t* codes, uint16_t* scales, int32_t* zeros, bool symmetric,
-                hipStream_t stream) {
+                bool int8, hipStream_t stream) {
   const int64_t words_per_row = K / 8;
   const int64_t total = N * words_per_row;
   const int seg = group / 8;
   const bool vec = ((reinterpret_cast<uintptr_t>(W) & 15u) == 0) && (ldw % 8 == 0);
-  if (symmetric)
-    launch_pack_t<true>(W, ldw, awq_s, words_per_row, total, seg, codes, scales, zeros, vec, stream);
+  if (int8)
+    launch_pack_t<false, true>(W, ldw, awq_s, words_per_row, total, seg, codes, scales, zeros, vec, stream);
+  else if (symmetric)
+    launch_pack_t<true, false>(W, ldw, awq_s, words_per_row, total, seg, codes, scales, zeros, vec, stream);
   else
-    launch_pack_t<false>(W, ldw, awq_s, words_per_row, total, seg, codes, scales, zeros, vec, stream);
+    launch_pack_t<false, false>(W, ldw, awq_s, words_per_row, total, seg, codes, scales, zeros, vec, stream);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 
