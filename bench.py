@@ -543,6 +543,38 @@ def comparisons(workload, fused_ms_per_step, fused_prefill, dev, stream, steps=4
             del W, X, yd, yq
     out["quantisation_error_vs_dense"] = {"M": Mq, "layers": errs}
 
+    # W8A16 decode step (M=1), same protocol: the pages' precision matrix puts
+    # its decode gain over 16-bit weights at about 1.5x
+    i8 = [w4.w4a16_pack_int8(w) for w in dense]
+    iset = sum(p.nbytes() for p in i8)
+    icopy = max(2, math.ceil(ROTATE_BYTES / iset))
+    icopies = [i8] + [[w4.PackedLinearInt8(p.codes.clone(), p.scales.clone(), p.zeros.clone())
+                       for p in i8] for _ in range(icopy - 1)]
+    ixs = [gen.activations(1, L.K, workload, L.name, device=dev) for L in layers]
+    iys = [torch.empty(1, L.N, dtype=torch.bfloat16, device=dev) for L in layers]
+
+    def int8_step(s):
+        for p, x, y in zip(icopies[s % icopy], ixs, iys):
+            w4.w4a16_gemv_int8(x, p, y)
+    us_i8 = _graph_us(stream, int8_step, steps)
+    i8_bytes = iset + sum(2 * (L.K + L.N) for L in layers)
+    rel8 = []
+    for L, W, p in zip(layers, dense, i8):
+        X = gen.activations(1, L.K, workload, L.name, device=dev)
+        yd = w4.w4a16_dense_gemv(X, W).float()
+        y8 = w4.w4a16_gemv_int8(X, p).float()
+        rel8.append(round(float((y8 - yd).norm() / yd.norm()), 6))
+    out["w8a16_decode_M1"] = {
+        "us_per_step": round(us_i8, 3), "GBps": round(i8_bytes / (us_i8 * 1e-6) / 1e9, 1),
+        "speedup_vs_dense_bf16": round(us_dense / us_i8, 3),
+        "w4a16_speedup_vs_w8a16": round(us_i8 / fused_us, 3),
+        "rotating_copies": icopy, "rel_l2_vs_dense": rel8,
+    }
+    log(f"[bench] W8A16 decode M=1: {us_i8:.1f} us/step ({i8_bytes / (us_i8 * 1e-6) / 1e9:.0f} GB/s), "
+        f"{us_dense / us_i8:.2f}x dense bf16; rel l2 {max(rel8):.5f}")
+    del icopies, ixs, iys, i8
+    torch.cuda.synchronize()
+
     # quantisation groups of 32 / 64 / 128 inputs: decode step (M=1, same
     # protocol as the headline), prefill at prefill_m, and the output error
     # against the dense BF16 layer
