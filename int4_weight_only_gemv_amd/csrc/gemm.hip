@@ -31,9 +31,10 @@
 // chunks of each 64-byte LDS row are XOR-swizzled by (row >> 1) & 3, so the
 // rows that one LDS cycle of a 16-byte-per-lane read serves fall on distinct
 // bank groups.  Codes are unpacked in natural k order, so X needs no
-// permutation.  Each lane loads the scale and zero point of one column of
-// its wave per group; lane permutes spread the factors to the accumulator
-// layout.  Tiles go to the 8 XCDs in contiguous runs with N fastest, so
+// permutation.  Each lane loads the scales and zero points of one column of
+// its wave per 128-input block; lane permutes spread the factors to the
+// accumulator layout.  Groups of 32 or 64 inputs (two or four per block) end
+// with the same rescale, every one or two K steps.  Tiles go to the 8 XCDs in contiguous runs with N fastest, so
 // blocks that share X rows share an L2.
 
 #include "common.h"
@@ -109,19 +110,19 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
 }
 
-// Memory operations each wave issues, in this order: at group position 0,
-// the next group's scale and zero-point loads and C_LOADS code copies; at every
+// Memory operations each wave issues, in this order: at block position 0,
+// the next block's scale and zero-point loads and C_LOADS code copies; at every
 // step, X_LOADS copies of X for the step four ahead.  Nothing is
-// conditional (indices are clamped to the last group / step), so the
+// conditional (indices are clamped to the last block / step), so the
 // in-order memory counter gives fixed waits.  At the step at position ST
 // the wait is for the X copies of the following step; what may stay in
 // flight is everything issued after them: two more steps of X copies and,
-// at positions 1 and 2, the group-start loads.  At position 3 the wait also
-// covers the next group's code copies (issued before the awaited X copies).
+// at positions 1 and 2, the block-start loads.  At position 3 the wait also
+// covers the next block's code copies (issued before the awaited X copies).
 template <class C, int ST>
 __device__ __forceinline__ void wait_step() {
-  constexpr int kGroupStart = 2 + C::C_LOADS;
-  if (ST == 1 || ST == 2) wait_vmcnt<2 * C::X_LOADS + kGroupStart>(); else wait_vmcnt<2 * C::X_LOADS>();
+  constexpr int kBlockStart = 2 + C::C_LOADS;
+  if (ST == 1 || ST == 2) wait_vmcnt<2 * C::X_LOADS + kBlockStart>(); else wait_vmcnt<2 * C::X_LOADS>();
 }
 
 // GS: K steps per quantisation group (1, 2 or 4: groups of 32, 64 or 128
