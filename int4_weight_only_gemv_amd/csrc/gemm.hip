@@ -461,6 +461,17 @@ void gemm_small_kernel(
   gemm_tile<TileSmall, GS>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, m_tiles, n_tiles);
 }
 
+// 128 x 128 tiles for groups of 32 or 64 inputs: two waves per SIMD, so that
+// the rescale every one or two steps has the registers it needs
+template <int GS>
+__global__ __launch_bounds__(TileSmall::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_small2_kernel(
+    const uint16_t* __restrict__ X, int M, int64_t ldx, const uint32_t* __restrict__ codes,
+    const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K,
+    uint16_t* __restrict__ Y, int64_t ldy, int m_tiles, int n_tiles) {
+  gemm_tile<TileSmall, GS>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, m_tiles, n_tiles);
+}
+
 // 64 x 128 tiles on two waves of 64 x 64, for layers whose 128 x 128 tiles
 // would still leave CUs idle (two waves per SIMD: at three the compiler
 // moves values into AGPRs)
@@ -491,8 +502,11 @@ int launch_tiles(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* code
   if constexpr (C::BM == TileBig::BM)
     hipLaunchKernelGGL(gemm_kernel<GS>, grid, block, 0, stream, X, (int)M, ldx, codes, scales,
                        zeros, (int)N, (int)K, Y, ldy, (int)mt, (int)nt);
-  else if constexpr (C::BM == TileSmall::BM)
+  else if constexpr (C::BM == TileSmall::BM && GS == kSteps)
     hipLaunchKernelGGL(gemm_small_kernel<GS>, grid, block, 0, stream, X, (int)M, ldx, codes, scales,
+                       zeros, (int)N, (int)K, Y, ldy, (int)mt, (int)nt);
+  else if constexpr (C::BM == TileSmall::BM)
+    hipLaunchKernelGGL(gemm_small2_kernel<GS>, grid, block, 0, stream, X, (int)M, ldx, codes, scales,
                        zeros, (int)N, (int)K, Y, ldy, (int)mt, (int)nt);
   else
     hipLaunchKernelGGL(gemm_tiny_kernel<GS>, grid, block, 0, stream, X, (int)M, ldx, codes, scales,
@@ -528,12 +542,21 @@ int launch_gemm_g128(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* 
 int launch_gemm(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
                 const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K, int group,
                 uint16_t* Y, int64_t ldy, hipStream_t stream) {
-  // Groups of 32 or 64: a rescale every one or two steps; the larger tiles
-  // would spill their accumulators, so 64 x 128 tiles only.
-  if (group == 32)
-    return launch_tiles<TileTiny, 1>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
-  if (group == 64)
-    return launch_tiles<TileTiny, 2>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
+  // Groups of 32 or 64: a rescale every one or two steps; 256 x 256 tiles
+  // would spill their accumulators, so 128 x 128 tiles at two waves per
+  // SIMD, or 64 x 128 tiles when those fill the rounds of CUs better.
+  if (group != kGroup) {
+    const int64_t cus = device_cu_count();
+    auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+    auto fill = [&](int64_t t) { return (double)t / (double)(((t + cus - 1) / cus) * cus); };
+    const bool tiny =
+        fill(tiles(TileTiny::BM, TileTiny::BN)) > fill(tiles(TileSmall::BM, TileSmall::BN)) + 1e-9;
+    if (group == 32)
+      return tiny ? launch_tiles<TileTiny, 1>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream)
+                  : launch_tiles<TileSmall, 1>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
+    return tiny ? launch_tiles<TileTiny, 2>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream)
+                : launch_tiles<TileSmall, 2>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
+  }
   return launch_gemm_g128(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
 }
 
