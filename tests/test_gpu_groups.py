@@ -151,3 +151,19 @@ def test_group_128_is_the_default_path():
     torch.cuda.synchronize()
     assert torch.equal(p.codes, q.codes) and torch.equal(p.zeros, q.zeros)
     assert torch.equal(p.scales.view(torch.int16), q.scales.view(torch.int16))
+
+
+@pytest.mark.parametrize("group", GROUPS)
+def test_linear_dispatch_boundary_and_awq(group):
+    """w4a16_linear at the decode / prefill boundary (M = 32, 33) on AWQ
+    pre-scaled weights packed with the smaller group."""
+    N, K = 640, 1024
+    W = gen.weights(N, K, "groups", "lin", shift=True, device=DEV)
+    s = gen.channel_vector(K, "groups", "lin", "awq").to(DEV)
+    p = w4.w4a16_pack(W, awq_s=s, group=group)
+    for M in (32, 33):
+        X = gen.activations(M, K, "groups", f"lin{M}", device=DEV)
+        y = w4.w4a16_linear(X, p)
+        torch.cuda.synchronize()
+        y_ref, mag = reference(gen.bits(X), gen.bits(W), awq_s=s.cpu().numpy(), group=group)
+        assert_output_close(y, y_ref, mag, label=f"group {group} linear M={M}")

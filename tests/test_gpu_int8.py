@@ -97,3 +97,18 @@ def test_gemv_oracle_packed_llama_layers_sampled(M):
         y_ref, mag = int8_reference(gen.bits(X), codes, scales, zeros, rows)
         assert_output_close(y[:, torch.as_tensor(rows, device=DEV)], y_ref, mag,
                             label=f"int8 {L.name} M={M}")
+
+
+@pytest.mark.parametrize("N,K", [(1, 128), (5, 256), (37, 32768)])
+def test_gemv_edge_shapes(N, K):
+    W = gen.weights(N, K, "int8", f"edge{N}x{K}", shift=True, device=DEV)
+    p = w4.w4a16_pack_int8(W)
+    torch.cuda.synchronize()
+    assert_int8_pack_equal(p, gen.bits(W))
+    codes, scales, zeros = O.quantize_pack_int8(gen.bits(W))
+    for M in (1, 3):
+        X = gen.activations(M, K, "int8", f"edge{N}x{K}", device=DEV)
+        y = w4.w4a16_gemv_int8(X, p)
+        torch.cuda.synchronize()
+        y_ref, mag = int8_reference(gen.bits(X), codes, scales, zeros)
+        assert_output_close(y, y_ref, mag, label=f"int8 edge M={M} {N}x{K}")
