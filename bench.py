@@ -570,6 +570,18 @@ def comparisons(workload, fused_ms_per_step, fused_prefill, dev, stream, steps=4
         "w4a16_speedup_vs_w8a16": round(us_i8 / fused_us, 3),
         "rotating_copies": icopy, "rel_l2_vs_dense": rel8,
     }
+    if fused_prefill is not None:
+        t8 = []
+        for L, p in zip(layers, i8):
+            x = gen.activations(prefill_m, L.K, "llama8b_prefill", L.name, device=dev)
+            y = torch.empty(prefill_m, L.N, dtype=torch.bfloat16, device=dev)
+            t8.append(_graph_us(stream, lambda r, x=x, p=p, y=y: w4.w4a16_gemm_int8(x, p, y), 5))
+            del x, y
+        flops = sum(2.0 * prefill_m * L.N * L.K for L in layers)
+        out[f"w8a16_prefill_M{prefill_m}"] = {
+            "TFLOPs": round(flops / (sum(t8) * 1e-6) / 1e12, 1),
+            "layers_ms": [round(t * 1e-3, 4) for t in t8]}
+        log(f"[bench] W8A16 prefill M={prefill_m}: {flops / (sum(t8) * 1e-6) / 1e12:.1f} TFLOP/s")
     log(f"[bench] W8A16 decode M=1: {us_i8:.1f} us/step ({i8_bytes / (us_i8 * 1e-6) / 1e9:.0f} GB/s), "
         f"{us_dense / us_i8:.2f}x dense bf16; rel l2 {max(rel8):.5f}")
     del icopies, ixs, iys, i8

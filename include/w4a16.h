@@ -58,7 +58,7 @@ extern "C" {
 #endif
 
 #define W4A16_GROUP 128
-#define W4A16_ABI_VERSION 5
+#define W4A16_ABI_VERSION 6
 #define W4A16_GEMV_MAX_M 32
 #define W4A16_DENSE_GEMV_MAX_M 8
 #define W4A16_INT8_GEMV_MAX_M 4
@@ -178,7 +178,7 @@ int w4a16_gemm_grouped(const uint16_t* X, int64_t M, int64_t ldx,
                        uint16_t* Y, int64_t ldy, void* stream);
 
 /*
- * w4a16_pack_int8, w4a16_gemv_int8 -- the W8A16 variant (Zeno AGI, "Weight-
+ * w4a16_pack_int8, w4a16_gemv_int8, w4a16_gemm_int8 -- the W8A16 variant (Zeno AGI, "Weight-
  * only vs mixed precision", its precision matrix: 8-bit weights, 16-bit
  * activations).  Codes are 8-bit, four per word: codes uint32_t [N][K/4],
  * byte j of word i of row n is q[n, 4i + j] (the byte stream is q row by
@@ -188,12 +188,17 @@ int w4a16_gemm_grouped(const uint16_t* X, int64_t M, int64_t ldx,
  * and K <= W4A16_INT8_GEMV_MAX_K (larger K: W4A16_ERR_UNSUPPORTED), with the
  * accuracy and alignment rules of w4a16_gemv; each code's two nibbles feed
  * the matrix product as exact BF16 operands, so no weight is rounded.
- * There is no prefill entry point for 8-bit codes.
+ * w4a16_gemm_int8 is the prefill product on the matrix cores, any M >= 1,
+ * with the rules of w4a16_gemm.
  */
 int w4a16_pack_int8(const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
                     const float* awq_s, uint32_t* codes, uint16_t* scales,
                     int32_t* zeros, void* stream);
 int w4a16_gemv_int8(const uint16_t* X, int64_t M, int64_t ldx,
+                    const uint32_t* codes, const uint16_t* scales,
+                    const int32_t* zeros, int64_t N, int64_t K,
+                    uint16_t* Y, int64_t ldy, void* stream);
+int w4a16_gemm_int8(const uint16_t* X, int64_t M, int64_t ldx,
                     const uint32_t* codes, const uint16_t* scales,
                     const int32_t* zeros, int64_t N, int64_t K,
                     uint16_t* Y, int64_t ldy, void* stream);

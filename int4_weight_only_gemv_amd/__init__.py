@@ -49,6 +49,7 @@ _SIGS = {
     "w4a16_pack_grouped": ([_p, _i64, _i64, _i64, _p, _i64, _p, _p, _p, _p], ctypes.c_int),
     "w4a16_pack_int8": ([_p, _i64, _i64, _i64, _p, _p, _p, _p, _p], ctypes.c_int),
     "w4a16_gemv_int8": ([_p, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _i64, _p], ctypes.c_int),
+    "w4a16_gemm_int8": ([_p, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _i64, _p], ctypes.c_int),
     "w4a16_gemv_grouped": ([_p, _i64, _i64, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _p], ctypes.c_int),
     "w4a16_gemm_grouped": ([_p, _i64, _i64, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _p], ctypes.c_int),
 }
@@ -188,6 +189,11 @@ def w4a16_pack_int8(W: torch.Tensor, awq_s: torch.Tensor | None = None) -> Packe
 def w4a16_gemv_int8(X: torch.Tensor, p: PackedLinearInt8, out: torch.Tensor | None = None) -> torch.Tensor:
     """Y = X . w_hat^T for 8-bit codes, 1 <= M <= 4 (decode)."""
     return _matmul(lib.w4a16_gemv_int8, "w4a16_gemv_int8", X, p, out)
+
+
+def w4a16_gemm_int8(X: torch.Tensor, p: PackedLinearInt8, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = X . w_hat^T for 8-bit codes on the matrix cores, any M (prefill)."""
+    return _matmul(lib.w4a16_gemm_int8, "w4a16_gemm_int8", X, p, out)
 
 
 def packed_from_i64(codes_i64: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor) -> PackedLinear:

@@ -11,6 +11,8 @@ int launch_pack(const uint16_t*, int64_t, int64_t, int64_t, const float*, int, u
                 uint16_t*, int32_t*, bool, bool, hipStream_t);
 int launch_gemv_int8(const uint16_t*, int64_t, int64_t, const uint32_t*, const uint16_t*,
                      const int32_t*, int64_t, int64_t, uint16_t*, int64_t, hipStream_t);
+int launch_gemm_int8(const uint16_t*, int64_t, int64_t, const uint32_t*, const uint16_t*,
+                     const int32_t*, int64_t, int64_t, uint16_t*, int64_t, hipStream_t);
 int launch_gemv(const uint16_t*, int64_t, int64_t, const uint32_t*, const uint16_t*,
                 const int32_t*, int64_t, int64_t, int, uint16_t*, int64_t, hipStream_t);
 int launch_gemm(const uint16_t*, int64_t, int64_t, const uint32_t*, const uint16_t*,
@@ -114,6 +116,14 @@ int w4a16_gemv_int8(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* c
   if (M > W4A16_INT8_GEMV_MAX_M) return W4A16_ERR_INVALID_ARG;
   if (K > W4A16_INT8_GEMV_MAX_K) return W4A16_ERR_UNSUPPORTED;
   return w4a16::launch_gemv_int8(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, (hipStream_t)stream);
+}
+
+int w4a16_gemm_int8(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
+                    const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K, uint16_t* Y,
+                    int64_t ldy, void* stream) {
+  int st = check_matmul(X, M, ldx, codes, scales, zeros, N, K, Y, ldy);
+  if (st != W4A16_OK) return st;
+  return w4a16::launch_gemm_int8(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, (hipStream_t)stream);
 }
 
 int w4a16_pack_grouped(const uint16_t* W, int64_t N, int64_t K, int64_t ldw, const float* awq_s,

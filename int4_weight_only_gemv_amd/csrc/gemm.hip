@@ -119,16 +119,22 @@ __device__ __forceinline__ void wait_vmcnt() {
 // flight is everything issued after them: two more steps of X copies and,
 // at positions 1 and 2, the block-start loads.  At position 3 the wait also
 // covers the next block's code copies (issued before the awaited X copies).
-template <class C, int ST>
+template <class C, int ST, int CL>
 __device__ __forceinline__ void wait_step() {
-  constexpr int kBlockStart = 2 + C::C_LOADS;
+  constexpr int kBlockStart = 2 + CL;   // CL: code copies per wave per block
   if (ST == 1 || ST == 2) wait_vmcnt<2 * C::X_LOADS + kBlockStart>(); else wait_vmcnt<2 * C::X_LOADS>();
 }
 
 // GS: K steps per quantisation group (1, 2 or 4: groups of 32, 64 or 128
 // inputs).  Codes always move in blocks of 128 inputs (four steps); a block
 // holds kSteps / GS groups.
-template <class C, int GS>
+// W8: the W8A16 variant (8-bit codes, byte j of word i is k = 4i + j, groups
+// of 128).  A code q = 16 h + l feeds two products on the same A fragment:
+// B = 128 + l (the INT4 operand) and B = 16 (128 + h) (the same mantissa
+// under exponent byte 0x45), both exact, so the accumulator gathers
+// sum x q + 17 * 128 * Xsum and the fold removes 17 * 128 + z.  Code rows are
+// 128 bytes per block in LDS, their 16-byte chunks XOR-swizzled by row & 7.
+template <class C, int GS, bool W8 = false>
 __device__ __forceinline__ void gemm_tile(
     const uint16_t* __restrict__ X, int M, int64_t ldx, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K,
@@ -136,8 +142,12 @@ __device__ __forceinline__ void gemm_tile(
   static_assert(GS == 1 || GS == 2 || GS == 4, "groups of 32, 64 or 128 inputs");
   constexpr int GPB = kSteps / GS;   // groups per 128-input block
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, MT = C::MT, NT = C::NT;
-  constexpr int X_STAGE = C::X_STAGE, C_GROUP = C::C_GROUP;
-  constexpr int X_LOADS = C::X_LOADS, C_LOADS = C::C_LOADS, XS_TILES = C::XS_TILES;
+  static_assert(!W8 || GS == kSteps, "8-bit codes use groups of 128");
+  constexpr int C_ROW_B = W8 ? 2 * C_ROW : C_ROW;            // code bytes per column per block
+  constexpr int X_STAGE = C::X_STAGE, C_GROUP = BN * C_ROW_B;
+  constexpr int X_LOADS = C::X_LOADS, C_LOADS = C_GROUP / 1024 / C::kWaves, XS_TILES = C::XS_TILES;
+  static_assert(C_LOADS == 2 || C_LOADS == 4, "copy split");
+  constexpr int CR_COPY = 1024 / C_ROW_B;                    // code rows per 1-KiB copy
   // one LDS object per buffer, so the compiler can tell the copies into one
   // buffer from the reads of another.  The X stages' larger alignment places
   // them first, below 64 KiB, where their addresses fit the immediate offset
@@ -179,16 +189,24 @@ __device__ __forceinline__ void gemm_tile(
   // Rows past M (N) read the last row and are never stored.
   const uint32_t swz = (uint32_t)(((lane & 3) ^ ((lane >> 3) & 3)) * 16);
   const char* xblk = reinterpret_cast<const char*>(X + (int64_t)m0 * ldx);
-  const char* cblk = reinterpret_cast<const char*>(codes + (int64_t)n0 * (K / 8));
+  const char* cblk = reinterpret_cast<const char*>(codes + (int64_t)n0 * (K / (W8 ? 4 : 8)));
   uint32_t xoffs[X_LOADS], coffs[C_LOADS];
 #pragma unroll
   for (int j = 0; j < X_LOADS; ++j)
     xoffs[j] = (uint32_t)(min(m0 + 16 * (X_LOADS * wave + j) + (lane >> 2), M - 1) - m0) * (uint32_t)(ldx * 2) + swz;
 #pragma unroll
-  for (int j = 0; j < C_LOADS; ++j)
-    coffs[j] = (uint32_t)(min(n0 + 16 * (C_LOADS * wave + j) + (lane >> 2), N - 1) - n0) * (uint32_t)(K / 2) + swz;
+  for (int j = 0; j < C_LOADS; ++j) {
+    if constexpr (W8) {
+      // lane -> code row (8 per copy) lane / 8, LDS slot lane % 8, which
+      // holds the row's 16-byte chunk slot ^ (row & 7)
+      const int row = CR_COPY * (C_LOADS * wave + j) + (lane >> 3);
+      coffs[j] = (uint32_t)(min(n0 + row, N - 1) - n0) * (uint32_t)K + (uint32_t)((((lane & 7) ^ (row & 7))) * 16);
+    } else {
+      coffs[j] = (uint32_t)(min(n0 + 16 * (C_LOADS * wave + j) + (lane >> 2), N - 1) - n0) * (uint32_t)(K / 2) + swz;
+    }
+  }
   const int xdst0 = 16 * X_LOADS * wave * (KS * 2);
-  const int cdst0 = 16 * C_LOADS * wave * C_ROW;
+  const int cdst0 = CR_COPY * C_LOADS * wave * C_ROW_B;
   // X copies of K step t (clamped by the caller)
   auto copy_x = [&](uint8_t* dst, int t) {
 #pragma unroll
@@ -200,8 +218,8 @@ __device__ __forceinline__ void gemm_tile(
   auto copy_codes = [&](uint8_t* dst, int g) {
 #pragma unroll
     for (int j = 0; j < C_LOADS; ++j)
-      __builtin_amdgcn_global_load_lds(cblk + (coffs[j] + (uint32_t)(g * C_ROW)),
-                                       (lds_void*)&dst[cdst0 + j * 16 * C_ROW], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(cblk + (coffs[j] + (uint32_t)(g * C_ROW_B)),
+                                       (lds_void*)&dst[cdst0 + j * 1024], 16, 0, 0);
   };
 
   // Scales and zero points: lane l of a wave fetches those of the wave's
@@ -250,7 +268,7 @@ __device__ __forceinline__ void gemm_tile(
   const int aoff = arow * (KS * 2) + ((q ^ ((arow >> 1) & 3)) * 16);
   const int brow = wn * WN + r16;
   const int bswz = (brow >> 1) & 3;
-  const int boff = brow * C_ROW + q * 4;
+  const int boff = W8 ? brow * C_ROW_B + (q & 1) * 8 : brow * C_ROW + q * 4;
   // Row tiles in a wave-dependent order: register row tile j is row tile
   // rowt(j), so that the tiles whose activation sums this wave computes
   // (XS_TILES wn ..) come first and their A fragments are af[0 ..].
@@ -269,7 +287,7 @@ __device__ __forceinline__ void gemm_tile(
   // move to the next group's scale (or, after the last group, apply it)
   auto group_end = [&](uint32_t s_fin, int z_fin, uint32_t s_next, bool last, const float* xbuf) {
     // this lane's column: bias + zero point and the scale factor
-    const float zl = (float)(128 + z_fin);
+    const float zl = (float)((W8 ? 17 * 128 : 128) + z_fin);
     const float sc = bf16_to_f32(s_fin);
     const float rl = last ? sc : sc * __builtin_amdgcn_rcpf(bf16_to_f32(s_next));
     // n tile nt's column r16 + 16 nt sits in that lane
@@ -293,12 +311,24 @@ __device__ __forceinline__ void gemm_tile(
   // Operand fragments of one K step, read from LDS one step ahead of use:
   // the raw code words of the 4 column tiles (chunk `pos` of the group
   // buffer) and A of the 8 row tiles.
+  // (8-bit codes: two words, inputs 8q .. 8q+7 of the step, from chunk
+  // 2 pos + q / 2 of the 128-byte row)
   u32x4 af[MT];
-  uint32_t bw[NT];
+  uint32_t bw[NT][W8 ? 2 : 1];
   auto read_b = [&](const uint8_t* cg, int pos) {
-    const int bo = boff + ((pos ^ bswz) * 16);
+    if constexpr (W8) {
+      const int bo = boff + (((2 * pos + (q >> 1)) ^ (brow & 7)) * 16);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) bw[nt] = *reinterpret_cast<const uint32_t*>(&cg[bo + nt * 16 * C_ROW]);
+      for (int nt = 0; nt < NT; ++nt) {
+        const uint2 v = *reinterpret_cast<const uint2*>(&cg[bo + nt * 16 * C_ROW_B]);
+        bw[nt][0] = v.x;
+        bw[nt][1] = v.y;
+      }
+    } else {
+      const int bo = boff + ((pos ^ bswz) * 16);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) bw[nt][0] = *reinterpret_cast<const uint32_t*>(&cg[bo + nt * 16 * C_ROW]);
+    }
   };
   // per-lane A read offsets of the row tiles, kept in registers (opaque to
   // the compiler) so that each read is one instruction: the stage buffer's
@@ -350,14 +380,16 @@ __device__ __forceinline__ void gemm_tile(
     uint8_t* cg_here = GP == 0 ? cg0 : cg1;
     uint8_t* cg_other = GP == 0 ? cg1 : cg0;
     const int g = s / kSteps;
-    wait_step<C, ST>();   // step s + 1 landed, every read of stage ST done
+    wait_step<C, ST, C_LOADS>();   // step s + 1 landed, every read of stage ST done
     block_barrier();
     // pin this step's fragments here, so the compiler cannot pull their uses
     // up into the previous step next to the reads that produced them
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) asm volatile("" : "+v"(af[mt]));
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) asm volatile("" : "+v"(bw[nt]));
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int w = 0; w < (W8 ? 2 : 1); ++w) asm volatile("" : "+v"(bw[nt][w]));
     if (ST == 0) {
       // the previous block's last group: its activation sums are in LDS
       if (s > 0)
@@ -385,9 +417,21 @@ __device__ __forceinline__ void gemm_tile(
 #pragma unroll
     for (int i = 0; i < XS_TILES; ++i)
       xpart[i] = mfma16x16x32(af[i], ones, ST % GS == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : xpart[i]);
-    u32x4 b[NT];
+    u32x4 b[NT], bh[W8 ? NT : 1];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) b[nt] = codes_to_bias128_natural(bw[nt]);
+    for (int nt = 0; nt < NT; ++nt) {
+      if constexpr (W8) {
+        const uint32_t l0 = bw[nt][0] & 0x0F0F0F0Fu, h0 = (bw[nt][0] >> 4) & 0x0F0F0F0Fu;
+        const uint32_t l1 = bw[nt][1] & 0x0F0F0F0Fu, h1 = (bw[nt][1] >> 4) & 0x0F0F0F0Fu;
+        constexpr uint32_t kExp16 = 0x45454545u;   // BF16 0x45mm = 16 (128 + m)
+        b[nt] = u32x4{__builtin_amdgcn_perm(kExpBytes, l0, 0x04010400u), __builtin_amdgcn_perm(kExpBytes, l0, 0x04030402u),
+                      __builtin_amdgcn_perm(kExpBytes, l1, 0x04010400u), __builtin_amdgcn_perm(kExpBytes, l1, 0x04030402u)};
+        bh[nt] = u32x4{__builtin_amdgcn_perm(kExp16, h0, 0x04010400u), __builtin_amdgcn_perm(kExp16, h0, 0x04030402u),
+                       __builtin_amdgcn_perm(kExp16, h1, 0x04010400u), __builtin_amdgcn_perm(kExp16, h1, 0x04030402u)};
+      } else {
+        b[nt] = codes_to_bias128_natural(bw[nt][0]);
+      }
+    }
     // the next step's fragments (past the last step: a harmless re-read):
     // code words into the registers just freed, each A row tile after its
     // products
@@ -396,7 +440,10 @@ __device__ __forceinline__ void gemm_tile(
     for (int mt = 0; mt < MT; ++mt) {
       const u32x4 a = af[mt];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma16x16x32(a, b[nt], acc[mt][nt]);
+      for (int nt = 0; nt < NT; ++nt) {
+        acc[mt][nt] = mfma16x16x32(a, b[nt], acc[mt][nt]);
+        if constexpr (W8) acc[mt][nt] = mfma16x16x32(a, bh[nt], acc[mt][nt]);
+      }
       read_a(xs_next, mt);
     }
     if (ST % GS == GS - 1) {
@@ -461,15 +508,16 @@ void gemm_small_kernel(
   gemm_tile<TileSmall, GS>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, m_tiles, n_tiles);
 }
 
-// 128 x 128 tiles for groups of 32 or 64 inputs: two waves per SIMD, so that
-// the rescale every one or two steps has the registers it needs
-template <int GS>
+// 128 x 128 tiles for groups of 32 or 64 inputs and for 8-bit codes: two
+// waves per SIMD, so that the more frequent rescale or the second set of B
+// operands has the registers it needs
+template <int GS, bool W8>
 __global__ __launch_bounds__(TileSmall::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_small2_kernel(
     const uint16_t* __restrict__ X, int M, int64_t ldx, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K,
     uint16_t* __restrict__ Y, int64_t ldy, int m_tiles, int n_tiles) {
-  gemm_tile<TileSmall, GS>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, m_tiles, n_tiles);
+  gemm_tile<TileSmall, GS, W8>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, m_tiles, n_tiles);
 }
 
 // 64 x 128 tiles on two waves of 64 x 64, for layers whose 128 x 128 tiles
@@ -487,7 +535,7 @@ void gemm_tiny_kernel(
 }  // namespace
 
 namespace {
-template <class C, int GS>
+template <class C, int GS, bool W8 = false>
 int launch_tiles(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
                  const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K, uint16_t* Y,
                  int64_t ldy, hipStream_t stream) {
@@ -495,19 +543,19 @@ int launch_tiles(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* code
   if (mt * nt >= ((int64_t)1 << 31)) return 3;
   // per-lane 32-bit byte offsets within a tile's rows of X, of the codes and
   // of the zero points
-  if ((C::BM - 1) * ldx * 2 + K * 2 >= ((int64_t)1 << 32) || C::BN * (K / 2) >= ((int64_t)1 << 32) ||
+  if ((C::BM - 1) * ldx * 2 + K * 2 >= ((int64_t)1 << 32) || C::BN * (W8 ? K : K / 2) >= ((int64_t)1 << 32) ||
       C::BN * (K / (KS * GS)) * 4 >= ((int64_t)1 << 32))
     return 3;
   const dim3 grid((unsigned)(mt * nt)), block(C::kThreads);
   if constexpr (C::BM == TileBig::BM)
     hipLaunchKernelGGL(gemm_kernel<GS>, grid, block, 0, stream, X, (int)M, ldx, codes, scales,
                        zeros, (int)N, (int)K, Y, ldy, (int)mt, (int)nt);
-  else if constexpr (C::BM == TileSmall::BM && GS == kSteps)
+  else if constexpr (C::BM == TileSmall::BM && GS == kSteps && !W8)
     hipLaunchKernelGGL(gemm_small_kernel<GS>, grid, block, 0, stream, X, (int)M, ldx, codes, scales,
                        zeros, (int)N, (int)K, Y, ldy, (int)mt, (int)nt);
   else if constexpr (C::BM == TileSmall::BM)
-    hipLaunchKernelGGL(gemm_small2_kernel<GS>, grid, block, 0, stream, X, (int)M, ldx, codes, scales,
-                       zeros, (int)N, (int)K, Y, ldy, (int)mt, (int)nt);
+    hipLaunchKernelGGL((gemm_small2_kernel<GS, W8>), grid, block, 0, stream, X, (int)M, ldx, codes,
+                       scales, zeros, (int)N, (int)K, Y, ldy, (int)mt, (int)nt);
   else
     hipLaunchKernelGGL(gemm_tiny_kernel<GS>, grid, block, 0, stream, X, (int)M, ldx, codes, scales,
                        zeros, (int)N, (int)K, Y, ldy, (int)mt, (int)nt);
@@ -558,6 +606,13 @@ int launch_gemm(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes
                 : launch_tiles<TileSmall, 2>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
   }
   return launch_gemm_g128(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
+}
+
+// W8A16 variant, any M >= 1 (checked by the caller): 128 x 128 tiles
+int launch_gemm_int8(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
+                     const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K, uint16_t* Y,
+                     int64_t ldy, hipStream_t stream) {
+  return launch_tiles<TileSmall, kSteps, true>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
 }
 
 }  // namespace w4a16

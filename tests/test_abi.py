@@ -29,7 +29,7 @@ def test_header_declares_expected_entry_points():
         "w4a16_awq_importance", "w4a16_awq_scale", "w4a16_awq_fold", "w4a16_scale_channels",
         "w4a16_dequantize_bf16", "w4a16_dense_gemv", "w4a16_dense_gemm", "w4a16_pack_symmetric",
         "w4a16_pack_grouped", "w4a16_gemv_grouped", "w4a16_gemm_grouped",
-        "w4a16_pack_int8", "w4a16_gemv_int8"])
+        "w4a16_pack_int8", "w4a16_gemv_int8", "w4a16_gemm_int8"])
 
 
 def test_every_declared_symbol_is_exported():
@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strerror():
-    assert lib.w4a16_abi_version() == 5
+    assert lib.w4a16_abi_version() == 6
     for st in range(5):
         assert lib.w4a16_strerror(st)
     assert b"unknown" in lib.w4a16_strerror(99)
@@ -215,6 +215,9 @@ def test_int8_validation():
     assert gemv(f, K=32896, ldx=32896) == UNSUPPORTED     # K <= 32768
     assert gemv(f, X=FAKE + 2) == MISALIGNED
     assert gemv(f, codes=FAKE + 4) == MISALIGNED
+    g = lib.w4a16_gemm_int8
+    assert gemv(g, M=0) == INVALID and gemv(g, K=200, ldx=200) == INVALID
+    assert gemv(g, scales=FAKE + 1) == MISALIGNED
     pk = lib.w4a16_pack_int8
     assert pk(p(FAKE), 16, 200, 200, p(0), p(FAKE), p(FAKE), p(FAKE), p(0)) == INVALID
     assert pk(p(FAKE), 16, 256, 256, p(0), p(FAKE + 8), p(FAKE), p(FAKE), p(0)) == MISALIGNED

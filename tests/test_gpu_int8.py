@@ -112,3 +112,51 @@ def test_gemv_edge_shapes(N, K):
         torch.cuda.synchronize()
         y_ref, mag = int8_reference(gen.bits(X), codes, scales, zeros)
         assert_output_close(y, y_ref, mag, label=f"int8 edge M={M} {N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 16, 128), (256, 1000, 2048), (300, 130, 640), (129, 2000, 4096)])
+def test_gemm(M, N, K):
+    W = gen.weights(N, K, "int8", f"gemm{M}", shift=True, device=DEV)
+    X = gen.activations(M, K, "int8", f"gemm{M}", device=DEV)
+    p = w4.w4a16_pack_int8(W)
+    y = w4.w4a16_gemm_int8(X, p)
+    torch.cuda.synchronize()
+    codes, scales, zeros = O.quantize_pack_int8(gen.bits(W))
+    rows = sample_rows(N, 96, seed=N)
+    y_ref, mag = int8_reference(gen.bits(X), codes, scales, zeros, rows)
+    assert_output_close(y[:, torch.as_tensor(rows, device=DEV)], y_ref, mag, label=f"int8 gemm {M}x{N}x{K}")
+
+
+def test_gemm_oracle_packed_canaries_and_llama_prefill_sampled():
+    # random 8-bit codes from a seeded generator, strided output with canaries
+    M, N, K = 1000, 1300, 512
+    rng = np.random.default_rng(70)
+    codes = rng.integers(0, 2 ** 32, size=(N, K // 4), dtype=np.uint64).astype(np.uint32)
+    scales = O.f32_to_bf16_rtz(rng.uniform(1e-5, 1e-3, size=(N, K // 128)).astype(np.float32))
+    zeros = rng.integers(0, 256, size=(N, K // 128)).astype(np.int32)
+    p = w4.PackedLinearInt8(torch.from_numpy(codes.view(np.int32)).to(DEV), gen.from_bits(scales, DEV),
+                            torch.from_numpy(zeros).to(DEV))
+    X = gen.activations(M, K, "int8", "canary", device=DEV)
+    canary = torch.full((M + 2, N + 16), -77.0, dtype=torch.bfloat16, device=DEV)
+    out = canary[1:M + 1, 8:N + 8]
+    w4.w4a16_gemm_int8(X, p, out=out)
+    torch.cuda.synchronize()
+    inner = torch.zeros_like(canary, dtype=torch.bool)
+    inner[1:M + 1, 8:N + 8] = True
+    assert torch.all(canary[~inner] == -77.0), "write outside Y"
+    rows, mrows = sample_rows(N, 64, seed=71), sample_rows(M, 40, seed=72)
+    midx, ridx = torch.as_tensor(mrows, device=DEV), torch.as_tensor(rows, device=DEV)
+    y_ref, mag = int8_reference(gen.bits(X[midx]), codes, scales, zeros, rows)
+    assert_output_close(out[midx][:, ridx], y_ref, mag, label="int8 gemm canary")
+    # the 8B-shaped gate_up projection at M = 4096, sampled
+    L = [l for l in gen.LLAMA8B if l.name == "gate_up"][0]
+    W = gen.weights(L.N, L.K, "int8", L.name, device=DEV)
+    X = gen.activations(4096, L.K, "int8", L.name, device=DEV)
+    p = w4.w4a16_pack_int8(W)
+    y = w4.w4a16_gemm_int8(X, p)
+    torch.cuda.synchronize()
+    rows, mrows = sample_rows(L.N, 24, seed=73), sample_rows(4096, 16, seed=74)
+    midx, ridx = torch.as_tensor(mrows, device=DEV), torch.as_tensor(rows, device=DEV)
+    codes, scales, zeros = O.quantize_pack_int8(gen.bits(W[ridx]))
+    y_ref, mag = int8_reference(gen.bits(X[midx]), codes, scales, zeros)
+    assert_output_close(y[midx][:, ridx], y_ref, mag, label="int8 gate_up M=4096")
