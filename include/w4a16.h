@@ -28,6 +28,15 @@
  *   Faults inside a kernel surface at the caller's next synchronisation.
  * - Inputs are finite; non-finite weights or activations give undefined
  *   (but memory-safe) results.
+ * - The matmuls accept any finite BF16 scale -- zero, negative and subnormal
+ *   ones included, which the packers never write but a container read in
+ *   place may hold -- and any int32 zero point, in any sequence along a row,
+ *   with the accuracy stated for each entry point.
+ * - Every size (M, N, K, T) must be below W4A16_MAX_DIM = 2^30; larger
+ *   sizes return W4A16_ERR_UNSUPPORTED.
+ * - The kernels are built for gfx950 only: an entry point whose arguments
+ *   pass the checks returns W4A16_ERR_UNSUPPORTED when the current HIP
+ *   device is not a gfx950 GPU (or there is no device).
  * - Results are deterministic: no atomics; the same inputs give the same bits.
  *
  * Storage layout of a packed weight matrix with N outputs and K inputs
@@ -58,17 +67,22 @@ extern "C" {
 #endif
 
 #define W4A16_GROUP 128
-#define W4A16_ABI_VERSION 6
+#define W4A16_ABI_VERSION 7
 #define W4A16_GEMV_MAX_M 32
 #define W4A16_DENSE_GEMV_MAX_M 8
 #define W4A16_INT8_GEMV_MAX_M 4
 #define W4A16_INT8_GEMV_MAX_K 32768
+#define W4A16_MAX_DIM ((int64_t)1 << 30)
+/* Limits of the matrix-core GEMMs (32-bit per-tile offsets): ldx (and ldw of
+   the dense GEMM) below W4A16_GEMM_MAX_LD, K below W4A16_GEMM_MAX_K. */
+#define W4A16_GEMM_MAX_LD ((int64_t)1 << 23)
+#define W4A16_GEMM_MAX_K ((int64_t)1 << 25)
 
 enum {
   W4A16_OK = 0,
   W4A16_ERR_INVALID_ARG = 1, /* null pointer, bad size, bad leading dimension */
   W4A16_ERR_MISALIGNED = 2,  /* a pointer or leading dimension breaks an alignment rule */
-  W4A16_ERR_UNSUPPORTED = 3, /* no gfx950 device, or a size beyond a documented limit */
+  W4A16_ERR_UNSUPPORTED = 3, /* the current device is not gfx950, or a size beyond a documented limit */
   W4A16_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
 };
 
@@ -135,6 +149,16 @@ int w4a16_pack_symmetric(const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
  * even) on store.  Requires 1 <= M <= 32, N >= 1, K >= 128, K % 128 == 0,
  * ldx >= K, ldy >= N; X 16-byte aligned and ldx % 8 == 0; codes 16-byte
  * aligned.  Y must not overlap the inputs.
+ *
+ * Accuracy (every matmul entry point).  No weight is rounded: per group the
+ * kernels form s * (sum_k x (128 + q) - (128 + z) sum_k x) from exact
+ * integer-valued BF16 operands in float32.  Besides half a BF16 ulp from the
+ * store, an output therefore carries float32 rounding relative to
+ * sum_g |s_g| (128 + |z_g|) |sum_{k in g} x_k|: far below the store's
+ * rounding for ordinary groups, but for a group whose weights all
+ * dequantise to zero (every q = z, such as the packer's all-zero groups,
+ * scale 1.0) an absolute residue of order 2^-22 |s| 128 |sum x| that the
+ * group's zero weights do not bound.
  */
 int w4a16_gemv(const uint16_t* X, int64_t M, int64_t ldx,
                const uint32_t* codes, const uint16_t* scales,
@@ -145,8 +169,14 @@ int w4a16_gemv(const uint16_t* X, int64_t M, int64_t ldx,
  * w4a16_gemm -- prefill-shaped fused dequantise-multiply on the BF16 matrix
  * cores, any M >= 1 (tuned for M >= 256).  Same arguments, layout, accuracy
  * and alignment rules as w4a16_gemv, without the limit on M.  The
- * dequantised weights feed the matrix cores as exact small integers and the
- * group scale is applied in float32, so no weight is ever rounded.
+ * dequantised weights feed the matrix cores as exact integer-valued BF16
+ * operands times a power of four, and the rest of each group's scale is
+ * applied in float32, so no weight is ever rounded and consecutive groups'
+ * scales may differ by any factor (a zero scale's group contributes at most
+ * 2^-120 (128 + q) x per input, relative to the running unit of its row's
+ * earlier scales).  Also requires ldx < W4A16_GEMM_MAX_LD,
+ * K < W4A16_GEMM_MAX_K and ceil(M/64) * ceil(N/128) < 2^31, otherwise
+ * W4A16_ERR_UNSUPPORTED.
  */
 int w4a16_gemm(const uint16_t* X, int64_t M, int64_t ldx,
                const uint32_t* codes, const uint16_t* scales,
@@ -161,8 +191,9 @@ int w4a16_gemm(const uint16_t* X, int64_t M, int64_t ldx,
  * common settings) name; 128 gives exactly w4a16_pack / w4a16_gemv /
  * w4a16_gemm).  scales and zeros are [N][K/group]; K must still be a
  * multiple of 128.  The quantiser rules of w4a16_pack apply per group; the
- * matmuls keep the accuracy rules of w4a16_gemv / w4a16_gemm.  For group 32
- * and 64 the matmuls also require scales and zeros 16-byte aligned.
+ * matmuls keep the accuracy rules of w4a16_gemv / w4a16_gemm (and the GEMM
+ * limits of w4a16_gemm: w4a16_gemv_grouped runs the GEMM for M > 8).  For
+ * group 32 and 64 the matmuls also require scales and zeros 16-byte aligned.
  * Any other group value: W4A16_ERR_INVALID_ARG.
  */
 int w4a16_pack_grouped(const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
@@ -189,7 +220,7 @@ int w4a16_gemm_grouped(const uint16_t* X, int64_t M, int64_t ldx,
  * accuracy and alignment rules of w4a16_gemv; each code's two nibbles feed
  * the matrix product as exact BF16 operands, so no weight is rounded.
  * w4a16_gemm_int8 is the prefill product on the matrix cores, any M >= 1,
- * with the rules of w4a16_gemm.
+ * with the rules and limits of w4a16_gemm.
  */
 int w4a16_pack_int8(const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
                     const float* awq_s, uint32_t* codes, uint16_t* scales,
@@ -243,6 +274,23 @@ int w4a16_scale_channels(const uint16_t* X, int64_t M, int64_t K,
                          int64_t ldo, void* stream);
 
 /*
+ * w4a16_awq_search_error -- the objective of AWQ's exponent search (Axe
+ * Corsa model card, "Stage 1: Activation-Aware Weight Scaling"; cyankiwi
+ * Quantization docs, "The Baseline: AWQ": a light grid search over the
+ * exponent, scored by the layer's output error): the relative L2 distance
+ *   err[0] = sqrt( sum_{m,n} (Y[m,n] - Yref[m,n])^2 / sum_{m,n} Yref[m,n]^2 )
+ * between two BF16 outputs Y [M][ldy] and Yref [M][ldr] (for example the
+ * quantised layer's and the dense layer's).  Sums in float64 in a fixed
+ * order (deterministic); an all-zero Yref gives inf or NaN.  err is one
+ * double in device memory, 8-byte aligned.  Runs as one workgroup: meant for
+ * calibration, not the inference path.  Requires M, N >= 1, ldy >= N,
+ * ldr >= N.
+ */
+int w4a16_awq_search_error(const uint16_t* Y, int64_t ldy, const uint16_t* Yref,
+                           int64_t ldr, int64_t M, int64_t N, double* err,
+                           void* stream);
+
+/*
  * Dense BF16 comparisons.  Not part of the fused path: they measure the
  * alternatives it is chosen over (Zeno AGI, "Weight-only vs mixed
  * precision": the table of offline versus fused dequantisation, the naive
@@ -277,7 +325,9 @@ int w4a16_dense_gemv(const uint16_t* X, int64_t M, int64_t ldx,
 /*
  * w4a16_dense_gemm -- dense BF16 prefill-shaped Y = X * W^T on the matrix
  * cores, any M >= 1.  Same arguments, accuracy and rules as
- * w4a16_dense_gemv without the limit on M.
+ * w4a16_dense_gemv without the limit on M; also requires ldx and ldw below
+ * W4A16_GEMM_MAX_LD and ceil(M/256) * ceil(N/256) < 2^31, otherwise
+ * W4A16_ERR_UNSUPPORTED.
  */
 int w4a16_dense_gemm(const uint16_t* X, int64_t M, int64_t ldx,
                      const uint16_t* W, int64_t ldw, int64_t N, int64_t K,

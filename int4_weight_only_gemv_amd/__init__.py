@@ -52,6 +52,7 @@ _SIGS = {
     "w4a16_gemm_int8": ([_p, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _i64, _p], ctypes.c_int),
     "w4a16_gemv_grouped": ([_p, _i64, _i64, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _p], ctypes.c_int),
     "w4a16_gemm_grouped": ([_p, _i64, _i64, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _p], ctypes.c_int),
+    "w4a16_awq_search_error": ([_p, _i64, _p, _i64, _i64, _i64, _p, _p], ctypes.c_int),
 }
 for _name, (_args, _ret) in _SIGS.items():
     _f = getattr(lib, _name)
@@ -295,29 +296,43 @@ def w4a16_scale_channels(X: torch.Tensor, gamma: torch.Tensor,
     return out
 
 
+def w4a16_awq_search_error(Y: torch.Tensor, Yref: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Relative L2 distance of two BF16 outputs [M][N] (the search
+    objective), as a float64 tensor of one element on the device."""
+    _need(Y, torch.bfloat16, "Y", 2)
+    _need(Yref, torch.bfloat16, "Yref", 2)
+    if Y.shape != Yref.shape:
+        raise ValueError("Y and Yref must have the same shape")
+    if out is None:
+        out = torch.empty(1, dtype=torch.float64, device=Y.device)
+    M, N = Y.shape
+    _check("w4a16_awq_search_error",
+           lib.w4a16_awq_search_error(_ptr(Y), Y.stride(0), _ptr(Yref), Yref.stride(0), M, N,
+                                      _ptr(out), _stream(Y)))
+    return out
+
+
 def w4a16_awq_search(W: torch.Tensor, Xcal: torch.Tensor, alphas, X: torch.Tensor | None = None):
     """AWQ's grid search over the exponent alpha of s = importance^alpha,
     run on this library's kernels: importance from Xcal, then per alpha the
     scale, the packed W diag(s), the activations X diag(s)^-1 through the
     folded producer weight bf16(1/s), the fused product, and its relative
-    L2 error against the dense BF16 product of X and W (X defaults to Xcal).
-    Only the final norms are torch reductions.  Returns (index of the best
-    alpha, list of errors)."""
+    L2 error against the dense BF16 product of X and W (X defaults to Xcal),
+    all library calls.  Returns (index of the best alpha, list of errors)."""
     _need(W, torch.bfloat16, "W", 2)
     X = Xcal if X is None else X
     K = W.shape[1]
     imp = w4a16_awq_importance(Xcal)
-    y_dense = w4a16_dense_gemm(X, W).float()
-    dnorm = torch.linalg.vector_norm(y_dense)
-    errs = []
-    for a in alphas:
+    y_dense = w4a16_dense_gemm(X, W)
+    err = torch.empty(len(alphas), dtype=torch.float64, device=W.device)
+    for i, a in enumerate(alphas):
         s = w4a16_awq_scale(imp, float(a))
         p = w4a16_pack(W, awq_s=s)
         gamma = torch.ones(K, dtype=torch.bfloat16, device=W.device)
         w4a16_awq_fold(s, gamma)
         Xs = w4a16_scale_channels(X, gamma)
-        y = w4a16_gemm(Xs, p).float()
-        errs.append(float(torch.linalg.vector_norm(y - y_dense) / dnorm))
+        w4a16_awq_search_error(w4a16_gemm(Xs, p), y_dense, out=err[i:i + 1])
+    errs = err.tolist()
     best = min(range(len(errs)), key=lambda i: errs[i])
     return best, errs
 

@@ -49,6 +49,36 @@ __global__ __launch_bounds__(256) void scale_channels_kernel(const uint16_t* __r
   Xout[m * ldo + k] = f32_to_bf16_rne(__fmul_rn(bf16_to_f32(X[m * ldx + k]), bf16_to_f32(gamma[k])));
 }
 
+// err[0] = sqrt(sum (Y - R)^2 / sum R^2) over an M x N output pair, the
+// objective of AWQ's exponent search.  One workgroup: each thread sums a
+// fixed strided share in float64, then a fixed-order tree in LDS, so the
+// result does not depend on timing.
+constexpr int kErrThreads = 1024;
+__global__ __launch_bounds__(kErrThreads) void rel_l2_kernel(const uint16_t* __restrict__ Y, int64_t ldy,
+                                                             const uint16_t* __restrict__ R, int64_t ldr,
+                                                             int64_t M, int64_t N, double* __restrict__ err) {
+  __shared__ double num[kErrThreads], den[kErrThreads];
+  double a = 0.0, b = 0.0;
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t n = threadIdx.x; n < N; n += kErrThreads) {
+      const double r = (double)bf16_to_f32(R[m * ldr + n]);
+      const double d = (double)bf16_to_f32(Y[m * ldy + n]) - r;
+      a += d * d;
+      b += r * r;
+    }
+  num[threadIdx.x] = a;
+  den[threadIdx.x] = b;
+  __syncthreads();
+  for (int h = kErrThreads / 2; h > 0; h >>= 1) {
+    if ((int)threadIdx.x < h) {
+      num[threadIdx.x] += num[threadIdx.x + h];
+      den[threadIdx.x] += den[threadIdx.x + h];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) err[0] = sqrt(num[0] / den[0]);
+}
+
 unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
 
 }  // namespace
@@ -75,6 +105,12 @@ int launch_scale_channels(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
                           const uint16_t* gamma, uint16_t* Xout, int64_t ldo, hipStream_t stream) {
   hipLaunchKernelGGL(scale_channels_kernel, dim3(blocks_for(M * K)), dim3(256), 0, stream, X, M, K,
                      ldx, gamma, Xout, ldo);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+int launch_rel_l2(const uint16_t* Y, int64_t ldy, const uint16_t* R, int64_t ldr, int64_t M, int64_t N,
+                  double* err, hipStream_t stream) {
+  hipLaunchKernelGGL(rel_l2_kernel, dim3(1), dim3(kErrThreads), 0, stream, Y, ldy, R, ldr, M, N, err);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 

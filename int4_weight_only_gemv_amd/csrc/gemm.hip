@@ -8,13 +8,21 @@
 // matrix cores add sum_k X (128 + q) into the accumulator; the same A
 // operand against a B of ones gives Xs[m] = sum_{k in g} X[m,k].
 //
-// One accumulator, rescaled per group.  The accumulator T is kept in units
-// of the current group's scale:
-//     end of group g:  T <- (T - (128 + z[n,g]) Xs[m]) * s[n,g] / s[n,g+1]
-// and after the last group the factor is s[n,G-1] itself, so T = Y.  The
-// scale ratios come from the hardware reciprocal (1 ulp) and one float32
-// multiply, a few 1e-7 relative each; the packer's scales are positive
-// normal BF16 values.
+// One accumulator, rescaled per group, in a per-column unit that stays near
+// one.  Group g's scale is split as s = u * 4^E with E = floor(log4 |s|)
+// (clamped to kEmin..kEmax) and u = s * 4^-E, so |u| lies in [1, 4) for
+// every normal scale.  The power of four goes into the B operand exactly:
+// its BF16 exponent byte becomes 0x43 + E, so B = 4^E (128 + q), still an
+// exact value, and the per-lane byte costs nothing in the unpack.  The
+// accumulator T is kept in units of the current group's u:
+//     end of group g:  T <- (T - 4^E (128 + z[n,g]) Xs[m]) * u_g / u_{g+1}
+// and after the last group the factor is u_{G-1} itself, so T = Y.  The
+// ratio of two units lies in (1/4, 4), so no sequence of scales can drive T
+// out of range: tiny groups after large ones (down to the smallest normal
+// BF16 scale), zero scales (the group then contributes at most 4^kEmin of
+// the running unit, and the unit is kept), subnormal and negative scales
+// all give the per-group result.  The unit ratio is a correctly rounded
+// float32 division, one rounding per group.
 //
 // Tiling.  A 512-thread block (8 waves, 2 along M x 4 along N) computes a
 // 256 x 256 tile of Y; each wave owns 128 x 64 (8 x 4 MFMA 16x16x32 tiles).
@@ -46,6 +54,23 @@ constexpr int KS = 32;                 // inputs per K step (a quarter group)
 constexpr int kSteps = kGroup / KS;    // K steps per group
 constexpr int C_ROW = kGroup / 2;      // bytes of codes per column per group (64)
 constexpr int kXcds = 8;
+
+// Range of the power-of-four exponent E folded into the B operands: the
+// exponent bytes 0x43 + E stay within 0x07 .. 0x7B, so B = 4^E (128 + q)
+// (and 4^E (256 + 16 h) for the high nibble of 8-bit codes) are normal BF16
+// values, and 4^E (128 + z) stays finite for any int32 z.
+constexpr int kEmin = -60, kEmax = 56;
+
+// Split of a group's scale (BF16 bits) into unit and exponent: E = floor(
+// log4 |s|) clamped to kEmin .. kEmax, u = s 4^-E (|u| in [1, 4) for normal
+// scales inside the clamp).  A zero scale keeps the previous unit (its group
+// then adds at most 4^kEmin (128 + q) per input, in that unit).
+__device__ __forceinline__ void split_scale(uint32_t sbits, float u_prev, int& E, float& u) {
+  const int e2 = (int)((sbits >> 7) & 0xFFu);   // biased exponent of the scale
+  E = min(max((e2 - 127) >> 1, kEmin), kEmax);
+  const float s = bf16_to_f32(sbits);
+  u = s == 0.f ? u_prev : __builtin_ldexpf(s, -2 * E);
+}
 
 // Block tile BM x BN on (BM / WM) x (BN / WN) waves, each computing a
 // WM x WN wave tile of 16x16 MFMA tiles.  The 256 x 256 tile (8 waves of
@@ -86,18 +111,20 @@ struct Ic {
   static constexpr int value = V;
 };
 
-// Eight codes of one word -> BF16 operands 128 + q in natural k order:
-// dword j holds (code 2j, code 2j+1).
-__device__ __forceinline__ u32x4 codes_to_bias128_natural(uint32_t w) {
+// Eight codes of one word -> BF16 operands 4^E (128 + q) in natural k
+// order: dword j holds (code 2j, code 2j+1).  eb holds the exponent byte
+// 0x43 + E in every byte (0x43: BF16 128.0, whose low mantissa bits count
+// in units of one).
+__device__ __forceinline__ u32x4 codes_to_bias128_natural(uint32_t w, uint32_t eb) {
   const uint32_t even = w & 0x0F0F0F0Fu;          // bytes q0 q2 q4 q6
   const uint32_t odd = (w >> 4) & 0x0F0F0F0Fu;    // bytes q1 q3 q5 q7
   const uint32_t lo = __builtin_amdgcn_perm(odd, even, 0x05010400u);  // q0 q1 q2 q3
   const uint32_t hi = __builtin_amdgcn_perm(odd, even, 0x07030602u);  // q4 q5 q6 q7
   u32x4 r;
-  r[0] = __builtin_amdgcn_perm(kExpBytes, lo, 0x04010400u);  // (q0, q1)
-  r[1] = __builtin_amdgcn_perm(kExpBytes, lo, 0x04030402u);  // (q2, q3)
-  r[2] = __builtin_amdgcn_perm(kExpBytes, hi, 0x04010400u);  // (q4, q5)
-  r[3] = __builtin_amdgcn_perm(kExpBytes, hi, 0x04030402u);  // (q6, q7)
+  r[0] = __builtin_amdgcn_perm(eb, lo, 0x04010400u);  // (q0, q1)
+  r[1] = __builtin_amdgcn_perm(eb, lo, 0x04030402u);  // (q2, q3)
+  r[2] = __builtin_amdgcn_perm(eb, hi, 0x04010400u);  // (q4, q5)
+  r[3] = __builtin_amdgcn_perm(eb, hi, 0x04030402u);  // (q6, q7)
   return r;
 }
 
@@ -130,10 +157,11 @@ __device__ __forceinline__ void wait_step() {
 // holds kSteps / GS groups.
 // W8: the W8A16 variant (8-bit codes, byte j of word i is k = 4i + j, groups
 // of 128).  A code q = 16 h + l feeds two products on the same A fragment:
-// B = 128 + l (the INT4 operand) and B = 16 (128 + h) (the same mantissa
-// under exponent byte 0x45), both exact, so the accumulator gathers
-// sum x q + 17 * 128 * Xsum and the fold removes 17 * 128 + z.  Code rows are
-// 128 bytes per block in LDS, their 16-byte chunks XOR-swizzled by row & 7.
+// B = 128 + l (the INT4 operand) and B = 256 + 16 h (8 h placed in mantissa
+// bits 3..6 under the same exponent byte with the exponent's low bit set),
+// both exact, so the accumulator gathers sum x q + 384 Xsum and the fold
+// removes 384 + z.  Code rows are 128 bytes per block in LDS, their 16-byte
+// chunks XOR-swizzled by row & 7.
 template <class C, int GS, bool W8 = false>
 __device__ __forceinline__ void gemm_tile(
     const uint16_t* __restrict__ X, int M, int64_t ldx, const uint32_t* __restrict__ codes,
@@ -283,20 +311,60 @@ __device__ __forceinline__ void gemm_tile(
   f32x4 xpart[XS_TILES];  // this wave's share of the group's activation sums
   const u32x4 ones = {kOnePair, kOnePair, kOnePair, kOnePair};
 
-  // fold a finished group into the accumulator: remove bias and zero point,
-  // move to the next group's scale (or, after the last group, apply it)
-  auto group_end = [&](uint32_t s_fin, int z_fin, uint32_t s_next, bool last, const float* xbuf) {
-    // this lane's column: bias + zero point and the scale factor
-    const float zl = (float)((W8 ? 17 * 128 : 128) + z_fin);
-    const float sc = bf16_to_f32(s_fin);
-    const float rl = last ? sc : sc * __builtin_amdgcn_rcpf(bf16_to_f32(s_next));
-    // n tile nt's column r16 + 16 nt sits in that lane
+  // This lane's metadata column: the unit u and exponent E of the current
+  // group (see split_scale), and per n tile the B exponent bytes of the
+  // current group for the accumulator layout's column r16 + 16 nt.
+  float u_col = 1.f;
+  int e_col = 0;
+  uint32_t eb[NT];
+  // Groups of 128: the transition is prepared a step ahead (off the
+  // critical path of the step that applies it), except on the 128 x 128
+  // tiles at three waves per SIMD, whose register budget has no room for it.
+  constexpr bool kPrep = GS == kSteps && (W8 || BM != TileSmall::BM);
+  // A group transition, prepared (per metadata column, in this lane) ahead
+  // of the step that applies it: the finished group's bias + zero point
+  // times its 4^E, the unit ratio, and the next group's unit and exponent.
+  float zl_p, rl_p, u_p;
+  int e_p;
+  auto spread_exponent = [&](int e) {
+    const int ebl = (int)((uint32_t)(0x43 + e) * 0x01010101u);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) eb[nt] = (uint32_t)__builtin_amdgcn_ds_bpermute((r16 + 16 * nt) * 4, ebl);
+  };
+  // the first group of the row: its unit and exponent
+  auto group_begin = [&](uint32_t s_first) {
+    split_scale(s_first, 1.f, e_col, u_col);
+    spread_exponent(e_col);
+  };
+  // prepare the end of the current group (zero point z_fin) and the move to
+  // the group with scale s_next, or, when last, the final application of the
+  // current unit; the current state does not change
+  auto prep_transition = [&](int z_fin, uint32_t s_next, bool last) {
+    zl_p = __builtin_ldexpf((float)z_fin + (W8 ? 384.f : 128.f), 2 * e_col);
+    rl_p = u_col;
+    u_p = u_col;
+    e_p = e_col;
+    if (!last) {
+      split_scale(s_next, u_col, e_p, u_p);
+      rl_p = u_col / u_p;
+    }
+  };
+  // apply the prepared transition: lane permutes move the column factors to
+  // the accumulator layout (column r16 + 16 nt), then the bias and zero
+  // point leave the accumulator and it moves to the next unit; the next
+  // group's exponent bytes follow the same way
+  auto apply_transition = [&](const float* xbuf, bool last) {
     float zb[NT], ratio[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int src = (r16 + 16 * nt) * 4;
-      zb[nt] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(zl)));
-      ratio[nt] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(rl)));
+      zb[nt] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(zl_p)));
+      ratio[nt] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(rl_p)));
+    }
+    if (!last) {
+      u_col = u_p;
+      e_col = e_p;
+      spread_exponent(e_col);
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -306,6 +374,12 @@ __device__ __forceinline__ void gemm_tile(
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[mt][nt][r] = fmaf(-zb[nt], xs[r], acc[mt][nt][r]) * ratio[nt];
     }
+  };
+  // fold a finished group into the accumulator in one go (transitions inside
+  // a 128-input block, and the last group)
+  auto group_end = [&](int z_fin, uint32_t s_next, bool last, const float* xbuf) {
+    prep_transition(z_fin, s_next, last);
+    apply_transition(xbuf, last);
   };
 
   // Operand fragments of one K step, read from LDS one step ahead of use:
@@ -364,6 +438,9 @@ __device__ __forceinline__ void gemm_tile(
   // (two static calls rather than one with a selected pointer, so the
   // compiler still tells the two code buffers apart)
   if (G & 1) prologue(cg1); else prologue(cg0);
+  // block 0's metadata landed before the prologue's barrier: the first
+  // group's unit and B exponent
+  group_begin(scale_of(s_nxt, 0));
 
   // One K step s at group position ST = s mod 4 of a group using code
   // buffer GP, whose X sits in stage ST; its fragments
@@ -392,9 +469,12 @@ __device__ __forceinline__ void gemm_tile(
       for (int w = 0; w < (W8 ? 2 : 1); ++w) asm volatile("" : "+v"(bw[nt][w]));
     if (ST == 0) {
       // the previous block's last group: its activation sums are in LDS
-      if (s > 0)
-        group_end(scale_of(s_cur, GPB - 1), z_cur[GPB - 1], scale_of(s_nxt, 0), false,
-                  xsum_lds[GS == kSteps ? GP ^ 1 : 1]);
+      if (s > 0) {
+        if constexpr (kPrep)
+          apply_transition(xsum_lds[GP ^ 1], false);   // prepared at the previous step
+        else
+          group_end(z_cur[GPB - 1], scale_of(s_nxt, 0), false, xsum_lds[GS == kSteps ? GP ^ 1 : 1]);
+      }
 #pragma unroll
       for (int i = 0; i < (GPB + 1) / 2; ++i) s_cur[i] = s_nxt[i];
 #pragma unroll
@@ -408,7 +488,11 @@ __device__ __forceinline__ void gemm_tile(
     } else if (ST % GS == 0) {
       // a group inside the block ends
       constexpr int i = ST / GS;
-      group_end(scale_of(s_cur, i - 1), z_cur[i - 1], scale_of(s_cur, i), false, xsum_lds[(i - 1) & 1]);
+      group_end(z_cur[i - 1], scale_of(s_cur, i), false, xsum_lds[(i - 1) & 1]);
+    } else if (kPrep && ST == kSteps - 1) {
+      // the next block's metadata landed with this step's wait: prepare the
+      // transition the next step applies (after the last group it is unused)
+      prep_transition(z_cur[0], scale_of(s_nxt, 0), false);
     }
     copy_x(xs_here, min(s + 4, steps - 1));
 
@@ -421,15 +505,17 @@ __device__ __forceinline__ void gemm_tile(
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       if constexpr (W8) {
-        const uint32_t l0 = bw[nt][0] & 0x0F0F0F0Fu, h0 = (bw[nt][0] >> 4) & 0x0F0F0F0Fu;
-        const uint32_t l1 = bw[nt][1] & 0x0F0F0F0Fu, h1 = (bw[nt][1] >> 4) & 0x0F0F0F0Fu;
-        constexpr uint32_t kExp16 = 0x45454545u;   // BF16 0x45mm = 16 (128 + m)
-        b[nt] = u32x4{__builtin_amdgcn_perm(kExpBytes, l0, 0x04010400u), __builtin_amdgcn_perm(kExpBytes, l0, 0x04030402u),
-                      __builtin_amdgcn_perm(kExpBytes, l1, 0x04010400u), __builtin_amdgcn_perm(kExpBytes, l1, 0x04030402u)};
-        bh[nt] = u32x4{__builtin_amdgcn_perm(kExp16, h0, 0x04010400u), __builtin_amdgcn_perm(kExp16, h0, 0x04030402u),
-                       __builtin_amdgcn_perm(kExp16, h1, 0x04010400u), __builtin_amdgcn_perm(kExp16, h1, 0x04030402u)};
+        // low nibbles l -> bytes l; high nibbles h -> bytes 0x80 | 8 h (BF16
+        // 0x43, 0x80 | 8h = 256 + 16 h; under 0x43 + E both scale by 4^E)
+        const uint32_t l0 = bw[nt][0] & 0x0F0F0F0Fu, h0 = ((bw[nt][0] >> 1) & 0x78787878u) | 0x80808080u;
+        const uint32_t l1 = bw[nt][1] & 0x0F0F0F0Fu, h1 = ((bw[nt][1] >> 1) & 0x78787878u) | 0x80808080u;
+        const uint32_t e = eb[nt];
+        b[nt] = u32x4{__builtin_amdgcn_perm(e, l0, 0x04010400u), __builtin_amdgcn_perm(e, l0, 0x04030402u),
+                      __builtin_amdgcn_perm(e, l1, 0x04010400u), __builtin_amdgcn_perm(e, l1, 0x04030402u)};
+        bh[nt] = u32x4{__builtin_amdgcn_perm(e, h0, 0x04010400u), __builtin_amdgcn_perm(e, h0, 0x04030402u),
+                       __builtin_amdgcn_perm(e, h1, 0x04010400u), __builtin_amdgcn_perm(e, h1, 0x04030402u)};
       } else {
-        b[nt] = codes_to_bias128_natural(bw[nt][0]);
+        b[nt] = codes_to_bias128_natural(bw[nt][0], eb[nt]);
       }
     }
     // the next step's fragments (past the last step: a harmless re-read):
@@ -483,7 +569,7 @@ __device__ __forceinline__ void gemm_tile(
   }
   wait_vmcnt<0>();   // the clamped copies past the last step
   __syncthreads();   // last group's activation sums (odd parity: see above)
-  group_end(scale_of(s_cur, GPB - 1), z_cur[GPB - 1], 0u, true, xsum_lds[1]);
+  group_end(z_cur[GPB - 1], 0u, true, xsum_lds[1]);
 
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)

@@ -72,8 +72,9 @@ constexpr int log2_exact(int v) { return v <= 1 ? 0 : 1 + log2_exact(v / 2); }
 // before the cross-lane sums.  Otherwise lg = 7 and the four lanes of a
 // group are summed first and fold once.
 // W8: the W8A16 variant, 8-bit codes (byte j of word i is k = 4i + j); each
-// byte's two nibbles h, l become BF16 128 + h and 128 + l like INT4 codes,
-// with two product chains per row, P = 16 P_h + P_l = sum x q + 17 * 128 * Xsum.
+// byte's nibbles l, h become exact BF16 operands 128 + l (like INT4 codes)
+// and 256 + 16 h (8 h in mantissa bits 3..6 with the exponent's low bit
+// set), so P = P_l + P_h = sum x q + 384 Xsum.
 template <int M, int R, int NB, bool PL, bool W8>
 __global__ __launch_bounds__(1024) void gemv_dot_kernel(
     const uint16_t* __restrict__ X, int64_t ldx, const uint32_t* __restrict__ codes,
@@ -171,7 +172,7 @@ __global__ __launch_bounds__(1024) void gemv_dot_kernel(
           for (int i = 0; i < 4; ++i) {
             // word i of vector v: inputs 16 v + 4 i .. +3, activation dwords d, d + 1
             const uint32_t w = cb[cur][j][v][i];
-            const uint32_t lb = w & 0x0F0F0F0Fu, hb = (w >> 4) & 0x0F0F0F0Fu;
+            const uint32_t lb = w & 0x0F0F0F0Fu, hb = ((w >> 1) & 0x78787878u) | 0x80808080u;
             const uint32_t l01 = __builtin_amdgcn_perm(kExpBytes, lb, 0x04010400u);
             const uint32_t l23 = __builtin_amdgcn_perm(kExpBytes, lb, 0x04030402u);
             const uint32_t h01 = __builtin_amdgcn_perm(kExpBytes, hb, 0x04010400u);
@@ -186,7 +187,7 @@ __global__ __launch_bounds__(1024) void gemv_dot_kernel(
             }
           }
 #pragma unroll
-        for (int m = 0; m < M; ++m) P[j][m] = fmaf(16.f, Ph[m], P[j][m]);
+        for (int m = 0; m < M; ++m) P[j][m] += Ph[m];
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -199,7 +200,7 @@ __global__ __launch_bounds__(1024) void gemv_dot_kernel(
       }
       if constexpr (PL) {
         const float s = bf16_to_f32(sb[cur][j]);
-        const float zb128 = (float)(128 + zb[cur][j]);
+        const float zb128 = (float)zb[cur][j] + 128.f;
 #pragma unroll
         for (int m = 0; m < M; ++m) P[j][m] = s * fmaf(-zb128, xsg[m], P[j][m]);
       }
@@ -223,7 +224,7 @@ __global__ __launch_bounds__(1024) void gemv_dot_kernel(
     {
       const uint32_t up = (lane & 1) ? ~0u : 0u;
       const float s = bf16_to_f32(sb[cur][0]);
-      const float zb128 = (float)((W8 ? 17 * 128 : 128) + zb[cur][0]);
+      const float zb128 = (float)zb[cur][0] + (W8 ? 384.f : 128.f);
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         const float send = pick(up, h[0][m], h[1][m]);
@@ -398,7 +399,7 @@ __global__ __launch_bounds__(1024) void gemv_quad_kernel(
       }
       // this lane's block: s * (P - (128 + z) * Xsum) for weight row j, group g[t]
       const float s = bf16_to_f32(sb[cur]);
-      const float zb128 = (float)(128 + zb[cur]);
+      const float zb128 = (float)zb[cur] + 128.f;
 #pragma unroll
       for (int m = 0; m < M; ++m)
         acc[m] = fmaf(s, fmaf(-zb128, xs[t][m / 4][m % 4], d[m / 4][m % 4]), acc[m]);
@@ -536,7 +537,7 @@ __global__ __launch_bounds__(1024) void gemv_quad_long_kernel(
                                 d[ms]);
         }
         const float s = bf16_to_f32(sb[cur]);
-        const float zb128 = (float)(128 + zb[cur]);
+        const float zb128 = (float)zb[cur] + 128.f;
 #pragma unroll
         for (int m = 0; m < M; ++m)
           acc[nb][m] = fmaf(s, fmaf(-zb128, xs[m / 4][m % 4], d[m / 4][m % 4]), acc[nb][m]);
@@ -681,7 +682,7 @@ __global__ __launch_bounds__(512) void gemv_tile_kernel(
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         const float sc = bf16_to_f32(sr[buf][rt]);
-        const float zb = (float)(128 + zr[buf][rt]);
+        const float zb = (float)zr[buf][rt] + 128.f;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll

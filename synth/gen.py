@@ -81,6 +81,58 @@ def activations(M: int, K: int, cfg, layer: str, *, role: str = "X",
     return x.to(torch.bfloat16)
 
 
+def hand_groups() -> dict:
+    """Constructed 128-value groups (float64 values, exactly representable in
+    BF16), the special cases of the quantiser: a constant group and its
+    negation, an all-zero group, a subnormal constant, alternating +-2^-125
+    (its scale is the smallest normal BF16 value), values on a grid far
+    from zero (large negative zero point), and an exact grid of step 2^-7."""
+    import numpy as np
+    j = np.arange(GROUP) % 16
+    return {
+        "const": np.full(GROUP, 0.375),
+        "neg_const": np.full(GROUP, -0.375),
+        "zero": np.zeros(GROUP),
+        "subnormal_const": np.full(GROUP, 2.0 ** -130),
+        "pm_2^-125": np.where(np.arange(GROUP) % 2 == 0, -(2.0 ** -125), 2.0 ** -125),
+        "far_from_zero": 100.0 + 0.5 * (np.arange(GROUP) % 8),
+        "grid_2^-7": (j - 8) * 2.0 ** -7,
+    }
+
+
+def extreme_weights(N: int, K: int, cfg, layer: str, *, device="cpu") -> torch.Tensor:
+    """BF16 weights [N][K] whose groups of 128 are either ordinary draws
+    (N(0, 0.02) or N(0, 1)) or one of hand_groups(), in a seeded random
+    order per row, so that tiny, zero and huge group scales follow ordinary
+    ones in every combination.  Even rows take no all-zero or subnormal
+    group (groups whose weights are all zero); odd rows take every kind."""
+    import numpy as np
+    assert K % GROUP == 0
+    G = K // GROUP
+    names = list(hand_groups())
+    hand = list(hand_groups().values())
+    rng = np.random.default_rng(seed_of(cfg, layer, "extreme") & 0xFFFFFFFF)
+    kind = rng.integers(0, 2 + len(hand), size=(N, G))
+    nonzero = [2 + i for i, n in enumerate(names) if n not in ("zero", "subnormal_const")]
+    pool = np.array([0, 1] + nonzero)
+    even = rng.integers(0, len(pool), size=(N, G))
+    kind[0::2] = pool[even[0::2]]
+    w = np.empty((N, K), dtype=np.float64)
+    ordinary = rng.standard_normal((N, K))
+    for n in range(N):
+        for g in range(G):
+            c = kind[n, g]
+            seg = slice(g * GROUP, (g + 1) * GROUP)
+            if c == 0:
+                w[n, seg] = 0.02 * ordinary[n, seg]
+            elif c == 1:
+                w[n, seg] = ordinary[n, seg]
+            else:
+                w[n, seg] = hand[c - 2]
+    t = torch.from_numpy(w.astype(np.float32)).to(torch.bfloat16)
+    return t.to(device)
+
+
 def channel_vector(K: int, cfg, layer: str, role: str, *, device="cpu") -> torch.Tensor:
     """A positive float32 per-channel vector exp(N(0, 0.5^2)), used as an
     arbitrary AWQ pre-scale when testing the packer on its own."""

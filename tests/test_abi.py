@@ -29,7 +29,7 @@ def test_header_declares_expected_entry_points():
         "w4a16_awq_importance", "w4a16_awq_scale", "w4a16_awq_fold", "w4a16_scale_channels",
         "w4a16_dequantize_bf16", "w4a16_dense_gemv", "w4a16_dense_gemm", "w4a16_pack_symmetric",
         "w4a16_pack_grouped", "w4a16_gemv_grouped", "w4a16_gemm_grouped",
-        "w4a16_pack_int8", "w4a16_gemv_int8", "w4a16_gemm_int8"])
+        "w4a16_pack_int8", "w4a16_gemv_int8", "w4a16_gemm_int8", "w4a16_awq_search_error"])
 
 
 def test_every_declared_symbol_is_exported():
@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strerror():
-    assert lib.w4a16_abi_version() == 6
+    assert lib.w4a16_abi_version() == 7
     for st in range(5):
         assert lib.w4a16_strerror(st)
     assert b"unknown" in lib.w4a16_strerror(99)
@@ -123,6 +123,11 @@ def test_awq_validation():
     assert lib.w4a16_scale_channels(p(FAKE), 2, 8, 7, p(FAKE), p(FAKE), 8, p(0)) == INVALID
     assert lib.w4a16_scale_channels(p(FAKE), 2, 8, 8, p(FAKE), p(FAKE), 7, p(0)) == INVALID
     assert lib.w4a16_scale_channels(p(FAKE), 2, 8, 8, p(FAKE + 1), p(FAKE), 8, p(0)) == MISALIGNED
+    e = lib.w4a16_awq_search_error
+    assert e(p(0), 8, p(FAKE), 8, 2, 8, p(FAKE), p(0)) == INVALID
+    assert e(p(FAKE), 8, p(FAKE), 8, 0, 8, p(FAKE), p(0)) == INVALID
+    assert e(p(FAKE), 7, p(FAKE), 8, 2, 8, p(FAKE), p(0)) == INVALID
+    assert e(p(FAKE), 8, p(FAKE), 8, 2, 8, p(FAKE + 4), p(0)) == MISALIGNED
 
 
 def test_binding_rejects_cpu_tensors():
@@ -222,3 +227,54 @@ def test_int8_validation():
     assert pk(p(FAKE), 16, 200, 200, p(0), p(FAKE), p(FAKE), p(FAKE), p(0)) == INVALID
     assert pk(p(FAKE), 16, 256, 256, p(0), p(FAKE + 8), p(FAKE), p(FAKE), p(0)) == MISALIGNED
     assert pk(p(0), 16, 256, 256, p(0), p(FAKE), p(FAKE), p(FAKE), p(0)) == INVALID
+
+
+def _no_gpu():
+    import torch
+    return torch.cuda.device_count() == 0
+
+
+@pytest.mark.parametrize("fn", ["w4a16_gemm", "w4a16_gemm_int8"])
+def test_gemm_offset_limits(fn):
+    f = getattr(lib, fn)
+    big = 1 << 23                                   # W4A16_GEMM_MAX_LD
+    assert gemv(f, ldx=big) == UNSUPPORTED
+    assert gemv(f, K=1 << 25, ldx=(1 << 25) + 8) == UNSUPPORTED   # W4A16_GEMM_MAX_K (ldx checked too)
+    # ceil(M/64) * ceil(N/128) tiles must stay below 2^31
+    assert gemv(f, M=1 << 29, N=1 << 29, ldy=1 << 29) == UNSUPPORTED
+
+
+def test_grouped_gemm_offset_limits():
+    f = lib.w4a16_gemm_grouped
+
+    def call(M=1, ldx=4096, K=4096, group=64):
+        return f(p(FAKE), M, ldx, p(FAKE), p(FAKE), p(FAKE), 4096, K, group, p(FAKE), 4096, p(0))
+    assert call(ldx=1 << 23) == UNSUPPORTED
+    g = lib.w4a16_gemv_grouped
+
+    def callv(M, ldx):
+        return g(p(FAKE), M, ldx, p(FAKE), p(FAKE), p(FAKE), 4096, 4096, 64, p(FAKE), 4096, p(0))
+    assert callv(16, 1 << 23) == UNSUPPORTED        # M > 8 runs the GEMM
+
+
+def test_dense_gemm_offset_limits():
+    f = lib.w4a16_dense_gemm
+    assert dense(f, ldx=1 << 23) == UNSUPPORTED
+    assert dense(f, ldw=1 << 23) == UNSUPPORTED
+
+
+def test_limits_match_header():
+    text = open(HEADER).read()
+    assert "#define W4A16_GEMM_MAX_LD ((int64_t)1 << 23)" in text
+    assert "#define W4A16_GEMM_MAX_K ((int64_t)1 << 25)" in text
+    assert "#define W4A16_MAX_DIM ((int64_t)1 << 30)" in text
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="only where no GPU is visible: the call would launch")
+def test_valid_call_without_a_device_is_unsupported():
+    # arguments that pass every check reach the device check, which finds no
+    # gfx950 device here and refuses before any launch
+    assert gemv() == UNSUPPORTED
+    assert gemv(lib.w4a16_gemm) == UNSUPPORTED
+    assert lib.w4a16_pack(p(FAKE), 16, 256, 256, p(0), p(FAKE), p(FAKE), p(FAKE), p(0)) == UNSUPPORTED
+    assert lib.w4a16_awq_fold(p(FAKE), 8, p(FAKE), p(0), p(0)) == UNSUPPORTED

@@ -114,3 +114,20 @@ def test_awq_search_matches_oracle(case):
     ref, ref_best = O.awq_search(Wb, Xb, alphas, Xeb)
     assert np.allclose(errs, ref, rtol=3e-2), (errs, ref)
     assert ref[best] <= ref[ref_best] * 1.02, (best, ref_best, ref)
+
+
+def test_search_error_entry_point():
+    """w4a16_awq_search_error against the plain definition of the relative
+    L2 distance, in float64, on strided outputs."""
+    M, N = 37, 1000
+    a = gen.activations(M, N, "awq", "err_a", device=DEV)
+    b = gen.activations(M, N + 24, "awq", "err_b", device=DEV)[:, 8:N + 8]
+    e = w4.w4a16_awq_search_error(a, b)
+    torch.cuda.synchronize()
+    ya = O.bf16_to_f32(gen.bits(a)).astype(np.float64)
+    yb = O.bf16_to_f32(gen.bits(b)).astype(np.float64)
+    want = np.sqrt(((ya - yb) ** 2).sum() / (yb ** 2).sum())
+    assert abs(float(e.item()) - want) <= 1e-12 * want
+    # deterministic, and zero for identical outputs
+    assert float(w4.w4a16_awq_search_error(a, b).item()) == float(e.item())
+    assert float(w4.w4a16_awq_search_error(b, b).item()) == 0.0
