@@ -291,6 +291,18 @@ int w4a16_awq_search_error(const uint16_t* Y, int64_t ldy, const uint16_t* Yref,
                            void* stream);
 
 /*
+ * w4a16_hbm_read_probe -- measurement helper, not part of the matmul path:
+ * reads `bytes` of device memory at buf with fully coalesced 16-byte loads
+ * (each wave instruction covers 1 KiB of consecutive bytes, several loads in
+ * flight per lane) and discards the data (sink, one uint32 in device memory,
+ * is written only for one particular XOR of the contents).  Timed over a
+ * buffer much larger than the last-level cache it gives the streaming-read
+ * ceiling the decode kernels are compared with, beside the specification's
+ * peak.  Requires bytes >= 16, bytes % 16 == 0, buf 16-byte aligned.
+ */
+int w4a16_hbm_read_probe(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
+
+/*
  * Dense BF16 comparisons.  Not part of the fused path: they measure the
  * alternatives it is chosen over (Zeno AGI, "Weight-only vs mixed
  * precision": the table of offline versus fused dequantisation, the naive

@@ -53,6 +53,7 @@ _SIGS = {
     "w4a16_gemv_grouped": ([_p, _i64, _i64, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _p], ctypes.c_int),
     "w4a16_gemm_grouped": ([_p, _i64, _i64, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _p], ctypes.c_int),
     "w4a16_awq_search_error": ([_p, _i64, _p, _i64, _i64, _i64, _p, _p], ctypes.c_int),
+    "w4a16_hbm_read_probe": ([_p, _i64, _p, _p], ctypes.c_int),
 }
 for _name, (_args, _ret) in _SIGS.items():
     _f = getattr(lib, _name)
@@ -335,6 +336,19 @@ def w4a16_awq_search(W: torch.Tensor, Xcal: torch.Tensor, alphas, X: torch.Tenso
     errs = err.tolist()
     best = min(range(len(errs)), key=lambda i: errs[i])
     return best, errs
+
+
+def w4a16_hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor | None = None) -> torch.Tensor:
+    """Stream-read every byte of `buf` (a contiguous device tensor whose size
+    is a multiple of 16 bytes) and discard it: the measurement helper behind
+    the measured HBM read ceiling.  Returns the sink word (device int32)."""
+    if not isinstance(buf, torch.Tensor) or not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    _check("w4a16_hbm_read_probe",
+           lib.w4a16_hbm_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(buf)))
+    return sink
 
 
 # ---------------------------------------------------------------------------

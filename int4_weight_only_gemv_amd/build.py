@@ -39,6 +39,7 @@ SOURCES = {
     "gemm.hip": [],
     "awq.hip": EXACT,
     "dense.hip": EXACT,
+    "probe.hip": [],
 }
 
 

@@ -25,6 +25,7 @@ int launch_awq_scale(const float*, int64_t, float, float*, hipStream_t);
 int launch_awq_fold(const float*, int64_t, uint16_t*, uint16_t*, hipStream_t);
 int launch_rel_l2(const uint16_t*, int64_t, const uint16_t*, int64_t, int64_t, int64_t, double*,
                   hipStream_t);
+int launch_hbm_read_probe(const void*, int64_t, uint32_t*, hipStream_t);
 int launch_scale_channels(const uint16_t*, int64_t, int64_t, int64_t, const uint16_t*, uint16_t*,
                           int64_t, hipStream_t);
 int launch_dequant_bf16(const uint32_t*, const uint16_t*, const int32_t*, int64_t, int64_t,
@@ -267,6 +268,13 @@ int w4a16_awq_search_error(const uint16_t* Y, int64_t ldy, const uint16_t* Yref,
   if (!aligned(Y, 2) || !aligned(Yref, 2) || !aligned(err, 8)) return W4A16_ERR_MISALIGNED;
   if (int dc = device_check()) return dc;
   return w4a16::launch_rel_l2(Y, ldy, Yref, ldr, M, N, err, (hipStream_t)stream);
+}
+
+int w4a16_hbm_read_probe(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink || bytes < 16 || bytes % 16) return W4A16_ERR_INVALID_ARG;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return W4A16_ERR_MISALIGNED;
+  if (int dc = device_check()) return dc;
+  return w4a16::launch_hbm_read_probe(buf, bytes, sink, (hipStream_t)stream);
 }
 
 int w4a16_dequantize_bf16(const uint32_t* codes, const uint16_t* scales, const int32_t* zeros,

@@ -64,6 +64,22 @@ __device__ __forceinline__ u32x4 x_pairs_from_natural(u32x4 d) {
   return r;
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// c + a.lo * b.lo + a.hi * b.hi on two BF16 pairs, float32 result.
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// up ? a : b as one bit-select on a lane mask (all ones or zero).  Written
+// as bit operations so that the compiler keeps the two values in registers
+// instead of turning a select between array elements into an indexed
+// access (which it lowers to a chain of compares and selects).
+__device__ __forceinline__ float pick(uint32_t up_mask, float a, float b) {
+  return __uint_as_float((__float_as_uint(a) & up_mask) | (__float_as_uint(b) & ~up_mask));
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
   return __builtin_bit_cast(bf16x8, v);
 }

@@ -17,13 +17,6 @@
 namespace w4a16 {
 namespace {
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
-                                         __builtin_bit_cast(bf16x2, b), c, false);
-}
-
 // ---------------------------------------------------------------------------
 // Offline expansion: w = BF16_RNE(fl32(fl32(q - z) * s)), one thread per code
 // word (eight weights, one 16-byte store)

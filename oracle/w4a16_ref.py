@@ -487,6 +487,86 @@ def awq_search(W_bits: np.ndarray, Xcal_bits: np.ndarray, alphas, X_bits: np.nda
 
 
 # ---------------------------------------------------------------------------
+# A chain of dependent decode linears (a decoder stack's weight stream)
+# ---------------------------------------------------------------------------
+#
+# The weight stream of a whole decoder (BASELINE config 5: 40 layers of four
+# INT4 linears) is a chain: each linear's input is formed from the output of
+# the one before by the layer's glue.  Readings (the pages describe the
+# linears and the AWQ fold, not the rest of the decoder):
+# * outputs are stored in BF16 (round to nearest even of the exact product),
+#   and each input is formed from the stored BF16 values;
+# * "prev": the previous output as is (o -> gate_up: the residual add and the
+#   normalisation are left out);
+# * "swiglu": the previous output holds the gate then the up projection
+#   ([gate | up], K each); x = silu(gate) * up with silu(g) = g / (1 + e^-g);
+# * "attn1": attention over a context of one cached token: the softmax over a
+#   single score is 1, so each query head's output is the value vector of its
+#   key/value head; the previous output holds [q | k | v] and head h (of
+#   head_dim inputs) reads v of key/value head h // group;
+# * an optional per-input-channel producer weight gamma (the folded AWQ
+#   1 / s, Axe Corsa model card, "Stage 1: Activation-Aware Weight Scaling")
+#   multiplies x;
+# * every formed input is rounded once to BF16 (nearest even).
+
+def f64_to_bf16_rne(x) -> np.ndarray:
+    """float64 -> BF16 bits, round to nearest even, one rounding (values in
+    the normal BF16 range): x = m 2^e with 1/2 <= |m| < 1, keep 8 significant
+    bits of m."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    r = np.ldexp(np.rint(m * 256.0), e - 8)          # np.rint: ties to even
+    return f32_to_bf16_rtz(r.astype(np.float32))     # r is exactly a BF16 value
+
+
+def silu_ref(g) -> np.ndarray:
+    """silu(g) = g / (1 + exp(-g)) in float64."""
+    g = np.asarray(g, dtype=np.float64)
+    return g / (1.0 + np.exp(-g))
+
+
+def chain_input(kind: str, y_prev_bits, K: int, params=None, gamma_bits=None,
+                x0_bits=None) -> np.ndarray:
+    """BF16 bits [M][K] of a chain linear's input (see the readings above).
+    kind: "x0" (the chain's own input x0_bits), "prev", "swiglu" or "attn1"
+    (params = (v_offset, head_dim, group))."""
+    if kind == "x0":
+        x = bf16_to_f32(np.asarray(x0_bits)[:, :K]).astype(np.float64)
+    elif kind == "prev":
+        x = bf16_to_f32(np.asarray(y_prev_bits)[:, :K]).astype(np.float64)
+    elif kind == "swiglu":
+        y = bf16_to_f32(np.asarray(y_prev_bits)).astype(np.float64)
+        x = silu_ref(y[:, :K]) * y[:, K:2 * K]
+    elif kind == "attn1":
+        v_off, head_dim, group = params
+        y = bf16_to_f32(np.asarray(y_prev_bits)).astype(np.float64)
+        k = np.arange(K)
+        src = v_off + (k // head_dim // group) * head_dim + k % head_dim
+        x = y[:, src]
+    else:
+        raise ValueError(kind)
+    if gamma_bits is not None:
+        x = x * bf16_to_f32(gamma_bits).astype(np.float64)[None, :]
+    return f64_to_bf16_rne(x)
+
+
+def chain_ref(x0_bits, linears):
+    """Run a chain.  linears: list of dicts with codes, scales, zeros (a packed
+    matrix), kind, optional params and gamma (BF16 bits [K]).  Returns the
+    list of (input BF16 bits [M][K], exact output float64 [M][N], stored
+    output BF16 bits [M][N]) per linear."""
+    out = []
+    y_prev = None
+    for L in linears:
+        K = L["codes"].shape[1] * 8
+        x = chain_input(L["kind"], y_prev, K, L.get("params"), L.get("gamma"), x0_bits)
+        y = matmul_ref(x, L["codes"], L["scales"], L["zeros"])
+        y_prev = f64_to_bf16_rne(y)
+        out.append((x, y, y_prev))
+    return out
+
+
+# ---------------------------------------------------------------------------
 # Parity gates on the floating-point output
 # ---------------------------------------------------------------------------
 

@@ -699,3 +699,104 @@ def check_awq_search_protects_salient(seed=18):
     assert errs[best] < 0.8 * errs[0], errs
     assert 0 < best < len(alphas) - 1, errs
     assert errs[-1] > errs[best] * 1.5, errs
+
+
+# ---------------------------------------------------------------------------
+# Chain of dependent linears (decoder-stack weight stream, its glue)
+# ---------------------------------------------------------------------------
+
+def _bf16_value(bits) -> Fraction:
+    return _frac_of_f32(O.bf16_to_f32(np.uint16(bits)))
+
+
+def check_f64_to_bf16_single_rounding(seed=31):
+    """float64 -> BF16 with one rounding to the nearest BF16 value, ties to
+    even, against exact rationals: random magnitudes, exact midpoints of
+    neighbouring BF16 values, and values one float64 ulp either side of them
+    (where a detour through float32 would round twice)."""
+    rng = np.random.default_rng(seed)
+    base = rng.standard_normal(400) * np.exp2(rng.integers(-40, 40, 400))
+    b = O.f32_to_bf16_rtz(base.astype(np.float32)).astype(np.int64)
+    lo = O.bf16_to_f32(b.astype(np.uint16)).astype(np.float64)
+    hi = O.bf16_to_f32((b + 1).astype(np.uint16)).astype(np.float64)
+    mid = (lo + hi) / 2                                  # exact in float64
+    xs = np.concatenate([base, mid, np.nextafter(mid, np.inf), np.nextafter(mid, -np.inf)])
+    got = O.f64_to_bf16_rne(xs)
+    for x, g in zip(xs, got):
+        fx = Fraction(float(x))
+        t = int(O.f32_to_bf16_rtz(np.float32(x)))
+        cands = [c for c in range(t - 2, t + 3) if 0 <= c < 0x10000 and (c & 0x7F80) != 0x7F80
+                 and (c >> 15) == (t >> 15)]
+        best = min(cands, key=lambda c: (abs(fx - _bf16_value(c)), c & 1))
+        assert int(g) == best, (x, hex(int(g)), hex(best))
+    # a value whose float32 rounding lands on a midpoint (float32 would round twice)
+    x = -0.011505127308113048
+    assert int(O.f64_to_bf16_rne(np.array([x]))[0]) == 0xBC3D
+
+
+def check_silu_identities():
+    """silu(g) - silu(-g) = g for every g (sigma(g) + sigma(-g) = 1),
+    silu(0) = 0, silu(g) -> g for large g and -> 0 for very negative g."""
+    g = np.linspace(-30, 30, 601)
+    d = O.silu_ref(g) - O.silu_ref(-g)
+    assert np.allclose(d, g, rtol=1e-14, atol=1e-14)
+    assert O.silu_ref(np.array([0.0]))[0] == 0.0
+    assert abs(O.silu_ref(np.array([50.0]))[0] - 50.0) < 1e-12
+    v = O.silu_ref(np.array([-50.0]))[0]
+    assert v < 0 and abs(v) < 1e-19
+    # sigma(1) = e / (1 + e): silu(1) = 0.7310585786300049 (to double precision)
+    assert abs(O.silu_ref(np.array([1.0]))[0] - 0.7310585786300049) < 1e-15
+
+
+def check_chain_input_hand():
+    """The glue of a chain linear on a hand example: four query heads of two
+    inputs, two key/value heads (group 2), previous output [q | k | v]."""
+    q = [1, 2, 3, 4, 5, 6, 7, 8]
+    k = [9, 10, 11, 12]
+    v = [13, 14, 15, 16]
+    y = _bf16_bits_of(np.array([q + k + v], np.float32))
+    x = O.chain_input("attn1", y, 8, params=(12, 2, 2))
+    assert list(O.bf16_to_f32(x)[0]) == [13, 14, 13, 14, 15, 16, 15, 16]
+    # the previous output as is, and a producer weight
+    x = O.chain_input("prev", y, 4)
+    assert list(O.bf16_to_f32(x)[0]) == [1, 2, 3, 4]
+    gam = _bf16_bits_of(np.array([0.5, 2.0, -1.0, 0.25], np.float32))
+    x = O.chain_input("prev", y, 4, gamma_bits=gam)
+    assert list(O.bf16_to_f32(x)[0]) == [0.5, 4.0, -3.0, 1.0]
+    # swiglu: [gate | up], silu(0) * u = 0; and the odd part: x(g) - x(-g) = g u
+    gate = np.array([0.0, 1.5, -2.0, 3.0], np.float32)
+    up = np.array([7.0, 1.0, 1.0, -1.0], np.float32)
+    xp = O.bf16_to_f32(O.chain_input("swiglu", _bf16_bits_of(np.concatenate([gate, up])[None]), 4))
+    xm = O.bf16_to_f32(O.chain_input("swiglu", _bf16_bits_of(np.concatenate([-gate, up])[None]), 4))
+    assert xp[0, 0] == 0.0
+    d = (xp - xm).astype(np.float64)[0]
+    assert np.all(np.abs(d - gate * up) <= 2 * 2.0 ** -8 * (np.abs(xp) + np.abs(xm))[0] + 1e-30)
+    # the chain's own input, truncated to K
+    x0 = _bf16_bits_of(np.array([[1, 2, 3, 4, 5, 6]], np.float32))
+    assert list(O.bf16_to_f32(O.chain_input("x0", None, 4, x0_bits=x0))[0]) == [1, 2, 3, 4]
+
+
+def check_chain_two_linears_exact(seed=33):
+    """A chain of two on-grid linears whose intermediate output is exactly a
+    BF16 value: the second output equals the dense product of the two weight
+    matrices (fp64, exact) -- the chain feeds the stored output of the first
+    linear, unchanged, into the second."""
+    rng = np.random.default_rng(seed)
+    M, K1, N1 = 3, 256, 128
+    # first linear: one weight 15 * 2^-4 per row at a random input, the rest 0
+    w1 = np.zeros((N1, K1), np.float64)
+    pos = rng.integers(0, K1, size=N1)
+    w1[np.arange(N1), pos] = 15 * 2.0 ** -4
+    x0 = rng.integers(-17, 18, size=(M, K1)).astype(np.float64)
+    # second linear: on-grid weights with every code in every group
+    W2_bits, _ = check_all_codes_on_grid(seed + 1, N=24, K=N1)
+    c1 = O.quantize_pack(_bf16_bits_of(w1.astype(np.float32)))
+    c2 = O.quantize_pack(W2_bits)
+    lin = [dict(codes=c1[0], scales=c1[1], zeros=c1[2], kind="x0"),
+           dict(codes=c2[0], scales=c2[1], zeros=c2[2], kind="prev")]
+    out = O.chain_ref(_bf16_bits_of(x0.astype(np.float32)), lin)
+    y1 = x0 @ w1.T
+    w2 = O.bf16_to_f32(W2_bits).astype(np.float64)
+    assert np.array_equal(out[0][1], y1)
+    assert np.array_equal(O.bf16_to_f32(out[0][2]).astype(np.float64), y1)   # exactly BF16
+    assert np.array_equal(out[1][1], y1 @ w2.T)

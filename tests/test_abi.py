@@ -29,7 +29,8 @@ def test_header_declares_expected_entry_points():
         "w4a16_awq_importance", "w4a16_awq_scale", "w4a16_awq_fold", "w4a16_scale_channels",
         "w4a16_dequantize_bf16", "w4a16_dense_gemv", "w4a16_dense_gemm", "w4a16_pack_symmetric",
         "w4a16_pack_grouped", "w4a16_gemv_grouped", "w4a16_gemm_grouped",
-        "w4a16_pack_int8", "w4a16_gemv_int8", "w4a16_gemm_int8", "w4a16_awq_search_error"])
+        "w4a16_pack_int8", "w4a16_gemv_int8", "w4a16_gemm_int8", "w4a16_awq_search_error",
+        "w4a16_hbm_read_probe"])
 
 
 def test_every_declared_symbol_is_exported():
@@ -123,6 +124,10 @@ def test_awq_validation():
     assert lib.w4a16_scale_channels(p(FAKE), 2, 8, 7, p(FAKE), p(FAKE), 8, p(0)) == INVALID
     assert lib.w4a16_scale_channels(p(FAKE), 2, 8, 8, p(FAKE), p(FAKE), 7, p(0)) == INVALID
     assert lib.w4a16_scale_channels(p(FAKE), 2, 8, 8, p(FAKE + 1), p(FAKE), 8, p(0)) == MISALIGNED
+    pr = lib.w4a16_hbm_read_probe
+    assert pr(p(0), 1024, p(FAKE), p(0)) == INVALID
+    assert pr(p(FAKE), 1000, p(FAKE), p(0)) == INVALID
+    assert pr(p(FAKE + 8), 1024, p(FAKE), p(0)) == MISALIGNED
     e = lib.w4a16_awq_search_error
     assert e(p(0), 8, p(FAKE), 8, 2, 8, p(FAKE), p(0)) == INVALID
     assert e(p(FAKE), 8, p(FAKE), 8, 0, 8, p(FAKE), p(0)) == INVALID

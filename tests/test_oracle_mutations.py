@@ -23,6 +23,8 @@ ALL_PINS = [
     lambda: P.check_all_codes_on_grid(seed=21, N=8, K=256, group=32),
     lambda: P.check_brute_force(seed=22, M=2, K=128, N=3, group=32),
     P.check_int8_on_grid_and_layout, P.check_int8_brute_force,
+    P.check_f64_to_bf16_single_rounding, P.check_silu_identities, P.check_chain_input_hand,
+    P.check_chain_two_linears_exact,
 ]
 
 
@@ -234,6 +236,49 @@ def _search_multiplies_x(W_bits, Xcal_bits, alphas, X_bits=None):
     return errs, int(np.argmin(errs))
 
 
+def _bf16_via_f32(x):
+    return R.f32_to_bf16_rne(np.asarray(x, np.float64).astype(np.float32))
+
+
+def _silu_sign(g):
+    g = np.asarray(g, dtype=np.float64)
+    return g / (1.0 + np.exp(g))
+
+
+_chain_input_orig = R.chain_input
+
+
+def _chain_attn_mod(kind, y_prev_bits, K, params=None, gamma_bits=None, x0_bits=None):
+    if kind == "attn1":
+        v_off, hd, group = params
+        y = R.bf16_to_f32(np.asarray(y_prev_bits)).astype(np.float64)
+        k = np.arange(K)
+        x = y[:, v_off + (k // hd % group) * hd + k % hd]
+        return R.f64_to_bf16_rne(x)
+    return _chain_input_orig(kind, y_prev_bits, K, params, gamma_bits, x0_bits)
+
+
+def _chain_swiglu_swapped(kind, y_prev_bits, K, params=None, gamma_bits=None, x0_bits=None):
+    if kind == "swiglu":
+        y = R.bf16_to_f32(np.asarray(y_prev_bits)).astype(np.float64)
+        return R.f64_to_bf16_rne(R.silu_ref(y[:, K:2 * K]) * y[:, :K])
+    return _chain_input_orig(kind, y_prev_bits, K, params, gamma_bits, x0_bits)
+
+
+def _chain_ignores_gamma(kind, y_prev_bits, K, params=None, gamma_bits=None, x0_bits=None):
+    return _chain_input_orig(kind, y_prev_bits, K, params, None, x0_bits)
+
+
+def _chain_ref_feeds_x0(x0_bits, linears):
+    out = []
+    for L in linears:
+        K = L["codes"].shape[1] * 8
+        x = R.chain_input("x0", None, K, None, L.get("gamma"), x0_bits)
+        y = R.matmul_ref(x, L["codes"], L["scales"], L["zeros"])
+        out.append((x, y, R.f64_to_bf16_rne(y)))
+    return out
+
+
 ORIG = {n: getattr(R, n) for n in ["group_scale_zero", "quantize"]}
 
 MUTATIONS = {
@@ -261,6 +306,12 @@ MUTATIONS = {
     "dequant_group_always_128": ("dequantize", _dequant_group_128),
     "int8_divide_by_256": ("quantize_int8", _quantize_int8_div256),
     "int8_bytes_reversed": ("pack_codes_int8", _pack_int8_reversed),
+    "bf16_store_rounds_twice": ("f64_to_bf16_rne", _bf16_via_f32),
+    "silu_sign_flipped": ("silu_ref", _silu_sign),
+    "attention_head_modulo": ("chain_input", _chain_attn_mod),
+    "swiglu_halves_swapped": ("chain_input", _chain_swiglu_swapped),
+    "chain_ignores_gamma": ("chain_input", _chain_ignores_gamma),
+    "chain_feeds_x0_everywhere": ("chain_ref", _chain_ref_feeds_x0),
 }
 
 

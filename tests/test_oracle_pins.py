@@ -169,3 +169,19 @@ def test_awq_search_alpha_zero_is_plain():
 
 def test_awq_search_protects_salient():
     P.check_awq_search_protects_salient()
+
+
+def test_f64_to_bf16_single_rounding():
+    P.check_f64_to_bf16_single_rounding()
+
+
+def test_silu_identities():
+    P.check_silu_identities()
+
+
+def test_chain_input_hand():
+    P.check_chain_input_hand()
+
+
+def test_chain_two_linears_exact():
+    P.check_chain_two_linears_exact()
