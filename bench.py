@@ -59,6 +59,8 @@ def parse():
                     help="skip the dense BF16 and naive-pipeline comparisons")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the decode sweep over the other M values and the 70B-shaped set")
+    ap.add_argument("--no-chain", action="store_true",
+                    help="skip the persistent chain decode (w4a16_chain_run)")
     return ap.parse_args()
 
 
@@ -290,6 +292,14 @@ def main():
     if not args.no_stack:
         stack = stack_decode(args.stack_tokens, dev, stream)
 
+    # ---- the same layers as chains of dependent linears in one persistent
+    # launch per token (w4a16_chain_run)
+    chain = None
+    if not args.no_chain:
+        chain = {"llama8b_layer": chain_llama8b(dev, stream, steps=args.steps)}
+        if not args.no_stack:
+            chain["stack40"] = chain_stack(args.stack_tokens, dev, stream)
+
     # ---- the alternatives the fused path is chosen over (dense BF16 layers,
     # the naive expand-then-multiply pipeline)
     compare = None
@@ -333,6 +343,7 @@ def main():
         "hbm_read_ceiling": ceiling,
         "decode_sweep": sweep,
         "stack": stack,
+        "decode_chain": chain,
         "comparisons": compare,
         "cpu_baseline": cpu,
     }
@@ -821,6 +832,126 @@ def stack_decode(tokens, dev, stream, Ms=(1, 8)):
 
 def host_threads() -> int:
     return len(os.sched_getaffinity(0))
+
+
+LLAMA8B_CHAIN = [("qkv", "x0", None), ("o", "attn1", (5120, 128, 4)), ("gate_up", "prev", None),
+                 ("down", "swiglu", None)]
+
+
+def chain_llama8b(dev, stream, steps=200, Ms=(1, 2)):
+    """The Llama-3-8B-shaped layer set as a decoder layer: qkv -> attention
+    over a one-token context -> o -> gate_up -> SwiGLU -> down, each linear's
+    input formed from the previous output, one persistent launch per token
+    (w4a16_chain_run), over rotating weight copies (>= 1 GiB) so that every
+    token streams its weights from HBM; HIP events on `stream`."""
+    import torch
+    import int4_weight_only_gemv_amd as w4
+    from synth import gen
+    spec = gen.WORKLOADS["llama8b_decode"]
+    layers = spec["layers"]
+    packed = []
+    for L in layers:
+        W = gen.weights(L.N, L.K, "llama8b_decode", L.name, device=dev)
+        packed.append(w4.w4a16_pack(W))
+        del W
+    set_bytes = sum(p.nbytes() for p in packed)
+    ncopy = max(2, math.ceil(ROTATE_BYTES / set_bytes))
+    copies = [packed] + [[w4.PackedLinear(p.codes.clone(), p.scales.clone(), p.zeros.clone())
+                          for p in packed] for _ in range(ncopy - 1)]
+    rows = []
+    for M in Ms:
+        outs = None
+        plans = []
+        for c in range(ncopy):
+            lin = [dict(p=p, input=kind, params=params) for p, (_, kind, params) in zip(copies[c], LLAMA8B_CHAIN)]
+            pl = w4.w4a16_chain_prepare(lin, M, outputs=outs)
+            outs = pl.outputs
+            plans.append(pl)
+        x0 = gen.activations(M, layers[0].K, "llama8b_decode", "chain_x0", device=dev)
+        with torch.cuda.stream(stream):
+            for pl in plans:
+                w4.w4a16_chain_run(pl, x0)
+            stream.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for s_ in range(steps):
+                w4.w4a16_chain_run(plans[s_ % ncopy], x0)
+            e1.record(stream)
+            e1.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        assert w4.w4a16_chain_status(plans[0]) == 0, "chain barrier timeout"
+        nbytes = sum(decode_bytes(L, M) for L in layers)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        rows.append({"M": M, "us_per_step": round(us, 3), "GBps": round(gbs, 1),
+                     "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "step_bytes": nbytes})
+        log(f"[bench] chain llama8b layer M={M}: {us:.2f} us/step, {gbs:.0f} GB/s")
+        del plans
+    del copies, packed
+    torch.cuda.synchronize()
+    return {"workload": "llama8b_decode as one decoder layer: qkv -> attention over one token -> o -> gate_up "
+                        "-> SwiGLU -> down (INT4 group 128), one persistent launch per token",
+            "rotating_copies": ncopy, "steps": steps, "results": rows}
+
+
+def chain_stack(tokens, dev, stream, Ms=(1, 2)):
+    """The 40-layer stack as one chain of 160 dependent linears (qkv <- down
+    of the layer before, o <- attention over one token, gate_up <- o, down
+    <- SwiGLU), AWQ-folded packing with each linear's producer weight
+    gamma' = bf16(1/s) applied as its input is formed; one persistent launch
+    per token (~10.7 GB of weights, far past the last-level cache)."""
+    import torch
+    import int4_weight_only_gemv_amd as w4
+    from synth import gen
+    spec = gen.WORKLOADS["stack40_decode"]
+    cfg, layers, depth = "stack40_decode", spec["layers"], spec["depth"]
+    kinds = {"qkv": ("prev", None), "o": ("attn1", (5120 + 1024, 128, 5)), "gate_up": ("prev", None),
+             "down": ("swiglu", None)}
+    lin = []
+    for d in range(depth):
+        for L in layers:
+            name = f"{L.name}.{d}"
+            W = gen.weights(L.N, L.K, cfg, name, device=dev)
+            xcal = gen.activations(spec["calib_tokens"], L.K, cfg, name, role="Xcal", device=dev)
+            s_awq = w4.w4a16_awq_scale(w4.w4a16_awq_importance(xcal), spec["awq_alpha"])
+            p = w4.w4a16_pack(W, awq_s=s_awq)
+            gamma = torch.ones(L.K, dtype=torch.bfloat16, device=dev)
+            w4.w4a16_awq_fold(s_awq, gamma)
+            kind, params = kinds[L.name]
+            if d == 0 and L.name == "qkv":
+                kind = "x0"
+            lin.append(dict(p=p, input=kind, params=params, gamma=gamma))
+            del W, xcal
+    torch.cuda.synchronize()
+    rows = []
+    for M in Ms:
+        plan = w4.w4a16_chain_prepare(lin, M)
+        x0 = gen.activations(M, layers[0].K, cfg, "chain_x0", device=dev)
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                w4.w4a16_chain_run(plan, x0)
+            stream.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(tokens):
+                w4.w4a16_chain_run(plan, x0)
+            e1.record(stream)
+            e1.synchronize()
+        ms = e0.elapsed_time(e1) / tokens
+        assert w4.w4a16_chain_status(plan) == 0, "chain barrier timeout"
+        nbytes = sum(decode_bytes(L, M) for L in layers) * depth
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        log(f"[bench] chain stack M={M}: {ms:.3f} ms/token, {gbs:.0f} GB/s")
+        rows.append({"M": M, "bytes_per_token": nbytes, "ms_per_token": round(ms, 4),
+                     "tokens_per_s": round(M * 1e3 / ms, 1), "GBps": round(gbs, 1),
+                     "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
+        del plan
+    del lin
+    torch.cuda.synchronize()
+    return {"workload": "40-layer decoder stack (hidden 5120, 40/8 heads of 128, SwiGLU 27648) as one chain of "
+                        "160 dependent linears, INT4 group 128, AWQ alpha 0.5 folded into each producer weight",
+            "tokens_timed": tokens, "results": rows}
 
 
 def cpu_baseline(layers, workload, spec, M, dev, row_stride=2, min_seconds=10.0):

@@ -67,7 +67,7 @@ extern "C" {
 #endif
 
 #define W4A16_GROUP 128
-#define W4A16_ABI_VERSION 7
+#define W4A16_ABI_VERSION 8
 #define W4A16_GEMV_MAX_M 32
 #define W4A16_DENSE_GEMV_MAX_M 8
 #define W4A16_INT8_GEMV_MAX_M 4
@@ -289,6 +289,105 @@ int w4a16_scale_channels(const uint16_t* X, int64_t M, int64_t K,
 int w4a16_awq_search_error(const uint16_t* Y, int64_t ldy, const uint16_t* Yref,
                            int64_t ldr, int64_t M, int64_t N, double* err,
                            void* stream);
+
+/*
+ * Decode of a chain of dependent linears in one persistent launch.
+ *
+ * A decoder's weight stream is a chain: each linear's input is formed from
+ * the previous linear's output.  Run one launch per linear, each launch pays
+ * its dispatch, ramp and tail and nothing streams in between (Zeno AGI,
+ * "Weight-only vs mixed precision", "7. The Marlin Kernel": round trips
+ * between kernels eat the benefit of the fused matmul).  w4a16_chain_run
+ * runs a whole chain in one cooperative launch: one block per CU, the rows
+ * of each linear spread over all blocks, a grid barrier between consecutive
+ * linears, the next linear's first weights already streaming through it.
+ *
+ * Linear l computes Y_l = X_l * w_hat_l^T (the arithmetic and accuracy of
+ * w4a16_gemv, groups of 128) with X_l [M][K_l] formed from the previous
+ * stored output Y_{l-1} (BF16) by its input kind, times gamma when given
+ * (float32 product), rounded once to BF16 (nearest even):
+ *   W4A16_CHAIN_X0      X_l[m,k] = X0[m,k] (the chain's input);
+ *   W4A16_CHAIN_PREV    X_l[m,k] = Y_{l-1}[m,k];
+ *   W4A16_CHAIN_SWIGLU  X_l[m,k] = silu(Y_{l-1}[m,k]) * Y_{l-1}[m,K+k], the
+ *                       previous output holding [gate | up];
+ *                       silu(g) = g / (1 + exp(-g)) in float32;
+ *   W4A16_CHAIN_ATTN1   attention over a one-token context (the softmax of a
+ *                       single score is 1, so each head returns its value
+ *                       vector): X_l[m, h*head_dim + d] =
+ *                       Y_{l-1}[m, v_offset + (h / group)*head_dim + d].
+ * gamma is the producer's per-input-channel weight into which an AWQ scale is
+ * folded (Axe Corsa model card, "Stage 1: Activation-Aware Weight Scaling").
+ */
+enum {
+  W4A16_CHAIN_X0 = 0,
+  W4A16_CHAIN_PREV = 1,
+  W4A16_CHAIN_SWIGLU = 2,
+  W4A16_CHAIN_ATTN1 = 3
+};
+#define W4A16_CHAIN_MAX_M 2
+#define W4A16_CHAIN_MAX_LINEARS 1024
+#define W4A16_CHAIN_MAX_K 32768
+#define W4A16_CHAIN_SPIN_LIMIT (1 << 22)   /* default polls of a barrier wait */
+#define W4A16_CHAIN_TIMEOUT 1              /* status: a barrier wait gave up */
+
+/* One linear of a chain (host memory; the pointers are device pointers). */
+typedef struct {
+  const uint32_t* codes;    /* packed matrix, N outputs, K inputs, groups of 128 */
+  const uint16_t* scales;
+  const int32_t* zeros;
+  const uint16_t* gamma;    /* optional BF16 [K] producer weight, NULL for none; 16-byte aligned */
+  uint16_t* Y;              /* BF16 [M][ldy] output; 16-byte aligned, ldy % 8 == 0 */
+  int64_t N, K, ldy;
+  int32_t input;            /* W4A16_CHAIN_*; linear 0 must take W4A16_CHAIN_X0 */
+  int32_t v_offset, head_dim, group;   /* W4A16_CHAIN_ATTN1 only */
+} w4a16_chain_linear;
+
+/* What w4a16_chain_prepare hands to w4a16_chain_run: plain data, caller
+   owned.  spin_limit may be lowered by the caller (it bounds every barrier
+   wait; W4A16_CHAIN_SPIN_LIMIT polls of about 50 ns by default). */
+typedef struct {
+  void* workspace;
+  int32_t n_linears, M, grid, max_k, max_rows, k0;
+  int32_t spin_limit, reserved;
+  int64_t lds_bytes;
+} w4a16_chain_plan;
+
+/* Device workspace bytes for a chain of n_linears (barrier state, status
+   word, descriptors). */
+int w4a16_chain_workspace_bytes(int n_linears, int64_t* bytes);
+
+/*
+ * w4a16_chain_prepare -- check a chain (host array of n_linears linears),
+ * write its descriptors into `workspace` (device memory, 256-byte aligned,
+ * at least w4a16_chain_workspace_bytes; it must stay allocated while the
+ * plan is used, and not be shared by two plans run concurrently) and fill
+ * *plan.  Synchronous: returns after the copy on `stream` completed, so the
+ * host array may be freed.  Requires 1 <= M <= W4A16_CHAIN_MAX_M, every K a
+ * multiple of 128 up to W4A16_CHAIN_MAX_K, inputs consistent with the
+ * previous linear's N (PREV: K <= N_{l-1}; SWIGLU: 2K <= N_{l-1}; ATTN1:
+ * K % head_dim == 0 and the gathered values inside N_{l-1}), outputs not
+ * overlapping any input; the LDS the plan needs must fit a CU (status 3).
+ */
+int w4a16_chain_prepare(const w4a16_chain_linear* linears, int n_linears, int64_t M,
+                        void* workspace, int64_t workspace_bytes,
+                        w4a16_chain_plan* plan, void* stream);
+
+/*
+ * w4a16_chain_run -- run a prepared chain on X0 (BF16 [M][ldx], 16-byte
+ * aligned, ldx % 8 == 0, ldx >= the largest K of the linears that take
+ * W4A16_CHAIN_X0), asynchronously on `stream`, one cooperative launch.
+ * Every Y_l is written.  Deterministic.
+ */
+int w4a16_chain_run(const w4a16_chain_plan* plan, const uint16_t* X0, int64_t ldx, void* stream);
+
+/*
+ * w4a16_chain_status -- synchronise `stream`, then report the plan's status
+ * word and clear the workspace's barrier state: 0, or W4A16_CHAIN_TIMEOUT if
+ * a barrier wait of a run since the last call gave up (that run's outputs
+ * are not valid, and the barrier state must be cleared by this call before
+ * the next run).  Synchronous.
+ */
+int w4a16_chain_status(const w4a16_chain_plan* plan, int* status, void* stream);
 
 /*
  * w4a16_hbm_read_probe -- measurement helper, not part of the matmul path:

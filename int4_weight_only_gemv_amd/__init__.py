@@ -54,6 +54,10 @@ _SIGS = {
     "w4a16_gemm_grouped": ([_p, _i64, _i64, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _p], ctypes.c_int),
     "w4a16_awq_search_error": ([_p, _i64, _p, _i64, _i64, _i64, _p, _p], ctypes.c_int),
     "w4a16_hbm_read_probe": ([_p, _i64, _p, _p], ctypes.c_int),
+    "w4a16_chain_workspace_bytes": ([ctypes.c_int, _p], ctypes.c_int),
+    "w4a16_chain_prepare": ([_p, ctypes.c_int, _i64, _p, _i64, _p, _p], ctypes.c_int),
+    "w4a16_chain_run": ([_p, _p, _i64, _p], ctypes.c_int),
+    "w4a16_chain_status": ([_p, _p, _p], ctypes.c_int),
 }
 for _name, (_args, _ret) in _SIGS.items():
     _f = getattr(lib, _name)
@@ -336,6 +340,91 @@ def w4a16_awq_search(W: torch.Tensor, Xcal: torch.Tensor, alphas, X: torch.Tenso
     errs = err.tolist()
     best = min(range(len(errs)), key=lambda i: errs[i])
     return best, errs
+
+
+# ---------------------------------------------------------------------------
+# Decode of a chain of dependent linears in one persistent launch
+# ---------------------------------------------------------------------------
+
+CHAIN_INPUTS = {"x0": 0, "prev": 1, "swiglu": 2, "attn1": 3}
+CHAIN_TIMEOUT = 1
+
+
+class ChainLinearC(ctypes.Structure):
+    """w4a16_chain_linear of w4a16.h."""
+    _fields_ = [("codes", _p), ("scales", _p), ("zeros", _p), ("gamma", _p), ("Y", _p),
+                ("N", _i64), ("K", _i64), ("ldy", _i64),
+                ("input", ctypes.c_int32), ("v_offset", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("group", ctypes.c_int32)]
+
+
+class ChainPlanC(ctypes.Structure):
+    """w4a16_chain_plan of w4a16.h."""
+    _fields_ = [("workspace", _p), ("n_linears", ctypes.c_int32), ("M", ctypes.c_int32),
+                ("grid", ctypes.c_int32), ("max_k", ctypes.c_int32), ("max_rows", ctypes.c_int32),
+                ("k0", ctypes.c_int32), ("spin_limit", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("lds_bytes", _i64)]
+
+
+class ChainPlan:
+    """A prepared chain: the plan, its workspace and the tensors it refers to
+    (kept alive here).  outputs[l] is linear l's BF16 output [M][N_l]."""
+
+    def __init__(self, plan, workspace, linears, outputs):
+        self.plan, self.workspace, self.linears, self.outputs = plan, workspace, linears, outputs
+
+
+def w4a16_chain_prepare(linears, M: int, outputs=None) -> ChainPlan:
+    """Prepare a chain of linears for w4a16_chain_run.  linears: a list of
+    dicts with "p" (a PackedLinear of groups of 128), "input" (one of
+    CHAIN_INPUTS; the first must be "x0"), optional "params" (v_offset,
+    head_dim, group) for "attn1" and optional "gamma" (BF16 [K]).  Outputs
+    are allocated here unless given ([M][N_l] BF16 tensors)."""
+    if not linears:
+        raise ValueError("empty chain")
+    dev = linears[0]["p"].codes.device
+    if outputs is None:   # rows padded to a multiple of 8 elements (16-byte aligned)
+        outputs = [torch.empty(M, (L["p"].N + 7) // 8 * 8, dtype=torch.bfloat16, device=dev)[:, :L["p"].N]
+                   for L in linears]
+    arr = (ChainLinearC * len(linears))()
+    for i, (L, y) in enumerate(zip(linears, outputs)):
+        p = L["p"]
+        if p.group != GROUP:
+            raise ValueError("chains take groups of 128")
+        _need(y, torch.bfloat16, "output", 2)
+        g = L.get("gamma")
+        if g is not None:
+            _need(g, torch.bfloat16, "gamma", 1)
+        v_off, hd, grp = L.get("params") or (0, 0, 0)
+        arr[i] = ChainLinearC(_ptr(p.codes), _ptr(p.scales), _ptr(p.zeros), _ptr(g), _ptr(y),
+                              p.N, p.K, y.stride(0), CHAIN_INPUTS[L["input"]], v_off, hd, grp)
+    nbytes = ctypes.c_int64(0)
+    _check("w4a16_chain_workspace_bytes", lib.w4a16_chain_workspace_bytes(len(linears), ctypes.byref(nbytes)))
+    ws = torch.empty(nbytes.value + 256, dtype=torch.uint8, device=dev)
+    off = (-ws.data_ptr()) % 256
+    ws_view = ws[off:off + nbytes.value]
+    plan = ChainPlanC()
+    _check("w4a16_chain_prepare", lib.w4a16_chain_prepare(arr, len(linears), M, _ptr(ws_view), nbytes.value,
+                                                          ctypes.byref(plan), _stream(ws)))
+    return ChainPlan(plan, ws, list(linears), outputs)
+
+
+def w4a16_chain_run(plan: ChainPlan, X0: torch.Tensor):
+    """Run the chain on X0 [M][K_0] (one launch); returns the outputs."""
+    _need(X0, torch.bfloat16, "X0", 2)
+    if X0.shape[0] != plan.plan.M:
+        raise ValueError(f"X0 has {X0.shape[0]} rows, the plan {plan.plan.M}")
+    _check("w4a16_chain_run", lib.w4a16_chain_run(ctypes.byref(plan.plan), _ptr(X0), X0.stride(0), _stream(X0)))
+    return plan.outputs
+
+
+def w4a16_chain_status(plan: ChainPlan) -> int:
+    """0, or CHAIN_TIMEOUT if a barrier wait gave up since the last call
+    (synchronises the current stream)."""
+    st = ctypes.c_int(0)
+    _check("w4a16_chain_status", lib.w4a16_chain_status(ctypes.byref(plan.plan), ctypes.byref(st),
+                                                        _stream(plan.workspace)))
+    return st.value
 
 
 def w4a16_hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor | None = None) -> torch.Tensor:

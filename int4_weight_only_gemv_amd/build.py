@@ -40,6 +40,7 @@ SOURCES = {
     "awq.hip": EXACT,
     "dense.hip": EXACT,
     "probe.hip": [],
+    "chain.hip": [],
 }
 
 

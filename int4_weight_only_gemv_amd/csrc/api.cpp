@@ -4,9 +4,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstring>
+#include <vector>
 
+#include "chain.h"
+#include "common.h"
 #include "w4a16.h"
 
 namespace w4a16 {
@@ -26,6 +30,9 @@ int launch_awq_fold(const float*, int64_t, uint16_t*, uint16_t*, hipStream_t);
 int launch_rel_l2(const uint16_t*, int64_t, const uint16_t*, int64_t, int64_t, int64_t, double*,
                   hipStream_t);
 int launch_hbm_read_probe(const void*, int64_t, uint32_t*, hipStream_t);
+int launch_chain(const void*, int, int, const uint16_t*, int64_t, unsigned*, int, int, int, int, size_t,
+                 hipStream_t);
+
 int launch_scale_channels(const uint16_t*, int64_t, int64_t, int64_t, const uint16_t*, uint16_t*,
                           int64_t, hipStream_t);
 int launch_dequant_bf16(const uint32_t*, const uint16_t*, const int32_t*, int64_t, int64_t,
@@ -268,6 +275,151 @@ int w4a16_awq_search_error(const uint16_t* Y, int64_t ldy, const uint16_t* Yref,
   if (!aligned(Y, 2) || !aligned(Yref, 2) || !aligned(err, 8)) return W4A16_ERR_MISALIGNED;
   if (int dc = device_check()) return dc;
   return w4a16::launch_rel_l2(Y, ldy, Yref, ldr, M, N, err, (hipStream_t)stream);
+}
+
+namespace {
+constexpr int64_t kChainHeader = w4a16::kChainHeaderBytes;   // barrier state and status word
+constexpr int64_t kChainMaxLds = 160 * 1024;
+constexpr int kChainSliceK = 2048;
+
+bool ranges_overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + (uintptr_t)bbytes && y < x + (uintptr_t)abytes;
+}
+}  // namespace
+
+int w4a16_chain_workspace_bytes(int n_linears, int64_t* bytes) {
+  if (!bytes || n_linears < 1 || n_linears > W4A16_CHAIN_MAX_LINEARS) return W4A16_ERR_INVALID_ARG;
+  *bytes = kChainHeader + (int64_t)n_linears * (int64_t)sizeof(w4a16::ChainDesc);
+  return W4A16_OK;
+}
+
+namespace {
+// Checks of a chain (host array) shared by w4a16_chain_prepare and
+// w4a16_chain_run_noalloc.
+int chain_check(const w4a16_chain_linear* L, int n, int64_t M) {
+  if (!L || n < 1 || n > W4A16_CHAIN_MAX_LINEARS) return W4A16_ERR_INVALID_ARG;
+  if (M < 1 || M > W4A16_CHAIN_MAX_M) return W4A16_ERR_INVALID_ARG;
+  for (int l = 0; l < n; ++l) {
+    const w4a16_chain_linear& a = L[l];
+    if (!a.codes || !a.scales || !a.zeros || !a.Y) return W4A16_ERR_INVALID_ARG;
+    if (a.N < 1 || a.K < W4A16_GROUP || a.K % W4A16_GROUP || a.ldy < a.N) return W4A16_ERR_INVALID_ARG;
+    if (a.N >= kMaxDim || a.K > W4A16_CHAIN_MAX_K) return W4A16_ERR_UNSUPPORTED;
+    if (!aligned(a.codes, 16) || !aligned(a.scales, 2) || !aligned(a.zeros, 4) || !aligned(a.Y, 16) ||
+        a.ldy % 8 || (a.gamma && !aligned(a.gamma, 16)))
+      return W4A16_ERR_MISALIGNED;
+    if (a.input < W4A16_CHAIN_X0 || a.input > W4A16_CHAIN_ATTN1) return W4A16_ERR_INVALID_ARG;
+    if (l == 0 && a.input != W4A16_CHAIN_X0) return W4A16_ERR_INVALID_ARG;
+    if (l > 0) {
+      const int64_t pn = L[l - 1].N;
+      if (a.input == W4A16_CHAIN_PREV && a.K > pn) return W4A16_ERR_INVALID_ARG;
+      if (a.input == W4A16_CHAIN_SWIGLU && 2 * a.K > pn) return W4A16_ERR_INVALID_ARG;
+      if (a.input == W4A16_CHAIN_ATTN1) {
+        if (a.head_dim < 1 || a.group < 1 || a.v_offset < 0 || a.K % a.head_dim) return W4A16_ERR_INVALID_ARG;
+        const int64_t kv_heads = (a.K / a.head_dim - 1) / a.group + 1;
+        if (a.v_offset + kv_heads * a.head_dim > pn) return W4A16_ERR_INVALID_ARG;
+      }
+    }
+    // an output may not overlap the matrix, metadata or producer weight it
+    // is computed from, nor the output its own input is formed from
+    const int64_t ybytes = ((M - 1) * a.ldy + a.N) * 2;
+    if (ranges_overlap(a.Y, ybytes, a.codes, a.N * (a.K / 2)) ||
+        ranges_overlap(a.Y, ybytes, a.scales, a.N * (a.K / W4A16_GROUP) * 2) ||
+        ranges_overlap(a.Y, ybytes, a.zeros, a.N * (a.K / W4A16_GROUP) * 4) ||
+        (a.gamma && ranges_overlap(a.Y, ybytes, a.gamma, a.K * 2)) ||
+        (l > 0 && ranges_overlap(a.Y, ybytes, L[l - 1].Y, ((M - 1) * L[l - 1].ldy + L[l - 1].N) * 2)))
+      return W4A16_ERR_INVALID_ARG;
+  }
+  return W4A16_OK;
+}
+
+// Descriptors (d[0 .. n)) and launch parameters of a checked chain.
+int chain_build(const w4a16_chain_linear* L, int n, int64_t M, w4a16::ChainDesc* d, w4a16_chain_plan* plan) {
+  const int grid = w4a16::device_cu_count();
+  int64_t max_k = 0, max_rows = 0, max_slices = 0, kx = 0;
+  for (int l = 0; l < n; ++l) {
+    const w4a16_chain_linear& a = L[l];
+    w4a16::ChainDesc& e = d[l];
+    e.codes = a.codes; e.scales = a.scales; e.zeros = a.zeros; e.gamma = a.gamma; e.y = a.Y; e.ldy = a.ldy;
+    e.N = (int32_t)a.N; e.K = (int32_t)a.K; e.input = a.input;
+    e.v_offset = a.v_offset; e.head_dim = a.head_dim; e.group = a.group;
+    const int64_t batches = (a.N + 3) / 4;
+    e.batches_per_block = (int32_t)(batches / grid);
+    e.batches_rem = (int32_t)(batches % grid);
+    e.slices = (int32_t)((a.K + kChainSliceK - 1) / kChainSliceK);
+    e.pad = 0;
+    max_k = std::max<int64_t>(max_k, a.K);
+    max_rows = std::max<int64_t>(max_rows, 4 * (e.batches_per_block + (e.batches_rem ? 1 : 0)));
+    max_slices = std::max<int64_t>(max_slices, e.slices);
+    if (a.input == W4A16_CHAIN_X0) kx = std::max<int64_t>(kx, a.K);   // the widest read of X0
+  }
+  const int64_t lds = M * (max_k / kChainSliceK + 1) * 4096 + M * (max_k / 32) * 4 + max_slices * max_rows * M * 4;
+  if (lds > kChainMaxLds) return W4A16_ERR_UNSUPPORTED;
+  plan->n_linears = n;
+  plan->M = (int32_t)M;
+  plan->grid = grid;
+  plan->max_k = (int32_t)max_k;
+  plan->max_rows = (int32_t)max_rows;
+  plan->k0 = (int32_t)kx;
+  plan->spin_limit = W4A16_CHAIN_SPIN_LIMIT;
+  plan->reserved = 0;
+  plan->lds_bytes = lds;
+  return W4A16_OK;
+}
+}  // namespace
+
+int w4a16_chain_prepare(const w4a16_chain_linear* L, int n, int64_t M, void* workspace, int64_t ws_bytes,
+                        w4a16_chain_plan* plan, void* stream) {
+  int64_t need = 0;
+  if (!L || !plan || !workspace) return W4A16_ERR_INVALID_ARG;
+  if (w4a16_chain_workspace_bytes(n, &need) != W4A16_OK || ws_bytes < need) return W4A16_ERR_INVALID_ARG;
+  if (!aligned(workspace, 256)) return W4A16_ERR_MISALIGNED;
+  if (int st = chain_check(L, n, M)) return st;
+  if (int dc = device_check()) return dc;
+  std::vector<w4a16::ChainDesc> d((size_t)n);
+  w4a16_chain_plan p{};
+  if (int st = chain_build(L, n, M, d.data(), &p)) return st;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = static_cast<char*>(workspace);
+  if (hipMemsetAsync(ws, 0, kChainHeader, s) != hipSuccess ||
+      hipMemcpyAsync(ws + kChainHeader, d.data(), d.size() * sizeof(w4a16::ChainDesc), hipMemcpyHostToDevice, s) !=
+          hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return W4A16_ERR_HIP;
+  p.workspace = workspace;
+  *plan = p;
+  return W4A16_OK;
+}
+
+int w4a16_chain_run(const w4a16_chain_plan* plan, const uint16_t* X0, int64_t ldx, void* stream) {
+  if (!plan || !plan->workspace || !X0) return W4A16_ERR_INVALID_ARG;
+  if (plan->n_linears < 1 || plan->n_linears > W4A16_CHAIN_MAX_LINEARS || plan->M < 1 ||
+      plan->M > W4A16_CHAIN_MAX_M || plan->grid < 1 || plan->max_k < W4A16_GROUP ||
+      plan->max_k > W4A16_CHAIN_MAX_K || plan->max_rows < 4 || plan->lds_bytes < 1 ||
+      plan->lds_bytes > kChainMaxLds || plan->spin_limit < 0 || ldx < plan->k0)
+    return W4A16_ERR_INVALID_ARG;
+  if (!aligned(X0, 16) || ldx % 8 || !aligned(plan->workspace, 256)) return W4A16_ERR_MISALIGNED;
+  if (int dc = device_check()) return dc;
+  char* ws = static_cast<char*>(plan->workspace);
+  return w4a16::launch_chain(ws + kChainHeader, plan->n_linears, plan->M, X0, ldx,
+                             reinterpret_cast<unsigned*>(ws), plan->spin_limit, plan->max_k, plan->max_rows,
+                             plan->grid, (size_t)plan->lds_bytes, (hipStream_t)stream);
+}
+
+int w4a16_chain_status(const w4a16_chain_plan* plan, int* status, void* stream) {
+  if (!plan || !plan->workspace || !status) return W4A16_ERR_INVALID_ARG;
+  if (int dc = device_check()) return dc;
+  hipStream_t s = (hipStream_t)stream;
+  // after a timeout the barrier count may be left mid-way: the whole barrier
+  // state is cleared (runs read the generation they start from)
+  char* header = static_cast<char*>(plan->workspace);
+  unsigned v = 0;
+  if (hipStreamSynchronize(s) != hipSuccess ||
+      hipMemcpy(&v, header + w4a16::kChainStatusWord * 4, 4, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemset(header, 0, kChainHeader) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+    return W4A16_ERR_HIP;
+  *status = (int)v;
+  return W4A16_OK;
 }
 
 int w4a16_hbm_read_probe(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {

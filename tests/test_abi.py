@@ -30,7 +30,8 @@ def test_header_declares_expected_entry_points():
         "w4a16_dequantize_bf16", "w4a16_dense_gemv", "w4a16_dense_gemm", "w4a16_pack_symmetric",
         "w4a16_pack_grouped", "w4a16_gemv_grouped", "w4a16_gemm_grouped",
         "w4a16_pack_int8", "w4a16_gemv_int8", "w4a16_gemm_int8", "w4a16_awq_search_error",
-        "w4a16_hbm_read_probe"])
+        "w4a16_hbm_read_probe", "w4a16_chain_workspace_bytes", "w4a16_chain_prepare",
+        "w4a16_chain_run", "w4a16_chain_status"])
 
 
 def test_every_declared_symbol_is_exported():
@@ -44,7 +45,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strerror():
-    assert lib.w4a16_abi_version() == 7
+    assert lib.w4a16_abi_version() == 8
     for st in range(5):
         assert lib.w4a16_strerror(st)
     assert b"unknown" in lib.w4a16_strerror(99)
