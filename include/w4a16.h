@@ -390,6 +390,24 @@ int w4a16_chain_run(const w4a16_chain_plan* plan, const uint16_t* X0, int64_t ld
 int w4a16_chain_status(const w4a16_chain_plan* plan, int* status, void* stream);
 
 /*
+ * w4a16_chain_run_noalloc -- prepare and run a chain in one call without
+ * allocating or taking a workspace, for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that
+ * forbid it).  Same chain rules and results as w4a16_chain_prepare +
+ * w4a16_chain_run; the barrier state and descriptors live in a fixed device
+ * array inside the library (one per GPU, kept until the process ends), so
+ * at most W4A16_CHAIN_NOALLOC_MAX_LINEARS linears (more:
+ * W4A16_ERR_UNSUPPORTED), and calls that overlap on one GPU race (the
+ * caller serialises them, e.g. on one stream).  The descriptors are copied
+ * from the call's own stack and the copy is waited for before the launch;
+ * the chain then runs asynchronously.  If status is not NULL the call also
+ * waits for the run and stores 0 or W4A16_CHAIN_TIMEOUT there.
+ */
+#define W4A16_CHAIN_NOALLOC_MAX_LINEARS 256
+int w4a16_chain_run_noalloc(const w4a16_chain_linear* linears, int n_linears, int64_t M,
+                            const uint16_t* X0, int64_t ldx, int* status, void* stream);
+
+/*
  * w4a16_hbm_read_probe -- measurement helper, not part of the matmul path:
  * reads `bytes` of device memory at buf with fully coalesced 16-byte loads
  * (each wave instruction covers 1 KiB of consecutive bytes, several loads in

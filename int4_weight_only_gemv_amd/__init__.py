@@ -58,6 +58,7 @@ _SIGS = {
     "w4a16_chain_prepare": ([_p, ctypes.c_int, _i64, _p, _i64, _p, _p], ctypes.c_int),
     "w4a16_chain_run": ([_p, _p, _i64, _p], ctypes.c_int),
     "w4a16_chain_status": ([_p, _p, _p], ctypes.c_int),
+    "w4a16_chain_run_noalloc": ([_p, ctypes.c_int, _i64, _p, _i64, _p, _p], ctypes.c_int),
 }
 for _name, (_args, _ret) in _SIGS.items():
     _f = getattr(lib, _name)
@@ -425,6 +426,36 @@ def w4a16_chain_status(plan: ChainPlan) -> int:
     _check("w4a16_chain_status", lib.w4a16_chain_status(ctypes.byref(plan.plan), ctypes.byref(st),
                                                         _stream(plan.workspace)))
     return st.value
+
+
+def w4a16_chain_run_noalloc(linears, X0: torch.Tensor, outputs=None, wait_status: bool = True):
+    """Prepare and run a chain in one call without a workspace (the
+    library's fixed device array; for callers that cannot allocate; calls on
+    one GPU must not overlap).  linears as for w4a16_chain_prepare; outputs
+    are allocated here unless given.  With wait_status the call waits for the
+    run and returns (outputs, status), status 0 or CHAIN_TIMEOUT; otherwise
+    (outputs, None)."""
+    _need(X0, torch.bfloat16, "X0", 2)
+    M = X0.shape[0]
+    dev = X0.device
+    if outputs is None:
+        outputs = [torch.empty(M, (L["p"].N + 7) // 8 * 8, dtype=torch.bfloat16, device=dev)[:, :L["p"].N]
+                   for L in linears]
+    arr = (ChainLinearC * len(linears))()
+    for i, (L, y) in enumerate(zip(linears, outputs)):
+        p = L["p"]
+        if p.group != GROUP:
+            raise ValueError("chains take groups of 128")
+        _need(y, torch.bfloat16, "output", 2)
+        g = L.get("gamma")
+        v_off, hd, grp = L.get("params") or (0, 0, 0)
+        arr[i] = ChainLinearC(_ptr(p.codes), _ptr(p.scales), _ptr(p.zeros), _ptr(g), _ptr(y),
+                              p.N, p.K, y.stride(0), CHAIN_INPUTS[L["input"]], v_off, hd, grp)
+    st = ctypes.c_int(-1)
+    _check("w4a16_chain_run_noalloc",
+           lib.w4a16_chain_run_noalloc(arr, len(linears), M, _ptr(X0), X0.stride(0),
+                                       ctypes.byref(st) if wait_status else None, _stream(X0)))
+    return outputs, (st.value if wait_status else None)
 
 
 def w4a16_hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor | None = None) -> torch.Tensor:

@@ -32,7 +32,8 @@ int launch_rel_l2(const uint16_t*, int64_t, const uint16_t*, int64_t, int64_t, i
 int launch_hbm_read_probe(const void*, int64_t, uint32_t*, hipStream_t);
 int launch_chain(const void*, int, int, const uint16_t*, int64_t, unsigned*, int, int, int, int, size_t,
                  hipStream_t);
-
+int launch_chain_noalloc(const ChainDesc*, int, int, const uint16_t*, int64_t, int, int, int, size_t, int*,
+                         hipStream_t);
 int launch_scale_channels(const uint16_t*, int64_t, int64_t, int64_t, const uint16_t*, uint16_t*,
                           int64_t, hipStream_t);
 int launch_dequant_bf16(const uint32_t*, const uint16_t*, const int32_t*, int64_t, int64_t,
@@ -389,6 +390,21 @@ int w4a16_chain_prepare(const w4a16_chain_linear* L, int n, int64_t M, void* wor
   p.workspace = workspace;
   *plan = p;
   return W4A16_OK;
+}
+
+int w4a16_chain_run_noalloc(const w4a16_chain_linear* L, int n, int64_t M, const uint16_t* X0, int64_t ldx,
+                            int* status, void* stream) {
+  if (!X0) return W4A16_ERR_INVALID_ARG;
+  if (n > W4A16_CHAIN_NOALLOC_MAX_LINEARS) return W4A16_ERR_UNSUPPORTED;
+  if (int st = chain_check(L, n, M)) return st;
+  if (!aligned(X0, 16) || ldx % 8) return W4A16_ERR_MISALIGNED;
+  if (int dc = device_check()) return dc;
+  w4a16::ChainDesc d[W4A16_CHAIN_NOALLOC_MAX_LINEARS];   // host staging on the stack: nothing allocated
+  w4a16_chain_plan p{};
+  if (int st = chain_build(L, n, M, d, &p)) return st;
+  if (ldx < p.k0) return W4A16_ERR_INVALID_ARG;
+  return w4a16::launch_chain_noalloc(d, n, (int)M, X0, ldx, p.max_k, p.max_rows, p.grid, (size_t)p.lds_bytes,
+                                     status, (hipStream_t)stream);
 }
 
 int w4a16_chain_run(const w4a16_chain_plan* plan, const uint16_t* X0, int64_t ldx, void* stream) {

@@ -40,6 +40,8 @@
 #include "chain.h"
 #include "common.h"
 
+#include <atomic>
+
 #include "w4a16.h"
 
 namespace w4a16 {
@@ -419,6 +421,66 @@ int launch_chain(const void* descs, int n_linears, int M, const uint16_t* X0, in
                        bar, spin_limit, max_k, max_rows);
   }
   return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+// ---------------------------------------------------------------------------
+// The same launch for callers that cannot allocate: barrier state and
+// descriptors in a file-scope device array of fixed size (one copy per GPU,
+// kept until the process ends; calls that overlap on one GPU race).
+// ---------------------------------------------------------------------------
+
+namespace {
+
+constexpr int64_t kScratchBytes = kChainHeaderBytes + (int64_t)W4A16_CHAIN_NOALLOC_MAX_LINEARS * sizeof(ChainDesc);
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// Device address of `scratch` on each device, looked up once per device with
+// that device current (the array's name is a host-side stand-in).
+constexpr int kMaxDevices = 64;
+std::atomic<void*> scratch_ptr[kMaxDevices];
+
+void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+// the barrier state must start at zero: a fill kernel (no memset node)
+__global__ void clear_words_kernel(unsigned* p, int words) {
+  for (int i = threadIdx.x; i < words; i += blockDim.x) p[i] = 0u;
+}
+
+}  // namespace
+
+int launch_chain_noalloc(const ChainDesc* d, int n_linears, int M, const uint16_t* X0, int64_t ldx, int max_k,
+                         int max_rows, int grid, size_t lds_bytes, int* status, hipStream_t stream) {
+  char* ws = static_cast<char*>(scratch_address());
+  if (!ws) return 4;
+  // descriptors: the host copy (the caller's stack) must be consumed before
+  // this call returns, so the copy is waited for
+  if (hipMemcpyAsync(ws + kChainHeaderBytes, d, (size_t)n_linears * sizeof(ChainDesc), hipMemcpyHostToDevice,
+                     stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return 4;
+  hipLaunchKernelGGL(clear_words_kernel, dim3(1), dim3(256), 0, stream, reinterpret_cast<unsigned*>(ws),
+                     (int)(kChainHeaderBytes / 4));
+  if (hipGetLastError() != hipSuccess) return 4;
+  if (int st = launch_chain(ws + kChainHeaderBytes, n_linears, M, X0, ldx, reinterpret_cast<unsigned*>(ws),
+                            W4A16_CHAIN_SPIN_LIMIT, max_k, max_rows, grid, lds_bytes, stream))
+    return st;
+  if (status) {
+    unsigned v = 0;
+    if (hipStreamSynchronize(stream) != hipSuccess ||
+        hipMemcpy(&v, ws + kChainStatusWord * 4, 4, hipMemcpyDeviceToHost) != hipSuccess)
+      return 4;
+    *status = (int)v;
+  }
+  return 0;
 }
 
 }  // namespace w4a16

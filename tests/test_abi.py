@@ -31,7 +31,7 @@ def test_header_declares_expected_entry_points():
         "w4a16_pack_grouped", "w4a16_gemv_grouped", "w4a16_gemm_grouped",
         "w4a16_pack_int8", "w4a16_gemv_int8", "w4a16_gemm_int8", "w4a16_awq_search_error",
         "w4a16_hbm_read_probe", "w4a16_chain_workspace_bytes", "w4a16_chain_prepare",
-        "w4a16_chain_run", "w4a16_chain_status"])
+        "w4a16_chain_run", "w4a16_chain_status", "w4a16_chain_run_noalloc"])
 
 
 def test_every_declared_symbol_is_exported():
