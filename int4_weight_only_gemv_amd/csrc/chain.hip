@@ -151,8 +151,8 @@ __device__ __forceinline__ void block_sync_lds() {
   asm volatile("" ::: "memory");
 }
 
-// Grid barrier, arrival half: the block's stores are complete (the caller
-// synchronised the block), thread 0 arrives on its group's counter, the last
+// Grid barrier, arrival half: the block's stores are complete (every wave
+// waited for its stores, then the block synchronised), thread 0 arrives on its group's counter, the last
 // of a group on the top counter, and the last of all resets the counters and
 // publishes the next generation.  Returns true in the thread that published.
 __device__ __forceinline__ bool grid_arrive(unsigned* bar, unsigned nblocks, unsigned gen) {
@@ -387,7 +387,10 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainDesc* _
     }
 
     if (l + 1 < n_linears) {
-      __syncthreads();                                   // the block's stores are complete
+      // the block's stores are complete before it arrives (a block barrier
+      // alone does not wait for global stores)
+      wait_vmcnt<0>();
+      __syncthreads();
       const bool published = grid_arrive(bar, nblocks, gen);
       // the next linear's first item streams through the barrier
       const ChainDesc dn = descs[l + 1];

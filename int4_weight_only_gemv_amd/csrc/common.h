@@ -64,6 +64,23 @@ __device__ __forceinline__ u32x4 x_pairs_from_natural(u32x4 d) {
   return r;
 }
 
+// Eight codes of one word -> BF16 operands 4^E (128 + q) in natural k
+// order: dword j holds (code 2j, code 2j+1).  eb holds the exponent byte
+// 0x43 + E in every byte (0x43: BF16 128.0, whose low mantissa bits count
+// in units of one).
+__device__ __forceinline__ u32x4 codes_to_bias128_natural(uint32_t w, uint32_t eb) {
+  const uint32_t even = w & 0x0F0F0F0Fu;          // bytes q0 q2 q4 q6
+  const uint32_t odd = (w >> 4) & 0x0F0F0F0Fu;    // bytes q1 q3 q5 q7
+  const uint32_t lo = __builtin_amdgcn_perm(odd, even, 0x05010400u);  // q0 q1 q2 q3
+  const uint32_t hi = __builtin_amdgcn_perm(odd, even, 0x07030602u);  // q4 q5 q6 q7
+  u32x4 r;
+  r[0] = __builtin_amdgcn_perm(eb, lo, 0x04010400u);  // (q0, q1)
+  r[1] = __builtin_amdgcn_perm(eb, lo, 0x04030402u);  // (q2, q3)
+  r[2] = __builtin_amdgcn_perm(eb, hi, 0x04010400u);  // (q4, q5)
+  r[3] = __builtin_amdgcn_perm(eb, hi, 0x04030402u);  // (q6, q7)
+  return r;
+}
+
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // c + a.lo * b.lo + a.hi * b.hi on two BF16 pairs, float32 result.
@@ -87,6 +104,59 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
 // D = A * B + C on a 16x16 output tile with K = 32 (BF16 in, FP32 out).
 __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One direct-to-LDS copy (global_load_lds_dwordx4): lane l's 16 bytes at src
+// land at lds_dst + 16 l.  lds_dst must be the same for the whole wave.
+// (Kept in a device function: inside a kernel body the target builtin stops
+// the host pass from emitting the kernel's launch stub.)
+__device__ __forceinline__ void copy16_to_lds(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 16, 0, 0);
+}
+
+// Block barrier that the compiler may not move memory accesses across
+// (the bare builtin does not order them at the IR level).
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Block barrier after this wave's LDS writes are done, leaving its global
+// and direct-to-LDS loads in flight (a __syncthreads() also waits for every
+// direct-to-LDS copy, since those count as LDS writes, which would drain a
+// prefetch ring at every barrier).  For LDS data written with ordinary
+// stores only.
+__device__ __forceinline__ void block_barrier_lds() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int V>
+struct Ic {
+  static constexpr int value = V;
+};
+
+// f(Ic<I>{}) for I = B .. E-1, in order (a loop whose index is a constant)
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(Ic<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Wait until at most n vector-memory operations of this wave are in flight
+// and all of its LDS operations are done (so LDS writes made before the
+// following barrier are visible to the whole block after it).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
 }
 
 // Compute units of the current device (queried once per device; host code).

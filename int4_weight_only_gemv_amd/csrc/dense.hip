@@ -137,26 +137,6 @@ constexpr int LOADS = STAGE / 1024 / (kGemmThreads / 64); // 1-KiB copies per wa
 constexpr int kXcds = 8;
 static_assert(LOADS == 2, "copy split");
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ void block_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// at most n vector-memory operations of this wave in flight, all LDS done
-template <int n>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(n < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
-}
-
-template <int V>
-struct Ic {
-  static constexpr int value = V;
-};
-
 __global__ __launch_bounds__(kGemmThreads) void dense_gemm_kernel(
     const uint16_t* __restrict__ X, int M, int64_t ldx, const uint16_t* __restrict__ W,
     int64_t ldw, int N, int K, uint16_t* __restrict__ Y, int64_t ldy, int m_tiles, int n_tiles) {

@@ -96,47 +96,6 @@ using TileBig = TileCfg<256, 256, 128, 64>;
 using TileSmall = TileCfg<128, 128, 64, 64>;
 using TileTiny = TileCfg<64, 128, 64, 64>;
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Block barrier that the compiler may not move memory accesses across
-// (the bare builtin does not order them at the IR level).
-__device__ __forceinline__ void block_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-template <int V>
-struct Ic {
-  static constexpr int value = V;
-};
-
-// Eight codes of one word -> BF16 operands 4^E (128 + q) in natural k
-// order: dword j holds (code 2j, code 2j+1).  eb holds the exponent byte
-// 0x43 + E in every byte (0x43: BF16 128.0, whose low mantissa bits count
-// in units of one).
-__device__ __forceinline__ u32x4 codes_to_bias128_natural(uint32_t w, uint32_t eb) {
-  const uint32_t even = w & 0x0F0F0F0Fu;          // bytes q0 q2 q4 q6
-  const uint32_t odd = (w >> 4) & 0x0F0F0F0Fu;    // bytes q1 q3 q5 q7
-  const uint32_t lo = __builtin_amdgcn_perm(odd, even, 0x05010400u);  // q0 q1 q2 q3
-  const uint32_t hi = __builtin_amdgcn_perm(odd, even, 0x07030602u);  // q4 q5 q6 q7
-  u32x4 r;
-  r[0] = __builtin_amdgcn_perm(eb, lo, 0x04010400u);  // (q0, q1)
-  r[1] = __builtin_amdgcn_perm(eb, lo, 0x04030402u);  // (q2, q3)
-  r[2] = __builtin_amdgcn_perm(eb, hi, 0x04010400u);  // (q4, q5)
-  r[3] = __builtin_amdgcn_perm(eb, hi, 0x04030402u);  // (q6, q7)
-  return r;
-}
-
-// Wait until at most n vector-memory operations of this wave are in flight
-// and all of its LDS operations are done (so LDS writes made before the
-// following barrier are visible to the whole block after it).
-template <int n>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(n < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
-}
-
 // Memory operations each wave issues, in this order: at block position 0,
 // the next block's scale and zero-point loads and C_LOADS code copies; at every
 // step, X_LOADS copies of X for the step four ahead.  Nothing is
