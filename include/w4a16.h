@@ -67,7 +67,7 @@ extern "C" {
 #endif
 
 #define W4A16_GROUP 128
-#define W4A16_ABI_VERSION 8
+#define W4A16_ABI_VERSION 9
 #define W4A16_GEMV_MAX_M 32
 #define W4A16_DENSE_GEMV_MAX_M 8
 #define W4A16_INT8_GEMV_MAX_M 4
@@ -164,6 +164,40 @@ int w4a16_gemv(const uint16_t* X, int64_t M, int64_t ldx,
                const uint32_t* codes, const uint16_t* scales,
                const int32_t* zeros, int64_t N, int64_t K,
                uint16_t* Y, int64_t ldy, void* stream);
+
+/*
+ * w4a16_gemv_workspace_bytes -- the workspace with which w4a16_gemv_ws may
+ * split the K inputs of a row over several blocks for this shape (decode at
+ * 9 <= M <= 32 with rows of more than 4096 inputs); 0 when the shape needs
+ * none.  The size depends on the current device (its compute-unit count).
+ * Returns W4A16_ERR_INVALID_ARG for shapes w4a16_gemv rejects.
+ */
+int w4a16_gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t* bytes);
+
+/*
+ * w4a16_gemv_ws -- w4a16_gemv with a caller-owned workspace: same
+ * arguments, layout, accuracy and limits, plus
+ *
+ *   workspace        device memory, 64-byte aligned, zero-filled before
+ *                    its first use, not overlapping X, Y or the packed
+ *                    matrix (W4A16_ERR_INVALID_ARG otherwise); may be NULL
+ *                    with workspace_bytes 0.
+ *   workspace_bytes  its size.
+ *
+ * With at least w4a16_gemv_workspace_bytes() bytes the decode kernel may
+ * split K over blocks, whose float32 partial sums meet in the workspace (a
+ * fixed summation order: results are deterministic, and may differ from
+ * the unsplit kernel's in the last bits).  With less, or none, the call is
+ * w4a16_gemv.  Each call leaves the workspace's counters at zero, so one
+ * workspace serves any sequence of calls of any shapes on one stream; calls
+ * that may run at the same time (other streams, concurrent graphs) need
+ * workspaces of their own.
+ */
+int w4a16_gemv_ws(const uint16_t* X, int64_t M, int64_t ldx,
+                  const uint32_t* codes, const uint16_t* scales,
+                  const int32_t* zeros, int64_t N, int64_t K,
+                  uint16_t* Y, int64_t ldy, void* workspace,
+                  int64_t workspace_bytes, void* stream);
 
 /*
  * w4a16_gemm -- prefill-shaped fused dequantise-multiply on the BF16 matrix

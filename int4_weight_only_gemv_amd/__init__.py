@@ -37,6 +37,8 @@ _SIGS = {
     "w4a16_strerror": ([ctypes.c_int], ctypes.c_char_p),
     "w4a16_pack": ([_p, _i64, _i64, _i64, _p, _p, _p, _p, _p], ctypes.c_int),
     "w4a16_gemv": ([_p, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _i64, _p], ctypes.c_int),
+    "w4a16_gemv_workspace_bytes": ([_i64, _i64, _i64, _p], ctypes.c_int),
+    "w4a16_gemv_ws": ([_p, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _i64, _p, _i64, _p], ctypes.c_int),
     "w4a16_gemm": ([_p, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _i64, _p], ctypes.c_int),
     "w4a16_awq_importance": ([_p, _i64, _i64, _i64, _p, _p], ctypes.c_int),
     "w4a16_awq_scale": ([_p, _i64, ctypes.c_float, _p, _p], ctypes.c_int),
@@ -240,10 +242,61 @@ def _matmul(fn, name, X: torch.Tensor, p: PackedLinear, out: torch.Tensor | None
     return out
 
 
-def w4a16_gemv(X: torch.Tensor, p: PackedLinear, out: torch.Tensor | None = None) -> torch.Tensor:
+# Decode workspaces, one per (device, stream): zero-filled tensors that grow
+# to the largest size asked for (each call leaves them reusable; see
+# w4a16_gemv_ws in include/w4a16.h).  No workspace is created or grown while
+# the stream is being captured into a graph: such a call runs unsplit.
+_workspaces: dict = {}
+
+
+def gemv_workspace(X: torch.Tensor, N: int, K: int) -> torch.Tensor | None:
+    """The cached decode workspace of X's device and current stream, grown to
+    what w4a16_gemv_ws can use for this shape (None when it needs none or the
+    stream is capturing and none is large enough yet)."""
+    nbytes = ctypes.c_int64(0)
+    _check("w4a16_gemv_workspace_bytes",
+           lib.w4a16_gemv_workspace_bytes(X.shape[0], N, K, ctypes.byref(nbytes)))
+    if nbytes.value == 0:
+        return None
+    stream = torch.cuda.current_stream(X.device)
+    key = (X.device.index, stream.cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes.value:
+        if torch.cuda.is_current_stream_capturing():
+            return ws if ws is not None and ws.numel() >= nbytes.value else None
+        ws = torch.zeros(nbytes.value, dtype=torch.uint8, device=X.device)
+        _workspaces[key] = ws
+    return ws
+
+
+def w4a16_gemv(X: torch.Tensor, p: PackedLinear, out: torch.Tensor | None = None,
+               workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Y = X . w_hat^T for 1 <= M <= 32 (decode); groups other than 128 go
-    through w4a16_gemv_grouped."""
-    return _matmul(lib.w4a16_gemv, "w4a16_gemv", X, p, out)
+    through w4a16_gemv_grouped.  With groups of 128 the call goes through
+    w4a16_gemv_ws with `workspace` (a zero-filled uint8 tensor) or, if None,
+    the cached workspace of the device and stream."""
+    if getattr(p, "group", GROUP) != GROUP:
+        return _matmul(lib.w4a16_gemv, "w4a16_gemv", X, p, out)
+    _need(X, torch.bfloat16, "X", 2)
+    M, K = X.shape
+    if K != p.K:
+        raise ValueError(f"X has K={K}, weights have K={p.K}")
+    if out is None:
+        out = torch.empty(M, p.N, dtype=torch.bfloat16, device=X.device)
+    else:
+        _need(out, torch.bfloat16, "out", 2)
+        if tuple(out.shape) != (M, p.N):
+            raise ValueError("out has the wrong shape")
+    if workspace is None and 9 <= M <= GEMV_MAX_M:
+        workspace = gemv_workspace(X, p.N, p.K)
+    if workspace is not None and (workspace.dtype != torch.uint8 or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    ws_ptr = _ptr(workspace) if workspace is not None else None
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    _check("w4a16_gemv_ws", lib.w4a16_gemv_ws(_ptr(X), M, X.stride(0), _ptr(p.codes), _ptr(p.scales),
+                                              _ptr(p.zeros), p.N, p.K, _ptr(out), out.stride(0), ws_ptr,
+                                              ws_bytes, _stream(X)))
+    return out
 
 
 def w4a16_gemm(X: torch.Tensor, p: PackedLinear, out: torch.Tensor | None = None) -> torch.Tensor:

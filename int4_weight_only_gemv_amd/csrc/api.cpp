@@ -21,7 +21,8 @@ int launch_gemv_int8(const uint16_t*, int64_t, int64_t, const uint32_t*, const u
 int launch_gemm_int8(const uint16_t*, int64_t, int64_t, const uint32_t*, const uint16_t*,
                      const int32_t*, int64_t, int64_t, uint16_t*, int64_t, hipStream_t);
 int launch_gemv(const uint16_t*, int64_t, int64_t, const uint32_t*, const uint16_t*,
-                const int32_t*, int64_t, int64_t, int, uint16_t*, int64_t, hipStream_t);
+                const int32_t*, int64_t, int64_t, int, uint16_t*, int64_t, void*, int64_t, hipStream_t);
+int64_t gemv_workspace_bytes(int64_t, int64_t, int64_t, int);
 int launch_gemm(const uint16_t*, int64_t, int64_t, const uint32_t*, const uint16_t*,
                 const int32_t*, int64_t, int64_t, int, uint16_t*, int64_t, hipStream_t);
 int launch_awq_importance(const uint16_t*, int64_t, int64_t, int64_t, float*, hipStream_t);
@@ -49,6 +50,11 @@ namespace {
 constexpr int64_t kMaxDim = (int64_t)1 << 30;  // N, K, M each below 2^30
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool ranges_overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + (uintptr_t)bbytes && y < x + (uintptr_t)abytes;
+}
 
 // The kernels are built for gfx950 only: the current HIP device must be one
 // (checked once per device, then cached; no device counts as unsupported).
@@ -195,8 +201,41 @@ int w4a16_gemv(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
   if (st != W4A16_OK) return st;
   if (M > W4A16_GEMV_MAX_M) return W4A16_ERR_INVALID_ARG;
   if (int dc = device_check()) return dc;
-  return w4a16::launch_gemv(X, M, ldx, codes, scales, zeros, N, K, W4A16_GROUP, Y, ldy,
+  return w4a16::launch_gemv(X, M, ldx, codes, scales, zeros, N, K, W4A16_GROUP, Y, ldy, nullptr, 0,
                             (hipStream_t)stream);
+}
+
+int w4a16_gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t* bytes) {
+  if (!bytes) return W4A16_ERR_INVALID_ARG;
+  *bytes = 0;
+  if (M < 1 || M > W4A16_GEMV_MAX_M || N < 1 || K < W4A16_GROUP || K % W4A16_GROUP)
+    return W4A16_ERR_INVALID_ARG;
+  if (N >= kMaxDim || K >= kMaxDim) return W4A16_ERR_UNSUPPORTED;
+  if (int dc = device_check()) return dc;   // the plan depends on the device's CU count
+  *bytes = w4a16::gemv_workspace_bytes(M, N, K, W4A16_GROUP);
+  return W4A16_OK;
+}
+
+int w4a16_gemv_ws(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
+                  const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K, uint16_t* Y,
+                  int64_t ldy, void* workspace, int64_t workspace_bytes, void* stream) {
+  int st = check_matmul(X, M, ldx, codes, scales, zeros, N, K, Y, ldy);
+  if (st != W4A16_OK) return st;
+  if (M > W4A16_GEMV_MAX_M || workspace_bytes < 0 || (workspace_bytes > 0 && !workspace))
+    return W4A16_ERR_INVALID_ARG;
+  if (workspace && !aligned(workspace, 64)) return W4A16_ERR_MISALIGNED;
+  if (workspace && workspace_bytes > 0) {
+    const int64_t G = K / W4A16_GROUP;
+    if (ranges_overlap(workspace, workspace_bytes, X, ((M - 1) * ldx + K) * 2) ||
+        ranges_overlap(workspace, workspace_bytes, Y, ((M - 1) * ldy + N) * 2) ||
+        ranges_overlap(workspace, workspace_bytes, codes, N * (K / 2)) ||
+        ranges_overlap(workspace, workspace_bytes, scales, N * G * 2) ||
+        ranges_overlap(workspace, workspace_bytes, zeros, N * G * 4))
+      return W4A16_ERR_INVALID_ARG;
+  }
+  if (int dc = device_check()) return dc;
+  return w4a16::launch_gemv(X, M, ldx, codes, scales, zeros, N, K, W4A16_GROUP, Y, ldy, workspace,
+                            workspace_bytes, (hipStream_t)stream);
 }
 
 int w4a16_gemv_grouped(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
@@ -207,7 +246,7 @@ int w4a16_gemv_grouped(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t
   if (M > W4A16_GEMV_MAX_M) return W4A16_ERR_INVALID_ARG;
   if (M > 8 && (st = check_gemm_limits(M, N, K, ldx)) != W4A16_OK) return st;   // the GEMM runs M > 8
   if (int dc = device_check()) return dc;
-  return w4a16::launch_gemv(X, M, ldx, codes, scales, zeros, N, K, (int)group, Y, ldy,
+  return w4a16::launch_gemv(X, M, ldx, codes, scales, zeros, N, K, (int)group, Y, ldy, nullptr, 0,
                             (hipStream_t)stream);
 }
 
@@ -283,10 +322,6 @@ constexpr int64_t kChainHeader = w4a16::kChainHeaderBytes;   // barrier state an
 constexpr int64_t kChainMaxLds = 160 * 1024;
 constexpr int kChainSliceK = 2048;
 
-bool ranges_overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
-  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
-  return x < y + (uintptr_t)bbytes && y < x + (uintptr_t)abytes;
-}
 }  // namespace
 
 int w4a16_chain_workspace_bytes(int n_linears, int64_t* bytes) {

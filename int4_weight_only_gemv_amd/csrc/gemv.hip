@@ -26,13 +26,18 @@
 // matrix cores as sixteen 4x4 blocks per instruction, so more activation
 // rows cost almost no vector ALU time.
 //
-// gemv_tile (the rest, up to M = 32): 16-row tiles of W meet X (M padded to
-// 16 or 32) on v_mfma_f32_16x16x32_bf16, one group of a tile per 16-byte
-// load per lane; the same A operand against a B of ones gives the per-group
-// activation sums.  The waves of a block split K and add their partial tiles
-// through LDS in a fixed order.
+// gemv_walk (9 <= M <= 32): 16-row tiles of W meet X (M padded to 16 or
+// 32) on v_mfma_f32_16x16x32_bf16.  A block of 16 waves holds the
+// activations of its run of K in registers and walks a run of row tiles,
+// codes streaming through LDS by direct-to-LDS copies; rows longer than 32
+// groups split K over blocks through a caller's workspace.
 //
-// No kernel uses atomics or workspace: results are deterministic.
+// gemv_ring (the shapes the others leave: long rows without a workspace,
+// M <= 8 rows too long for gemv_dot and gemv_quad): one 16-row tile per
+// block, its waves splitting K, codes through a two-stage LDS ring.
+//
+// Sums across waves and blocks run in a fixed order: results are
+// deterministic.
 
 #include "common.h"
 
@@ -565,158 +570,467 @@ __global__ __launch_bounds__(1024) void gemv_quad_long_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// gemv_tile (9 <= M <= 32, and the shapes the other kernels leave): weights
-// on the matrix cores, codes streamed
+// Shared pieces of the matrix-core decode kernels (9 <= M <= 32)
 // ---------------------------------------------------------------------------
 //
-// D = A B on v_mfma_f32_16x16x32_bf16 with A = 16 activation rows (M padded)
-// and B = 16 weight rows, so lane (r16, q) of a result tile holds weight row
-// r16 for activation rows 4q .. 4q+3 and needs one scale / zero point.  One
-// 16-byte load per lane brings four code words of one row: a row tile's
-// group (16 rows x 64 B) per instruction; word 4q + t feeds k-step t, so
-// k-step t covers inputs 32q + 8t .. +7 of the group in lane group q, and
-// the activation fragment of lane (m, q) for k-step t is the 16 bytes of X
-// at that position, paired like the codes.  The same A against a B of ones
-// gives the activation sums of the group in the result layout.  A wave runs
-// RT row tiles over its share of the groups, the next group's codes and
-// activations in flight; the waves of a block split K and add their partial
-// tiles through LDS in a fixed order.
+// Matrix-core layout (v_mfma_f32_16x16x32_bf16): lane (r16, q) holds A row
+// r16 (an activation row) and B column r16 (a weight row) for inputs
+// 8q .. 8q+7 of a K step, and result column r16 for activation rows
+// 4q .. 4q+3.  K step t of a group covers its inputs 32t .. 32t+31: lane
+// (r16, q) takes the group's code word 4t + q and the activations
+// 32t + 8q .. +7 of its row.  The same A against a B of ones gives the
+// group's activation sums.  Per group and weight row
+//     acc += s * (P - (128 + z) * Xsum),   P = sum_k x (128 + q),
+// with one exact product, as in the other kernels.
+//
+// Codes travel by direct-to-LDS copies (global_load_lds_dwordx4) of 8 code
+// rows x 128 bytes (two groups): whole 128-byte lines, the pattern that reads
+// HBM fastest, and code bytes in flight hold no registers.  A copy puts row
+// r's 16-byte chunk c into slot c ^ r (^ 1 for the second copy of a 16-row
+// tile) of the row's 128 LDS bytes, which spreads the 4-byte B reads of one
+// instruction over all 64 banks.
 
-constexpr int kTileMaxWaves = 8;
+constexpr int kRingCopy = 1024;   // one copy: 8 code rows x 128 bytes
 
-template <int MT, int RT>
-__global__ __launch_bounds__(512) void gemv_tile_kernel(
+// ---------------------------------------------------------------------------
+// gemv_walk (9 <= M <= 32): activations held, row tiles walked
+// ---------------------------------------------------------------------------
+//
+// A block of 16 waves owns a run of 16-row tiles of W and a run of at most 32
+// groups of K (all of K, or one of KS equal runs; KS > 1 needs a workspace).
+// Wave w owns two groups of the run: it reads their activations once, as
+// whole 128-byte lines, moves them into the A layout with lane permutes, and
+// keeps them (and their activation sums) in registers for every row tile of
+// the block, so X crosses the L2 once per block.  The two groups' slot in
+// the run is (w + block) % 16, so that at any moment the blocks read
+// different parts of X.  The block's scales and zero points come into LDS
+// with coalesced loads (rows padded to an odd number of words, so that the
+// 16 rows of one read instruction fall on distinct banks).  Then each wave
+// streams its two groups of every row tile through a two-tile ring in LDS,
+// one tile ahead, and per tile the 16 waves' partial tiles are added through
+// LDS in a fixed order.  The issue order is: the first tile's code copies,
+// the activations, the scales and zero points; inside the walk the only
+// global operations are the code copies, so a fixed count of the in-order
+// memory counter tells when a tile has landed.  The barriers inside the walk
+// wait for LDS only (a __syncthreads() would also wait for the ring's
+// copies in flight).
+//
+// KS = 1: the outputs collect in LDS and leave with coalesced stores.
+// KS > 1: each block stores its partial outputs into the workspace with
+// 32-bit agent-scope atomic stores (coherent across the XCDs' L2 caches),
+// waits for them, then counts itself in on its row range's counter; the
+// block that arrives last adds the KS partials in the order of their runs,
+// stores Y and resets the counter to zero for the next launch.  Results do
+// not depend on arrival order.
+
+constexpr int kWalkWaves = 16;
+constexpr int kWalkGroups = 2 * kWalkWaves;   // groups per block
+constexpr int kWalkTile = 2 * kRingCopy;      // one wave's codes of a row tile
+constexpr int kWalkRing = 2;                  // ring depth (tiles)
+constexpr int kWalkMetaMax = 4096;            // scales (and zero points) per block
+// LDS row strides of the block's tables, an odd number of 4-byte words
+constexpr int kWalkSStride = 2 * kWalkGroups + 2;   // scales: 34 BF16 per row
+constexpr int kWalkZStride = kWalkGroups + 1;       // zero points: 33 per row
+constexpr int kWalkOStride = 34;                    // outputs: 34 BF16 per row (32 columns of M)
+// Workspace of the split-K walk: a fixed region of kWalkMaxRanges counters,
+// one per row range on its own 64-byte line (the same place for every shape;
+// each launch leaves its counters at zero), then the partial outputs,
+// [range][run][16 tmax rows][32 columns of M] floats.
+constexpr int kWalkMaxRanges = 1024;
+constexpr int64_t kWalkCounterBytes = 64;
+
+// dynamic LDS of a block walking at most tmax tiles
+constexpr int walk_lds_bytes(int MT, int tmax) {
+  return kWalkWaves * kWalkRing * kWalkTile             // code rings
+         + 16 * tmax * kWalkSStride * 2                 // scales
+         + 16 * tmax * kWalkZStride * 4                 // zero points
+         + kWalkWaves * MT * 1024                       // partial tiles
+         + 16 * tmax * kWalkOStride * 2;                // outputs
+}
+
+template <int MT>
+__global__ __launch_bounds__(1024) void gemv_walk_kernel(
     const uint16_t* __restrict__ X, int M, int64_t ldx, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K,
-    uint16_t* __restrict__ Y, int64_t ldy) {
-  __shared__ float red[kTileMaxWaves][RT * MT * 4][kWave];
-
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int S = blockDim.x / kWave;
-  const int G = K / kGroup;
+    uint16_t* __restrict__ Y, int64_t ldy, int tiles, int tmax, int KS, unsigned* __restrict__ ws) {
+  constexpr int D = kWalkRing;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, q = lane >> 4;
-  const int gb = (G * wave) / S, ge = (G * (wave + 1)) / S;
+  const int G = K / kGroup;
+  // block = (row range, run ks of the KS runs of K groups)
+  const int nranges = (int)gridDim.x / KS;
+  const int range = (int)blockIdx.x / KS, ks = (int)blockIdx.x - range * KS;
+  const int t0 = (int)(((int64_t)tiles * range) / nranges);
+  const int T = (int)(((int64_t)tiles * (range + 1)) / nranges) - t0;
+  const int r0 = 16 * t0;
+  const int rows = min(16 * T, N - r0);
+  const int kb0 = (G * ks) / KS, GB = (G * (ks + 1)) / KS - kb0;   // the block's groups
+  const int gl = 2 * (((int)blockIdx.x + wave) % kWalkWaves);      // the wave's, block-local
+  const int g0 = kb0 + gl, ng = max(0, min(2, GB - gl));
 
-  // weight rows of this lane (one per row tile), clamped for loads
-  const u32x4* crow[RT];
-  const uint16_t* srow[RT];
-  const int32_t* zrow[RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int n = min((int)blockIdx.x * 16 * RT + 16 * rt + r16, N - 1);
-    crow[rt] = reinterpret_cast<const u32x4*>(codes + (int64_t)n * (K / 8)) + q;
-    srow[rt] = scales + (int64_t)n * G;
-    zrow[rt] = zeros + (int64_t)n * G;
-  }
-  // activation rows of this lane (A operand rows r16 + 16 mt); rows past M
-  // read row 0 and are zeroed after the load
-  const u32x4* xrow[MT];
-  bool xvalid[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = r16 + 16 * mt;
-    xvalid[mt] = m < M;
-    xrow[mt] = reinterpret_cast<const u32x4*>(X + (int64_t)(xvalid[mt] ? m : 0) * ldx) + 4 * q;
-  }
+  uint8_t* my = smem + wave * (D * kWalkTile);
+  uint16_t* meta_s = reinterpret_cast<uint16_t*>(smem + kWalkWaves * D * kWalkTile);
+  int32_t* meta_z = reinterpret_cast<int32_t*>(meta_s + 16 * tmax * kWalkSStride);
+  float* red = reinterpret_cast<float*>(meta_z + 16 * tmax * kWalkZStride);
+  uint16_t* out = reinterpret_cast<uint16_t*>(red + kWalkWaves * MT * 256);
 
-  const u32x4 ones = {kOnePair, kOnePair, kOnePair, kOnePair};
-  f32x4 acc[RT][MT];
+  // 1. code copies of tile 0: lane -> row lane / 8 of a copy's 8, LDS slot
+  //    lane % 8, which takes the row's chunk slot ^ row ^ h (copy h of the
+  //    tile's two); rows past N re-read row N - 1
+  const int crow = lane >> 3;
+  auto copy_tile = [&](int t) {
+    uint8_t* dst = my + (t % D) * kWalkTile;
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[rt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  if (gb < ge) {
-    u32x4 cw[2][RT];          // code words of a group: word 4q + t in element t
-    u32x4 xr[2][4][MT];       // activation fragments of a group, per k-step
-    uint32_t sr[2][RT];
-    int zr[2][RT];
-    auto load = [&](int buf, int g) {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        cw[buf][rt] = __builtin_nontemporal_load(crow[rt] + g * 4);
-        sr[buf][rt] = srow[rt][g];
-        zr[buf][rt] = zrow[rt][g];
-      }
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) xr[buf][t][mt] = xrow[mt][g * 16 + t];
-    };
-    auto compute = [&](int buf) {
-      f32x4 P[RT][MT], xs[MT];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        u32x4 a[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          u32x4 raw = xr[buf][t][mt];
-          if (!xvalid[mt]) raw = u32x4{0u, 0u, 0u, 0u};
-          a[mt] = x_pairs_from_natural(raw);
-          xs[mt] = mfma16x16x32(a[mt], ones, t == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : xs[mt]);
-        }
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          const u32x4 b = codes_to_bias128_pairs(cw[buf][rt][t]);
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            P[rt][mt] = mfma16x16x32(a[mt], b, t == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : P[rt][mt]);
-        }
-      }
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const float sc = bf16_to_f32(sr[buf][rt]);
-        const float zb = (float)zr[buf][rt] + 128.f;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[rt][mt][i] = fmaf(sc, fmaf(-zb, xs[mt][i], P[rt][mt][i]), acc[rt][mt][i]);
-      }
-    };
-    load(0, gb);
-    int g = gb;
-    for (; g + 1 < ge; g += 2) {
-      load(1, g + 1);
-      compute(0);
-      if (g + 2 < ge) load(0, g + 2);
-      compute(1);
+    for (int h = 0; h < 2; ++h) {
+      const int n = min(r0 + 16 * t + 8 * h + crow, N - 1);
+      const int chunk = min(4 * g0 + ((lane & 7) ^ crow ^ h), 4 * max(g0 + ng, 1) - 1);
+      copy16_to_lds(reinterpret_cast<const char*>(codes) + (int64_t)n * (K / 2) + 16 * chunk,
+                    dst + h * kRingCopy);
     }
-    if (g < ge) compute(0);
-  }
-
-  if (S > 1) {
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) red[wave][(rt * MT + mt) * 4 + i][lane] = acc[rt][mt][i];
-    __syncthreads();
-    if (wave != 0) return;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = red[0][(rt * MT + mt) * 4 + i][lane];
-          for (int w = 1; w < S; ++w) v += red[w][(rt * MT + mt) * 4 + i][lane];
-          acc[rt][mt][i] = v;
-        }
-  }
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int n = (int)blockIdx.x * 16 * RT + 16 * rt + r16;
-    if (n >= N) continue;
+  };
+  if (ng > 0 && T > 0) copy_tile(0);
+  asm volatile("" ::: "memory");
+  // 2. activations of the wave's two groups (rows past M re-read row M - 1;
+  //    their results are not stored), read as whole 128-byte lines: window
+  //    w (inputs 64 w .. 64 w + 63 of the pair of groups) of rows 8h .. 8h+7
+  //    of activation tile mt, lane l holding row l / 8, inputs 8 (l % 8) ..
+  u32x4 xr[MT][4][2];
+  if (ng > 0) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 16 * mt + 4 * q + i;
-        if (m < M) Y[(int64_t)m * ldy + n] = f32_to_bf16_rne(acc[rt][mt][i]);
+      for (int h = 0; h < 2; ++h) {
+        const uint16_t* xrow = X + (int64_t)min(16 * mt + 8 * h + (lane >> 3), M - 1) * ldx + 8 * (lane & 7);
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          xr[mt][w][h] = *reinterpret_cast<const u32x4*>(xrow + (g0 + min(w >> 1, ng - 1)) * kGroup + 64 * (w & 1));
       }
+  }
+  asm volatile("" ::: "memory");
+  // 3. the block's scales and zero points: rows r0 .. r0 + rows - 1, groups
+  //    kb0 .. kb0 + GB - 1
+  const int nmeta = rows * GB;
+  uint32_t sv[kWalkMetaMax / 1024];
+  int zv[kWalkMetaMax / 1024];
+#pragma unroll
+  for (int k = 0; k < kWalkMetaMax / 1024; ++k) {
+    const int e = (int)threadIdx.x + 1024 * k;
+    if (e < nmeta) {
+      const int r = e / GB, g = e - r * GB;
+      sv[k] = scales[(int64_t)(r0 + r) * G + kb0 + g];
+      zv[k] = zeros[(int64_t)(r0 + r) * G + kb0 + g];
+    }
+  }
+  asm volatile("" ::: "memory");
+
+  // the A fragments: lane (r16, q) of K step t of group g takes row r16,
+  // inputs 32 t + 8 q .. of the group, i.e. window 2 g + t / 2, chunk
+  // 4 (t % 2) + q, held by lane 8 (r16 % 8) + 4 (t % 2) + q of half r16 / 8;
+  // then paired like the codes (code j with code j + 4 of a word)
+  u32x4 xb[2][4][MT];
+  if (ng > 0) {
+    const bool lo = r16 < 8;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const int src = 4 * (8 * (r16 & 7) + 4 * s2 + q);
+          u32x4 f;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const uint32_t a = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)xr[mt][w][0][d]);
+            const uint32_t b = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)xr[mt][w][1][d]);
+            f[d] = lo ? a : b;
+          }
+          xb[w >> 1][2 * (w & 1) + s2][mt] = x_pairs_from_natural(f);
+        }
+  }
+  // activation sums of the two groups, in the result layout
+  const u32x4 ones = {kOnePair, kOnePair, kOnePair, kOnePair};
+  f32x4 xs[2][MT];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+      if (ng > 0) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) a = mfma16x16x32(xb[g][t][mt], ones, a);
+      }
+      xs[g][mt] = a;
+    }
+#pragma unroll
+  for (int k = 0; k < kWalkMetaMax / 1024; ++k) {
+    const int e = (int)threadIdx.x + 1024 * k;
+    if (e < nmeta) {
+      const int r = e / GB, g = e - r * GB;
+      meta_s[r * kWalkSStride + g] = (uint16_t)sv[k];
+      meta_z[r * kWalkZStride + g] = zv[k];
+    }
+  }
+  __syncthreads();
+
+  // KS > 1: this block's partial outputs in the workspace
+  unsigned* part = ws + (int64_t)kWalkMaxRanges * (kWalkCounterBytes / 4) +
+                   ((int64_t)range * KS + ks) * (16 * tmax * 32);
+  // B word of K step k of group g: this lane's row sits in copy r16 / 8 at
+  // row r16 % 8, word 4k + q of the group in chunk 4g + k, which the copy put
+  // in slot (4g + k) ^ swizzle; bits 4..6 of the offset hold the slot
+  const int bsw = (r16 & 7) ^ (r16 >> 3);
+  const int boffx = ((r16 >> 3) * kRingCopy + 128 * (r16 & 7) + 4 * q) | (16 * bsw);
+  auto tile = [&](int t, auto slotc) {
+    constexpr int slot = decltype(slotc)::value;
+    f32x4 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (ng > 0) {
+      // tile t landed (nothing is issued after it but the next tile's
+      // copies, issued just below); then the copies of tile t + 1 into the
+      // slot tile t - 1 freed
+      wait_vmcnt<0>();
+      asm volatile("" ::: "memory");
+      if (t + 1 < T) copy_tile(t + 1);
+      asm volatile("" ::: "memory");
+      const uint8_t* st = my + slot * kWalkTile;
+      const int row = 16 * t + r16;   // block-local row of this lane
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        if (g < ng) {
+          const float s = bf16_to_f32(meta_s[row * kWalkSStride + gl + g]);
+          const float z128 = (float)meta_z[row * kWalkZStride + gl + g] + 128.f;
+          f32x4 P[MT];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(st + (boffx ^ (16 * (4 * g + k))));
+            const u32x4 bv = codes_to_bias128_pairs(w);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              P[mt] = mfma16x16x32(xb[g][k][mt], bv, k == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : P[mt]);
+          }
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[mt][i] = fmaf(s, fmaf(-z128, xs[g][mt][i], P[mt][i]), acc[mt][i]);
+        }
+      }
+    }
+    // the waves' partial tiles, added in a fixed order (tile element
+    // e = 64 v + l: activation tile v / 4, i = v % 4)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[(wave * MT * 4 + mt * 4 + i) * 64 + lane] = acc[mt][i];
+    block_barrier_lds();
+    for (int e = threadIdx.x; e < MT * 256; e += 1024) {
+      float sum = red[e];
+#pragma unroll
+      for (int w = 1; w < kWalkWaves; ++w) sum += red[w * MT * 256 + e];
+      const int v = e >> 6, l = e & 63;
+      const int m = 16 * (v >> 2) + 4 * (l >> 4) + (v & 3);
+      const int r = 16 * t + (l & 15);
+      if (KS == 1)
+        out[r * kWalkOStride + m] = f32_to_bf16_rne(sum);
+      else
+        __hip_atomic_store(part + r * 32 + m, __float_as_uint(sum), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    block_barrier_lds();
+  };
+  // tiles in pairs, so that each tile's ring slot is a constant
+  for (int t = 0; t < T; t += 2) {
+    tile(t, Ic<0>{});
+    if (t + 1 < T) tile(t + 1, Ic<1>{});
+  }
+
+  if (KS == 1) {
+    // the block's outputs: Y[m][r0 + r], consecutive threads on consecutive r
+    for (int e = threadIdx.x; e < rows * M; e += 1024) {
+      const int m = e / rows, r = e - m * rows;
+      Y[(int64_t)m * ldy + r0 + r] = out[r * kWalkOStride + m];
+    }
+    return;
+  }
+  // the block's partial stores are complete before it counts itself in (a
+  // block barrier alone does not wait for global stores); the last of the
+  // range's KS blocks adds the partials in the order of their runs
+  wait_vmcnt<0>();
+  __syncthreads();
+  unsigned* counter = ws + (int64_t)range * (kWalkCounterBytes / 4);
+  unsigned* last = reinterpret_cast<unsigned*>(out);
+  if (threadIdx.x == 0) {
+    const unsigned a = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *last = a == (unsigned)(KS - 1);
+  }
+  __syncthreads();
+  if (!*last) return;
+  const unsigned* part0 = ws + (int64_t)kWalkMaxRanges * (kWalkCounterBytes / 4) +
+                          (int64_t)range * KS * (16 * tmax * 32);
+  for (int e = threadIdx.x; e < rows * M; e += 1024) {
+    const int m = e / rows, r = e - m * rows;
+    float sum = 0.f;
+    for (int k = 0; k < KS; ++k)
+      sum += __uint_as_float(__hip_atomic_load(part0 + (int64_t)k * (16 * tmax * 32) + r * 32 + m,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    Y[(int64_t)m * ldy + r0 + r] = f32_to_bf16_rne(sum);
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// gemv_ring (M <= 32, the shapes gemv_walk leaves: rows longer than 32
+// groups without a workspace, and M <= 8 rows too long for gemv_dot and
+// gemv_quad)
+// ---------------------------------------------------------------------------
+//
+// A block owns 16 weight rows and all of K; its 8 waves split K into
+// contiguous runs of groups.  A wave streams its run of codes through a ring
+// of two stages in LDS (a stage is two groups, one copy of 8 rows x 128
+// bytes per 8 rows), and loads each group's activations, scales and zero
+// points one group ahead into registers.  Memory operations of a wave, in
+// issue order: at each stage start the copies of the next stage, at each
+// group the activations, scales and zero points of the next group; nothing
+// past the run is issued, so a fixed count of the in-order memory counter
+// tells when a stage has landed.  The waves' partial tiles are added through
+// LDS in a fixed order.
+
+constexpr int kRingWaves = 8;
+constexpr int kRingStage = 2 * kRingCopy;   // one wave's stage: 16 rows x two groups
+
+template <int MT>
+__global__ __launch_bounds__(kRingWaves * 64) void gemv_ring_kernel(
+    const uint16_t* __restrict__ X, int M, int64_t ldx, const uint32_t* __restrict__ codes,
+    const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K,
+    uint16_t* __restrict__ Y, int64_t ldy) {
+  constexpr int W = kRingWaves, S = 2;
+  constexpr int kBatch = 4 * MT + 2;        // memory operations per group batch
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[W * S * kRingStage];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, q = lane >> 4;
+  const int G = K / kGroup;
+  const int gb = (G * wave) / W, ge = (G * (wave + 1)) / W;   // this wave's groups
+  const int NG = ge - gb, NS = (NG + 1) / 2;
+  const int n0 = blockIdx.x * 16;
+  uint8_t* my = ring + wave * (S * kRingStage);
+
+  f32x4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (NG > 0) {
+    // copies: lane -> row lane / 8 of the copy's 8, LDS slot lane % 8, which
+    // takes the row's chunk slot ^ row ^ h (rows past N re-read row N - 1)
+    const int crow = lane >> 3;
+    const char* cptr[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      cptr[h] = reinterpret_cast<const char*>(codes) + (int64_t)min(n0 + 8 * h + crow, N - 1) * (K / 2);
+    const int clast = 4 * ge - 1;   // the run's last 16-byte chunk
+    auto copy_stage = [&](int slot, int j) {
+      uint8_t* dst = my + slot * kRingStage;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        copy16_to_lds(cptr[h] + 16 * min(4 * gb + 8 * j + ((lane & 7) ^ crow ^ h), clast), dst + h * kRingCopy);
+    };
+
+    // activations of rows 16 mt + r16 (rows past M re-read row M - 1; their
+    // results are not stored), scales and zero points of this lane's row
+    const u32x4* xp[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      xp[mt] = reinterpret_cast<const u32x4*>(X + (int64_t)min(16 * mt + r16, M - 1) * ldx) + q;
+    const int nrow = min(n0 + r16, N - 1);
+    const uint16_t* sp = scales + (int64_t)nrow * G + gb;
+    const int32_t* zp = zeros + (int64_t)nrow * G + gb;
+    u32x4 xb[2][4][MT];
+    uint32_t sb[2];
+    int zb[2];
+    auto load_batch = [&](int b, int i) {   // group gb + i into batch b
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) xb[b][t][mt] = xp[mt][(gb + i) * 16 + 4 * t];
+      sb[b] = sp[i];
+      zb[b] = zp[i];
+    };
+
+    const int bsw = (r16 & 7) ^ (r16 >> 3);
+    const int boffx = ((r16 >> 3) * kRingCopy + 128 * (r16 & 7) + 4 * q) | (16 * bsw);
+    const u32x4 ones = {kOnePair, kOnePair, kOnePair, kOnePair};
+    auto compute = [&](int b, const uint8_t* st, auto gsc) {
+      constexpr int gs = decltype(gsc)::value;
+      f32x4 xs[MT], P[MT];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(st + (boffx ^ (16 * (4 * gs + t))));
+        const u32x4 bv = codes_to_bias128_natural(w, kExpBytes);   // natural order, like X
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          xs[mt] = mfma16x16x32(xb[b][t][mt], ones, t == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : xs[mt]);
+          P[mt] = mfma16x16x32(xb[b][t][mt], bv, t == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : P[mt]);
+        }
+      }
+      const float s = bf16_to_f32(sb[b]);
+      const float z128 = (float)zb[b] + 128.f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mt][i] = fmaf(s, fmaf(-z128, xs[mt][i], P[mt][i]), acc[mt][i]);
+    };
+
+    // prologue: stage 0 and batch 0
+    copy_stage(0, 0);
+    asm volatile("" ::: "memory");
+    load_batch(0, 0);
+    asm volatile("" ::: "memory");
+    for (int i0 = 0; i0 < NG; i0 += 2) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i = i0 + u;
+        if (i >= NG) break;
+        const int j = i >> 1;
+        if (u == 0) {
+          // stage j landed: its copies are followed by at least one batch
+          // (batch 0 in the prologue, batch i - 1 after), so waiting until
+          // at most one batch is in flight covers them.  Then the copies of
+          // stage j + 1 into the slot stage j - 1 freed.
+          wait_vmcnt<kBatch>();
+          asm volatile("" ::: "memory");
+          if (j + 1 < NS) copy_stage((j + 1) & 1, j + 1);
+          asm volatile("" ::: "memory");
+        }
+        if (i + 1 < NG) load_batch(u ^ 1, i + 1);
+        asm volatile("" ::: "memory");
+        if (u == 1)
+          compute(1, my + (j & 1) * kRingStage, Ic<1>{});
+        else
+          compute(0, my + (j & 1) * kRingStage, Ic<0>{});
+      }
+    }
+  }
+
+  // sum the waves' tiles in a fixed order (the ring is free once every copy
+  // of this block has landed)
+  wait_vmcnt<0>();
+  __syncthreads();
+  constexpr int V = MT * 4;   // values per lane
+  float* red = reinterpret_cast<float*>(ring);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[(wave * V + mt * 4 + i) * 64 + lane] = acc[mt][i];
+  __syncthreads();
+  for (int e = threadIdx.x; e < V * 64; e += W * 64) {
+    float sum = red[e];
+    for (int w = 1; w < W; ++w) sum += red[w * V * 64 + e];
+    const int v = e >> 6, l = e & 63;
+    const int n = n0 + (l & 15);
+    const int m = 16 * (v >> 2) + 4 * (l >> 4) + (v & 3);
+    if (n < N && m < M) Y[(int64_t)m * ldy + n] = f32_to_bf16_rne(sum);
   }
 }
 
@@ -927,10 +1241,91 @@ int launch_gemv_int8(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* 
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 
-// group: 32, 64 or 128 inputs per quantisation group (checked by the caller)
+// ---------------------------------------------------------------------------
+// gemv_walk / gemv_ring launches
+// ---------------------------------------------------------------------------
+
+namespace {
+
+// The walk's plan for a shape: KS runs of K (the fewest with at most 32
+// groups each), row ranges (one block per CU, more when a range's scales
+// would not fit the block's table), tiles per range.  Returns false when
+// the walk does not apply (KS > 1 without room for the split).
+struct WalkPlan {
+  int KS, nranges, tiles, tmax;
+  int64_t ws_bytes;   // workspace the split needs (0 for KS = 1)
+};
+
+bool walk_plan(int64_t N, int64_t K, WalkPlan& p) {
+  const int G = (int)(K / kGroup);
+  p.KS = (G + kWalkGroups - 1) / kWalkGroups;
+  const int GB = (G + p.KS - 1) / p.KS;
+  p.tiles = (int)((N + 15) / 16);
+  const int tcap = kWalkMetaMax / (16 * GB);   // tiles whose scales fit the table (>= 8)
+  p.nranges = max(1, min(p.tiles, device_cu_count() / p.KS));
+  p.nranges = max(p.nranges, (p.tiles + tcap - 1) / tcap);
+  p.tmax = (p.tiles + p.nranges - 1) / p.nranges;
+  if (p.KS > 1 && p.nranges > kWalkMaxRanges) return false;
+  if ((int64_t)p.nranges * p.KS >= ((int64_t)1 << 31)) return false;
+  p.ws_bytes = p.KS == 1 ? 0
+                         : (int64_t)kWalkMaxRanges * kWalkCounterBytes +
+                               (int64_t)p.nranges * p.KS * (16 * p.tmax * 32) * 4;
+  return true;
+}
+
+template <int MT>
+int launch_walk(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes, const uint16_t* scales,
+                const int32_t* zeros, int64_t N, int64_t K, uint16_t* Y, int64_t ldy, const WalkPlan& p,
+                void* workspace, hipStream_t stream) {
+  static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_walk_kernel<MT>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               160 * 1024) == hipSuccess;
+  if (!attr) return 4;
+  hipLaunchKernelGGL(gemv_walk_kernel<MT>, dim3((unsigned)(p.nranges * p.KS)), dim3(1024),
+                     walk_lds_bytes(MT, p.tmax), stream, X, (int)M, ldx, codes, scales, zeros, (int)N,
+                     (int)K, Y, ldy, p.tiles, p.tmax, p.KS, reinterpret_cast<unsigned*>(workspace));
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+template <int MT>
+int launch_ring(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes, const uint16_t* scales,
+                const int32_t* zeros, int64_t N, int64_t K, uint16_t* Y, int64_t ldy, hipStream_t stream) {
+  hipLaunchKernelGGL(gemv_ring_kernel<MT>, dim3((unsigned)((N + 15) / 16)), dim3(kRingWaves * 64), 0,
+                     stream, X, (int)M, ldx, codes, scales, zeros, (int)N, (int)K, Y, ldy);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+// M <= 32 on the matrix cores (groups of 128): the walk when it applies
+// (with a workspace of at least its ws_bytes when it splits K), the ring
+// otherwise.  Rows past 16 (32) of M take the second activation tile.
+int launch_gemv_mt(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
+                   const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K, uint16_t* Y,
+                   int64_t ldy, void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  WalkPlan p;
+  if (walk_plan(N, K, p) && (p.KS == 1 || (workspace != nullptr && workspace_bytes >= p.ws_bytes))) {
+    return M <= 16 ? launch_walk<1>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, p, workspace, stream)
+                   : launch_walk<2>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, p, workspace, stream);
+  }
+  return M <= 16 ? launch_ring<1>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream)
+                 : launch_ring<2>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
+}
+
+}  // namespace
+
+// Workspace that lets launch_gemv split K for this shape (0: none needed).
+int64_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int group) {
+  if (group != kGroup || M <= 8) return 0;
+  WalkPlan p;
+  return walk_plan(N, K, p) ? p.ws_bytes : 0;
+}
+
+// group: 32, 64 or 128 inputs per quantisation group (checked by the caller).
+// workspace (may be null): zero-filled device memory of workspace_bytes,
+// left zero-filled; with at least gemv_workspace_bytes() the decode kernel
+// for 9 <= M <= 32 may split K over blocks.
 int launch_gemv(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
                 const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K, int group,
-                uint16_t* Y, int64_t ldy, hipStream_t stream) {
+                uint16_t* Y, int64_t ldy, void* workspace, int64_t workspace_bytes, hipStream_t stream) {
   if (group != kGroup)
     return launch_gemv_small_groups(X, M, ldx, codes, scales, zeros, N, K, group == 32 ? 5 : 6, Y,
                                     ldy, stream);
@@ -960,26 +1355,7 @@ int launch_gemv(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes
     }
     return hipGetLastError() == hipSuccess ? 0 : 4;
   }
-  // Row tiles per wave: more for tall layers (each activation fragment is
-  // reused by every tile); four waves per block split K.  Fitted to timings
-  // of the 8B- and 70B-shaped layers at M = 8, 16, 32.
-  const int n_ = (int)N, k_ = (int)K, m_ = (int)M;
-  const int G = k_ / kGroup;
-  const int S = max(1, min(4, G / 2));
-  const dim3 block(S * kWave);
-  int rt = n_ >= 16384 ? 4 : (n_ >= 6144 ? 2 : 1);
-  if (M > 16 && rt > 2) rt = 2;   // four tiles of 32 activation rows would spill
-  const dim3 grid((unsigned)((n_ + 16 * rt - 1) / (16 * rt)));
-#define W4A16_TILE(MT, RT)                                                                       \
-  hipLaunchKernelGGL((gemv_tile_kernel<MT, RT>), grid, block, 0, stream, X, m_, ldx, codes, scales, \
-                     zeros, n_, k_, Y, ldy)
-  if (M <= 16) {
-    if (rt == 4) W4A16_TILE(1, 4); else if (rt == 2) W4A16_TILE(1, 2); else W4A16_TILE(1, 1);
-  } else {
-    if (rt == 2) W4A16_TILE(2, 2); else W4A16_TILE(2, 1);
-  }
-#undef W4A16_TILE
-  return hipGetLastError() == hipSuccess ? 0 : 4;
+  return launch_gemv_mt(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, workspace, workspace_bytes, stream);
 }
 
 }  // namespace w4a16
