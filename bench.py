@@ -248,6 +248,8 @@ def main():
                          "frac": round(flops[dom_p] / times[dom_p] / 1e12 / BF16_PEAK_TFLOPS, 4),
                          "traffic": None},
         }
+        prefill["roofline"]["traffic"] = measured_traffic(
+            layers[dom_p], Mp, "gemm_llama8b_prefill_m4096_traffic.json", ("gemm.hip", "common.h"))
         log(f"[bench] prefill M={Mp}: {tf:.1f} TFLOP/s")
         del pxs, pys
         # the other prefill batch sizes of the layer set, same protocol
@@ -416,29 +418,30 @@ def single_linear(dev, stream, M=1, reps=400):
             "launches_timed": reps}
 
 
-def kernel_source_digest() -> str:
-    """sha256 of the decode kernel's sources (the counters recorded under
-    profiles/ only apply to the code they were taken on)."""
+def kernel_source_digest(files=("gemv.hip", "common.h")) -> str:
+    """sha256 of a kernel's sources (the counters recorded under profiles/
+    only apply to the code they were taken on)."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("gemv.hip", "common.h"):
+    for f in files:
         with open(os.path.join(ROOT, "int4_weight_only_gemv_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic(layer, M):
-    """HBM bytes per launch of the dominant decode launch, from the FETCH_SIZE
-    and WRITE_SIZE counters recorded in profiles/ (each scaled by what the
+def measured_traffic(layer, M, name="gemv_llama8b_decode_m1_traffic.json",
+                     sources=("gemv.hip", "common.h")):
+    """HBM bytes per launch of a dominant launch, from the FETCH_SIZE and
+    WRITE_SIZE counters recorded in profiles/ (each scaled by what the
     counter read for a copy of known size), or None when they were taken on
     other kernel sources or another shape."""
-    path = os.path.join(ROOT, "profiles", "gemv_llama8b_decode_m1_traffic.json")
+    path = os.path.join(ROOT, "profiles", name)
     try:
         with open(path) as f:
             rec = json.load(f)
     except OSError:
         return None
-    if rec.get("source_sha256") != kernel_source_digest():
+    if rec.get("source_sha256") != kernel_source_digest(sources):
         return None
     if (rec.get("N"), rec.get("K"), rec.get("M")) != (layer.N, layer.K, M):
         return None
