@@ -56,6 +56,84 @@ constexpr int kMaxSlices = 16;    // K <= 32768 on this kernel
 constexpr int pow2_at_least(int v) { return v <= 1 ? 1 : 2 * pow2_at_least((v + 1) / 2); }
 constexpr int log2_exact(int v) { return v <= 1 ? 0 : 1 + log2_exact(v / 2); }
 
+// Cross-lane sums without LDS: DPP for lanes within a 16-lane row, the
+// permlane swaps across rows.  DPP quad_perm [1,0,3,2] / [2,3,0,1] reads lane
+// l ^ 1 / l ^ 2; row_ror:n gives lane l the value of lane l - n (mod 16) of
+// its row; v_permlane32_swap exchanges the upper 32 lanes of its first operand
+// with the lower 32 of its second, v_permlane16_swap the odd 16-lane rows of
+// its first operand with the even rows of its second.
+constexpr int kDppXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppRor8 = 0x128;    // row_ror:8: lane l ^ 8
+constexpr int kDppRor12 = 0x12C;   // row_ror:12: lane l + 4 (mod 16)
+
+template <int C>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), C, 0xF, 0xF, false));
+}
+
+// x(l) + x(l ^ 2^bit) for lane bit 5, 4 or 3, in every lane; for bit 2
+// exact only in lanes whose bit 2 is clear.
+template <int BIT>
+__device__ __forceinline__ float pair_sum(float x) {
+  if constexpr (BIT >= 4) {
+    const auto r = BIT == 5 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false)
+                            : __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else if constexpr (BIT == 3) {
+    return x + dpp<kDppRor8>(x);
+  } else {
+    static_assert(BIT == 2, "lane bits 2..5");
+    return x + dpp<kDppRor12>(x);
+  }
+}
+
+// One halving step on lane bit 5, 4 or 3: lanes whose bit is clear end with
+// a(l) + a(l ^ 2^bit), lanes whose bit is set with b(l) + b(l ^ 2^bit).
+template <int BIT>
+__device__ __forceinline__ float halve(float a, float b, int lane) {
+  if constexpr (BIT >= 4) {
+    const auto r = BIT == 5 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false)
+                            : __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else {
+    static_assert(BIT == 3, "halving on lane bits 3..5");
+    return pick((lane & 8) ? ~0u : 0u, pair_sum<3>(b), pair_sum<3>(a));
+  }
+}
+
+// Sum of MP = 2^LM values per lane over lane bits 2..5 (the 16 lane groups of
+// four): halving on bits 5, 4, .. (value i + MP/2 moves to the lanes whose
+// bit 5 is set, and so on), then plain sums on the remaining bits.  After it,
+// a lane whose bits 2 .. 5-LM are clear holds in part[0] the sum of value m
+// over its four-lane position, m read from its bits 5 .. 6-LM (bit 5 the
+// highest).
+template <int MP, int LM>
+__device__ __forceinline__ void lane_tree_sum(float* part, int lane) {
+  static_assert(MP == (1 << LM) && LM <= 3, "at most 8 values per lane");
+  static_for<0, LM>([&](auto bi) {
+    constexpr int b = decltype(bi)::value, n = MP >> b;
+#pragma unroll
+    for (int i = 0; i < n / 2; ++i) part[i] = halve<5 - b>(part[i], part[i + n / 2], lane);
+  });
+  static_for<LM, 4>([&](auto bi) {
+    constexpr int b = decltype(bi)::value;
+    part[0] = pair_sum<5 - b>(part[0]);
+  });
+}
+
+// The value index a lane holds after lane_tree_sum<MP, LM>, and whether it
+// holds a finished sum.
+template <int MP, int LM>
+__device__ __forceinline__ bool tree_result(int lane, int& m) {
+  m = 0;
+  int half = MP / 2;
+#pragma unroll
+  for (int b = 0; b < LM; ++b, half >>= 1)
+    if (lane & (32 >> b)) m += half;
+  return ((lane >> 2) & ((16 >> LM) - 1)) == 0;
+}
+
 // PL: groups smaller than 128 inputs (lg = log2 of the group size, 5 or 6):
 // each lane folds scale and zero point into its own 32 products for all R
 // rows (the fold is linear, so a group split over lanes sums correctly)
@@ -137,8 +215,8 @@ __global__ __launch_bounds__(1024) void gemv_dot_kernel(
     if constexpr (PL) {
       xsg[m] = sum;
     } else {
-      sum += __shfl_xor(sum, 1);
-      xsg[m] = sum + __shfl_xor(sum, 2);
+      sum += dpp<kDppXor1>(sum);
+      xsg[m] = sum + dpp<kDppXor2>(sum);
     }
   }
 
@@ -195,7 +273,7 @@ __global__ __launch_bounds__(1024) void gemv_dot_kernel(
         for (int m = 0; m < M; ++m) P[j][m] = s * fmaf(-zb128, xsg[m], P[j][m]);
       }
     }
-    // Sum over the 4 lanes of the group with a halving butterfly (lane bit 1
+    // Sum over the 4 lanes of the group, halving on the rows (lane bit 1
     // picks rows {0,1} or {2,3}, bit 0 one of those), so that lane l ends
     // with the group sums of row l % 4 ...
     float h[2][M];
@@ -204,11 +282,8 @@ __global__ __launch_bounds__(1024) void gemv_dot_kernel(
 #pragma unroll
       for (int r = 0; r < 2; ++r)
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-          const float send = pick(up, P[r][m], P[r + 2][m]);
-          const float keep = pick(up, P[r + 2][m], P[r][m]);
-          h[r][m] = keep + __shfl_xor(send, 2);
-        }
+        for (int m = 0; m < M; ++m)
+          h[r][m] = pick(up, P[r + 2][m] + dpp<kDppXor2>(P[r + 2][m]), P[r][m] + dpp<kDppXor2>(P[r][m]));
     }
     float part[MP];
     {
@@ -217,9 +292,7 @@ __global__ __launch_bounds__(1024) void gemv_dot_kernel(
       const float zb128 = (float)zb[cur][0] + (W8 ? 384.f : 128.f);
 #pragma unroll
       for (int m = 0; m < M; ++m) {
-        const float send = pick(up, h[0][m], h[1][m]);
-        const float keep = pick(up, h[1][m], h[0][m]);
-        const float q = keep + __shfl_xor(send, 1);
+        const float q = pick(up, h[1][m] + dpp<kDppXor1>(h[1][m]), h[0][m] + dpp<kDppXor1>(h[0][m]));
         // ... and removes the bias and zero point of that (row, group) once
         // (already done per lane with PL)
         part[m] = PL ? q : s * fmaf(-zb128, xsg[m], q);
@@ -227,30 +300,10 @@ __global__ __launch_bounds__(1024) void gemv_dot_kernel(
 #pragma unroll
       for (int m = M; m < MP; ++m) part[m] = 0.f;
     }
-    // then over the 16 groups of the slice (lane bits 2..5): halving on the
-    // activation rows first, plain sums after
-    int mask = 4;
-#pragma unroll
-    for (int cur_n = MP; cur_n > 1; cur_n >>= 1) {
-      const uint32_t up = (lane & mask) ? ~0u : 0u;
-#pragma unroll
-      for (int i = 0; i < cur_n / 2; ++i) {
-        const float send = pick(up, part[i], part[i + cur_n / 2]);
-        const float keep = pick(up, part[i + cur_n / 2], part[i]);
-        part[i] = keep + __shfl_xor(send, mask);
-      }
-      mask <<= 1;
-    }
-#pragma unroll
-    for (; mask <= 32; mask <<= 1) part[0] += __shfl_xor(part[0], mask);
-    // lane l < 4 MP holds row l % 4 and activation row m from its bits 2..
-    if (lane < 4 * MP) {
-      int m = 0, half = MP / 2;
-#pragma unroll
-      for (int b = 0; b < LM; ++b, half >>= 1)
-        if (lane & (4 << b)) m += half;
-      if (m < M) red[wave][nb * R * M + (lane & 3) * M + m] = part[0];
-    }
+    // then over the 16 groups of the slice (lane bits 2..5)
+    lane_tree_sum<MP, LM>(part, lane);
+    int m;
+    if (tree_result<MP, LM>(lane, m) && m < M) red[wave][nb * R * M + (lane & 3) * M + m] = part[0];
   }
   __syncthreads();
   for (int idx = threadIdx.x; idx < RB * M; idx += blockDim.x) {
@@ -296,15 +349,19 @@ __device__ __forceinline__ f32x4 mfma4x4x4(uint32_t a0, uint32_t a1, uint32_t b0
                                                 __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
 }
 
+constexpr int kQuadRing = 3;      // code vectors in flight per lane
+
 template <int M, int T, int NB>
 __global__ __launch_bounds__(1024) void gemv_quad_kernel(
     const uint16_t* __restrict__ X, int Mrt, int64_t ldx, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K, int lg,
     uint16_t* __restrict__ Y, int64_t ldy) {
   constexpr int MS = (M + 3) / 4;             // activation row sets of four
-  constexpr int MP = pow2_at_least(M);        // values per lane in the halving butterfly
+  constexpr int MP = pow2_at_least(M);        // values per lane in the lane tree
   constexpr int LM = log2_exact(MP);
-  static_assert(LM <= 4, "at most 16 values per lane");
+  constexpr int F = NB * T;                   // items: (batch of four rows, slice)
+  // (two rows of activation sets and two slices fill the registers: two deep)
+  constexpr int D = F < kQuadRing ? F : (M > 4 && T > 1 ? 2 : kQuadRing);
   __shared__ float red[kQuadMaxWaves][NB * 4 * M];
 
   const int lane = threadIdx.x & 63;
@@ -327,16 +384,19 @@ __global__ __launch_bounds__(1024) void gemv_quad_kernel(
   const int row0 = blockIdx.x * NB * 4;
   const u32x4* cbase = reinterpret_cast<const u32x4*>(codes);
 
-  u32x4 cb[2];
-  uint32_t sb[2];
-  int zb[2];
-  auto load = [&](int buf, int nb, int t) {
+  // item f = (batch f / T, slice f % T) in ring slot f % D
+  u32x4 cb[D];
+  uint32_t sb[D];
+  int zb[D];
+  auto load = [&](int slot, int f) {
+    const int nb = f / T, t = f % T;
     const int row = min(row0 + nb * 4 + j, N - 1);
-    cb[buf] = __builtin_nontemporal_load(cbase + (int64_t)row * vpr + kc[t] / 32);
-    sb[buf] = scales[(int64_t)row * G + g[t]];
-    zb[buf] = zeros[(int64_t)row * G + g[t]];
+    cb[slot] = __builtin_nontemporal_load(cbase + (int64_t)row * vpr + kc[t] / 32);
+    sb[slot] = scales[(int64_t)row * G + g[t]];
+    zb[slot] = zeros[(int64_t)row * G + g[t]];
   };
-  load(0, 0, 0);  // the weight stream first
+#pragma unroll
+  for (int f = 0; f < D; ++f) load(f, f);     // the weight stream first
 
   // lane (bq, i) holds activation rows i, i + 4 of its 32 inputs, paired
   // like the codes, and every lane the sums of the 32 inputs of its block
@@ -372,14 +432,17 @@ __global__ __launch_bounds__(1024) void gemv_quad_kernel(
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const int f = nb * T + t;
-      const int cur = f & 1;
-      if (f + 1 < NB * T) load(cur ^ 1, (f + 1) / T, (f + 1) % T);
+      const int slot = f % D;
+      const u32x4 c = cb[slot];
+      const float s = bf16_to_f32(sb[slot]);
+      const float zb128 = (float)zb[slot] + 128.f;
+      if (f + D < F) load(slot, f + D);
       f32x4 d[MS];
 #pragma unroll
       for (int ms = 0; ms < MS; ++ms) d[ms] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const u32x4 q = codes_to_bias128_pairs(cb[cur][i]);
+        const u32x4 q = codes_to_bias128_pairs(c[i]);
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -388,37 +451,15 @@ __global__ __launch_bounds__(1024) void gemv_quad_kernel(
                               d[ms]);
       }
       // this lane's block: s * (P - (128 + z) * Xsum) for weight row j, group g[t]
-      const float s = bf16_to_f32(sb[cur]);
-      const float zb128 = (float)zb[cur] + 128.f;
 #pragma unroll
       for (int m = 0; m < M; ++m)
         acc[m] = fmaf(s, fmaf(-zb128, xs[t][m / 4][m % 4], d[m / 4][m % 4]), acc[m]);
     }
-    // sum over the 16 blocks (lane bits 2..5): halving on the activation
-    // rows first (bit 5 first), plain sums after
-    int mask = 32;
-#pragma unroll
-    for (int cur_n = MP; cur_n > 1; cur_n >>= 1) {
-      const uint32_t up = (lane & mask) ? ~0u : 0u;
-#pragma unroll
-      for (int i = 0; i < cur_n / 2; ++i) {
-        const float send = pick(up, acc[i], acc[i + cur_n / 2]);
-        const float keep = pick(up, acc[i + cur_n / 2], acc[i]);
-        acc[i] = keep + __shfl_xor(send, mask);
-      }
-      mask >>= 1;
-    }
-#pragma unroll
-    for (; mask >= 4; mask >>= 1) acc[0] += __shfl_xor(acc[0], mask);
-    // lane (bq, j) now holds weight row j and activation row m from the top
-    // LM bits of bq; the lanes with zero low bits store it
-    if ((bq & ((16 >> LM) - 1)) == 0) {
-      int m = 0, half = MP / 2;
-#pragma unroll
-      for (int b = 0; b < LM; ++b, half >>= 1)
-        if (lane & (32 >> b)) m += half;
-      if (m < M) red[wave][nb * 4 * M + j * M + m] = acc[0];
-    }
+    // sum over the 16 blocks (lane bits 2..5); lane (bq, j) then holds
+    // weight row j and activation row m
+    lane_tree_sum<MP, LM>(acc, lane);
+    int m;
+    if (tree_result<MP, LM>(lane, m) && m < M) red[wave][nb * 4 * M + j * M + m] = acc[0];
   }
   __syncthreads();
   for (int idx = threadIdx.x; idx < NB * 4 * M; idx += blockDim.x) {
@@ -536,27 +577,9 @@ __global__ __launch_bounds__(1024) void gemv_quad_long_kernel(
   }
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    int mask = 32;
-#pragma unroll
-    for (int cur_n = MP; cur_n > 1; cur_n >>= 1) {
-      const uint32_t up = (lane & mask) ? ~0u : 0u;
-#pragma unroll
-      for (int i = 0; i < cur_n / 2; ++i) {
-        const float send = pick(up, acc[nb][i], acc[nb][i + cur_n / 2]);
-        const float keep = pick(up, acc[nb][i + cur_n / 2], acc[nb][i]);
-        acc[nb][i] = keep + __shfl_xor(send, mask);
-      }
-      mask >>= 1;
-    }
-#pragma unroll
-    for (; mask >= 4; mask >>= 1) acc[nb][0] += __shfl_xor(acc[nb][0], mask);
-    if ((bq & ((16 >> LM) - 1)) == 0) {
-      int m = 0, half = MP / 2;
-#pragma unroll
-      for (int b = 0; b < LM; ++b, half >>= 1)
-        if (lane & (32 >> b)) m += half;
-      if (m < M) red[wave][nb * 4 * M + j * M + m] = acc[nb][0];
-    }
+    lane_tree_sum<MP, LM>(acc[nb], lane);
+    int m;
+    if (tree_result<MP, LM>(lane, m) && m < M) red[wave][nb * 4 * M + j * M + m] = acc[nb][0];
   }
   __syncthreads();
   for (int idx = threadIdx.x; idx < NB * 4 * M; idx += blockDim.x) {
@@ -1067,8 +1090,8 @@ void launch_dot(const uint16_t* X, int64_t ldx, const uint32_t* codes, const uin
   // timings of every decode layer of the 8B- and 70B-shaped sets and the
   // 40-layer stack.
   constexpr int R = 4;
-  // more batches would spill at M = 4 (with 8-bit codes, from M = 3)
-  constexpr int kMaxNB = (W8 && M >= 3) ? 1 : (M >= 4 ? 2 : 8);
+  // more batches would spill: from M = 3, and at M = 2 with 8-bit codes
+  constexpr int kMaxNB = M >= 3 ? 1 : ((W8 && M == 2) ? 3 : 8);
   const int S = (K + kSlice - 1) / kSlice;
   const int cus = cu_count();
   auto balance = [&](int nb) {
@@ -1114,26 +1137,28 @@ template <int M, int T>
 void launch_quad_t(const uint16_t* X, int Mrt, int64_t ldx, const uint32_t* codes,
                    const uint16_t* scales, const int32_t* zeros, int N, int K, int lg, uint16_t* Y,
                    int64_t ldy, hipStream_t stream) {
-  // Rows per block: 4 x NB.  The largest NB (at most 8) whose block count
+  // Rows per block: 4 x NB.  The largest NB (at most 8; 4 with two slices
+  // of eight activation rows, whose registers are full) whose block count
   // fills the CUs evenly; fitted to timings of the decode layers of the 8B-
   // and 70B-shaped sets and the 40-layer stack at M = 4 and 8.
+  constexpr int kMaxNB = (M > 4 && T > 1) ? 4 : 8;
   const int cus = cu_count();
   auto balance = [&](int nb) {
     const double per_cu = (double)((N + 4 * nb - 1) / (4 * nb)) / cus;
     return per_cu / std::ceil(per_cu);
   };
   int nb = 0;
-  for (int c = 8; c >= 1 && nb == 0; --c)
+  for (int c = kMaxNB; c >= 1 && nb == 0; --c)
     if (balance(c) >= 0.95) nb = c;
   if (nb == 0) {
     nb = 1;
-    for (int c = 2; c <= 8; ++c)
+    for (int c = 2; c <= kMaxNB; ++c)
       if (balance(c) > balance(nb) + 1e-9) nb = c;
   }
   switch (nb) {
 #define W4A16_QUAD(V)                                                                     \
   case V:                                                                                 \
-    launch_quad_nb<M, T, V>(X, Mrt, ldx, codes, scales, zeros, N, K, lg, Y, ldy, stream); \
+    launch_quad_nb<M, T, (V <= kMaxNB ? V : kMaxNB)>(X, Mrt, ldx, codes, scales, zeros, N, K, lg, Y, ldy, stream); \
     break;
     W4A16_QUAD(8) W4A16_QUAD(7) W4A16_QUAD(6) W4A16_QUAD(5) W4A16_QUAD(4) W4A16_QUAD(3)
     W4A16_QUAD(2)
