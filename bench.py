@@ -204,6 +204,13 @@ def main():
     ceiling = hbm_read_ceiling(dev, stream)
     roofline["measured_ceiling_GBps"] = ceiling["GBps"]
     roofline["frac_of_measured_ceiling"] = round(roofline["achieved"] / ceiling["GBps"], 4)
+    # the same read probe over exactly the dominant launch's bytes, one
+    # launch per graph node over rotating buffers: what a plain stream of
+    # that size reaches, launch cost included
+    same = same_size_read(dev, stream, decode_bytes(layers[dom], M))
+    ceiling["same_size_read"] = same
+    roofline["same_size_read_us"] = same["us_per_launch"]
+    roofline["frac_of_same_size_read"] = round(same["us_per_launch"] / per_layer[dom]["us"], 4)
     log(f"[bench] measured read ceiling: {ceiling['GBps']:.0f} GB/s "
         f"({ceiling['GBps'] / HBM_PEAK_GBS:.3f} of {HBM_PEAK_GBS:.0f})")
 
@@ -387,6 +394,23 @@ def hbm_read_ceiling(dev, stream, nbytes=2 << 30, reps=20):
     return {"GBps": round(gbs, 1), "bytes": nbytes, "reps": reps, "us_per_read": round(sec * 1e6, 2),
             "spec_GBps": HBM_PEAK_GBS, "frac_of_spec": round(gbs / HBM_PEAK_GBS, 4),
             "kernel": "w4a16_hbm_read_probe (16-byte loads, 1 KiB per wave instruction)"}
+
+
+def same_size_read(dev, stream, nbytes, reps=200):
+    """The read probe over `nbytes` (rounded down to 16 bytes) per launch,
+    a graph of `reps` launches over rotating buffers (>= 1 GiB in all),
+    timed with HIP events on `stream`."""
+    import torch
+    import int4_weight_only_gemv_amd as w4
+    n16 = nbytes // 16
+    ncopy = max(2, math.ceil(ROTATE_BYTES / (16 * n16)))
+    bufs = [torch.ones(4 * n16, dtype=torch.int32, device=dev) for _ in range(ncopy)]
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    us = _graph_us(stream, lambda r: w4.w4a16_hbm_read_probe(bufs[r % ncopy], sink), reps)
+    del bufs
+    torch.cuda.synchronize()
+    return {"bytes": 16 * n16, "us_per_launch": round(us, 3), "GBps": round(16 * n16 / (us * 1e-6) / 1e9, 1),
+            "rotating_buffers": ncopy, "launches_timed": reps}
 
 
 def single_linear(dev, stream, M=1, reps=400):

@@ -1137,31 +1137,35 @@ template <int M, int T>
 void launch_quad_t(const uint16_t* X, int Mrt, int64_t ldx, const uint32_t* codes,
                    const uint16_t* scales, const int32_t* zeros, int N, int K, int lg, uint16_t* Y,
                    int64_t ldy, hipStream_t stream) {
-  // Rows per block: 4 x NB.  The largest NB (at most 8; 4 with two slices
-  // of eight activation rows, whose registers are full) whose block count
-  // fills the CUs evenly; fitted to timings of the decode layers of the 8B-
-  // and 70B-shaped sets and the 40-layer stack at M = 4 and 8.
-  constexpr int kMaxNB = (M > 4 && T > 1) ? 4 : 8;
+  // Rows per block: 4 x NB.  The largest NB whose block count fills the CUs
+  // evenly, from 16 batches (8 with two slices per wave; 4 with two slices
+  // of eight activation rows, whose registers are full).  Few long blocks
+  // stream best: the gate_up shape (28672 rows) runs 512 blocks of 14
+  // batches at 0.83-0.89 of the time of 1024 blocks of 7.  Fitted to timings
+  // of the decode layers of the 8B- and 70B-shaped sets and the 40-layer
+  // stack at M = 4, 5 and 8.
+  constexpr int kMaxNB = T > 1 ? (M > 4 ? 4 : 8) : 16;
+  constexpr int kNBs[] = {16, 14, 12, 10, 8, 7, 6, 5, 4, 3, 2, 1};
   const int cus = cu_count();
   auto balance = [&](int nb) {
     const double per_cu = (double)((N + 4 * nb - 1) / (4 * nb)) / cus;
     return per_cu / std::ceil(per_cu);
   };
   int nb = 0;
-  for (int c = kMaxNB; c >= 1 && nb == 0; --c)
-    if (balance(c) >= 0.95) nb = c;
+  for (int c : kNBs)
+    if (nb == 0 && c <= kMaxNB && balance(c) >= 0.95) nb = c;
   if (nb == 0) {
     nb = 1;
-    for (int c = 2; c <= kMaxNB; ++c)
-      if (balance(c) > balance(nb) + 1e-9) nb = c;
+    for (int c : kNBs)
+      if (c <= kMaxNB && balance(c) > balance(nb) + 1e-9) nb = c;
   }
   switch (nb) {
 #define W4A16_QUAD(V)                                                                     \
   case V:                                                                                 \
     launch_quad_nb<M, T, (V <= kMaxNB ? V : kMaxNB)>(X, Mrt, ldx, codes, scales, zeros, N, K, lg, Y, ldy, stream); \
     break;
-    W4A16_QUAD(8) W4A16_QUAD(7) W4A16_QUAD(6) W4A16_QUAD(5) W4A16_QUAD(4) W4A16_QUAD(3)
-    W4A16_QUAD(2)
+    W4A16_QUAD(16) W4A16_QUAD(14) W4A16_QUAD(12) W4A16_QUAD(10) W4A16_QUAD(8) W4A16_QUAD(7)
+    W4A16_QUAD(6) W4A16_QUAD(5) W4A16_QUAD(4) W4A16_QUAD(3) W4A16_QUAD(2)
 #undef W4A16_QUAD
     default:
       launch_quad_nb<M, T, 1>(X, Mrt, ldx, codes, scales, zeros, N, K, lg, Y, ldy, stream);
