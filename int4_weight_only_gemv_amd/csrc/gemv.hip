@@ -360,9 +360,12 @@ __global__ __launch_bounds__(1024) void gemv_quad_kernel(
   constexpr int MP = pow2_at_least(M);        // values per lane in the lane tree
   constexpr int LM = log2_exact(MP);
   constexpr int F = NB * T;                   // items: (batch of four rows, slice)
-  // (two rows of activation sets and two slices fill the registers: two deep)
-  constexpr int D = F < kQuadRing ? F : (M > 4 && T > 1 ? 2 : kQuadRing);
+  constexpr int D = F < kQuadRing ? F : kQuadRing;
+  // two slices of eight activation rows fill the registers: the activation
+  // sums then wait in LDS (each lane its own)
+  constexpr bool kXsLds = M > 4 && T > 1;
   __shared__ float red[kQuadMaxWaves][NB * 4 * M];
+  __shared__ f32x4 xs_lds[kXsLds ? kQuadMaxWaves : 1][kXsLds ? T * MS : 1][kWave];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -401,7 +404,7 @@ __global__ __launch_bounds__(1024) void gemv_quad_kernel(
   // lane (bq, i) holds activation rows i, i + 4 of its 32 inputs, paired
   // like the codes, and every lane the sums of the 32 inputs of its block
   u32x4 xa[T][MS][4];
-  f32x4 xs[T][MS];
+  f32x4 xs[kXsLds ? 1 : T][kXsLds ? 1 : MS];
 #pragma unroll
   for (int t = 0; t < T; ++t)
 #pragma unroll
@@ -421,7 +424,8 @@ __global__ __launch_bounds__(1024) void gemv_quad_kernel(
 #pragma unroll
         for (int h = 0; h < 2; ++h)
           sum = mfma4x4x4(xa[t][ms][i][2 * h], xa[t][ms][i][2 * h + 1], kOnePair, kOnePair, sum);
-      xs[t][ms] = sum;
+      if constexpr (kXsLds) xs_lds[wave][t * MS + ms][lane] = sum;
+      else xs[t][ms] = sum;
     }
 
 #pragma unroll
@@ -452,8 +456,10 @@ __global__ __launch_bounds__(1024) void gemv_quad_kernel(
       }
       // this lane's block: s * (P - (128 + z) * Xsum) for weight row j, group g[t]
 #pragma unroll
-      for (int m = 0; m < M; ++m)
-        acc[m] = fmaf(s, fmaf(-zb128, xs[t][m / 4][m % 4], d[m / 4][m % 4]), acc[m]);
+      for (int m = 0; m < M; ++m) {
+        const float xsm = kXsLds ? xs_lds[wave][t * MS + m / 4][lane][m % 4] : xs[kXsLds ? 0 : t][kXsLds ? 0 : m / 4][m % 4];
+        acc[m] = fmaf(s, fmaf(-zb128, xsm, d[m / 4][m % 4]), acc[m]);
+      }
     }
     // sum over the 16 blocks (lane bits 2..5); lane (bq, j) then holds
     // weight row j and activation row m

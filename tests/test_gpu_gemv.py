@@ -86,6 +86,17 @@ def test_matrix_core_small_m_shapes(M, N, K):
     check_case(w4.w4a16_gemv, M, N, K, "gemv", f"quad{N}x{K}", shift=True, label=f"M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("N,K", [(28669, 4096), (16379, 4096), (10233, 2048)])
+def test_matrix_core_small_m_long_blocks_ragged(N, K):
+    # row counts whose even fill of the CUs takes 14, 16 and 10 four-row
+    # batches per block, each with a partial last block (its rows clamp)
+    tail = np.arange(N - 64, N)
+    for M in (3, 6, 8):
+        rows = np.unique(np.concatenate([sample_rows(N, 96, seed=N + M), tail]))
+        check_case(w4.w4a16_gemv, M, N, K, "gemv", f"quadnb{N}x{K}", shift=True, rows=rows,
+                   label=f"M={M} N={N} K={K}")
+
+
 def test_on_grid_weights_match_unquantised_matmul():
     import oracle_pins as P
     W_bits, _ = P.check_all_codes_on_grid(seed=31, N=80, K=512)
