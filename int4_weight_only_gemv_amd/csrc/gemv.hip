@@ -863,8 +863,9 @@ __global__ __launch_bounds__(1024) void gemv_walk_kernel(
       const int r = 16 * t + (l & 15);
       if (KS == 1)
         out[r * kWalkOStride + m] = f32_to_bf16_rne(sum);
-      else
-        __hip_atomic_store(part + r * 32 + m, __float_as_uint(sum), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else   // in the reduction's own order: a wave's stores are contiguous
+        __hip_atomic_store(part + t * (MT * 256) + e, __float_as_uint(sum), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
     block_barrier_lds();
   };
@@ -897,12 +898,16 @@ __global__ __launch_bounds__(1024) void gemv_walk_kernel(
   if (!*last) return;
   const unsigned* part0 = ws + (int64_t)kWalkMaxRanges * (kWalkCounterBytes / 4) +
                           (int64_t)range * KS * (16 * tmax * 32);
-  for (int e = threadIdx.x; e < rows * M; e += 1024) {
-    const int m = e / rows, r = e - m * rows;
+  for (int ea = threadIdx.x; ea < T * MT * 256; ea += 1024) {
+    const int t = ea / (MT * 256), e = ea - t * (MT * 256);
+    const int v = e >> 6, l = e & 63;
+    const int m = 16 * (v >> 2) + 4 * (l >> 4) + (v & 3);
+    const int r = 16 * t + (l & 15);
+    if (r >= rows || m >= M) continue;
     float sum = 0.f;
     for (int k = 0; k < KS; ++k)
-      sum += __uint_as_float(__hip_atomic_load(part0 + (int64_t)k * (16 * tmax * 32) + r * 32 + m,
-                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      sum += __uint_as_float(__hip_atomic_load(part0 + (int64_t)k * (16 * tmax * 32) + ea, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT));
     Y[(int64_t)m * ldy + r0 + r] = f32_to_bf16_rne(sum);
   }
   if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
