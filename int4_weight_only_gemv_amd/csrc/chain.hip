@@ -286,8 +286,8 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainDesc* _
           xp[m][i] = v;
         }
         if (active) s = xsum[m * (max_k / 32) + c];
-        s += __shfl_xor(s, 1);
-        xsg[m] = s + __shfl_xor(s, 2);
+        s += dpp<kDppXor1>(s);
+        xsg[m] = s + dpp<kDppXor2>(s);
       }
       float P[R][M];
 #pragma unroll
@@ -310,11 +310,8 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainDesc* _
 #pragma unroll
         for (int r = 0; r < 2; ++r)
 #pragma unroll
-          for (int m = 0; m < M; ++m) {
-            const float send = pick(up, P[r][m], P[r + 2][m]);
-            const float keep = pick(up, P[r + 2][m], P[r][m]);
-            h[r][m] = keep + __shfl_xor(send, 2);
-          }
+          for (int m = 0; m < M; ++m)
+            h[r][m] = pick(up, P[r + 2][m] + dpp<kDppXor2>(P[r + 2][m]), P[r][m] + dpp<kDppXor2>(P[r][m]));
       }
       float part[MP];
       {
@@ -323,9 +320,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainDesc* _
         const float zb128 = (float)zb[buf] + 128.f;
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-          const float send = pick(up, h[0][m], h[1][m]);
-          const float keep = pick(up, h[1][m], h[0][m]);
-          const float q = keep + __shfl_xor(send, 1);
+          const float q = pick(up, h[1][m] + dpp<kDppXor1>(h[1][m]), h[0][m] + dpp<kDppXor1>(h[0][m]));
           // ... and removes the bias and zero point of that (row, group)
           part[m] = s * fmaf(-zb128, xsg[m], q);
         }
@@ -333,25 +328,10 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainDesc* _
         for (int m = M; m < MP; ++m) part[m] = 0.f;
       }
       // then over the 16 groups of the slice (lane bits 2..5)
-      int mask = 4;
-#pragma unroll
-      for (int cur_n = MP; cur_n > 1; cur_n >>= 1) {
-        const uint32_t up = (lane & mask) ? ~0u : 0u;
-#pragma unroll
-        for (int i = 0; i < cur_n / 2; ++i) {
-          const float send = pick(up, part[i], part[i + cur_n / 2]);
-          const float keep = pick(up, part[i + cur_n / 2], part[i]);
-          part[i] = keep + __shfl_xor(send, mask);
-        }
-        mask <<= 1;
-      }
-#pragma unroll
-      for (; mask <= 32; mask <<= 1) part[0] += __shfl_xor(part[0], mask);
-      // lane l < 4 MP holds row l % 4 and activation row (lane >> 2)
-      if (lane < 4 * MP) {
-        const int m = lane >> 2;
-        if (m < M) red[((size_t)sl * max_rows + batch * R + (lane & 3)) * M + m] = part[0];
-      }
+      lane_tree_sum<MP, MP == 1 ? 0 : 1>(part, lane);
+      int m;
+      if (tree_result<MP, MP == 1 ? 0 : 1>(lane, m) && m < M)
+        red[((size_t)sl * max_rows + batch * R + (lane & 3)) * M + m] = part[0];
     };
     int it = wave;
     while (true) {

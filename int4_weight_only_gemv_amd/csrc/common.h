@@ -159,6 +159,87 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
 }
 
+constexpr int pow2_at_least(int v) { return v <= 1 ? 1 : 2 * pow2_at_least((v + 1) / 2); }
+constexpr int log2_exact(int v) { return v <= 1 ? 0 : 1 + log2_exact(v / 2); }
+
+// Cross-lane sums without LDS: DPP for lanes within a 16-lane row, the
+// permlane swaps across rows.  DPP quad_perm [1,0,3,2] / [2,3,0,1] reads lane
+// l ^ 1 / l ^ 2; row_ror:n gives lane l the value of lane l - n (mod 16) of
+// its row; v_permlane32_swap exchanges the upper 32 lanes of its first operand
+// with the lower 32 of its second, v_permlane16_swap the odd 16-lane rows of
+// its first operand with the even rows of its second.
+constexpr int kDppXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppRor8 = 0x128;    // row_ror:8: lane l ^ 8
+constexpr int kDppRor12 = 0x12C;   // row_ror:12: lane l + 4 (mod 16)
+
+template <int C>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), C, 0xF, 0xF, false));
+}
+
+// x(l) + x(l ^ 2^bit) for lane bit 5, 4 or 3, in every lane; for bit 2
+// exact only in lanes whose bit 2 is clear.
+template <int BIT>
+__device__ __forceinline__ float pair_sum(float x) {
+  if constexpr (BIT >= 4) {
+    const auto r = BIT == 5 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false)
+                            : __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else if constexpr (BIT == 3) {
+    return x + dpp<kDppRor8>(x);
+  } else {
+    static_assert(BIT == 2, "lane bits 2..5");
+    return x + dpp<kDppRor12>(x);
+  }
+}
+
+// One halving step on lane bit 5, 4 or 3: lanes whose bit is clear end with
+// a(l) + a(l ^ 2^bit), lanes whose bit is set with b(l) + b(l ^ 2^bit).
+template <int BIT>
+__device__ __forceinline__ float halve(float a, float b, int lane) {
+  if constexpr (BIT >= 4) {
+    const auto r = BIT == 5 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false)
+                            : __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else {
+    static_assert(BIT == 3, "halving on lane bits 3..5");
+    return pick((lane & 8) ? ~0u : 0u, pair_sum<3>(b), pair_sum<3>(a));
+  }
+}
+
+// Sum of MP = 2^LM values per lane over lane bits 2..5 (the 16 lane groups of
+// four): halving on bits 5, 4, .. (value i + MP/2 moves to the lanes whose
+// bit 5 is set, and so on), then plain sums on the remaining bits.  After it,
+// a lane whose bits 2 .. 5-LM are clear holds in part[0] the sum of value m
+// over its four-lane position, m read from its bits 5 .. 6-LM (bit 5 the
+// highest).
+template <int MP, int LM>
+__device__ __forceinline__ void lane_tree_sum(float* part, int lane) {
+  static_assert(MP == (1 << LM) && LM <= 3, "at most 8 values per lane");
+  static_for<0, LM>([&](auto bi) {
+    constexpr int b = decltype(bi)::value, n = MP >> b;
+#pragma unroll
+    for (int i = 0; i < n / 2; ++i) part[i] = halve<5 - b>(part[i], part[i + n / 2], lane);
+  });
+  static_for<LM, 4>([&](auto bi) {
+    constexpr int b = decltype(bi)::value;
+    part[0] = pair_sum<5 - b>(part[0]);
+  });
+}
+
+// The value index a lane holds after lane_tree_sum<MP, LM>, and whether it
+// holds a finished sum.
+template <int MP, int LM>
+__device__ __forceinline__ bool tree_result(int lane, int& m) {
+  m = 0;
+  int half = MP / 2;
+#pragma unroll
+  for (int b = 0; b < LM; ++b, half >>= 1)
+    if (lane & (32 >> b)) m += half;
+  return ((lane >> 2) & ((16 >> LM) - 1)) == 0;
+}
+
 // Compute units of the current device (queried once per device; host code).
 inline int device_cu_count() {
   static int counts[64] = {0};
