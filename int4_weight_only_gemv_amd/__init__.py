@@ -287,7 +287,7 @@ def w4a16_gemv(X: torch.Tensor, p: PackedLinear, out: torch.Tensor | None = None
         _need(out, torch.bfloat16, "out", 2)
         if tuple(out.shape) != (M, p.N):
             raise ValueError("out has the wrong shape")
-    if workspace is None and 9 <= M <= GEMV_MAX_M:
+    if workspace is None and 3 <= M <= GEMV_MAX_M:   # M <= 2 never splits K
         workspace = gemv_workspace(X, p.N, p.K)
     if workspace is not None and (workspace.dtype != torch.uint8 or not workspace.is_contiguous()):
         raise ValueError("workspace must be a contiguous uint8 tensor")

@@ -20,8 +20,9 @@
 // per-row partial sums are folded across lanes (DPP and permlane swaps, no
 // LDS), then across the K slices of the block through LDS in a fixed order.
 //
-// gemv_quad (3 <= M <= 8, K <= 16384): the same streaming pattern (four rows
-// x 256 contiguous bytes per load instruction), but the products run on the
+// gemv_quad (3 <= M <= 8, K <= 16384, or longer rows split over blocks
+// through a caller's workspace): the same streaming pattern (four rows x 256
+// contiguous bytes per load instruction), but the products run on the
 // matrix cores as sixteen 4x4 blocks per instruction, so more activation
 // rows cost almost no vector ALU time.
 //
@@ -269,11 +270,18 @@ __device__ __forceinline__ f32x4 mfma4x4x4(uint32_t a0, uint32_t a1, uint32_t b0
 
 constexpr int kQuadRing = 3;      // code vectors in flight per lane
 
-template <int M, int T, int NB>
+// Split-K workspace (shared by the quad and walk kernels): a fixed region of
+// kSplitMaxRanges counters, one per 64-byte line, then the partial outputs.
+// Each launch leaves every counter at zero.
+constexpr int kSplitMaxRanges = 1024;
+constexpr int kSplitCounterBytes = 64;
+constexpr int64_t kSplitCounterWords = (int64_t)kSplitMaxRanges * kSplitCounterBytes / 4;
+
+template <int M, int T, int NB, bool SPLIT>
 __global__ __launch_bounds__(1024) void gemv_quad_kernel(
     const uint16_t* __restrict__ X, int Mrt, int64_t ldx, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K, int lg,
-    uint16_t* __restrict__ Y, int64_t ldy) {
+    uint16_t* __restrict__ Y, int64_t ldy, int KS, unsigned* __restrict__ ws) {
   constexpr int MS = (M + 3) / 4;             // activation row sets of four
   constexpr int MP = pow2_at_least(M);        // values per lane in the lane tree
   constexpr int LM = log2_exact(MP);
@@ -293,16 +301,20 @@ __global__ __launch_bounds__(1024) void gemv_quad_kernel(
   const int G = K >> lg;                      // groups of 2^lg inputs (32, 64 or 128)
   const int64_t vpr = K / 32;                 // 16-byte vectors per code row
 
+  // block = (range of NB batches of four rows, run ks of the KS runs of K)
+  if constexpr (!SPLIT) KS = 1;
+  const int range = (int)blockIdx.x / KS, ks = (int)blockIdx.x - range * KS;
+  const int Kr = K / KS, kb = ks * Kr;        // the run: inputs kb .. kb + Kr - 1
   int kc[T], g[T];
   bool act[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     const int k = (wave * T + t) * kQuadSlice + 32 * bq;
-    act[t] = k < K;
-    kc[t] = act[t] ? k : K - 32;              // inactive lanes read valid memory, weigh zero
+    act[t] = k < Kr;
+    kc[t] = kb + (act[t] ? k : Kr - 32);      // inactive lanes read valid memory, weigh zero
     g[t] = kc[t] >> lg;                       // a block of 32 inputs lies in one group
   }
-  const int row0 = blockIdx.x * NB * 4;
+  const int row0 = range * NB * 4;
   const u32x4* cbase = reinterpret_cast<const u32x4*>(codes);
 
   // item f = (batch f / T, slice f % T) in ring slot f % D
@@ -386,14 +398,47 @@ __global__ __launch_bounds__(1024) void gemv_quad_kernel(
     if (tree_result<MP, LM>(lane, m) && m < M) red[wave][nb * 4 * M + j * M + m] = acc[0];
   }
   __syncthreads();
+  if (!SPLIT) {
+    for (int idx = threadIdx.x; idx < NB * 4 * M; idx += blockDim.x) {
+      const int r = idx / M, m = idx - r * M;
+      const int row = row0 + r;
+      if (row >= N || m >= Mrt) continue;
+      float v = red[0][idx];
+      for (int w = 1; w < S; ++w) v += red[w][idx];
+      Y[m * ldy + row] = f32_to_bf16_rne(v);
+    }
+    return;
+  }
+  // K split over KS blocks: this block's sums go to the workspace with
+  // coherent stores (contiguous per wave instruction); it waits for them,
+  // counts itself in on its range's counter, and the last of the KS adds
+  // the partials in run order, stores Y and resets the counter
+  unsigned* part = ws + kSplitCounterWords + ((int64_t)range * KS + ks) * (NB * 4 * M);
+  for (int idx = threadIdx.x; idx < NB * 4 * M; idx += blockDim.x) {
+    float v = red[0][idx];
+    for (int w = 1; w < S; ++w) v += red[w][idx];
+    __hip_atomic_store(part + idx, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+  unsigned* counter = ws + (int64_t)range * (kSplitCounterBytes / 4);
+  __shared__ unsigned last;
+  if (threadIdx.x == 0)
+    last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(KS - 1);
+  __syncthreads();
+  if (!last) return;
+  const unsigned* part0 = ws + kSplitCounterWords + (int64_t)range * KS * (NB * 4 * M);
   for (int idx = threadIdx.x; idx < NB * 4 * M; idx += blockDim.x) {
     const int r = idx / M, m = idx - r * M;
     const int row = row0 + r;
     if (row >= N || m >= Mrt) continue;
-    float v = red[0][idx];
-    for (int w = 1; w < S; ++w) v += red[w][idx];
+    float v = 0.f;
+    for (int k = 0; k < KS; ++k)
+      v += __uint_as_float(__hip_atomic_load(part0 + (int64_t)k * (NB * 4 * M) + idx, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT));
     Y[m * ldy + row] = f32_to_bf16_rne(v);
   }
+  if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Long rows (more slices than one wave can hold the activations of): each
@@ -579,12 +624,12 @@ constexpr int kWalkMetaMax = 4096;            // scales (and zero points) per bl
 constexpr int kWalkSStride = 2 * kWalkGroups + 2;   // scales: 34 BF16 per row
 constexpr int kWalkZStride = kWalkGroups + 1;       // zero points: 33 per row
 constexpr int kWalkOStride = 34;                    // outputs: 34 BF16 per row (32 columns of M)
-// Workspace of the split-K walk: a fixed region of kWalkMaxRanges counters,
-// one per row range on its own 64-byte line (the same place for every shape;
-// each launch leaves its counters at zero), then the partial outputs,
-// [range][run][16 tmax rows][32 columns of M] floats.
-constexpr int kWalkMaxRanges = 1024;
-constexpr int64_t kWalkCounterBytes = 64;
+// Workspace of the split-K walk: the shared counter region (one counter per
+// row range on its own 64-byte line, the same place for every shape and
+// kernel), then the partial outputs, [range][run][tmax tiles][MT x 256]
+// floats in the lanes' order.
+constexpr int kWalkMaxRanges = kSplitMaxRanges;
+constexpr int64_t kWalkCounterBytes = kSplitCounterBytes;
 
 // dynamic LDS of a block walking at most tmax tiles
 constexpr int walk_lds_bytes(int MT, int tmax) {
@@ -1058,8 +1103,9 @@ void launch_quad_nb(const uint16_t* X, int Mrt, int64_t ldx, const uint32_t* cod
                     int64_t ldy, hipStream_t stream) {
   const int slices = (K + kQuadSlice - 1) / kQuadSlice;
   const int S = (slices + T - 1) / T;
-  hipLaunchKernelGGL((gemv_quad_kernel<M, T, NB>), dim3((unsigned)((N + 4 * NB - 1) / (4 * NB))),
-                     dim3(S * kWave), 0, stream, X, Mrt, ldx, codes, scales, zeros, N, K, lg, Y, ldy);
+  hipLaunchKernelGGL((gemv_quad_kernel<M, T, NB, false>), dim3((unsigned)((N + 4 * NB - 1) / (4 * NB))),
+                     dim3(S * kWave), 0, stream, X, Mrt, ldx, codes, scales, zeros, N, K, lg, Y, ldy, 1,
+                     nullptr);
 }
 
 template <int M, int T>
@@ -1141,6 +1187,81 @@ bool launch_quad_long(const uint16_t* X, int Mrt, int64_t ldx, const uint32_t* c
   }
 #undef W4A16_QL
   return true;
+}
+
+// K split over KS blocks through a caller's workspace, 3 <= M <= 8: rows
+// longer than 8192 inputs (M > 4), or 8192 < K <= 16384 (M <= 4; longer
+// rows run faster on the long-row kernel).  KS = 2 or 4 runs with one
+// 512-input slice per wave (at most 16 waves), else two runs of two slices;
+// then the largest NB whose block count fills the CUs evenly.  Measured on
+// the down projections at M = 8: 8B (K = 14336) 16.1 -> 14.0 us, 70B
+// (K = 28672) 56.9 -> 46.9 us, the stack's (K = 27648) 54.6 -> 39.9 us.
+constexpr int kQuadSplitMinNB2 = 4, kQuadSplitMaxNB2 = 5;
+
+struct QuadSplitPlan {
+  int KS, T, NB, ranges;
+  int64_t ws_bytes;
+};
+
+template <int MT>
+bool quad_split_plan(int64_t N, int64_t K, QuadSplitPlan& p) {
+  if (K <= 8192 || (MT == 4 && K > 16384)) return false;
+  p.KS = 0;
+  for (int t = 1; t <= 2 && p.KS == 0; ++t)
+    for (int ks : {2, 4})
+      if (p.KS == 0 && K % ((int64_t)kQuadSlice * ks) == 0 && K / ks / kQuadSlice <= (int64_t)kQuadMaxWaves * t) {
+        p.KS = ks;
+        p.T = t;
+      }
+  if (p.KS == 0) return false;
+  const int cus = cu_count();
+  auto ranges = [&](int nb) { return (int)((N + 4 * nb - 1) / (4 * nb)); };
+  auto balance = [&](int nb) {
+    const double per_cu = (double)ranges(nb) * p.KS / cus;
+    return per_cu / std::ceil(per_cu);
+  };
+  constexpr int kNBs[] = {8, 6, 5, 4, 3, 2};
+  // two slices of eight activation rows fill the registers: 4 or 5 batches
+  // (other counts spill)
+  const bool full = MT > 4 && p.T > 1;
+  auto allowed = [&](int c) {
+    return (!full || (c >= kQuadSplitMinNB2 && c <= kQuadSplitMaxNB2)) && ranges(c) <= kSplitMaxRanges;
+  };
+  p.NB = 0;
+  for (int c : kNBs)
+    if (p.NB == 0 && allowed(c) && balance(c) >= 0.95) p.NB = c;
+  if (p.NB == 0)
+    for (int c : kNBs)
+      if (allowed(c) && (p.NB == 0 || balance(c) > balance(p.NB) + 1e-9)) p.NB = c;
+  if (p.NB == 0) return false;
+  p.ranges = ranges(p.NB);
+  p.ws_bytes = (int64_t)kSplitMaxRanges * kSplitCounterBytes + (int64_t)p.ranges * p.KS * p.NB * 4 * MT * 4;
+  return true;
+}
+
+template <int MT, int T, int NB>
+void launch_quad_split_nb(const uint16_t* X, int Mrt, int64_t ldx, const uint32_t* codes, const uint16_t* scales,
+                          const int32_t* zeros, int N, int K, uint16_t* Y, int64_t ldy, const QuadSplitPlan& p,
+                          void* workspace, hipStream_t stream) {
+  const int S = (K / p.KS / kQuadSlice + T - 1) / T;
+  hipLaunchKernelGGL((gemv_quad_kernel<MT, T, NB, true>), dim3((unsigned)(p.ranges * p.KS)), dim3(S * kWave), 0,
+                     stream, X, Mrt, ldx, codes, scales, zeros, N, K, 7, Y, ldy, p.KS,
+                     reinterpret_cast<unsigned*>(workspace));
+}
+
+template <int MT>
+void launch_quad_split(const uint16_t* X, int Mrt, int64_t ldx, const uint32_t* codes, const uint16_t* scales,
+                       const int32_t* zeros, int N, int K, uint16_t* Y, int64_t ldy, const QuadSplitPlan& p,
+                       void* workspace, hipStream_t stream) {
+#define W4A16_QS(TV, V)                                                                                  \
+  if constexpr (!(MT > 4 && TV > 1 && (V > kQuadSplitMaxNB2 || V < kQuadSplitMinNB2)))                  \
+    if (p.T == TV && p.NB == V) {                                                                        \
+      launch_quad_split_nb<MT, TV, V>(X, Mrt, ldx, codes, scales, zeros, N, K, Y, ldy, p, workspace, stream); \
+      return;                                                                                            \
+    }
+  W4A16_QS(1, 8) W4A16_QS(1, 6) W4A16_QS(1, 5) W4A16_QS(1, 4) W4A16_QS(1, 3) W4A16_QS(1, 2)
+  W4A16_QS(2, 8) W4A16_QS(2, 6) W4A16_QS(2, 5) W4A16_QS(2, 4) W4A16_QS(2, 3) W4A16_QS(2, 2)
+#undef W4A16_QS
 }
 
 // 3 <= M <= 8, K <= 16384: one wave slice of 512 inputs (T = 1) up to 16
@@ -1272,15 +1393,19 @@ int launch_gemv_mt(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* co
 
 // Workspace that lets launch_gemv split K for this shape (0: none needed).
 int64_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int group) {
-  if (group != kGroup || M <= 8) return 0;
+  if (group != kGroup || M <= 2) return 0;
+  if (M <= 8) {
+    QuadSplitPlan q;
+    return (M <= 4 ? quad_split_plan<4>(N, K, q) : quad_split_plan<8>(N, K, q)) ? q.ws_bytes : 0;
+  }
   WalkPlan p;
   return walk_plan(N, K, p) ? p.ws_bytes : 0;
 }
 
 // group: 32, 64 or 128 inputs per quantisation group (checked by the caller).
 // workspace (may be null): zero-filled device memory of workspace_bytes,
-// left zero-filled; with at least gemv_workspace_bytes() the decode kernel
-// for 9 <= M <= 32 may split K over blocks.
+// left zero-filled; with at least gemv_workspace_bytes() the decode kernels
+// for 3 <= M <= 32 may split K over blocks.
 int launch_gemv(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
                 const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K, int group,
                 uint16_t* Y, int64_t ldy, void* workspace, int64_t workspace_bytes, hipStream_t stream) {
@@ -1288,6 +1413,17 @@ int launch_gemv(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes
     return launch_gemv_small_groups(X, M, ldx, codes, scales, zeros, N, K, group == 32 ? 5 : 6, Y,
                                     ldy, stream);
   constexpr int lg = 7;
+  if (M >= 3 && M <= 8 && workspace != nullptr) {
+    QuadSplitPlan q;
+    const bool plan = M <= 4 ? quad_split_plan<4>(N, K, q) : quad_split_plan<8>(N, K, q);
+    if (plan && workspace_bytes >= q.ws_bytes) {
+      if (M <= 4)
+        launch_quad_split<4>(X, (int)M, ldx, codes, scales, zeros, (int)N, (int)K, Y, ldy, q, workspace, stream);
+      else
+        launch_quad_split<8>(X, (int)M, ldx, codes, scales, zeros, (int)N, (int)K, Y, ldy, q, workspace, stream);
+      return hipGetLastError() == hipSuccess ? 0 : 4;
+    }
+  }
   if (M >= 3 && M <= 8 && K <= (int64_t)2 * kQuadSlice * kQuadMaxWaves) {
     if (M <= 4)
       launch_quad<4>(X, (int)M, ldx, codes, scales, zeros, (int)N, (int)K, lg, Y, ldy, stream);

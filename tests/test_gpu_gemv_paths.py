@@ -1,8 +1,9 @@
-"""The decode kernels for 9 <= M <= 32 and their workspace, against the CPU
-oracle: the walk over row tiles (rows of at most 32 groups), the walk that
-splits K over blocks through a caller's workspace (longer rows), and the
-ring kernel that takes longer rows without a workspace (and rows too long
-for the small-M kernels).  Outputs are the oracle's fp64 product of the
+"""The decode kernels that can split K through a caller's workspace, against
+the CPU oracle: for 9 <= M <= 32 the walk over row tiles (rows of at most 32
+groups), the walk that splits K over blocks (longer rows), and the ring
+kernel that takes longer rows without a workspace (and rows too long for the
+small-M kernels); for 3 <= M <= 8 the four-row matrix-core kernel with and
+without its K split.  Outputs are the oracle's fp64 product of the
 packed matrix (Axe Corsa model card, "The Two-Stage Pipeline"), sampled
 rows on the large shapes."""
 import ctypes
@@ -74,8 +75,35 @@ def test_split_and_unsplit_against_the_oracle(N, K):
             assert int(ws[:65536].count_nonzero()) == 0
 
 
+# (N, K) for 3 <= M <= 8: two runs of one slice per wave (K = 14336, 9216,
+# 16384), four runs (28672, M > 4), two runs of two slices (27648, M > 4);
+# rows past 16384 inputs at M <= 4 are not split (the long-row kernel runs)
+QUAD_SPLIT_SHAPES = [(300, 14336), (40, 28672), (700, 27648), (37, 9216), (5, 16384)]
+
+
+@pytest.mark.parametrize("N,K", QUAD_SPLIT_SHAPES)
+def test_small_m_split_and_unsplit_against_the_oracle(N, K):
+    W = gen.weights(N, K, "gemv", f"qsplit{N}x{K}", shift=True, device=DEV)
+    p = w4.w4a16_pack(W)
+    rows = sample_rows(N, 160, seed=N + K) if N > 500 else None
+    for M in (3, 4, 5, 8):
+        X = gen.activations(M, K, "gemv", f"qsplit{N}x{K}", device=DEV)
+        need = ws_bytes(M, N, K)
+        assert (need > 0) == (M > 4 or K <= 16384), (M, N, K, need)
+        y0 = plain(X, p)
+        check(y0, X, W, rows, f"unsplit M={M} N={N} K={K}")
+        if need:
+            ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+            y1 = split(X, p, ws)
+            check(y1, X, W, rows, f"split M={M} N={N} K={K}")
+            y2 = split(X, p, ws)
+            assert torch.equal(y1, y2), "split-K result not deterministic"
+            assert int(ws[:65536].count_nonzero()) == 0
+
+
 def test_one_workspace_serves_a_sequence_of_shapes():
-    shapes = [(700, 8192, 32), (300, 4096, 16), (3000, 14336, 9), (40, 4608, 17), (700, 8192, 9)]
+    shapes = [(700, 8192, 32), (300, 14336, 5), (300, 4096, 16), (3000, 14336, 9), (40, 28672, 8),
+              (40, 4608, 17), (37, 9216, 3), (700, 8192, 9)]
     need = max(ws_bytes(M, N, K) for N, K, M in shapes)
     ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
     for i, (N, K, M) in enumerate(shapes):
