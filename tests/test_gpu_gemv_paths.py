@@ -132,3 +132,33 @@ def test_rows_too_long_for_the_small_m_kernels(M):
     W = gen.weights(N, K, "gemv", "longrow", shift=True, device=DEV)
     X = gen.activations(M, K, "gemv", "longrow", device=DEV)
     check(plain(X, w4.w4a16_pack(W)), X, W, None, f"long rows M={M}")
+
+
+@pytest.mark.parametrize("M,N,K", [(8, 300, 14336), (5, 40, 28672), (16, 700, 8192), (32, 3000, 14336)])
+def test_split_k_in_a_replayed_graph(M, N, K):
+    # the split paths' counters reset themselves inside each launch (no fill
+    # is recorded in the graph): every replay, with other work on the stream
+    # between replays, gives the eager result bit for bit
+    W = gen.weights(N, K, "gemv", f"graph{N}x{K}", device=DEV)
+    X = gen.activations(M, K, "gemv", f"graph{N}x{K}", device=DEV)
+    p = w4.w4a16_pack(W)
+    need = ws_bytes(M, N, K)
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    y_eager = split(X, p, ws)
+    y = torch.empty_like(y_eager)
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        w4.w4a16_gemv(X, p, y, workspace=ws)
+        stream.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            w4.w4a16_gemv(X, p, y, workspace=ws)
+    for i in range(4):
+        y.fill_(0)
+        y_other = plain(gen.activations(M, K, "gemv", f"graph{i}", device=DEV), p)   # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager), f"replay {i} differs from the eager result"
+        assert int(ws[:65536].count_nonzero()) == 0
+        del y_other
