@@ -168,9 +168,8 @@ int w4a16_gemv(const uint16_t* X, int64_t M, int64_t ldx,
 /*
  * w4a16_gemv_workspace_bytes -- the workspace with which w4a16_gemv_ws may
  * split the K inputs of a row over several blocks for this shape (decode at
- * 9 <= M <= 32 with rows of more than 4096 inputs, at 5 <= M <= 8 with rows
- * of more than 8192 inputs, at 3 <= M <= 4 with 8192 < K <= 16384); 0 when
- * the shape needs none.  The size depends on the current device (its compute-unit count).
+ * 9 <= M <= 32 with rows of more than 4096 inputs, at 3 <= M <= 8 with
+ * rows of more than 8192 inputs); 0 when the shape needs none.  The size depends on the current device (its compute-unit count).
  * Returns W4A16_ERR_INVALID_ARG for shapes w4a16_gemv rejects.
  */
 int w4a16_gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t* bytes);

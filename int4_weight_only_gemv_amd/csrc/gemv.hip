@@ -1190,12 +1190,15 @@ bool launch_quad_long(const uint16_t* X, int Mrt, int64_t ldx, const uint32_t* c
 }
 
 // K split over KS blocks through a caller's workspace, 3 <= M <= 8: rows
-// longer than 8192 inputs (M > 4), or 8192 < K <= 16384 (M <= 4; longer
-// rows run faster on the long-row kernel).  KS = 2 or 4 runs with one
-// 512-input slice per wave (at most 16 waves), else two runs of two slices;
-// then the largest NB whose block count fills the CUs evenly.  Measured on
-// the down projections at M = 8: 8B (K = 14336) 16.1 -> 14.0 us, 70B
-// (K = 28672) 56.9 -> 46.9 us, the stack's (K = 27648) 54.6 -> 39.9 us.
+// longer than 8192 inputs.  KS = 2 or 4 runs with one
+// 512-input slice per wave (at most 16 waves; a run's last slice may be
+// partial, its idle lanes weigh zero), else two runs of two slices; then
+// the largest NB (up to 16 with one slice per wave: few long blocks stream
+// best) whose block count fills the CUs evenly.  Measured on the down
+// projections at M = 8: 8B (K = 14336) 16.1 -> 14.0 us, 70B (K = 28672)
+// 56.9 -> 46.9 -> 39.3 us (16 batches), the stack's (K = 27648, four runs of
+// 13.5 slices, 10 batches) 54.6 -> 39.9 -> 29.3 us; at M = 4 the stack's
+// 25.6 -> 23.1 us against the long-row kernel (the 70B shape's even).
 constexpr int kQuadSplitMinNB2 = 4, kQuadSplitMaxNB2 = 5;
 
 struct QuadSplitPlan {
@@ -1205,11 +1208,12 @@ struct QuadSplitPlan {
 
 template <int MT>
 bool quad_split_plan(int64_t N, int64_t K, QuadSplitPlan& p) {
-  if (K <= 8192 || (MT == 4 && K > 16384)) return false;
+  if (K <= 8192) return false;
   p.KS = 0;
   for (int t = 1; t <= 2 && p.KS == 0; ++t)
     for (int ks : {2, 4})
-      if (p.KS == 0 && K % ((int64_t)kQuadSlice * ks) == 0 && K / ks / kQuadSlice <= (int64_t)kQuadMaxWaves * t) {
+      if (p.KS == 0 && K % ((int64_t)32 * ks) == 0 &&
+          (K / ks + kQuadSlice - 1) / kQuadSlice <= (int64_t)kQuadMaxWaves * t) {
         p.KS = ks;
         p.T = t;
       }
@@ -1220,12 +1224,13 @@ bool quad_split_plan(int64_t N, int64_t K, QuadSplitPlan& p) {
     const double per_cu = (double)ranges(nb) * p.KS / cus;
     return per_cu / std::ceil(per_cu);
   };
-  constexpr int kNBs[] = {8, 6, 5, 4, 3, 2};
-  // two slices of eight activation rows fill the registers: 4 or 5 batches
-  // (other counts spill)
+  constexpr int kNBs[] = {16, 14, 12, 10, 8, 6, 5, 4, 3, 2};
+  // two slices per wave: at most 8 batches; of eight activation rows: 4 or
+  // 5 (other counts spill)
   const bool full = MT > 4 && p.T > 1;
   auto allowed = [&](int c) {
-    return (!full || (c >= kQuadSplitMinNB2 && c <= kQuadSplitMaxNB2)) && ranges(c) <= kSplitMaxRanges;
+    return (!full || (c >= kQuadSplitMinNB2 && c <= kQuadSplitMaxNB2)) && (p.T == 1 || c <= 8) &&
+           ranges(c) <= kSplitMaxRanges;
   };
   p.NB = 0;
   for (int c : kNBs)
@@ -1243,7 +1248,7 @@ template <int MT, int T, int NB>
 void launch_quad_split_nb(const uint16_t* X, int Mrt, int64_t ldx, const uint32_t* codes, const uint16_t* scales,
                           const int32_t* zeros, int N, int K, uint16_t* Y, int64_t ldy, const QuadSplitPlan& p,
                           void* workspace, hipStream_t stream) {
-  const int S = (K / p.KS / kQuadSlice + T - 1) / T;
+  const int S = ((K / p.KS + kQuadSlice - 1) / kQuadSlice + T - 1) / T;
   hipLaunchKernelGGL((gemv_quad_kernel<MT, T, NB, true>), dim3((unsigned)(p.ranges * p.KS)), dim3(S * kWave), 0,
                      stream, X, Mrt, ldx, codes, scales, zeros, N, K, 7, Y, ldy, p.KS,
                      reinterpret_cast<unsigned*>(workspace));
@@ -1259,6 +1264,7 @@ void launch_quad_split(const uint16_t* X, int Mrt, int64_t ldx, const uint32_t* 
       launch_quad_split_nb<MT, TV, V>(X, Mrt, ldx, codes, scales, zeros, N, K, Y, ldy, p, workspace, stream); \
       return;                                                                                            \
     }
+  W4A16_QS(1, 16) W4A16_QS(1, 14) W4A16_QS(1, 12) W4A16_QS(1, 10)
   W4A16_QS(1, 8) W4A16_QS(1, 6) W4A16_QS(1, 5) W4A16_QS(1, 4) W4A16_QS(1, 3) W4A16_QS(1, 2)
   W4A16_QS(2, 8) W4A16_QS(2, 6) W4A16_QS(2, 5) W4A16_QS(2, 4) W4A16_QS(2, 3) W4A16_QS(2, 2)
 #undef W4A16_QS
