@@ -18,7 +18,9 @@
  * ---------------------------------------
  * - Pointers are DEVICE pointers (memory of the current HIP device) unless a
  *   comment says otherwise.  The caller allocates and frees every buffer; the
- *   library allocates nothing and keeps no mutable global state.
+ *   library allocates no memory at run time.  Its only global state is a
+ *   per-device record of the architecture check and the fixed device array
+ *   of w4a16_chain_run_noalloc.
  * - BF16 values are passed as their uint16_t bit patterns.
  * - Every call is asynchronous on `stream` (a hipStream_t; NULL means the
  *   default stream).  It returns once the work is enqueued; buffers must stay
@@ -37,7 +39,9 @@
  * - The kernels are built for gfx950 only: an entry point whose arguments
  *   pass the checks returns W4A16_ERR_UNSUPPORTED when the current HIP
  *   device is not a gfx950 GPU (or there is no device).
- * - Results are deterministic: no atomics; the same inputs give the same bits.
+ * - Results are deterministic: the same inputs give the same bits.  (The
+ *   paths that split K over blocks, and the chain, count arrivals with
+ *   atomics but add their partial sums in a fixed order.)
  *
  * Storage layout of a packed weight matrix with N outputs and K inputs
  * (K a multiple of 128):
@@ -332,7 +336,7 @@ int w4a16_awq_search_error(const uint16_t* Y, int64_t ldy, const uint16_t* Yref,
  * its dispatch, ramp and tail and nothing streams in between (Zeno AGI,
  * "Weight-only vs mixed precision", "7. The Marlin Kernel": round trips
  * between kernels eat the benefit of the fused matmul).  w4a16_chain_run
- * runs a whole chain in one cooperative launch: one block per CU, the rows
+ * runs a whole chain in one launch: one block per CU (all resident), the rows
  * of each linear spread over all blocks, a grid barrier between consecutive
  * linears, the next linear's first weights already streaming through it.
  *
@@ -409,7 +413,8 @@ int w4a16_chain_prepare(const w4a16_chain_linear* linears, int n_linears, int64_
 /*
  * w4a16_chain_run -- run a prepared chain on X0 (BF16 [M][ldx], 16-byte
  * aligned, ldx % 8 == 0, ldx >= the largest K of the linears that take
- * W4A16_CHAIN_X0), asynchronously on `stream`, one cooperative launch.
+ * W4A16_CHAIN_X0), asynchronously on `stream`, in one launch of one block
+ * per compute unit (all resident at once).
  * Every Y_l is written.  Deterministic.
  */
 int w4a16_chain_run(const w4a16_chain_plan* plan, const uint16_t* X0, int64_t ldx, void* stream);
