@@ -134,7 +134,8 @@ def test_rows_too_long_for_the_small_m_kernels(M):
     check(plain(X, w4.w4a16_pack(W)), X, W, None, f"long rows M={M}")
 
 
-@pytest.mark.parametrize("M,N,K", [(8, 300, 14336), (5, 40, 28672), (16, 700, 8192), (32, 3000, 14336)])
+@pytest.mark.parametrize("M,N,K", [(8, 300, 14336), (5, 40, 28672), (4, 2555, 27648), (16, 700, 8192),
+                                   (32, 3000, 14336)])
 def test_split_k_in_a_replayed_graph(M, N, K):
     # the split paths' counters reset themselves inside each launch (no fill
     # is recorded in the graph): every replay, with other work on the stream
