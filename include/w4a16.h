@@ -71,7 +71,7 @@ extern "C" {
 #endif
 
 #define W4A16_GROUP 128
-#define W4A16_ABI_VERSION 9
+#define W4A16_ABI_VERSION 10
 #define W4A16_GEMV_MAX_M 32
 #define W4A16_DENSE_GEMV_MAX_M 8
 #define W4A16_INT8_GEMV_MAX_M 4
@@ -220,6 +220,39 @@ int w4a16_gemm(const uint16_t* X, int64_t M, int64_t ldx,
                const uint32_t* codes, const uint16_t* scales,
                const int32_t* zeros, int64_t N, int64_t K,
                uint16_t* Y, int64_t ldy, void* stream);
+
+/*
+ * w4a16_gemm_workspace_bytes -- the workspace with which w4a16_gemm_ws may
+ * split the K inputs of each output tile over 2, 4 or 8 blocks for this
+ * shape (when the shape has too few large output tiles to fill the device's
+ * compute units, typically M up to ~2048; at most 128 MiB); 0 when it
+ * splits nothing.  The size depends on the current device (its compute-unit
+ * count).  Returns W4A16_ERR_INVALID_ARG for shapes w4a16_gemm rejects.
+ */
+int w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t* bytes);
+
+/*
+ * w4a16_gemm_ws -- w4a16_gemm with a caller-owned workspace: same
+ * arguments, layout, limits and accuracy rules, plus
+ *
+ *   workspace        device memory, 16-byte aligned, not overlapping X, Y or
+ *                    the packed matrix (W4A16_ERR_INVALID_ARG otherwise);
+ *                    any contents (it holds float32 partial outputs during
+ *                    the call); may be NULL with workspace_bytes 0.
+ *   workspace_bytes  its size.
+ *
+ * With at least w4a16_gemm_workspace_bytes() bytes the product may split K:
+ * each run's float32 partial tile goes to the workspace and a second launch
+ * adds the runs in a fixed order and rounds once to BF16, so results are
+ * deterministic (they may differ from the unsplit product's in the last
+ * bit).  With less, or none, the call is w4a16_gemm.  Calls that may run at
+ * the same time need workspaces of their own.
+ */
+int w4a16_gemm_ws(const uint16_t* X, int64_t M, int64_t ldx,
+                  const uint32_t* codes, const uint16_t* scales,
+                  const int32_t* zeros, int64_t N, int64_t K,
+                  uint16_t* Y, int64_t ldy, void* workspace,
+                  int64_t workspace_bytes, void* stream);
 
 /*
  * w4a16_pack_grouped, w4a16_gemv_grouped, w4a16_gemm_grouped -- the same

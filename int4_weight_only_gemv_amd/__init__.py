@@ -40,6 +40,8 @@ _SIGS = {
     "w4a16_gemv_workspace_bytes": ([_i64, _i64, _i64, _p], ctypes.c_int),
     "w4a16_gemv_ws": ([_p, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _i64, _p, _i64, _p], ctypes.c_int),
     "w4a16_gemm": ([_p, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _i64, _p], ctypes.c_int),
+    "w4a16_gemm_workspace_bytes": ([_i64, _i64, _i64, _p], ctypes.c_int),
+    "w4a16_gemm_ws": ([_p, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _i64, _p, _i64, _p], ctypes.c_int),
     "w4a16_awq_importance": ([_p, _i64, _i64, _i64, _p, _p], ctypes.c_int),
     "w4a16_awq_scale": ([_p, _i64, ctypes.c_float, _p, _p], ctypes.c_int),
     "w4a16_awq_fold": ([_p, _i64, _p, _p, _p], ctypes.c_int),
@@ -299,10 +301,61 @@ def w4a16_gemv(X: torch.Tensor, p: PackedLinear, out: torch.Tensor | None = None
     return out
 
 
-def w4a16_gemm(X: torch.Tensor, p: PackedLinear, out: torch.Tensor | None = None) -> torch.Tensor:
+# Prefill workspaces, one per (device, stream), separate from the decode
+# ones (whose counters must stay zero): scratch for the float32 partial
+# outputs of a split K, grown to the largest size asked for; none is created
+# or grown while the stream is being captured.
+_gemm_workspaces: dict = {}
+
+
+def gemm_workspace(X: torch.Tensor, N: int, K: int) -> torch.Tensor | None:
+    """The cached prefill workspace of X's device and current stream, grown
+    to what w4a16_gemm_ws can use for this shape (None when it needs none or
+    the stream is capturing and none is large enough yet)."""
+    nbytes = ctypes.c_int64(0)
+    _check("w4a16_gemm_workspace_bytes",
+           lib.w4a16_gemm_workspace_bytes(X.shape[0], N, K, ctypes.byref(nbytes)))
+    if nbytes.value == 0:
+        return None
+    stream = torch.cuda.current_stream(X.device)
+    key = (X.device.index, stream.cuda_stream)
+    ws = _gemm_workspaces.get(key)
+    if ws is None or ws.numel() < nbytes.value:
+        if torch.cuda.is_current_stream_capturing():
+            return ws if ws is not None and ws.numel() >= nbytes.value else None
+        ws = torch.empty(nbytes.value, dtype=torch.uint8, device=X.device)
+        _gemm_workspaces[key] = ws
+    return ws
+
+
+def w4a16_gemm(X: torch.Tensor, p: PackedLinear, out: torch.Tensor | None = None,
+               workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Y = X . w_hat^T on the matrix cores, any M (prefill); groups other than
-    128 go through w4a16_gemm_grouped."""
-    return _matmul(lib.w4a16_gemm, "w4a16_gemm", X, p, out)
+    128 go through w4a16_gemm_grouped.  With groups of 128 the call goes
+    through w4a16_gemm_ws with `workspace` (a uint8 tensor) or, if None, the
+    cached prefill workspace of the device and stream."""
+    if getattr(p, "group", GROUP) != GROUP:
+        return _matmul(lib.w4a16_gemm, "w4a16_gemm", X, p, out)
+    _need(X, torch.bfloat16, "X", 2)
+    M, K = X.shape
+    if K != p.K:
+        raise ValueError(f"X has K={K}, weights have K={p.K}")
+    if out is None:
+        out = torch.empty(M, p.N, dtype=torch.bfloat16, device=X.device)
+    else:
+        _need(out, torch.bfloat16, "out", 2)
+        if tuple(out.shape) != (M, p.N):
+            raise ValueError("out has the wrong shape")
+    if workspace is None:
+        workspace = gemm_workspace(X, p.N, p.K)
+    if workspace is not None and (workspace.dtype != torch.uint8 or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    ws_ptr = _ptr(workspace) if workspace is not None else None
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    _check("w4a16_gemm_ws", lib.w4a16_gemm_ws(_ptr(X), M, X.stride(0), _ptr(p.codes), _ptr(p.scales),
+                                              _ptr(p.zeros), p.N, p.K, _ptr(out), out.stride(0), ws_ptr,
+                                              ws_bytes, _stream(X)))
+    return out
 
 
 def w4a16_linear(X: torch.Tensor, p: PackedLinear, out: torch.Tensor | None = None) -> torch.Tensor:

@@ -24,7 +24,9 @@ int launch_gemv(const uint16_t*, int64_t, int64_t, const uint32_t*, const uint16
                 const int32_t*, int64_t, int64_t, int, uint16_t*, int64_t, void*, int64_t, hipStream_t);
 int64_t gemv_workspace_bytes(int64_t, int64_t, int64_t, int);
 int launch_gemm(const uint16_t*, int64_t, int64_t, const uint32_t*, const uint16_t*,
-                const int32_t*, int64_t, int64_t, int, uint16_t*, int64_t, hipStream_t);
+                const int32_t*, int64_t, int64_t, int, uint16_t*, int64_t, hipStream_t, void* = nullptr,
+                int64_t = 0);
+int64_t gemm_workspace_bytes(int64_t, int64_t, int64_t);
 int launch_awq_importance(const uint16_t*, int64_t, int64_t, int64_t, float*, hipStream_t);
 int launch_awq_scale(const float*, int64_t, float, float*, hipStream_t);
 int launch_awq_fold(const float*, int64_t, uint16_t*, uint16_t*, hipStream_t);
@@ -260,6 +262,39 @@ int w4a16_gemm(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
   if (int dc = device_check()) return dc;
   return w4a16::launch_gemm(X, M, ldx, codes, scales, zeros, N, K, W4A16_GROUP, Y, ldy,
                             (hipStream_t)stream);
+}
+
+int w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t* bytes) {
+  if (!bytes) return W4A16_ERR_INVALID_ARG;
+  *bytes = 0;
+  if (M < 1 || N < 1 || K < W4A16_GROUP || K % W4A16_GROUP) return W4A16_ERR_INVALID_ARG;
+  if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return W4A16_ERR_UNSUPPORTED;
+  if (int dc = device_check()) return dc;   // the plan depends on the device's CU count
+  *bytes = w4a16::gemm_workspace_bytes(M, N, K);
+  return W4A16_OK;
+}
+
+int w4a16_gemm_ws(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
+                  const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K, uint16_t* Y,
+                  int64_t ldy, void* workspace, int64_t workspace_bytes, void* stream) {
+  int st = check_matmul(X, M, ldx, codes, scales, zeros, N, K, Y, ldy);
+  if (st != W4A16_OK) return st;
+  st = check_gemm_limits(M, N, K, ldx);
+  if (st != W4A16_OK) return st;
+  if (workspace_bytes < 0 || (workspace_bytes > 0 && !workspace)) return W4A16_ERR_INVALID_ARG;
+  if (workspace && !aligned(workspace, 16)) return W4A16_ERR_MISALIGNED;
+  if (workspace && workspace_bytes > 0) {
+    const int64_t G = K / W4A16_GROUP;
+    if (ranges_overlap(workspace, workspace_bytes, X, ((M - 1) * ldx + K) * 2) ||
+        ranges_overlap(workspace, workspace_bytes, Y, ((M - 1) * ldy + N) * 2) ||
+        ranges_overlap(workspace, workspace_bytes, codes, N * (K / 2)) ||
+        ranges_overlap(workspace, workspace_bytes, scales, N * G * 2) ||
+        ranges_overlap(workspace, workspace_bytes, zeros, N * G * 4))
+      return W4A16_ERR_INVALID_ARG;
+  }
+  if (int dc = device_check()) return dc;
+  return w4a16::launch_gemm(X, M, ldx, codes, scales, zeros, N, K, W4A16_GROUP, Y, ldy, (hipStream_t)stream,
+                            workspace_bytes > 0 ? workspace : nullptr, workspace_bytes);
 }
 
 int w4a16_gemm_grouped(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,

@@ -121,11 +121,16 @@ __device__ __forceinline__ void wait_step() {
 // both exact, so the accumulator gathers sum x q + 384 Xsum and the fold
 // removes 384 + z.  Code rows are 128 bytes per block in LDS, their 16-byte
 // chunks XOR-swizzled by row & 7.
-template <class C, int GS, bool W8 = false>
+// SPLIT: the block runs one run of Kl inputs of its tile (X, codes, scales
+// and zeros already offset to the run's start; K stays the row length of the
+// packed matrix) and stores the float32 partial tile to part[M][N] instead of
+// the BF16 tile to Y.  bid is the tile's block index.
+template <class C, int GS, bool W8 = false, bool SPLIT = false>
 __device__ __forceinline__ void gemm_tile(
     const uint16_t* __restrict__ X, int M, int64_t ldx, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K,
-    uint16_t* __restrict__ Y, int64_t ldy, int m_tiles, int n_tiles) {
+    uint16_t* __restrict__ Y, int64_t ldy, int m_tiles, int n_tiles, int bid, int Kl,
+    float* __restrict__ part) {
   static_assert(GS == 1 || GS == 2 || GS == 4, "groups of 32, 64 or 128 inputs");
   constexpr int GPB = kSteps / GS;   // groups per 128-input block
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, MT = C::MT, NT = C::NT;
@@ -149,7 +154,7 @@ __device__ __forceinline__ void gemm_tile(
   // XCD-aware tile order: consecutive block ids land on different XCDs, so
   // give XCD x the contiguous run of tiles [x T/8, (x+1) T/8), N fastest.
   const int T = m_tiles * n_tiles;
-  int t = blockIdx.x;
+  int t = bid;
   if (T % kXcds == 0) t = (t % kXcds) * (T / kXcds) + t / kXcds;
   const int m0 = (t / n_tiles) * BM;
   const int n0 = (t % n_tiles) * BN;
@@ -159,8 +164,8 @@ __device__ __forceinline__ void gemm_tile(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int wm = wave % C::WAVES_M, wn = wave / C::WAVES_M;
   const int r16 = lane & 15, q = lane >> 4;
-  const int G = K / kGroup;           // 128-input blocks
-  const int GR = G * GPB;             // quantisation groups per row
+  const int G = Kl / kGroup;          // 128-input blocks (of the run)
+  const int GR = (K / kGroup) * GPB;  // quantisation groups per row
   const int steps = kSteps * G;
 
   // ---- direct-to-LDS copies, addressed as a block-uniform base plus a
@@ -539,7 +544,11 @@ __device__ __forceinline__ void gemm_tile(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + wm * WM + rowt(mt) * 16 + 4 * q + r;
-        if (m < M) Y[(int64_t)m * ldy + n] = f32_to_bf16_rne(acc[mt][nt][r]);
+        if constexpr (SPLIT) {
+          if (m < M) part[(int64_t)m * N + n] = acc[mt][nt][r];
+        } else {
+          if (m < M) Y[(int64_t)m * ldy + n] = f32_to_bf16_rne(acc[mt][nt][r]);
+        }
       }
     }
 }
@@ -550,7 +559,8 @@ __global__ __launch_bounds__(TileBig::kThreads) void gemm_kernel(
     const uint16_t* __restrict__ X, int M, int64_t ldx, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K,
     uint16_t* __restrict__ Y, int64_t ldy, int m_tiles, int n_tiles) {
-  gemm_tile<TileBig, GS>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, m_tiles, n_tiles);
+  gemm_tile<TileBig, GS>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, m_tiles, n_tiles, (int)blockIdx.x, K,
+                         nullptr);
 }
 
 // three blocks per CU: the register budget of three waves per SIMD (without
@@ -561,7 +571,8 @@ void gemm_small_kernel(
     const uint16_t* __restrict__ X, int M, int64_t ldx, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K,
     uint16_t* __restrict__ Y, int64_t ldy, int m_tiles, int n_tiles) {
-  gemm_tile<TileSmall, GS>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, m_tiles, n_tiles);
+  gemm_tile<TileSmall, GS>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, m_tiles, n_tiles, (int)blockIdx.x, K,
+                           nullptr);
 }
 
 // 128 x 128 tiles for groups of 32 or 64 inputs and for 8-bit codes: two
@@ -573,7 +584,8 @@ void gemm_small2_kernel(
     const uint16_t* __restrict__ X, int M, int64_t ldx, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K,
     uint16_t* __restrict__ Y, int64_t ldy, int m_tiles, int n_tiles) {
-  gemm_tile<TileSmall, GS, W8>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, m_tiles, n_tiles);
+  gemm_tile<TileSmall, GS, W8>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, m_tiles, n_tiles, (int)blockIdx.x,
+                               K, nullptr);
 }
 
 // 64 x 128 tiles on two waves of 64 x 64, for layers whose 128 x 128 tiles
@@ -585,7 +597,64 @@ void gemm_tiny_kernel(
     const uint16_t* __restrict__ X, int M, int64_t ldx, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K,
     uint16_t* __restrict__ Y, int64_t ldy, int m_tiles, int n_tiles) {
-  gemm_tile<TileTiny, GS>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, m_tiles, n_tiles);
+  gemm_tile<TileTiny, GS>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, m_tiles, n_tiles, (int)blockIdx.x, K,
+                          nullptr);
+}
+
+// K split over ksplit equal runs of whole 128-input blocks (groups of 128):
+// block b computes tile b % T over run b / T and stores its float32 partial
+// tile to part + run M N; split_reduce_kernel then adds the runs in order.
+template <class C>
+__device__ __forceinline__ void gemm_split_tile(
+    const uint16_t* __restrict__ X, int M, int64_t ldx, const uint32_t* __restrict__ codes,
+    const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K, int m_tiles,
+    int n_tiles, int ksplit, float* __restrict__ part) {
+  const int T = m_tiles * n_tiles;
+  const int ks = (int)blockIdx.x / T, Kl = K / ksplit;
+  const int64_t kb = (int64_t)ks * Kl;
+  gemm_tile<C, kSteps, false, true>(X + kb, M, ldx, codes + kb / 8, scales + kb / kGroup, zeros + kb / kGroup, N,
+                                    K, nullptr, 0, m_tiles, n_tiles, (int)blockIdx.x - ks * T, Kl,
+                                    part + (int64_t)ks * M * N);
+}
+
+__global__ __launch_bounds__(TileBig::kThreads) void gemm_split_kernel(
+    const uint16_t* __restrict__ X, int M, int64_t ldx, const uint32_t* __restrict__ codes,
+    const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K, int m_tiles,
+    int n_tiles, int ksplit, float* __restrict__ part) {
+  gemm_split_tile<TileBig>(X, M, ldx, codes, scales, zeros, N, K, m_tiles, n_tiles, ksplit, part);
+}
+
+__global__ __launch_bounds__(TileSmall::kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void gemm_small_split_kernel(
+    const uint16_t* __restrict__ X, int M, int64_t ldx, const uint32_t* __restrict__ codes,
+    const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K, int m_tiles,
+    int n_tiles, int ksplit, float* __restrict__ part) {
+  gemm_split_tile<TileSmall>(X, M, ldx, codes, scales, zeros, N, K, m_tiles, n_tiles, ksplit, part);
+}
+
+// Y[m][n] = BF16 of the sum of the ksplit partials in run order (fixed, so
+// the result is deterministic): four consecutive outputs per thread when
+// rows are a multiple of four long, else one.
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part, int ksplit, int M,
+                                                           int N, uint16_t* __restrict__ Y, int64_t ldy) {
+  const int64_t MN = (int64_t)M * N;
+  if (N % 4 == 0) {
+    const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (e >= MN) return;
+    f32x4 v = *reinterpret_cast<const f32x4*>(part + e);
+    for (int k = 1; k < ksplit; ++k) v += *reinterpret_cast<const f32x4*>(part + (int64_t)k * MN + e);
+    const int64_t m = e / N, n = e - m * N;
+    uint16_t* y = Y + m * ldy + n;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = f32_to_bf16_rne(v[i]);
+  } else {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= MN) return;
+    float v = part[e];
+    for (int k = 1; k < ksplit; ++k) v += part[(int64_t)k * MN + e];
+    const int64_t m = e / N, n = e - m * N;
+    Y[m * ldy + n] = f32_to_bf16_rne(v);
+  }
 }
 
 }  // namespace
@@ -594,7 +663,7 @@ namespace {
 template <class C, int GS, bool W8 = false>
 int launch_tiles(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
                  const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K, uint16_t* Y,
-                 int64_t ldy, hipStream_t stream) {
+                 int64_t ldy, hipStream_t stream, int ksplit = 1, float* part = nullptr) {
   const int64_t mt = (M + C::BM - 1) / C::BM, nt = (N + C::BN - 1) / C::BN;
   if (mt * nt >= ((int64_t)1 << 31)) return 3;
   // per-lane 32-bit byte offsets within a tile's rows of X, of the codes and
@@ -603,6 +672,25 @@ int launch_tiles(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* code
       C::BN * (K / (KS * GS)) * 4 >= ((int64_t)1 << 32))
     return 3;
   const dim3 grid((unsigned)(mt * nt)), block(C::kThreads);
+  if (ksplit > 1) {
+    // K split over ksplit runs through the float32 partials in `part`
+    if constexpr (GS == kSteps && !W8 && C::BM != TileTiny::BM) {
+      const dim3 sgrid((unsigned)(mt * nt * ksplit));
+      if constexpr (C::BM == TileBig::BM)
+        hipLaunchKernelGGL(gemm_split_kernel, sgrid, block, 0, stream, X, (int)M, ldx, codes, scales, zeros,
+                           (int)N, (int)K, (int)mt, (int)nt, ksplit, part);
+      else
+        hipLaunchKernelGGL(gemm_small_split_kernel, sgrid, block, 0, stream, X, (int)M, ldx, codes, scales,
+                           zeros, (int)N, (int)K, (int)mt, (int)nt, ksplit, part);
+      const int64_t per = N % 4 == 0 ? 4 : 1;
+      const int64_t threads = (M * N + per - 1) / per;
+      hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, part,
+                         ksplit, (int)M, (int)N, Y, ldy);
+      return hipGetLastError() == hipSuccess ? 0 : 4;
+    } else {
+      return 3;
+    }
+  }
   if constexpr (C::BM == TileBig::BM)
     hipLaunchKernelGGL(gemm_kernel<GS>, grid, block, 0, stream, X, (int)M, ldx, codes, scales,
                        zeros, (int)N, (int)K, Y, ldy, (int)mt, (int)nt);
@@ -627,25 +715,64 @@ namespace {
 // Between 128 x 128 and 64 x 128 tiles the one whose block count fills the
 // rounds of CUs better wins, ties to the larger tile (measured on the
 // 8B-shaped layers, M = 512 .. 4096).
-int launch_gemm_g128(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
-                     const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K, uint16_t* Y,
-                     int64_t ldy, hipStream_t stream) {
+// With a workspace, K may instead be split over KS = 2, 4 or 8 runs of at
+// least 1024 inputs (float32 partials of at most kGemmSplitMaxBytes, added
+// by a second launch): the smallest KS whose 256 x 256 blocks fill at least
+// three quarters of the rounds of CUs, else the smallest whose 128 x 128
+// blocks do.  Measured on the 8B-shaped layers (M = 512: 425 -> 306 us for the
+// four; down 174 -> 85 us, o 55 -> 42 us; M = 1024: down 205 -> 140 us, o 64
+// -> 59; M = 2048: down 303 -> 254 us); the shapes whose large tiles already
+// fill the CUs are not split.
+constexpr int64_t kGemmSplitMaxBytes = (int64_t)128 << 20;
+
+struct GemmPlan {
+  int cfg;       // 0: 256 x 256, 1: 128 x 128, 2: 64 x 128
+  int ksplit;    // runs of K (1: no split)
+  int64_t ws_bytes;
+};
+
+GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, bool split) {
   const int64_t cus = device_cu_count();
   auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   auto fill = [&](int64_t t) { return (double)t / (double)(((t + cus - 1) / cus) * cus); };
-  const int64_t big = tiles(TileBig::BM, TileBig::BN);
-  if (4 * big >= 3 * cus)
-    return launch_tiles<TileBig, kSteps>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
-  if (fill(tiles(TileTiny::BM, TileTiny::BN)) > fill(tiles(TileSmall::BM, TileSmall::BN)) + 1e-9)
+  const int64_t big = tiles(TileBig::BM, TileBig::BN), small = tiles(TileSmall::BM, TileSmall::BN);
+  if (4 * big >= 3 * cus) return GemmPlan{0, 1, 0};
+  if (split) {
+    auto ok = [&](int ks) {
+      return K % (kGroup * ks) == 0 && K / ks >= 1024 && (int64_t)ks * M * N * 4 <= kGemmSplitMaxBytes;
+    };
+    for (int ks : {2, 4, 8})
+      if (ok(ks) && fill(big * ks) >= 0.75) return GemmPlan{0, ks, (int64_t)ks * M * N * 4};
+    for (int ks : {2, 4, 8})
+      if (ok(ks) && fill(small * ks) >= 0.75 && fill(small * ks) > fill(small) + 1e-9)
+        return GemmPlan{1, ks, (int64_t)ks * M * N * 4};
+  }
+  if (fill(tiles(TileTiny::BM, TileTiny::BN)) > fill(small) + 1e-9) return GemmPlan{2, 1, 0};
+  return GemmPlan{1, 1, 0};
+}
+
+int launch_gemm_g128(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
+                     const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K, uint16_t* Y,
+                     int64_t ldy, void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  GemmPlan p = gemm_plan(M, N, K, workspace != nullptr);
+  if (p.ksplit > 1 && workspace_bytes < p.ws_bytes) p = gemm_plan(M, N, K, false);
+  float* part = reinterpret_cast<float*>(workspace);
+  if (p.cfg == 0)
+    return launch_tiles<TileBig, kSteps>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream, p.ksplit, part);
+  if (p.cfg == 2)
     return launch_tiles<TileTiny, kSteps>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
-  return launch_tiles<TileSmall, kSteps>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
+  return launch_tiles<TileSmall, kSteps>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream, p.ksplit, part);
 }
 }  // namespace
+
+// Workspace with which launch_gemm may split K for this shape (groups of
+// 128; 0: none needed).
+int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) { return gemm_plan(M, N, K, true).ws_bytes; }
 
 // group: 32, 64 or 128 inputs per quantisation group (checked by the caller)
 int launch_gemm(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
                 const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K, int group,
-                uint16_t* Y, int64_t ldy, hipStream_t stream) {
+                uint16_t* Y, int64_t ldy, hipStream_t stream, void* workspace, int64_t workspace_bytes) {
   // Groups of 32 or 64: a rescale every one or two steps; 256 x 256 tiles
   // would spill their accumulators, so 128 x 128 tiles at two waves per
   // SIMD, or 64 x 128 tiles when those fill the rounds of CUs better.
@@ -661,7 +788,7 @@ int launch_gemm(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes
     return tiny ? launch_tiles<TileTiny, 2>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream)
                 : launch_tiles<TileSmall, 2>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
   }
-  return launch_gemm_g128(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
+  return launch_gemm_g128(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, workspace, workspace_bytes, stream);
 }
 
 // W8A16 variant, any M >= 1 (checked by the caller): 128 x 128 tiles

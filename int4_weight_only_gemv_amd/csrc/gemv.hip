@@ -1286,7 +1286,7 @@ void launch_quad(const uint16_t* X, int Mrt, int64_t ldx, const uint32_t* codes,
 }  // namespace
 
 int launch_gemm(const uint16_t*, int64_t, int64_t, const uint32_t*, const uint16_t*, const int32_t*,
-                int64_t, int64_t, int, uint16_t*, int64_t, hipStream_t);
+                int64_t, int64_t, int, uint16_t*, int64_t, hipStream_t, void* = nullptr, int64_t = 0);
 
 namespace {
 // Groups of 32 or 64 inputs (lg = 5, 6): the per-lane fold of gemv_dot for

@@ -32,7 +32,7 @@ def test_header_declares_expected_entry_points():
         "w4a16_pack_int8", "w4a16_gemv_int8", "w4a16_gemm_int8", "w4a16_awq_search_error",
         "w4a16_hbm_read_probe", "w4a16_chain_workspace_bytes", "w4a16_chain_prepare",
         "w4a16_chain_run", "w4a16_chain_status", "w4a16_chain_run_noalloc",
-        "w4a16_gemv_workspace_bytes", "w4a16_gemv_ws"])
+        "w4a16_gemv_workspace_bytes", "w4a16_gemv_ws", "w4a16_gemm_workspace_bytes", "w4a16_gemm_ws"])
 
 
 def test_every_declared_symbol_is_exported():
@@ -46,7 +46,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strerror():
-    assert lib.w4a16_abi_version() == 9
+    assert lib.w4a16_abi_version() == 10
     for st in range(5):
         assert lib.w4a16_strerror(st)
     assert b"unknown" in lib.w4a16_strerror(99)
@@ -116,6 +116,33 @@ def test_gemv_ws_validation():
     assert lib.w4a16_gemv_workspace_bytes(33, 4096, 4096, ctypes.byref(n)) == INVALID
     assert lib.w4a16_gemv_workspace_bytes(16, 4096, 4000, ctypes.byref(n)) == INVALID
     assert lib.w4a16_gemv_workspace_bytes(16, 1 << 30, 4096, ctypes.byref(n)) == UNSUPPORTED
+
+
+def gemm_ws(ws=FAKE + (1 << 24), nbytes=1 << 20, X=FAKE, M=512, ldx=4096, codes=FAKE, scales=FAKE,
+            zeros=FAKE, N=4096, K=4096, Y=FAKE, ldy=4096):
+    return lib.w4a16_gemm_ws(p(X), M, ldx, p(codes), p(scales), p(zeros), N, K, p(Y), ldy, p(ws), nbytes,
+                             p(0))
+
+
+def test_gemm_ws_validation():
+    # the matmul and GEMM-limit checks first, then the workspace's
+    assert gemm_ws(X=0) == INVALID and gemm_ws(K=4000) == INVALID and gemm_ws(X=FAKE + 2) == MISALIGNED
+    assert gemm_ws(ldx=1 << 23, ws=FAKE + (1 << 40)) == UNSUPPORTED
+    assert gemm_ws(nbytes=-1) == INVALID
+    assert gemm_ws(ws=0, nbytes=64) == INVALID                  # no pointer for a size
+    assert gemm_ws(ws=FAKE + (1 << 24) + 8) == MISALIGNED       # 16-byte alignment
+    # overlapping the activations, the output or the packed matrix
+    assert gemm_ws(ws=FAKE, nbytes=64) == INVALID
+    assert gemm_ws(X=1 << 28, ws=(1 << 28) + 511 * 8192 + 64, nbytes=64) == INVALID
+    assert gemm_ws(Y=1 << 28, ws=(1 << 28) + 4096, nbytes=64) == INVALID
+    assert gemm_ws(codes=1 << 28, ws=(1 << 28) + 8 * 1024 * 1024 - 64, nbytes=64) == INVALID
+    assert gemm_ws(scales=1 << 28, ws=(1 << 28) + 4096 * 32 * 2 - 64, nbytes=64) == INVALID
+    assert gemm_ws(zeros=1 << 28, ws=(1 << 28) + 4096 * 32 * 4 - 64, nbytes=64) == INVALID
+    n = ctypes.c_int64(7)
+    assert lib.w4a16_gemm_workspace_bytes(512, 4096, 4096, None) == INVALID
+    assert lib.w4a16_gemm_workspace_bytes(0, 4096, 4096, ctypes.byref(n)) == INVALID and n.value == 0
+    assert lib.w4a16_gemm_workspace_bytes(512, 4096, 4000, ctypes.byref(n)) == INVALID
+    assert lib.w4a16_gemm_workspace_bytes(512, 1 << 30, 4096, ctypes.byref(n)) == UNSUPPORTED
 
 
 @pytest.mark.parametrize("fn", ["w4a16_pack", "w4a16_pack_symmetric"])
@@ -311,7 +338,9 @@ def test_valid_call_without_a_device_is_unsupported():
     assert gemv() == UNSUPPORTED
     assert gemv(lib.w4a16_gemm) == UNSUPPORTED
     assert gemv_ws() == UNSUPPORTED
+    assert gemm_ws() == UNSUPPORTED
     n = ctypes.c_int64(7)
+    assert lib.w4a16_gemm_workspace_bytes(512, 4096, 4096, ctypes.byref(n)) == UNSUPPORTED and n.value == 0
     assert lib.w4a16_gemv_workspace_bytes(16, 4096, 14336, ctypes.byref(n)) == UNSUPPORTED and n.value == 0
     assert lib.w4a16_pack(p(FAKE), 16, 256, 256, p(0), p(FAKE), p(FAKE), p(FAKE), p(0)) == UNSUPPORTED
     assert lib.w4a16_awq_fold(p(FAKE), 8, p(FAKE), p(0), p(0)) == UNSUPPORTED

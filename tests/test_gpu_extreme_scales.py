@@ -87,8 +87,10 @@ def modified_scales(scales, what, seed):
 
 
 # (M, N, K): the three tile kernels of the group-128 GEMM -- 64 x 128 tiles,
-# 128 x 128 tiles (48 large tiles), 256 x 256 tiles (4 x 49 large tiles)
-GEMM_SHAPES = [(300, 520, 1536), (500, 6100, 512), (1000, 12300, 384)]
+# 128 x 128 tiles (48 large tiles), 256 x 256 tiles (4 x 49 large tiles) --
+# and 256 x 256 tiles with K split over 8 runs through the binding's
+# workspace (2 x 12 large tiles, K = 8192)
+GEMM_SHAPES = [(300, 520, 1536), (500, 6100, 512), (1000, 12300, 384), (300, 3000, 8192)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
@@ -159,6 +161,16 @@ def test_scales_outside_the_packer_group128(what):
     y = w4.w4a16_gemm(X, p)
     check(y, gen.bits(X), (codes, scales, zeros), f"{what} scales, large tiles",
           rows=sample_rows(N, 96, seed=3), mrows=sample_rows(M, 48, seed=4))
+    # the same tiles with K split over 8 runs (binding's workspace)
+    M, N, K = 300, 3000, 8192
+    Wb = gen.bits(gen.weights(N, K, "extreme", "meta_split"))
+    codes, scales, zeros = O.quantize_pack(Wb)
+    scales = modified_scales(scales, what, seed=11 + len(what))
+    p = to_dev_packed(codes, scales, zeros)
+    X = gen.activations(M, K, "extreme", "meta_split", device=DEV)
+    y = w4.w4a16_gemm(X, p)
+    check(y, gen.bits(X), (codes, scales, zeros), f"{what} scales, split K",
+          rows=sample_rows(N, 96, seed=13), mrows=sample_rows(M, 48, seed=14))
 
 
 @pytest.mark.parametrize("group", [32, 64])

@@ -13,11 +13,16 @@ w4 = pytest.importorskip("int4_weight_only_gemv_amd")
 DEV = "cuda"
 
 
-def check_case(M, N, K, cfg, layer, shift=False, rows=None, mrows=None, label=""):
+def plain_gemm(X, p, out=None):
+    """w4a16_gemm without a workspace: the tile kernels alone, never a split K."""
+    return w4._matmul(w4.lib.w4a16_gemm, "w4a16_gemm", X, p, out)
+
+
+def check_case(M, N, K, cfg, layer, shift=False, rows=None, mrows=None, label="", split=False):
     W = gen.weights(N, K, cfg, layer, shift=shift, device=DEV)
     X = gen.activations(M, K, cfg, layer, device=DEV)
     p = w4.w4a16_pack(W)
-    y = w4.w4a16_gemm(X, p)
+    y = w4.w4a16_gemm(X, p) if split else plain_gemm(X, p)
     torch.cuda.synchronize()
     if mrows is not None:
         midx = torch.as_tensor(mrows, device=DEV)
@@ -42,8 +47,11 @@ def test_llama8b_prefill_sampled(M):
     for layer in gen.LLAMA8B:
         rows = sample_rows(layer.N, 48, seed=layer.N + M)
         mrows = sample_rows(M, 32, seed=M + 7)
-        check_case(M, layer.N, layer.K, "llama8b_prefill", layer.name, rows=rows, mrows=mrows,
-                   label=f"{layer.name} M={M}")
+        # the binding's w4a16_gemm, with its cached workspace (K split where
+        # the large tiles do not fill the CUs), and the tile kernels alone
+        for split in (True, False):
+            check_case(M, layer.N, layer.K, "llama8b_prefill", layer.name, rows=rows, mrows=mrows,
+                       label=f"{layer.name} M={M} split={split}", split=split)
         torch.cuda.empty_cache()
 
 
@@ -68,12 +76,12 @@ def test_canaries_and_determinism():
     X = gen.activations(M, K, "gemm", "canary", device=DEV)
     canary = torch.full((M + 3, N + 24), -77.0, dtype=torch.bfloat16, device=DEV)
     out = canary[2:M + 2, 16:N + 16]
-    w4.w4a16_gemm(X, p, out=out)
+    plain_gemm(X, p, out=out)
     torch.cuda.synchronize()
     inner = torch.zeros_like(canary, dtype=torch.bool)
     inner[2:M + 2, 16:N + 16] = True
     assert torch.all(canary[~inner] == -77.0), "write outside Y"
-    y2 = w4.w4a16_gemm(X, p)
+    y2 = plain_gemm(X, p)
     torch.cuda.synchronize()
     assert torch.equal(out, y2)
     y_ref, mag = reference(gen.bits(X), gen.bits(W))
@@ -90,7 +98,7 @@ def test_large_tiles_ragged_with_canaries():
     X = gen.activations(M, K, "gemm", "big_ragged", device=DEV)
     canary = torch.full((M + 3, N + 24), -77.0, dtype=torch.bfloat16, device=DEV)
     out = canary[1:M + 1, 8:N + 8]
-    w4.w4a16_gemm(X, p, out=out)
+    plain_gemm(X, p, out=out)
     torch.cuda.synchronize()
     inner = torch.zeros_like(canary, dtype=torch.bool)
     inner[1:M + 1, 8:N + 8] = True
