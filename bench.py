@@ -247,8 +247,9 @@ def main():
             "metric": f"prefill GEMM TFLOP/s (M={Mp})",
             "value": round(tf, 1), "unit": "TFLOP/s",
             "ms_per_step": round(sum(times) * 1e3, 4),
-            "layers": [{"layer": L.name, "ms": round(t * 1e3, 4),
-                        "TFLOPs": round(f / t / 1e12, 1)} for L, t, f in zip(layers, times, flops)],
+            "layers": [{"layer": L.name, "ms": round(t * 1e3, 4), "TFLOPs": round(f / t / 1e12, 1),
+                        "split_k_workspace_bytes": gemm_split_bytes(Mp, L.N, L.K)}
+                       for L, t, f in zip(layers, times, flops)],
             "roofline": {"bound": "mfma", "kernel": f"w4a16_gemm ({layers[dom_p].name}, M={Mp})",
                          "achieved": round(flops[dom_p] / times[dom_p] / 1e12, 1),
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -284,7 +285,8 @@ def main():
             otf = sum(oflops) / sum(otimes) / 1e12
             prefill["other_M"].append({
                 "M": Mo, "TFLOPs": round(otf, 1), "ms_per_step": round(sum(otimes) * 1e3, 4),
-                "layers": [{"layer": L.name, "ms": round(t * 1e3, 4), "TFLOPs": round(f / t / 1e12, 1)}
+                "layers": [{"layer": L.name, "ms": round(t * 1e3, 4), "TFLOPs": round(f / t / 1e12, 1),
+                            "split_k_workspace_bytes": gemm_split_bytes(Mo, L.N, L.K)}
                            for L, t, f in zip(layers, otimes, oflops)]})
             log(f"[bench] prefill M={Mo}: {otf:.1f} TFLOP/s")
             del oxs, oys
@@ -440,6 +442,16 @@ def single_linear(dev, stream, M=1, reps=400):
             "us_per_launch": round(us, 3), "GBps": round(gbs, 1),
             "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "rotating_copies": ncopy,
             "launches_timed": reps}
+
+
+def gemm_split_bytes(M, N, K) -> int:
+    """The workspace with which w4a16_gemm splits K for this shape (0: the
+    shape runs unsplit)."""
+    import ctypes
+    import int4_weight_only_gemv_amd as w4
+    n = ctypes.c_int64(0)
+    w4._check("w4a16_gemm_workspace_bytes", w4.lib.w4a16_gemm_workspace_bytes(M, N, K, ctypes.byref(n)))
+    return int(n.value)
 
 
 def kernel_source_digest(files=("gemv.hip", "common.h")) -> str:

@@ -72,6 +72,12 @@ __device__ __forceinline__ void split_scale(uint32_t sbits, float u_prev, int& E
   u = s == 0.f ? u_prev : __builtin_ldexpf(s, -2 * E);
 }
 
+// XCD-aware tile order: consecutive block ids land on different XCDs, so
+// XCD x gets the contiguous run of tiles [x T/8, (x+1) T/8), N fastest.
+__device__ __forceinline__ int tile_of(int bid, int T) {
+  return T % kXcds == 0 ? (bid % kXcds) * (T / kXcds) + bid / kXcds : bid;
+}
+
 // Block tile BM x BN on (BM / WM) x (BN / WN) waves, each computing a
 // WM x WN wave tile of 16x16 MFMA tiles.  The 256 x 256 tile (8 waves of
 // 128 x 64) is the main one; 128 x 128 (4 waves of 64 x 64) keeps the CUs
@@ -123,8 +129,8 @@ __device__ __forceinline__ void wait_step() {
 // chunks XOR-swizzled by row & 7.
 // SPLIT: the block runs one run of Kl inputs of its tile (X, codes, scales
 // and zeros already offset to the run's start; K stays the row length of the
-// packed matrix) and stores the float32 partial tile to part[M][N] instead of
-// the BF16 tile to Y.  bid is the tile's block index.
+// packed matrix) and stores the float32 partial tile to part[BM][BN] (its own
+// slab) instead of the BF16 tile to Y.  bid is the tile's block index.
 template <class C, int GS, bool W8 = false, bool SPLIT = false>
 __device__ __forceinline__ void gemm_tile(
     const uint16_t* __restrict__ X, int M, int64_t ldx, const uint32_t* __restrict__ codes,
@@ -151,11 +157,7 @@ __device__ __forceinline__ void gemm_tile(
   // store into the same buffer comes two groups later)
   __shared__ __attribute__((aligned(16))) float xsum_lds[2][BM];
 
-  // XCD-aware tile order: consecutive block ids land on different XCDs, so
-  // give XCD x the contiguous run of tiles [x T/8, (x+1) T/8), N fastest.
-  const int T = m_tiles * n_tiles;
-  int t = bid;
-  if (T % kXcds == 0) t = (t % kXcds) * (T / kXcds) + t / kXcds;
+  const int t = tile_of(bid, m_tiles * n_tiles);
   const int m0 = (t / n_tiles) * BM;
   const int n0 = (t % n_tiles) * BN;
 
@@ -545,7 +547,7 @@ __device__ __forceinline__ void gemm_tile(
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + wm * WM + rowt(mt) * 16 + 4 * q + r;
         if constexpr (SPLIT) {
-          if (m < M) part[(int64_t)m * N + n] = acc[mt][nt][r];
+          if (m < M) part[(m - m0) * BN + (n - n0)] = acc[mt][nt][r];
         } else {
           if (m < M) Y[(int64_t)m * ldy + n] = f32_to_bf16_rne(acc[mt][nt][r]);
         }
@@ -601,60 +603,58 @@ void gemm_tiny_kernel(
                           nullptr);
 }
 
-// K split over ksplit equal runs of whole 128-input blocks (groups of 128):
-// block b computes tile b % T over run b / T and stores its float32 partial
-// tile to part + run M N; split_reduce_kernel then adds the runs in order.
+// K split over ksplit equal runs of whole 128-input blocks (groups of 128)
+// for the R tiles of block index t_full .. t_full + R - 1 (all tiles, or
+// those past the last whole round of CUs): block b computes split tile
+// r = b % R over run b / R and stores its float32 partial tile to the slab
+// part + (run R + r) BM BN; split_reduce_kernel then adds the runs in order.
 template <class C>
 __device__ __forceinline__ void gemm_split_tile(
     const uint16_t* __restrict__ X, int M, int64_t ldx, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K, int m_tiles,
-    int n_tiles, int ksplit, float* __restrict__ part) {
-  const int T = m_tiles * n_tiles;
-  const int ks = (int)blockIdx.x / T, Kl = K / ksplit;
+    int n_tiles, int t_full, int R, int ksplit, float* __restrict__ part) {
+  const int r = (int)blockIdx.x % R, ks = (int)blockIdx.x / R, Kl = K / ksplit;
   const int64_t kb = (int64_t)ks * Kl;
   gemm_tile<C, kSteps, false, true>(X + kb, M, ldx, codes + kb / 8, scales + kb / kGroup, zeros + kb / kGroup, N,
-                                    K, nullptr, 0, m_tiles, n_tiles, (int)blockIdx.x - ks * T, Kl,
-                                    part + (int64_t)ks * M * N);
+                                    K, nullptr, 0, m_tiles, n_tiles, t_full + r, Kl,
+                                    part + ((int64_t)ks * R + r) * (C::BM * C::BN));
 }
 
 __global__ __launch_bounds__(TileBig::kThreads) void gemm_split_kernel(
     const uint16_t* __restrict__ X, int M, int64_t ldx, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K, int m_tiles,
-    int n_tiles, int ksplit, float* __restrict__ part) {
-  gemm_split_tile<TileBig>(X, M, ldx, codes, scales, zeros, N, K, m_tiles, n_tiles, ksplit, part);
+    int n_tiles, int t_full, int R, int ksplit, float* __restrict__ part) {
+  gemm_split_tile<TileBig>(X, M, ldx, codes, scales, zeros, N, K, m_tiles, n_tiles, t_full, R, ksplit, part);
 }
 
 __global__ __launch_bounds__(TileSmall::kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void gemm_small_split_kernel(
     const uint16_t* __restrict__ X, int M, int64_t ldx, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N, int K, int m_tiles,
-    int n_tiles, int ksplit, float* __restrict__ part) {
-  gemm_split_tile<TileSmall>(X, M, ldx, codes, scales, zeros, N, K, m_tiles, n_tiles, ksplit, part);
+    int n_tiles, int t_full, int R, int ksplit, float* __restrict__ part) {
+  gemm_split_tile<TileSmall>(X, M, ldx, codes, scales, zeros, N, K, m_tiles, n_tiles, t_full, R, ksplit, part);
 }
 
-// Y[m][n] = BF16 of the sum of the ksplit partials in run order (fixed, so
-// the result is deterministic): four consecutive outputs per thread when
-// rows are a multiple of four long, else one.
-__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part, int ksplit, int M,
-                                                           int N, uint16_t* __restrict__ Y, int64_t ldy) {
-  const int64_t MN = (int64_t)M * N;
-  if (N % 4 == 0) {
-    const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-    if (e >= MN) return;
-    f32x4 v = *reinterpret_cast<const f32x4*>(part + e);
-    for (int k = 1; k < ksplit; ++k) v += *reinterpret_cast<const f32x4*>(part + (int64_t)k * MN + e);
-    const int64_t m = e / N, n = e - m * N;
-    uint16_t* y = Y + m * ldy + n;
+// The split tiles' outputs: Y = BF16 of the sum of the ksplit partial slabs
+// in run order (fixed, so the result is deterministic); four consecutive
+// outputs of a tile row per thread, stored where they fall inside Y.
+template <int BM, int BN>
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part, int ksplit, int R,
+                                                           int t_full, int m_tiles, int n_tiles, int M, int N,
+                                                           uint16_t* __restrict__ Y, int64_t ldy) {
+  constexpr int TILE = BM * BN;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)R * (TILE / 4)) return;
+  const int r = (int)(idx / (TILE / 4)), e = (int)(idx - (int64_t)r * (TILE / 4)) * 4;
+  const int t = tile_of(t_full + r, m_tiles * n_tiles);
+  const int m = (t / n_tiles) * BM + e / BN, n = (t % n_tiles) * BN + e % BN;
+  if (m >= M) return;
+  f32x4 v = *reinterpret_cast<const f32x4*>(part + (int64_t)r * TILE + e);
+  for (int k = 1; k < ksplit; ++k) v += *reinterpret_cast<const f32x4*>(part + ((int64_t)k * R + r) * TILE + e);
+  uint16_t* y = Y + (int64_t)m * ldy + n;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) y[i] = f32_to_bf16_rne(v[i]);
-  } else {
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (e >= MN) return;
-    float v = part[e];
-    for (int k = 1; k < ksplit; ++k) v += part[(int64_t)k * MN + e];
-    const int64_t m = e / N, n = e - m * N;
-    Y[m * ldy + n] = f32_to_bf16_rne(v);
-  }
+  for (int i = 0; i < 4; ++i)
+    if (n + i < N) y[i] = f32_to_bf16_rne(v[i]);
 }
 
 }  // namespace
@@ -663,7 +663,7 @@ namespace {
 template <class C, int GS, bool W8 = false>
 int launch_tiles(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
                  const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K, uint16_t* Y,
-                 int64_t ldy, hipStream_t stream, int ksplit = 1, float* part = nullptr) {
+                 int64_t ldy, hipStream_t stream, int ksplit = 1, float* part = nullptr, int64_t t_full = 0) {
   const int64_t mt = (M + C::BM - 1) / C::BM, nt = (N + C::BN - 1) / C::BN;
   if (mt * nt >= ((int64_t)1 << 31)) return 3;
   // per-lane 32-bit byte offsets within a tile's rows of X, of the codes and
@@ -673,19 +673,29 @@ int launch_tiles(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* code
     return 3;
   const dim3 grid((unsigned)(mt * nt)), block(C::kThreads);
   if (ksplit > 1) {
-    // K split over ksplit runs through the float32 partials in `part`
+    // tiles of block index < t_full whole (the same kernel as unsplit, on a
+    // grid of t_full blocks), the other R split over ksplit runs through the
+    // float32 partial slabs in `part`
     if constexpr (GS == kSteps && !W8 && C::BM != TileTiny::BM) {
-      const dim3 sgrid((unsigned)(mt * nt * ksplit));
+      const int64_t R = mt * nt - t_full;
+      if (t_full > 0) {
+        if constexpr (C::BM == TileBig::BM)
+          hipLaunchKernelGGL(gemm_kernel<GS>, dim3((unsigned)t_full), block, 0, stream, X, (int)M, ldx, codes,
+                             scales, zeros, (int)N, (int)K, Y, ldy, (int)mt, (int)nt);
+        else
+          hipLaunchKernelGGL(gemm_small_kernel<GS>, dim3((unsigned)t_full), block, 0, stream, X, (int)M, ldx,
+                             codes, scales, zeros, (int)N, (int)K, Y, ldy, (int)mt, (int)nt);
+      }
+      const dim3 sgrid((unsigned)(R * ksplit));
       if constexpr (C::BM == TileBig::BM)
         hipLaunchKernelGGL(gemm_split_kernel, sgrid, block, 0, stream, X, (int)M, ldx, codes, scales, zeros,
-                           (int)N, (int)K, (int)mt, (int)nt, ksplit, part);
+                           (int)N, (int)K, (int)mt, (int)nt, (int)t_full, (int)R, ksplit, part);
       else
         hipLaunchKernelGGL(gemm_small_split_kernel, sgrid, block, 0, stream, X, (int)M, ldx, codes, scales,
-                           zeros, (int)N, (int)K, (int)mt, (int)nt, ksplit, part);
-      const int64_t per = N % 4 == 0 ? 4 : 1;
-      const int64_t threads = (M * N + per - 1) / per;
-      hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, part,
-                         ksplit, (int)M, (int)N, Y, ldy);
+                           zeros, (int)N, (int)K, (int)mt, (int)nt, (int)t_full, (int)R, ksplit, part);
+      const int64_t threads = R * (C::BM * C::BN / 4);
+      hipLaunchKernelGGL((split_reduce_kernel<C::BM, C::BN>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                         stream, part, ksplit, (int)R, (int)t_full, (int)mt, (int)nt, (int)M, (int)N, Y, ldy);
       return hipGetLastError() == hipSuccess ? 0 : 4;
     } else {
       return 3;
@@ -716,18 +726,21 @@ namespace {
 // rounds of CUs better wins, ties to the larger tile (measured on the
 // 8B-shaped layers, M = 512 .. 4096).
 // With a workspace, K may instead be split over KS = 2, 4 or 8 runs of at
-// least 1024 inputs (float32 partials of at most kGemmSplitMaxBytes, added
-// by a second launch): the smallest KS whose 256 x 256 blocks fill at least
-// three quarters of the rounds of CUs, else the smallest whose 128 x 128
-// blocks do.  Measured on the 8B-shaped layers (M = 512: 425 -> 306 us for the
-// four; down 174 -> 85 us, o 55 -> 42 us; M = 1024: down 205 -> 140 us, o 64
-// -> 59; M = 2048: down 303 -> 254 us); the shapes whose large tiles already
-// fill the CUs are not split.
+// least 1024 inputs (float32 partial tiles of at most kGemmSplitMaxBytes,
+// added by a further launch).  When the large tiles fill the CUs: the tiles
+// past the last whole round, if splitting them KS = 2 or 4 ways makes them
+// take at most half a round (384 tiles: one round of whole tiles, then 128
+// tiles over 2 runs).  Otherwise, every tile: the smallest KS whose 256 x 256
+// blocks fill at least three quarters of the rounds of CUs, else the smallest
+// whose 128 x 128 blocks do.  Measured on the 8B-shaped layers (M = 512: 425
+// -> 306 us for the four; down 174 -> 85 us, o 55 -> 42 us; M = 1024: down 205
+// -> 140 us, o 64 -> 59; M = 2048: down 303 -> 254 us).
 constexpr int64_t kGemmSplitMaxBytes = (int64_t)128 << 20;
 
 struct GemmPlan {
-  int cfg;       // 0: 256 x 256, 1: 128 x 128, 2: 64 x 128
-  int ksplit;    // runs of K (1: no split)
+  int cfg;         // 0: 256 x 256, 1: 128 x 128, 2: 64 x 128
+  int ksplit;      // runs of K (1: no split)
+  int64_t t_full;  // tiles (by block index) computed whole; the rest are split
   int64_t ws_bytes;
 };
 
@@ -736,19 +749,27 @@ GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K, bool split) {
   auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   auto fill = [&](int64_t t) { return (double)t / (double)(((t + cus - 1) / cus) * cus); };
   const int64_t big = tiles(TileBig::BM, TileBig::BN), small = tiles(TileSmall::BM, TileSmall::BN);
-  if (4 * big >= 3 * cus) return GemmPlan{0, 1, 0};
-  if (split) {
-    auto ok = [&](int ks) {
-      return K % (kGroup * ks) == 0 && K / ks >= 1024 && (int64_t)ks * M * N * 4 <= kGemmSplitMaxBytes;
-    };
-    for (int ks : {2, 4, 8})
-      if (ok(ks) && fill(big * ks) >= 0.75) return GemmPlan{0, ks, (int64_t)ks * M * N * 4};
-    for (int ks : {2, 4, 8})
-      if (ok(ks) && fill(small * ks) >= 0.75 && fill(small * ks) > fill(small) + 1e-9)
-        return GemmPlan{1, ks, (int64_t)ks * M * N * 4};
+  auto ok = [&](int ks, int64_t split_tiles, int64_t tile) {
+    return K % (kGroup * ks) == 0 && K / ks >= 1024 && (int64_t)ks * split_tiles * tile * 4 <= kGemmSplitMaxBytes;
+  };
+  constexpr int64_t kBig = (int64_t)TileBig::BM * TileBig::BN, kSmall = (int64_t)TileSmall::BM * TileSmall::BN;
+  if (4 * big >= 3 * cus) {
+    const int64_t rem = big % cus;
+    if (split && big > cus && rem > 0)
+      for (int ks : {2, 4})
+        if (ok(ks, rem, kBig) && ((rem * ks + cus - 1) / cus) * 2 <= ks)
+          return GemmPlan{0, ks, big - rem, ks * rem * kBig * 4};
+    return GemmPlan{0, 1, 0, 0};
   }
-  if (fill(tiles(TileTiny::BM, TileTiny::BN)) > fill(small) + 1e-9) return GemmPlan{2, 1, 0};
-  return GemmPlan{1, 1, 0};
+  if (split) {
+    for (int ks : {2, 4, 8})
+      if (ok(ks, big, kBig) && fill(big * ks) >= 0.75) return GemmPlan{0, ks, 0, ks * big * kBig * 4};
+    for (int ks : {2, 4, 8})
+      if (ok(ks, small, kSmall) && fill(small * ks) >= 0.75 && fill(small * ks) > fill(small) + 1e-9)
+        return GemmPlan{1, ks, 0, ks * small * kSmall * 4};
+  }
+  if (fill(tiles(TileTiny::BM, TileTiny::BN)) > fill(small) + 1e-9) return GemmPlan{2, 1, 0, 0};
+  return GemmPlan{1, 1, 0, 0};
 }
 
 int launch_gemm_g128(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* codes,
@@ -758,10 +779,12 @@ int launch_gemm_g128(const uint16_t* X, int64_t M, int64_t ldx, const uint32_t* 
   if (p.ksplit > 1 && workspace_bytes < p.ws_bytes) p = gemm_plan(M, N, K, false);
   float* part = reinterpret_cast<float*>(workspace);
   if (p.cfg == 0)
-    return launch_tiles<TileBig, kSteps>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream, p.ksplit, part);
+    return launch_tiles<TileBig, kSteps>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream, p.ksplit, part,
+                                         p.t_full);
   if (p.cfg == 2)
     return launch_tiles<TileTiny, kSteps>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream);
-  return launch_tiles<TileSmall, kSteps>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream, p.ksplit, part);
+  return launch_tiles<TileSmall, kSteps>(X, M, ldx, codes, scales, zeros, N, K, Y, ldy, stream, p.ksplit, part,
+                                         p.t_full);
 }
 }  // namespace
 

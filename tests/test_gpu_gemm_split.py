@@ -46,11 +46,14 @@ def check(y, X, W, rows, mrows, label):
     return assert_output_close(y[:, ridx], y_ref, mag, label=label)
 
 
-# (M, N, K): 256 x 256 tiles over 8 runs (2 x 12 tiles, K = 8192; N % 4 == 0
-# and not: four outputs per reducing thread or one), over 4 runs (4 x 16
-# tiles, K = 14336, the down projection's shape), and 128 x 128 tiles over 2
-# runs (the o projection's shape at M = 512)
-SPLIT_SHAPES = [(300, 3000, 8192), (300, 3001, 8192), (1000, 4096, 14336), (512, 4096, 4096)]
+# (M, N, K): every tile split -- 256 x 256 tiles over 8 runs (2 x 12 tiles,
+# K = 8192; N % 4 == 0 and not), over 4 runs (4 x 16 tiles, K = 14336, the
+# down projection's shape), 128 x 128 tiles over 2 runs (the o projection's
+# shape at M = 512) -- and one round of whole 256 x 256 tiles with the tiles
+# past it split over 2 runs (4 x 80 tiles: 64 split; 4 x 79: 60 split, and a
+# tile count that is not a multiple of the eight XCDs keeps the plain order)
+SPLIT_SHAPES = [(300, 3000, 8192), (300, 3001, 8192), (1000, 4096, 14336), (512, 4096, 4096),
+                (1000, 20400, 2048), (1000, 20200, 2048)]
 
 
 @pytest.mark.parametrize("M,N,K", SPLIT_SHAPES)
@@ -92,10 +95,21 @@ def test_too_small_a_workspace_runs_the_unsplit_kernel():
     assert torch.equal(split(X, p, ws), plain(X, p))
 
 
-def test_shapes_that_fill_the_device_are_not_split():
-    # the 8B-shaped gate_up at M = 4096 (1792 large tiles) and a tall thin
-    # product with too few inputs per run
+def test_split_plans():
+    tile = 256 * 256 * 4
+    # whole rounds of large tiles: not split (the 8B-shaped gate_up at
+    # M = 4096, 1792 tiles; o and down at M = 4096, 256 tiles)
     assert ws_bytes(4096, 28672, 4096) == 0
+    assert ws_bytes(4096, 4096, 14336) == 0
+    # a round and a half (qkv at M = 4096, 384 tiles; gate_up at M = 2048,
+    # 896): the last 128 tiles over 2 runs
+    assert ws_bytes(4096, 6144, 4096) == 2 * 128 * tile
+    assert ws_bytes(2048, 28672, 4096) == 2 * 128 * tile
+    # a remainder too large for half a round (gate_up at M = 1024, 448 tiles)
+    assert ws_bytes(1024, 28672, 4096) == 0
+    # too few large tiles: all split (down at M = 512: 32 tiles over 8 runs)
+    assert ws_bytes(512, 4096, 14336) == 8 * 32 * tile
+    # too few inputs per run
     assert ws_bytes(512, 4096, 1024) == 0
 
 
