@@ -1,5 +1,5 @@
-// C ABI of the W4A16 library: synchronous argument checks, then one launch
-// on the caller's stream.  See include/w4a16.h for the contract.
+// C ABI of the W4A16 library: synchronous argument checks, then the call's
+// launches on the caller's stream.  See include/w4a16.h for the contract.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
