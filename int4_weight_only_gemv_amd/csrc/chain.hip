@@ -8,24 +8,28 @@
 // blocks, about 1.5-3 us each, and nothing streams in between ("Weight-Only
 // Quantization and Mixed Precision", "7. The Marlin Kernel": round trips
 // between separate kernels eat the benefit).  Here one block per CU runs the
-// whole chain:
+// whole chain.  Wave 0 is the control wave; waves 1..15 stream weights:
 //
 //   for each linear l:
-//     stage X_l in LDS: formed from the previous output by the linear's glue
-//       (as is, SwiGLU of [gate | up], or single-key attention: each head's
-//       value vector), times the optional producer weight, rounded to BF16,
-//       and stored pair-permuted with the activation sums of every 32 inputs;
-//     the block's rows of W_l, four rows x 2048 inputs per wave item, with
-//       the exact operands 128 + q and the per-group fold of the decode
-//       kernel (s (P - (128 + z) Xsum), v_dot2_f32_bf16);
-//     the K slices of a row summed in LDS in a fixed order, Y_l stored BF16;
-//     all blocks meet at a grid barrier; right after arriving, each wave
-//     issues the loads of its first item of W_{l+1} (they do not depend on
-//     X), so the weight stream flows through the barrier and the staging of
-//     X_{l+1}.
+//     all waves stage X_l in LDS: formed from the previous output by the
+//       linear's glue (as is, SwiGLU of [gate | up], or single-key attention:
+//       each head's value vector), times the optional producer weight,
+//       rounded to BF16, stored pair-permuted with the activation sums of
+//       every 32 inputs (consecutive lanes read consecutive 8-input octets
+//       with coherent 64-bit loads, several octets' loads in flight);
+//     the streaming waves take the block's rows of W_l, four rows x 2048
+//       inputs per item, with the exact operands 128 + q and the per-group
+//       fold of the decode kernel (s (P - (128 + z) Xsum), v_dot2_f32_bf16);
+//       each keeps two items in flight in registers, and its load cursor runs
+//       on into the next linears, so the weight stream continues through
+//       the steps below;
+//     the control wave adds the K slices of each row in LDS in a fixed
+//       order, stores Y_l in BF16, waits for its stores and meets the other
+//       blocks at a grid barrier while the streaming waves wait at a block
+//       barrier with their loads in flight.
 //
 // The outputs pass between blocks (and the XCDs' separate L2 caches) as
-// 32-bit agent-scope atomic stores and loads, which are coherent across the
+// agent-scope atomic stores (32-bit) and loads (32- and 64-bit), coherent across the
 // device without the L2 write-back and invalidation an agent-scope fence
 // costs (measured on MI355X: 5.3 against 1.7 us per barrier).  The barrier
 // is two-level: blocks arrive on 16 counters on separate cache lines, the
@@ -51,96 +55,107 @@ namespace {
 constexpr int kChainWaves = 16;
 constexpr int kChainThreads = kChainWaves * 64;
 constexpr int kChainSlice = 2048;     // inputs per wave item: 64 lanes x 32
+constexpr int kRing = 2;              // weight items in flight per streaming wave
+constexpr int kStageU = 2;            // input octets per thread and staging pass
 
 constexpr int kGroups = kChainGroups, kGenCopies = kChainGenCopies;
 constexpr int kTopWord = kChainTopWord, kStatusWord = kChainStatusWord, kGenWord0 = kChainGenWord0;
 
+// Coherent accesses through global-address-space pointers: the pointers
+// come from descriptors in memory, and as generic pointers the loads would be
+// flat loads, which also count on the LDS counter and serialise the staging.
+typedef __attribute__((address_space(1))) unsigned g_u32;
+typedef __attribute__((address_space(1))) const unsigned g_cu32;
+typedef __attribute__((address_space(1))) const uint64_t g_cu64;
+
 __device__ __forceinline__ unsigned ld_coherent(const unsigned* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load((g_cu32*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void st_coherent(unsigned* p, unsigned v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store((g_u32*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The 32 inputs of chunk c of activation row m, formed by the linear's glue,
-// times gamma, rounded to BF16, as four natural-order dwords of pairs.  The
-// previous output is read with coherent 32-bit loads (two BF16 values each;
-// rows are 16-byte aligned, a chunk never straddles a head of ATTN1 when
-// head_dim % 32 == 0, otherwise element by element).
+__device__ __forceinline__ uint64_t ld_coherent64(const uint64_t* p) {
+  return __hip_atomic_load((g_cu64*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ float lo16(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi16(unsigned w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-__device__ __forceinline__ void form_chunk(const ChainDesc& d, const ChainDesc* prev, const uint16_t* X0,
-                                           int64_t ldx, int m, int c, u32x4 raw[4]) {
-  const int k0 = 32 * c;
-  float v[32];
-  if (d.input == W4A16_CHAIN_X0) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(X0 + (int64_t)m * ldx + k0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const u32x4 w = p[i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[8 * i + 2 * j] = lo16(w[j]);
-        v[8 * i + 2 * j + 1] = hi16(w[j]);
-      }
-    }
+// Four BF16 values of a 64-bit word, in order.
+__device__ __forceinline__ void unpack4(uint64_t w, float* v) {
+  v[0] = lo16((unsigned)w);
+  v[1] = hi16((unsigned)w);
+  v[2] = lo16((unsigned)(w >> 32));
+  v[3] = hi16((unsigned)(w >> 32));
+}
+
+// The 8 inputs 8o .. 8o+7 of activation row m as formed by the linear's glue
+// (before the producer weight), in two steps so that a thread can issue the
+// loads of several octets before it waits for the first: fetch_octet loads
+// the raw BF16 words (consecutive lanes take consecutive octets, so every
+// load instruction of a wave covers one contiguous run of the previous
+// output: two coherent 64-bit loads per octet and source, rows 16-byte
+// aligned), form_octet applies the glue.  Single-key attention reads whole
+// octets when heads are a multiple of 8 inputs and the value block starts at
+// a multiple of 4; otherwise form_octet reads it element by element.
+__device__ __forceinline__ bool attn_octets(const ChainDesc& d) {
+  return d.head_dim % 8 == 0 && d.v_offset % 4 == 0;
+}
+
+template <int KIND>
+__device__ __forceinline__ void fetch_octet(const ChainDesc& d, const ChainDesc* prev, const uint16_t* X0,
+                                            int64_t ldx, int m, int o, uint64_t w[4]) {
+  const int k0 = 8 * o;
+  if constexpr (KIND == W4A16_CHAIN_X0) {
+    const uint64_t* p = reinterpret_cast<const uint64_t*>(X0 + (int64_t)m * ldx + k0);
+    w[0] = p[0];
+    w[1] = p[1];
   } else {
-    const unsigned* row = reinterpret_cast<const unsigned*>(prev->y + (int64_t)m * prev->ldy);
-    if (d.input == W4A16_CHAIN_PREV) {
-#pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const unsigned w = ld_coherent(row + k0 / 2 + t);
-        v[2 * t] = lo16(w);
-        v[2 * t + 1] = hi16(w);
-      }
-    } else if (d.input == W4A16_CHAIN_SWIGLU) {
-#pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const unsigned wg = ld_coherent(row + k0 / 2 + t), wu = ld_coherent(row + (d.K + k0) / 2 + t);
-        const float g0 = lo16(wg), g1 = hi16(wg);
-        v[2 * t] = g0 * __builtin_amdgcn_rcpf(1.f + __expf(-g0)) * lo16(wu);
-        v[2 * t + 1] = g1 * __builtin_amdgcn_rcpf(1.f + __expf(-g1)) * hi16(wu);
-      }
-    } else {   // W4A16_CHAIN_ATTN1
-      if (d.head_dim % 32 == 0 && (d.v_offset & 1) == 0) {
-        const int h = k0 / d.head_dim;
-        const int src = d.v_offset + (h / d.group) * d.head_dim + (k0 - h * d.head_dim);   // even
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          const unsigned w = ld_coherent(row + src / 2 + t);
-          v[2 * t] = lo16(w);
-          v[2 * t + 1] = hi16(w);
-        }
-      } else {
-#pragma unroll 4
-        for (int t = 0; t < 32; ++t) {
-          const int k = k0 + t;
-          const int h = k / d.head_dim;
-          const int e = d.v_offset + (h / d.group) * d.head_dim + (k - h * d.head_dim);
-          const unsigned w = ld_coherent(row + e / 2);
-          v[t] = (e & 1) ? hi16(w) : lo16(w);
-        }
-      }
+    const uint64_t* row = reinterpret_cast<const uint64_t*>(prev->y + (int64_t)m * prev->ldy);
+    if constexpr (KIND == W4A16_CHAIN_PREV) {
+      w[0] = ld_coherent64(row + 2 * o);
+      w[1] = ld_coherent64(row + 2 * o + 1);
+    } else if constexpr (KIND == W4A16_CHAIN_SWIGLU) {
+      w[0] = ld_coherent64(row + 2 * o);
+      w[1] = ld_coherent64(row + 2 * o + 1);
+      w[2] = ld_coherent64(row + d.K / 4 + 2 * o);
+      w[3] = ld_coherent64(row + d.K / 4 + 2 * o + 1);
+    } else {   // W4A16_CHAIN_ATTN1 with whole octets (attn_octets)
+      const int h = k0 / d.head_dim;
+      const int src = d.v_offset + (h / d.group) * d.head_dim + (k0 - h * d.head_dim);   // multiple of 4
+      w[0] = ld_coherent64(row + src / 4);
+      w[1] = ld_coherent64(row + src / 4 + 1);
     }
   }
-  if (d.gamma) {
-    const u32x4* gp = reinterpret_cast<const u32x4*>(d.gamma + k0);
+}
+
+// KIND: the glue, or -1 for single-key attention read element by element
+template <int KIND>
+__device__ __forceinline__ void form_octet(const ChainDesc& d, const ChainDesc* prev, int m, int o,
+                                           const uint64_t w[4], float v[8]) {
+  if constexpr (KIND == W4A16_CHAIN_SWIGLU) {
+    float g[8], u[8];
+    unpack4(w[0], g);
+    unpack4(w[1], g + 4);
+    unpack4(w[2], u);
+    unpack4(w[3], u + 4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const u32x4 w = gp[i];
+    for (int t = 0; t < 8; ++t) v[t] = g[t] * __builtin_amdgcn_rcpf(1.f + __expf(-g[t])) * u[t];
+  } else if constexpr (KIND >= 0) {
+    unpack4(w[0], v);
+    unpack4(w[1], v + 4);
+  } else {
+    const unsigned* row32 = reinterpret_cast<const unsigned*>(prev->y + (int64_t)m * prev->ldy);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[8 * i + 2 * j] *= lo16(w[j]);
-        v[8 * i + 2 * j + 1] *= hi16(w[j]);
-      }
+    for (int t = 0; t < 8; ++t) {
+      const int k = 8 * o + t;
+      const int h = k / d.head_dim;
+      const int e = d.v_offset + (h / d.group) * d.head_dim + (k - h * d.head_dim);
+      const unsigned x = ld_coherent(row32 + e / 2);
+      v[t] = (e & 1) ? hi16(x) : lo16(x);
     }
   }
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      raw[i][j] = (uint32_t)f32_to_bf16_rne(v[8 * i + 2 * j]) | ((uint32_t)f32_to_bf16_rne(v[8 * i + 2 * j + 1]) << 16);
 }
 
 // Block barrier without a wait on vector memory (the compiler may not move
@@ -187,6 +202,8 @@ __device__ __forceinline__ void grid_wait(unsigned* bar, unsigned gen, bool publ
   block_sync_lds();
 }
 
+typedef const __attribute__((address_space(4))) ChainDesc CDesc;
+
 template <int M>
 __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainDesc* __restrict__ descs, int n_linears,
                                                               const uint16_t* __restrict__ X0, int64_t ldx,
@@ -194,6 +211,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainDesc* _
                                                               int max_k, int max_rows) {
   constexpr int R = 4;                          // rows per item
   constexpr int MP = M == 1 ? 1 : 2;            // values per lane after the group step
+  constexpr int S = kChainWaves - 1;            // streaming waves
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   // X of the current linear, pair-permuted, [m][chunk c = 64 slice + lane][i]
   // stored as [m][slice][i][lane] (16 bytes per lane and i: conflict-free reads)
@@ -203,75 +221,164 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainDesc* _
   float* red = xsum + (size_t)M * (max_k / 32);                                  // [slice][row][m]
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int sw = wave - 1;                      // index of a streaming wave (waves 1 .. 15)
   const unsigned nblocks = gridDim.x;
   const int b = blockIdx.x;
   unsigned gen = 0;
   if (threadIdx.x == 0) gen = ld_coherent(bar + kGenWord0 + 16 * (blockIdx.x % kGenCopies));
 
-  // double-buffered item loads: four code rows and one scale / zero point
-  u32x4 cb[2][R];
-  uint32_t sb[2];
-  int zb[2];
-  auto item_load = [&](int buf, const ChainDesc& d, int row0, int it) {
-    const int batch = it / d.slices, sl = it - batch * d.slices;
-    const int chunks = d.K / 32;
-    const int c = min(sl * 64 + lane, chunks - 1);    // inactive lanes read valid memory
-    const int64_t vrow = d.K / 32;                     // 16-byte vectors per code row
-    const u32x4* cbase = reinterpret_cast<const u32x4*>(d.codes) + c;
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-      const int row = min(row0 + batch * R + j, d.N - 1);
-      cb[buf][j] = __builtin_nontemporal_load(cbase + (int64_t)row * vrow);
-    }
-    const int G = d.K / kGroup;
-    const int mrow = min(row0 + batch * R + (lane & 3), d.N - 1);
-    sb[buf] = d.scales[(int64_t)mrow * G + c / 4];
-    zb[buf] = d.zeros[(int64_t)mrow * G + c / 4];
-  };
-  auto block_rows = [&](const ChainDesc& d, int& row0, int& nb) {
-    nb = d.batches_per_block + (b < d.batches_rem ? 1 : 0);
-    row0 = R * (b * d.batches_per_block + min(b, d.batches_rem));
+  // descriptors read through the constant address space: wave-uniform
+  // scalar loads, which wait on their own counter (a vector load here would
+  // make the next wait drain the weight stream)
+  CDesc* cdesc = (CDesc*)descs;
+  auto block_rows = [&](int per_block, int rem, int& row0, int& nb) {
+    nb = per_block + (b < rem ? 1 : 0);
+    row0 = R * (b * per_block + min(b, rem));
   };
 
-  // the first linear's first item
-  {
-    const ChainDesc d = descs[0];
-    int row0, nb;
-    block_rows(d, row0, nb);
-    if (wave < nb * d.slices) item_load(0, d, row0, wave);
+  // The weight stream of a streaming wave: its items of every linear in
+  // chain order (item sw + k S of each linear, k = 0, 1, ...: a 4-row batch
+  // and a 2048-input slice), kRing loads ahead of the products, in kRing
+  // register buffers.  The cursor (cl, ck) names the next entry to load; it
+  // runs ahead into the following linears, so the stream goes on through the
+  // reduction, the grid barrier and the staging of the next input.  Entries
+  // past the chain's end load the workspace header instead (valid memory,
+  // values unused).  At a linear's start every load has landed, and the
+  // buffers are rotated so that buffer 0 holds its first item; within the
+  // linear each product then waits only for its own buffer.
+  u32x4 cb[kRing][R];
+  uint16_t sb[kRing];
+  int zb[kRing];
+  auto items_of = [&](int l) {
+    const int nb = cdesc[l].batches_per_block + (b < cdesc[l].batches_rem ? 1 : 0);
+    return nb * cdesc[l].slices;
+  };
+  auto entries_of = [&](int l) {
+    const int items = items_of(l);
+    return sw < items ? (items - sw + S - 1) / S : 0;
+  };
+  int cl = 0, ck = 0;
+  auto settle = [&]() {
+    while (cl < n_linears && ck >= entries_of(cl)) {
+      cl += 1;
+      ck = 0;
+    }
+  };
+  auto stream_load = [&](int buf) {
+    const u32x4* cbase = reinterpret_cast<const u32x4*>(bar) + lane;
+    const uint16_t* sbase = reinterpret_cast<const uint16_t*>(bar);
+    const int32_t* zbase = reinterpret_cast<const int32_t*>(bar);
+    int64_t vrow = 0, G = 0;
+    int rowb = 0, nmax = 0, c4 = lane >> 2;
+    const int it = sw + ck * S;
+    if (cl < n_linears && it < items_of(cl)) {
+      const int K = cdesc[cl].K, slices = cdesc[cl].slices;
+      int row0, nb;
+      block_rows(cdesc[cl].batches_per_block, cdesc[cl].batches_rem, row0, nb);
+      const int batch = it / slices, sl = it - batch * slices;
+      const int c = min(sl * 64 + lane, K / 32 - 1);   // inactive lanes read valid memory
+      vrow = K / 32;
+      G = K / kGroup;
+      rowb = row0 + batch * R;
+      nmax = cdesc[cl].N - 1;
+      c4 = c / 4;
+      cbase = reinterpret_cast<const u32x4*>(cdesc[cl].codes) + c;
+      sbase = cdesc[cl].scales;
+      zbase = cdesc[cl].zeros;
+    }
+#pragma unroll
+    for (int j = 0; j < R; ++j) cb[buf][j] = __builtin_nontemporal_load(cbase + (int64_t)min(rowb + j, nmax) * vrow);
+    const int64_t mi = (int64_t)min(rowb + (lane & 3), nmax) * G + c4;
+    sb[buf] = sbase[mi];
+    zb[buf] = zbase[mi];
+    ck += 1;
+    settle();
+  };
+
+  if (wave > 0) {
+    settle();
+    static_for<0, kRing>([&](auto j) { stream_load(decltype(j)::value); });
   }
+  int phase = 0;   // buffer of the oldest entry in flight
 
   for (int l = 0; l < n_linears; ++l) {
     const ChainDesc d = descs[l];
     const ChainDesc* prev = l > 0 ? descs + (l - 1) : nullptr;
     int row0, nb;
-    block_rows(d, row0, nb);
-    const int chunks = d.K / 32;
+    block_rows(d.batches_per_block, d.batches_rem, row0, nb);
     const int items = nb * d.slices;
 
-    // ---- stage X_l: one 32-input chunk per thread and step (the loads of
-    // the previous output wait behind the prefetched weights, which were
-    // issued first and land during the barrier)
-    for (int e = threadIdx.x; e < M * chunks; e += kChainThreads) {
-      const int m = e / chunks, c = e - m * chunks;
-      u32x4 raw[4];
-      form_chunk(d, prev, X0, ldx, m, c, raw);
-      float sum = 0.f;
+    // ---- stage X_l: octets (8 inputs) of the activation rows, kStageU per
+    // thread and pass with all their loads issued first; the four lanes of a
+    // 32-input chunk add their sums
+    const int octs = d.K / 8;
+    // every block reads the whole input at the same moment: each starts at
+    // its own 32-input chunk (block-dependent rotation) so that the blocks
+    // spread over the memory channels
+    const int shift = 4 * ((b * 37) % (octs / 4));
+    auto octet_of = [&](int e, int& m, int& o) {
+      m = e / octs;
+      o = e - m * octs + shift;
+      if (o >= octs) o -= octs;
+    };
+    auto stage = [&](auto kind_c) {
+      constexpr int KIND = decltype(kind_c)::value;
+      for (int e0 = threadIdx.x; e0 < M * octs; e0 += kStageU * kChainThreads) {
+        uint64_t w[kStageU][4];
+        u32x4 gw[kStageU];
+        static_for<0, kStageU>([&](auto uu) {
+          constexpr int u = decltype(uu)::value;
+          const int e = e0 + u * kChainThreads;
+          if (e < M * octs) {
+            int m, o;
+            octet_of(e, m, o);
+            if constexpr (KIND >= 0) fetch_octet<KIND>(d, prev, X0, ldx, m, o, w[u]);
+            if (d.gamma) gw[u] = *reinterpret_cast<const u32x4*>(d.gamma + 8 * o);
+          }
+        });
+        static_for<0, kStageU>([&](auto uu) {
+          constexpr int u = decltype(uu)::value;
+          const int e = e0 + u * kChainThreads;
+          if (e < M * octs) {
+            int m, o;
+            octet_of(e, m, o);
+            float v[8];
+            form_octet<KIND>(d, prev, m, o, w[u], v);
+            if (d.gamma) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+              for (int j = 0; j < 4; ++j) {
+                v[2 * j] *= lo16(gw[u][j]);
+                v[2 * j + 1] *= hi16(gw[u][j]);
+              }
+            }
+            u32x4 raw;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sum = dot2(raw[i][j], kOnePair, sum);
-      const int sl = c >> 6, ln = c & 63;
+            for (int j = 0; j < 4; ++j)
+              raw[j] = (uint32_t)f32_to_bf16_rne(v[2 * j]) | ((uint32_t)f32_to_bf16_rne(v[2 * j + 1]) << 16);
+            float sum = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xs[((size_t)(m * xsl + sl) * 4 + i) * 64 + ln] = x_pairs_from_natural(raw[i]);
-      xsum[m * (max_k / 32) + c] = sum;
-    }
+            for (int j = 0; j < 4; ++j) sum = dot2(raw[j], kOnePair, sum);
+            sum += dpp<kDppXor1>(sum);
+            sum += dpp<kDppXor2>(sum);
+            const int c = o >> 2, i = o & 3, sl = c >> 6, ln = c & 63;
+            xs[((size_t)(m * xsl + sl) * 4 + i) * 64 + ln] = x_pairs_from_natural(raw);
+            if (i == 0) xsum[m * (max_k / 32) + c] = sum;
+          }
+        });
+      }
+    };
+    if (d.input == W4A16_CHAIN_X0) stage(Ic<W4A16_CHAIN_X0>{});
+    else if (d.input == W4A16_CHAIN_PREV) stage(Ic<W4A16_CHAIN_PREV>{});
+    else if (d.input == W4A16_CHAIN_SWIGLU) stage(Ic<W4A16_CHAIN_SWIGLU>{});
+    else if (attn_octets(d)) stage(Ic<W4A16_CHAIN_ATTN1>{});
+    else stage(Ic<-1>{});
     block_sync_lds();
 
     // ---- the block's rows: items (4-row batch, 2048-input slice)
     auto compute = [&](int buf, int it) {
       const int batch = it / d.slices, sl = it - batch * d.slices;
+      const int chunks = d.K / 32;
       const int c = sl * 64 + lane;
       const bool active = c < chunks;
       u32x4 xp[M][4];
@@ -333,50 +440,87 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainDesc* _
       if (tree_result<MP, MP == 1 ? 0 : 1>(lane, m) && m < M)
         red[((size_t)sl * max_rows + batch * R + (lane & 3)) * M + m] = part[0];
     };
-    int it = wave;
-    while (true) {
-      if (it >= items) break;
-      if (it + kChainWaves < items) item_load(1, d, row0, it + kChainWaves);
-      compute(0, it);
-      it += kChainWaves;
-      if (it >= items) break;
-      if (it + kChainWaves < items) item_load(0, d, row0, it + kChainWaves);
-      compute(1, it);
-      it += kChainWaves;
+    if (wave > 0) {
+      // the prefetched items have landed behind the staging loads (or are
+      // waited for here, in waves that staged nothing)
+      wait_vmcnt<0>();
+      // rotate the ring so that buffer 0 holds the oldest entry
+      static_for<1, kRing>([&](auto rr) {
+        constexpr int r = decltype(rr)::value;
+        if (phase == r) {
+          u32x4 tc[kRing][R];
+          uint16_t ts[kRing];
+          int tz[kRing];
+#pragma unroll
+          for (int j = 0; j < kRing; ++j) {
+#pragma unroll
+            for (int q = 0; q < R; ++q) tc[j][q] = cb[(j + r) % kRing][q];
+            ts[j] = sb[(j + r) % kRing];
+            tz[j] = zb[(j + r) % kRing];
+          }
+#pragma unroll
+          for (int j = 0; j < kRing; ++j) {
+#pragma unroll
+            for (int q = 0; q < R; ++q) cb[j][q] = tc[j][q];
+            sb[j] = ts[j];
+            zb[j] = tz[j];
+          }
+        }
+      });
+      int it = sw;
+      for (; it + (kRing - 1) * S < items; it += kRing * S) {
+        static_for<0, kRing>([&](auto jj) {
+          constexpr int j = decltype(jj)::value;
+          compute(j, it + j * S);
+          stream_load(j);
+        });
+      }
+      // the last, partial round: its buffers are refilled, the rest keep
+      // entries of the following linears, and the oldest entry is then in
+      // buffer `phase`
+      phase = 0;
+      static_for<0, kRing - 1>([&](auto jj) {
+        constexpr int j = decltype(jj)::value;
+        if (it + j * S < items) {
+          compute(j, it + j * S);
+          stream_load(j);
+          phase = j + 1;
+        }
+      });
     }
     block_sync_lds();
 
-    // ---- the K slices of each row in a fixed order, BF16 store of row pairs
-    // as coherent 32-bit stores (rows start at a multiple of 4; an odd last
-    // row of the linear updates its half of the word atomically)
-    const int rows = min(R * nb, d.N - row0);
-    auto row_value = [&](int r, int m) {
-      float v = red[(size_t)r * M + m];
-      for (int sl = 1; sl < d.slices; ++sl) v += red[((size_t)sl * max_rows + r) * M + m];
-      return (uint32_t)f32_to_bf16_rne(v);
-    };
-    for (int e = threadIdx.x; e < ((rows + 1) / 2) * M; e += kChainThreads) {
-      const int r = 2 * (e / M), m = e - (e / M) * M;
-      unsigned* yw = reinterpret_cast<unsigned*>(d.y + (int64_t)m * d.ldy + row0 + r);
-      if (r + 1 < rows) {
-        st_coherent(yw, row_value(r, m) | (row_value(r + 1, m) << 16));
-      } else {
-        __hip_atomic_fetch_and(yw, 0xFFFF0000u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_fetch_or(yw, row_value(r, m), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // ---- wave 0: the K slices of each row in a fixed order, BF16 store of
+    // row pairs as coherent 32-bit stores (rows start at a multiple of 4; an
+    // odd last row of the linear updates its half of the word atomically),
+    // then the grid barrier; the streaming waves wait at the block barrier
+    // with their next loads in flight
+    if (wave == 0) {
+      const int rows = min(R * nb, d.N - row0);
+      auto row_value = [&](int r, int m) {
+        float v = red[(size_t)r * M + m];
+        for (int sl = 1; sl < d.slices; ++sl) v += red[((size_t)sl * max_rows + r) * M + m];
+        return (uint32_t)f32_to_bf16_rne(v);
+      };
+      for (int e = lane; e < ((rows + 1) / 2) * M; e += 64) {
+        const int r = 2 * (e / M), m = e - (e / M) * M;
+        unsigned* yw = reinterpret_cast<unsigned*>(d.y + (int64_t)m * d.ldy + row0 + r);
+        if (r + 1 < rows) {
+          st_coherent(yw, row_value(r, m) | (row_value(r + 1, m) << 16));
+        } else {
+          __hip_atomic_fetch_and(yw, 0xFFFF0000u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_fetch_or(yw, row_value(r, m), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
     }
-
     if (l + 1 < n_linears) {
-      // the block's stores are complete before it arrives (a block barrier
-      // alone does not wait for global stores)
-      wait_vmcnt<0>();
-      __syncthreads();
-      const bool published = grid_arrive(bar, nblocks, gen);
-      // the next linear's first item streams through the barrier
-      const ChainDesc dn = descs[l + 1];
-      int r0n, nbn;
-      block_rows(dn, r0n, nbn);
-      if (wave < nbn * dn.slices) item_load(0, dn, r0n, wave);
+      // the block's stores (all in wave 0) are complete before it arrives:
+      // a block barrier does not wait for global stores
+      bool published = false;
+      if (wave == 0) {
+        wait_vmcnt<0>();
+        published = grid_arrive(bar, nblocks, gen);
+      }
       grid_wait(bar, gen, published, spin_limit);
       gen += 1u;
     }
