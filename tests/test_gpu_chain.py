@@ -114,6 +114,31 @@ def test_ragged_chain():
         check_chain(spec, "chain_ragged", M, f"ragged M={M}")
 
 
+def test_attention_gather_element_by_element():
+    # value blocks that start off a multiple of 4 inputs, or heads that are
+    # not a multiple of 8 inputs, are gathered element by element
+    spec = [
+        ("a", 700, 256, "x0", None, False),
+        ("b", 300, 640, "attn1", (301, 20, 4), True),    # 32 heads of 20 over 8 kv heads, odd offset
+        ("c", 500, 256, "attn1", (2, 64, 2), False),     # 4 heads of 64 over 2 kv heads, offset 2
+    ]
+    for M in (1, 2):
+        check_chain(spec, "chain_gather", M, f"gather M={M}")
+
+
+@pytest.mark.parametrize("M", [1, 2])
+def test_long_inputs_staged_in_several_passes(M):
+    # inputs longer than one staging pass (2048 octets of 8 per row set):
+    # SwiGLU over 17408 (M = 1) or 9216 (M = 2) inputs, then a plain one
+    K = 17408 if M == 1 else 9216
+    spec = [
+        ("a", 2 * K, 256, "x0", None, False),
+        ("b", 400, K, "swiglu", None, True),
+        ("c", 256, 384, "prev", None, False),
+    ]
+    check_chain(spec, "chain_long", M, f"long inputs M={M}")
+
+
 def test_llama8b_decoder_layer_chain():
     # the Llama-3-8B-shaped layer: 32 q / 8 kv heads of 128, SwiGLU 14336
     spec = [
