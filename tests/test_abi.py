@@ -344,3 +344,61 @@ def test_valid_call_without_a_device_is_unsupported():
     assert lib.w4a16_gemv_workspace_bytes(16, 4096, 14336, ctypes.byref(n)) == UNSUPPORTED and n.value == 0
     assert lib.w4a16_pack(p(FAKE), 16, 256, 256, p(0), p(FAKE), p(FAKE), p(FAKE), p(0)) == UNSUPPORTED
     assert lib.w4a16_awq_fold(p(FAKE), 8, p(FAKE), p(0), p(0)) == UNSUPPORTED
+
+
+def _chain(specs):
+    """A host array of chain linears at fake, well-separated device addresses;
+    specs: dicts overriding the defaults of each linear."""
+    arr = (w4.ChainLinearC * len(specs))()
+    for i, sp in enumerate(specs):
+        base = FAKE * (16 + 64 * i)
+        d = dict(codes=base, scales=base + (1 << 24), zeros=base + (2 << 24), gamma=0, Y=base + (3 << 24),
+                 N=1024, K=1024, ldy=1024, input=0 if i == 0 else 1, v_offset=0, head_dim=0, group=0)
+        d.update(sp)
+        for k, v in d.items():
+            setattr(arr[i], k, v)
+    return arr
+
+
+def chain_prepare(specs, M=1, ws=FAKE * 8192, nbytes=1 << 20):
+    arr = _chain(specs)
+    plan = w4.ChainPlanC()
+    return lib.w4a16_chain_prepare(arr, len(specs), M, p(ws), nbytes, ctypes.byref(plan), p(0))
+
+
+def test_chain_validation():
+    two = [{}, {}]
+    assert chain_prepare([]) == INVALID                          # no linears
+    assert chain_prepare(two, M=0) == INVALID
+    assert chain_prepare(two, M=3) == INVALID                    # W4A16_CHAIN_MAX_M
+    assert chain_prepare(two, nbytes=64) == INVALID              # workspace too small
+    assert chain_prepare(two, ws=FAKE * 8192 + 128) == MISALIGNED
+    assert chain_prepare([{"input": 1}, {}]) == INVALID          # the first linear takes X0
+    assert chain_prepare([{}, {"K": 1000}]) == INVALID           # K % 128
+    assert chain_prepare([{}, {"K": 2048}]) == INVALID           # PREV wider than the previous output
+    assert chain_prepare([{"N": 2048}, {"input": 2, "K": 1152}]) == INVALID   # SwiGLU needs 2K outputs
+    assert chain_prepare([{}, {"input": 3, "K": 512, "head_dim": 0, "group": 1}]) == INVALID
+    assert chain_prepare([{}, {"input": 3, "K": 512, "head_dim": 128, "group": 1,
+                               "v_offset": 600}]) == INVALID     # value block past the previous output
+    assert chain_prepare([{}, {"input": 4}]) == INVALID          # unknown input kind
+    assert chain_prepare([{}, {"ldy": 1000}]) == INVALID         # ldy < N
+    assert chain_prepare([{}, {"ldy": 1028, "N": 1028}]) == MISALIGNED   # ldy % 8
+    assert chain_prepare([{}, {"Y": FAKE * 80 + 8}]) == MISALIGNED
+    assert chain_prepare([{}, {"gamma": FAKE * 90 + 4}]) == MISALIGNED
+    assert chain_prepare([{"K": 32896}, {}]) == UNSUPPORTED      # W4A16_CHAIN_MAX_K
+    a = _chain(two)
+    assert chain_prepare([{}, {"Y": a[1].codes}]) == INVALID     # output over its own matrix
+    assert chain_prepare([{}, {"Y": a[0].Y}]) == INVALID         # output over its input
+    # every check passes: no device here
+    assert chain_prepare(two) == UNSUPPORTED
+
+
+def test_chain_noalloc_validation():
+    arr = _chain([{}, {}])
+    st = ctypes.c_int(-1)
+    assert lib.w4a16_chain_run_noalloc(arr, 2, 1, p(0), 1024, ctypes.byref(st), p(0)) == INVALID
+    assert lib.w4a16_chain_run_noalloc(arr, 2, 1, p(FAKE + 8), 1024, ctypes.byref(st), p(0)) == MISALIGNED
+    assert lib.w4a16_chain_run_noalloc(arr, 2, 1, p(FAKE), 1020, ctypes.byref(st), p(0)) == MISALIGNED
+    big = _chain([{}] * 257)
+    assert lib.w4a16_chain_run_noalloc(big, 257, 1, p(FAKE), 1024, ctypes.byref(st), p(0)) == UNSUPPORTED
+    assert lib.w4a16_chain_run_noalloc(arr, 2, 1, p(FAKE), 1024, ctypes.byref(st), p(0)) == UNSUPPORTED

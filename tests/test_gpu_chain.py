@@ -139,6 +139,16 @@ def test_long_inputs_staged_in_several_passes(M):
     check_chain(spec, "chain_long", M, f"long inputs M={M}")
 
 
+def test_longest_input_at_two_rows():
+    # the documented maximum input length (32768) at M = 2 (its LDS plan is
+    # exactly the 160 KiB a block may hold)
+    spec = [
+        ("a", 32768, 256, "x0", None, False),
+        ("b", 260, 32768, "prev", None, True),
+    ]
+    check_chain(spec, "chain_max_k", 2, "K = 32768 M=2")
+
+
 def test_llama8b_decoder_layer_chain():
     # the Llama-3-8B-shaped layer: 32 q / 8 kv heads of 128, SwiGLU 14336
     spec = [
