@@ -14,7 +14,10 @@ in one more; the timed region replays K steps (whole rotations, then single
 steps for any remainder) back to back between two device synchronisations.
 
 value = algorithmic bytes per step / time per step, with algorithmic bytes
-= packed codes + BF16 scales + INT32 zeros + X + Y.
+= packed codes + BF16 scales + INT32 zeros + X + Y.  Every figure is timed
+after ~0.05-0.2 s of untimed runs of the same work (W = 4000 warm-up steps
+for the headline): the GPU's clocks rise under sustained load, which the
+vector work of the kernels feels (prefill most, 10-15%; decode a few %).
 
 Also reported (same JSON line):
   roofline      the dominant kernel (the gate_up launch) timed alone with HIP
@@ -48,7 +51,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=600)
-    ap.add_argument("--warmup", type=int, default=60)
+    ap.add_argument("--warmup", type=int, default=4000)   # ~0.12 s of steps: steady clocks
     ap.add_argument("--m", type=int, default=1)
     ap.add_argument("--workload", default="llama8b_decode")
     ap.add_argument("--no-prefill", action="store_true")
@@ -160,8 +163,8 @@ def main():
             with torch.cuda.graph(g, stream=stream):
                 for r in range(reps):
                     linear(xs[i], copies[r % ncopy][i], ys[i])
-            g.replay()
-            stream.synchronize()
+        steady(stream, [g.replay], 0.05)
+        with torch.cuda.stream(stream):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -482,10 +485,11 @@ def measured_traffic(layer, M, name="gemv_llama8b_decode_m1_traffic.json",
     return rec.get("hbm_bytes_per_launch")
 
 
-def decode_sweep(workload, Ms, dev, stream, steps=40):
+def decode_sweep(workload, Ms, dev, stream, steps=40, replays=5):
     """Decode throughput of one layer set at several batch sizes M: the four
     launches of a step in order, replicated weight copies past the last-level
-    cache, a graph of `steps` steps timed with HIP events on its stream."""
+    cache, a graph of `steps` steps replayed for ~0.1 s untimed, then
+    `replays` times timed with HIP events on its stream."""
     import torch
     import int4_weight_only_gemv_amd as w4
     from synth import gen
@@ -513,15 +517,18 @@ def decode_sweep(workload, Ms, dev, stream, steps=40):
                 for s in range(steps):
                     for p, x, y in zip(copies[s % ncopy], xs, ys):
                         w4.w4a16_gemv(x, p, y)
-            g.replay()
-            stream.synchronize()
+        # the matrix-core and dot-product kernels at these M do more vector
+        # work per byte than M = 1: warm the clocks as for prefill
+        steady(stream, [g.replay], 0.1)
+        with torch.cuda.stream(stream):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            g.replay()
+            for _ in range(replays):
+                g.replay()
             e1.record(stream)
             e1.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / steps
+        us = e0.elapsed_time(e1) * 1e3 / (steps * replays)
         nbytes = sum(decode_bytes(L, M) for L in layers)
         gbs = nbytes / (us * 1e-6) / 1e9
         rows.append({"M": M, "us_per_step": round(us, 3), "GBps": round(gbs, 1),
@@ -531,12 +538,14 @@ def decode_sweep(workload, Ms, dev, stream, steps=40):
     del copies, packed
     torch.cuda.synchronize()
     return {"workload": workload, "step_bytes_M1": sum(decode_bytes(L, 1) for L in layers),
-            "rotating_copies": ncopy, "steps_per_graph": steps, "results": rows}
+            "rotating_copies": ncopy, "steps_per_graph": steps, "graph_replays_timed": replays,
+            "results": rows}
 
 
 def _graph_us(stream, body, reps):
     """Average microseconds of `body` over `reps` replays captured in one
-    graph (after one untimed replay), timed with HIP events on `stream`."""
+    graph (after ~0.05 s of untimed replays), timed with HIP events on
+    `stream`."""
     import torch
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(stream):
@@ -545,8 +554,8 @@ def _graph_us(stream, body, reps):
         with torch.cuda.graph(g, stream=stream):
             for r in range(reps):
                 body(r)
-        g.replay()
-        stream.synchronize()
+    steady(stream, [g.replay], 0.05)
+    with torch.cuda.stream(stream):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
