@@ -870,9 +870,8 @@ def stack_decode(tokens, dev, stream, Ms=(1, 8)):
             with torch.cuda.graph(g, stream=stream):
                 for p, x, y in run:
                     w4.w4a16_gemv(x, p, y)
-            for _ in range(3):
-                g.replay()
-            stream.synchronize()
+        steady(stream, [g.replay], 0.1)
+        with torch.cuda.stream(stream):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -932,10 +931,8 @@ def chain_llama8b(dev, stream, steps=200, Ms=(1, 2)):
             outs = pl.outputs
             plans.append(pl)
         x0 = gen.activations(M, layers[0].K, "llama8b_decode", "chain_x0", device=dev)
+        steady(stream, [lambda pl=pl: w4.w4a16_chain_run(pl, x0) for pl in plans], 0.1)
         with torch.cuda.stream(stream):
-            for pl in plans:
-                w4.w4a16_chain_run(pl, x0)
-            stream.synchronize()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -991,10 +988,8 @@ def chain_stack(tokens, dev, stream, Ms=(1, 2)):
     for M in Ms:
         plan = w4.w4a16_chain_prepare(lin, M)
         x0 = gen.activations(M, layers[0].K, cfg, "chain_x0", device=dev)
+        steady(stream, [lambda: w4.w4a16_chain_run(plan, x0)], 0.1)
         with torch.cuda.stream(stream):
-            for _ in range(3):
-                w4.w4a16_chain_run(plan, x0)
-            stream.synchronize()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
