@@ -424,7 +424,8 @@ typedef struct {
 } w4a16_chain_plan;
 
 /* Device workspace bytes for a chain of n_linears (barrier state, status
-   word, descriptors). */
+   word, a 128 KiB region where a linear whose output is exactly [gate | up]
+   of a SwiGLU input leaves that input formed, the descriptors). */
 int w4a16_chain_workspace_bytes(int n_linears, int64_t* bytes);
 
 /*
@@ -466,8 +467,9 @@ int w4a16_chain_status(const w4a16_chain_plan* plan, int* status, void* stream);
  * allocating or taking a workspace, for callers that cannot allocate device
  * memory (code under graph capture, tight serving loops, harnesses that
  * forbid it).  Same chain rules and results as w4a16_chain_prepare +
- * w4a16_chain_run; the barrier state and descriptors live in a fixed device
- * array inside the library (one per GPU, kept until the process ends), so
+ * w4a16_chain_run; the barrier state, the SwiGLU input region and the
+ * descriptors live in a fixed device array inside the library (about 155
+ * KiB, one per GPU, kept until the process ends), so
  * at most W4A16_CHAIN_NOALLOC_MAX_LINEARS linears (more:
  * W4A16_ERR_UNSUPPORTED), and calls that overlap on one GPU race (the
  * caller serialises them, e.g. on one stream).  The descriptors are copied

@@ -361,7 +361,7 @@ constexpr int kChainSliceK = 2048;
 
 int w4a16_chain_workspace_bytes(int n_linears, int64_t* bytes) {
   if (!bytes || n_linears < 1 || n_linears > W4A16_CHAIN_MAX_LINEARS) return W4A16_ERR_INVALID_ARG;
-  *bytes = kChainHeader + (int64_t)n_linears * (int64_t)sizeof(w4a16::ChainDesc);
+  *bytes = w4a16::kChainDescOffset + (int64_t)n_linears * (int64_t)sizeof(w4a16::ChainDesc);
   return W4A16_OK;
 }
 
@@ -414,13 +414,18 @@ int chain_build(const w4a16_chain_linear* L, int n, int64_t M, w4a16::ChainDesc*
     e.codes = a.codes; e.scales = a.scales; e.zeros = a.zeros; e.gamma = a.gamma; e.y = a.Y; e.ldy = a.ldy;
     e.N = (int32_t)a.N; e.K = (int32_t)a.K; e.input = a.input;
     e.v_offset = a.v_offset; e.head_dim = a.head_dim; e.group = a.group;
-    const int64_t batches = (a.N + 3) / 4;
+    // a producer of exactly [gate | up] for a SwiGLU consumer pairs its rows
+    // (gate k and up pair + k in one block) and forms that input once
+    const bool paired = l + 1 < n && L[l + 1].input == W4A16_CHAIN_SWIGLU && a.N == 2 * L[l + 1].K;
+    e.pair = paired ? (int32_t)L[l + 1].K : 0;
+    e.glued = (l > 0 && a.input == W4A16_CHAIN_SWIGLU && L[l - 1].N == 2 * a.K) ? 1 : 0;
+    const int64_t batches = paired ? L[l + 1].K / 4 : (a.N + 3) / 4;
     e.batches_per_block = (int32_t)(batches / grid);
     e.batches_rem = (int32_t)(batches % grid);
     e.slices = (int32_t)((a.K + kChainSliceK - 1) / kChainSliceK);
     e.pad = 0;
     max_k = std::max<int64_t>(max_k, a.K);
-    max_rows = std::max<int64_t>(max_rows, 4 * (e.batches_per_block + (e.batches_rem ? 1 : 0)));
+    max_rows = std::max<int64_t>(max_rows, (paired ? 8 : 4) * (e.batches_per_block + (e.batches_rem ? 1 : 0)));
     max_slices = std::max<int64_t>(max_slices, e.slices);
     if (a.input == W4A16_CHAIN_X0) kx = std::max<int64_t>(kx, a.K);   // the widest read of X0
   }
@@ -453,7 +458,7 @@ int w4a16_chain_prepare(const w4a16_chain_linear* L, int n, int64_t M, void* wor
   hipStream_t s = (hipStream_t)stream;
   char* ws = static_cast<char*>(workspace);
   if (hipMemsetAsync(ws, 0, kChainHeader, s) != hipSuccess ||
-      hipMemcpyAsync(ws + kChainHeader, d.data(), d.size() * sizeof(w4a16::ChainDesc), hipMemcpyHostToDevice, s) !=
+      hipMemcpyAsync(ws + w4a16::kChainDescOffset, d.data(), d.size() * sizeof(w4a16::ChainDesc), hipMemcpyHostToDevice, s) !=
           hipSuccess ||
       hipStreamSynchronize(s) != hipSuccess)
     return W4A16_ERR_HIP;
@@ -487,7 +492,7 @@ int w4a16_chain_run(const w4a16_chain_plan* plan, const uint16_t* X0, int64_t ld
   if (!aligned(X0, 16) || ldx % 8 || !aligned(plan->workspace, 256)) return W4A16_ERR_MISALIGNED;
   if (int dc = device_check()) return dc;
   char* ws = static_cast<char*>(plan->workspace);
-  return w4a16::launch_chain(ws + kChainHeader, plan->n_linears, plan->M, X0, ldx,
+  return w4a16::launch_chain(ws + w4a16::kChainDescOffset, plan->n_linears, plan->M, X0, ldx,
                              reinterpret_cast<unsigned*>(ws), plan->spin_limit, plan->max_k, plan->max_rows,
                              plan->grid, (size_t)plan->lds_bytes, (hipStream_t)stream);
 }

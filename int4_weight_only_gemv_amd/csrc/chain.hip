@@ -99,15 +99,23 @@ __device__ __forceinline__ void unpack4(uint64_t w, float* v) {
 // aligned), form_octet applies the glue.  Single-key attention reads whole
 // octets when heads are a multiple of 8 inputs and the value block starts at
 // a multiple of 4; otherwise form_octet reads it element by element.
+// Staging kind of an input its producer already formed (SwiGLU and the
+// producer weight applied, rounded to BF16) into the workspace's glue region.
+constexpr int kGlued = 4;
+
 __device__ __forceinline__ bool attn_octets(const ChainDesc& d) {
   return d.head_dim % 8 == 0 && d.v_offset % 4 == 0;
 }
 
 template <int KIND>
 __device__ __forceinline__ void fetch_octet(const ChainDesc& d, const ChainDesc* prev, const uint16_t* X0,
-                                            int64_t ldx, int m, int o, uint64_t w[4]) {
+                                            int64_t ldx, const uint16_t* glue, int m, int o, uint64_t w[4]) {
   const int k0 = 8 * o;
-  if constexpr (KIND == W4A16_CHAIN_X0) {
+  if constexpr (KIND == kGlued) {
+    const uint64_t* row = reinterpret_cast<const uint64_t*>(glue + (int64_t)m * d.K);
+    w[0] = ld_coherent64(row + 2 * o);
+    w[1] = ld_coherent64(row + 2 * o + 1);
+  } else if constexpr (KIND == W4A16_CHAIN_X0) {
     const uint64_t* p = reinterpret_cast<const uint64_t*>(X0 + (int64_t)m * ldx + k0);
     w[0] = p[0];
     w[1] = p[1];
@@ -222,7 +230,8 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainDesc* _
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int sw = wave - 1;                      // index of a streaming wave (waves 1 .. 15)
+  const int sw = wave - 1;
+  uint16_t* glue = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(bar) + kChainHeaderBytes);                      // index of a streaming wave (waves 1 .. 15)
   const unsigned nblocks = gridDim.x;
   const int b = blockIdx.x;
   unsigned gen = 0;
@@ -232,9 +241,15 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainDesc* _
   // scalar loads, which wait on their own counter (a vector load here would
   // make the next wait drain the weight stream)
   CDesc* cdesc = (CDesc*)descs;
-  auto block_rows = [&](int per_block, int rem, int& row0, int& nb) {
-    nb = per_block + (b < rem ? 1 : 0);
+  // the block's rows of a linear: nb batches of R from row0 on; a paired
+  // linear (pair > 0) has nb / 2 batches of gate rows from row0 and as many
+  // of up rows from pair + row0, in that order
+  auto block_rows = [&](int per_block, int rem, int pair, int& row0, int& nb) {
+    nb = (per_block + (b < rem ? 1 : 0)) * (pair > 0 ? 2 : 1);
     row0 = R * (b * per_block + min(b, rem));
+  };
+  auto row_of = [&](int pair, int row0, int nb, int li) {   // global row of block-local row li
+    return (pair > 0 && li >= R * (nb / 2)) ? pair + row0 + (li - R * (nb / 2)) : row0 + li;
   };
 
   // The weight stream of a streaming wave: its items of every linear in
@@ -251,7 +266,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainDesc* _
   uint16_t sb[kRing];
   int zb[kRing];
   auto items_of = [&](int l) {
-    const int nb = cdesc[l].batches_per_block + (b < cdesc[l].batches_rem ? 1 : 0);
+    const int nb = (cdesc[l].batches_per_block + (b < cdesc[l].batches_rem ? 1 : 0)) * (cdesc[l].pair > 0 ? 2 : 1);
     return nb * cdesc[l].slices;
   };
   auto entries_of = [&](int l) {
@@ -275,12 +290,12 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainDesc* _
     if (cl < n_linears && it < items_of(cl)) {
       const int K = cdesc[cl].K, slices = cdesc[cl].slices;
       int row0, nb;
-      block_rows(cdesc[cl].batches_per_block, cdesc[cl].batches_rem, row0, nb);
+      block_rows(cdesc[cl].batches_per_block, cdesc[cl].batches_rem, cdesc[cl].pair, row0, nb);
       const int batch = it / slices, sl = it - batch * slices;
       const int c = min(sl * 64 + lane, K / 32 - 1);   // inactive lanes read valid memory
       vrow = K / 32;
       G = K / kGroup;
-      rowb = row0 + batch * R;
+      rowb = row_of(cdesc[cl].pair, row0, nb, batch * R);   // a batch never straddles the halves
       nmax = cdesc[cl].N - 1;
       c4 = c / 4;
       cbase = reinterpret_cast<const u32x4*>(cdesc[cl].codes) + c;
@@ -306,8 +321,20 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainDesc* _
     const ChainDesc d = descs[l];
     const ChainDesc* prev = l > 0 ? descs + (l - 1) : nullptr;
     int row0, nb;
-    block_rows(d.batches_per_block, d.batches_rem, row0, nb);
+    block_rows(d.batches_per_block, d.batches_rem, d.pair, row0, nb);
     const int items = nb * d.slices;
+    // a paired producer: wave 0 fetches the next producer weight of its
+    // first two passes of gate-row pairs now, while it has nothing in flight
+    const int half = R * (nb / 2);
+    const uint16_t* gnext = d.pair > 0 ? descs[l + 1].gamma : nullptr;
+    uint32_t gpre[2] = {0x3F803F80u, 0x3F803F80u};   // BF16 (1, 1) without a producer weight
+    if (wave == 0 && gnext) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int e = lane + 64 * q;
+        if (e < (half / 2) * M) gpre[q] = *reinterpret_cast<const uint32_t*>(gnext + row0 + 2 * (e / M));
+      }
+    }
 
     // ---- stage X_l: octets (8 inputs) of the activation rows, kStageU per
     // thread and pass with all their loads issued first; the four lanes of a
@@ -333,8 +360,8 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainDesc* _
           if (e < M * octs) {
             int m, o;
             octet_of(e, m, o);
-            if constexpr (KIND >= 0) fetch_octet<KIND>(d, prev, X0, ldx, m, o, w[u]);
-            if (d.gamma) gw[u] = *reinterpret_cast<const u32x4*>(d.gamma + 8 * o);
+            if constexpr (KIND >= 0) fetch_octet<KIND>(d, prev, X0, ldx, glue, m, o, w[u]);
+            if (KIND != kGlued && d.gamma) gw[u] = *reinterpret_cast<const u32x4*>(d.gamma + 8 * o);
           }
         });
         static_for<0, kStageU>([&](auto uu) {
@@ -345,7 +372,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainDesc* _
             octet_of(e, m, o);
             float v[8];
             form_octet<KIND>(d, prev, m, o, w[u], v);
-            if (d.gamma) {
+            if (KIND != kGlued && d.gamma) {
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
                 v[2 * j] *= lo16(gw[u][j]);
@@ -370,7 +397,10 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainDesc* _
     };
     if (d.input == W4A16_CHAIN_X0) stage(Ic<W4A16_CHAIN_X0>{});
     else if (d.input == W4A16_CHAIN_PREV) stage(Ic<W4A16_CHAIN_PREV>{});
-    else if (d.input == W4A16_CHAIN_SWIGLU) stage(Ic<W4A16_CHAIN_SWIGLU>{});
+    else if (d.input == W4A16_CHAIN_SWIGLU) {
+      if (d.glued) stage(Ic<kGlued>{});
+      else stage(Ic<W4A16_CHAIN_SWIGLU>{});
+    }
     else if (attn_octets(d)) stage(Ic<W4A16_CHAIN_ATTN1>{});
     else stage(Ic<-1>{});
     block_sync_lds();
@@ -495,7 +525,39 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(const ChainDesc* _
     // odd last row of the linear updates its half of the word atomically),
     // then the grid barrier; the streaming waves wait at the block barrier
     // with their next loads in flight
-    if (wave == 0) {
+    if (wave == 0 && d.pair > 0) {
+      // paired rows, per pass a pair of gate rows r, r + 1 and their up rows:
+      // the four outputs stored, and the next input k = row0 + r, r + 1
+      // formed from the stored BF16 values (silu(g) u times the next
+      // producer weight, the float32 steps of the SwiGLU staging, rounded to
+      // BF16) into the glue region [m][pair]
+      auto row_value = [&](int r, int m) {
+        float v = red[(size_t)r * M + m];
+        for (int sl = 1; sl < d.slices; ++sl) v += red[((size_t)sl * max_rows + r) * M + m];
+        return (uint32_t)f32_to_bf16_rne(v);
+      };
+      auto swiglu = [&](uint32_t gb, uint32_t ub, float gamma) {
+        const float g = bf16_to_f32(gb), u = bf16_to_f32(ub);
+        float v = g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
+        if (gnext) v *= gamma;
+        return (uint32_t)f32_to_bf16_rne(v);
+      };
+      unsigned* gwords = reinterpret_cast<unsigned*>(glue);
+      int q = 0;
+      for (int e = lane; e < (half / 2) * M; e += 64, ++q) {
+        const int r = 2 * (e / M), m = e - (e / M) * M;
+        const uint32_t g0 = row_value(r, m), g1 = row_value(r + 1, m);
+        const uint32_t u0 = row_value(half + r, m), u1 = row_value(half + r + 1, m);
+        uint16_t* yrow = d.y + (int64_t)m * d.ldy;
+        st_coherent(reinterpret_cast<unsigned*>(yrow + row0 + r), g0 | (g1 << 16));
+        st_coherent(reinterpret_cast<unsigned*>(yrow + d.pair + row0 + r), u0 | (u1 << 16));
+        const uint32_t gw = q == 0   ? gpre[0]
+                            : q == 1 ? gpre[1]
+                                     : (gnext ? *reinterpret_cast<const uint32_t*>(gnext + row0 + r) : 0x3F803F80u);
+        st_coherent(gwords + ((int64_t)m * d.pair + row0 + r) / 2,
+                    swiglu(g0, u0, lo16(gw)) | (swiglu(g1, u1, hi16(gw)) << 16));
+      }
+    } else if (wave == 0) {
       const int rows = min(R * nb, d.N - row0);
       auto row_value = [&](int r, int m) {
         float v = red[(size_t)r * M + m];
@@ -558,7 +620,7 @@ int launch_chain(const void* descs, int n_linears, int M, const uint16_t* X0, in
 
 namespace {
 
-constexpr int64_t kScratchBytes = kChainHeaderBytes + (int64_t)W4A16_CHAIN_NOALLOC_MAX_LINEARS * sizeof(ChainDesc);
+constexpr int64_t kScratchBytes = kChainDescOffset + (int64_t)W4A16_CHAIN_NOALLOC_MAX_LINEARS * sizeof(ChainDesc);
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 // Device address of `scratch` on each device, looked up once per device with
@@ -590,14 +652,14 @@ int launch_chain_noalloc(const ChainDesc* d, int n_linears, int M, const uint16_
   if (!ws) return 4;
   // descriptors: the host copy (the caller's stack) must be consumed before
   // this call returns, so the copy is waited for
-  if (hipMemcpyAsync(ws + kChainHeaderBytes, d, (size_t)n_linears * sizeof(ChainDesc), hipMemcpyHostToDevice,
+  if (hipMemcpyAsync(ws + kChainDescOffset, d, (size_t)n_linears * sizeof(ChainDesc), hipMemcpyHostToDevice,
                      stream) != hipSuccess ||
       hipStreamSynchronize(stream) != hipSuccess)
     return 4;
   hipLaunchKernelGGL(clear_words_kernel, dim3(1), dim3(256), 0, stream, reinterpret_cast<unsigned*>(ws),
                      (int)(kChainHeaderBytes / 4));
   if (hipGetLastError() != hipSuccess) return 4;
-  if (int st = launch_chain(ws + kChainHeaderBytes, n_linears, M, X0, ldx, reinterpret_cast<unsigned*>(ws),
+  if (int st = launch_chain(ws + kChainDescOffset, n_linears, M, X0, ldx, reinterpret_cast<unsigned*>(ws),
                             W4A16_CHAIN_SPIN_LIMIT, max_k, max_rows, grid, lds_bytes, stream))
     return st;
   if (status) {
