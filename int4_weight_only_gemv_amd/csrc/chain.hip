@@ -24,9 +24,11 @@
 //       on into the next linears, so the weight stream continues through
 //       the steps below;
 //     the control wave adds the K slices of each row in LDS in a fixed
-//       order, stores Y_l in BF16, waits for its stores and meets the other
-//       blocks at a grid barrier while the streaming waves wait at a block
-//       barrier with their loads in flight.
+//       order, stores Y_l in BF16 (a producer of exactly [gate | up] for a
+//       SwiGLU input owns gate and up rows k, K' + k and also stores that
+//       input, formed once, in the workspace's glue region), waits for its
+//       stores and meets the other blocks at a grid barrier while the
+//       streaming waves wait at a block barrier with their loads in flight.
 //
 // The outputs pass between blocks (and the XCDs' separate L2 caches) as
 // agent-scope atomic stores (32-bit) and loads (32- and 64-bit), coherent across the
