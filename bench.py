@@ -114,8 +114,10 @@ def main():
     step_bytes = sum(decode_bytes(L, M) for L in layers)
 
     # ---- HIP graphs: one per copy (the four launches of one step) and one
-    # for a whole rotation through the copies (ncopy steps in order), so the
-    # host submits one graph per ncopy steps instead of one per step
+    # for `rpg` whole rotations through the copies (ncopy steps in order,
+    # ~40 steps per graph), so the host submits one graph per ~40 steps
+    # instead of one per step (each graph launch costs some GPU time of its
+    # own: ~1 us per step with one rotation of 10 steps per graph)
     stream = torch.cuda.Stream()
     graphs = []
     with torch.cuda.stream(stream):
@@ -129,19 +131,22 @@ def main():
                 for p, x, y in zip(copies[c], xs, ys):
                     linear(x, p, y)
             graphs.append(g)
+        rpg = max(1, round(40 / ncopy))
         rotation = torch.cuda.CUDAGraph()
         with torch.cuda.graph(rotation, stream=stream):
-            for c in range(ncopy):
-                for p, x, y in zip(copies[c], xs, ys):
-                    linear(x, p, y)
+            for _ in range(rpg):
+                for c in range(ncopy):
+                    for p, x, y in zip(copies[c], xs, ys):
+                        linear(x, p, y)
     torch.cuda.synchronize()
+    per_graph = rpg * ncopy
 
     def run_steps(n):
-        """n decode steps, copy (s mod ncopy) at step s, as whole rotations
-        plus single steps for the remainder."""
-        for _ in range(n // ncopy):
+        """n decode steps, copy (s mod ncopy) at step s, as graphs of whole
+        rotations plus single steps for the remainder."""
+        for _ in range(n // per_graph):
             rotation.replay()
-        for s in range(n - n % ncopy, n):
+        for s in range(n - n % per_graph, n):
             graphs[s % ncopy].replay()
 
     with torch.cuda.stream(stream):
@@ -342,7 +347,7 @@ def main():
         "dtype_detail": "bf16 activations x int4 weights (exact bf16 operands 128+q), fp32 accumulate, bf16 output",
         "data": "synthetic",
         "config": {"workload": workload_label(args.workload, spec),
-                   "M": M, "step_bytes": step_bytes, "rotating_copies": ncopy,
+                   "M": M, "step_bytes": step_bytes, "rotating_copies": ncopy, "steps_per_graph": per_graph,
                    "parallelism": "single GPU",
                    "headline_choice": "value is the decode step of the Llama-3-8B-shaped layer set at M=1, "
                                       "the configuration the metric is quoted on; the "
