@@ -139,6 +139,19 @@ def test_long_inputs_staged_in_several_passes(M):
     check_chain(spec, "chain_long", M, f"long inputs M={M}")
 
 
+def test_paired_swiglu_producer_with_few_rows():
+    # [gate | up] of 2 x 256 rows: 64 gate batches, so most blocks own none;
+    # the consumer's producer weight is applied where the input is formed
+    spec = [
+        ("a", 512, 384, "x0", None, False),
+        ("b", 300, 256, "swiglu", None, True),
+        ("c", 2 * 640, 300 - 300 % 128, "prev", None, False),
+        ("d", 200, 640, "swiglu", None, False),
+    ]
+    for M in (1, 2):
+        check_chain(spec, "chain_pair_few", M, f"paired few rows M={M}")
+
+
 def test_longest_input_at_two_rows():
     # the documented maximum input length (32768) at M = 2 (its LDS plan is
     # exactly the 160 KiB a block may hold)
